@@ -1,0 +1,368 @@
+"""CPU oracle for scaled quantize / dequantize / STE backward.
+
+TEST INFRASTRUCTURE ONLY.  The product path (``tensor_quantization_amd``)
+never imports this package; only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` use it.  It wraps ``tq_oracle.c``
+(plain scalar C, binary32 arithmetic, ``-ffp-contract=off``) with numpy
+arrays.  Float tensors of type f16 / bf16 are passed as ``uint16`` bit
+patterns, f32 as ``float32``.
+
+Every function states the definition it follows in ``tq_oracle.c``; the
+readings taken where the pages are silent are documented there and in
+the design doc.  Functions pinned to outside facts are listed in the tests
+(``tests/test_oracle_*.py``); the choices the pages leave open (NVFP4 scale
+bits, MX clipping, the asymmetric formula, degenerate groups) are pinned only
+by internal invariants -- "parity unpinned" against any outside source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+FTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+CODES = {"s8": 0, "u8": 1, "s4": 2, "u4": 3}
+GRANS = {"tensor": 0, "channel": 1, "token": 2, "group": 3}
+FP4_KINDS = {"nvfp4": 0, "mxfp4": 1}
+FP4_GROUP = {"nvfp4": 16, "mxfp4": 32}
+
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(_LIB_PATH)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _shape_arr(shape):
+    return (ctypes.c_int64 * len(shape))(*shape)
+
+
+def _storage(ft):
+    return np.float32 if ft == "f32" else np.uint16
+
+
+def _check_float(x, ft):
+    assert x.dtype == _storage(ft), (x.dtype, ft)
+    return np.ascontiguousarray(x)
+
+
+def code_bits(code):
+    return 4 if code in ("s4", "u4") else 8
+
+
+def default_q_range(code, symmetric):
+    """docs.rs quantize::default_q_range (S8 [-128,127], U8 [0,255]), the
+    4-bit widths alongside, and the symmetric reading [-qmax, qmax]."""
+    qmin, qmax = ctypes.c_int(), ctypes.c_int()
+    rc = lib().orc_default_q_range(CODES[code], int(bool(symmetric)), ctypes.byref(qmin), ctypes.byref(qmax))
+    if rc:
+        raise ValueError("no default range for %s symmetric=%s" % (code, symmetric))
+    return qmin.value, qmax.value
+
+
+def packed_shape(shape, code):
+    shape = tuple(shape)
+    if code_bits(code) == 4:
+        return shape[:-1] + (shape[-1] // 2,)
+    return shape
+
+
+def scale_shape(shape, gran, axis=0, group_size=0):
+    shape = tuple(shape)
+    if gran == "tensor":
+        return (1,)
+    if gran == "token":
+        return (int(np.prod(shape[:-1], dtype=np.int64)),)
+    if gran == "channel":
+        return (shape[axis],)
+    s = list(shape)
+    s[axis] //= group_size
+    return tuple(s)
+
+
+def _gran_args(gran, axis, group_size):
+    return GRANS[gran], int(axis), int(group_size)
+
+
+# ----------------------------------------------------------------- integer
+def quant_int(x, xt, gran, axis=0, group_size=0, code="s8", qmin=None, qmax=None,
+              symmetric=True, scale=None, zp=None):
+    """Quantize to integer codes.  Returns (q, scale, zp); q is packed two
+    per byte along the last dim for 4-bit codes; zp is None if symmetric.
+    Pass ``scale`` (and ``zp``) to quantize with static parameters."""
+    x = _check_float(x, xt)
+    if qmin is None:
+        qmin, qmax = default_q_range(code, symmetric)
+    sshape = scale_shape(x.shape, gran, axis, group_size)
+    static = scale is not None
+    q = np.zeros(packed_shape(x.shape, code), np.uint8)
+    s = np.ascontiguousarray(scale, np.float32).copy() if static else np.zeros(sshape, np.float32)
+    if symmetric:
+        z = None
+    else:
+        z = np.ascontiguousarray(zp).view(np.uint8).copy() if static else np.zeros(sshape, np.uint8)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_quant_int(_p(x), FTYPES[xt], x.ndim, _shape_arr(x.shape), g, a,
+                             ctypes.c_int64(gsz), CODES[code], qmin, qmax, int(bool(symmetric)),
+                             int(static), _p(q), _p(s), _p(z))
+    if rc:
+        raise ValueError("oracle rejected quant_int arguments")
+    if z is not None and code in ("s8", "s4"):
+        z = z.view(np.int8)
+    return q, s, z
+
+
+def dequant_int(q, code, shape, gran, axis=0, group_size=0, scale=None, zp=None, yt="f32"):
+    q = np.ascontiguousarray(q, np.uint8)
+    y = np.zeros(tuple(shape), _storage(yt))
+    zpa = None if zp is None else np.ascontiguousarray(zp).view(np.uint8)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_dequant_int(_p(q), CODES[code], len(shape), _shape_arr(shape), g, a,
+                               ctypes.c_int64(gsz), _p(np.ascontiguousarray(scale, np.float32)),
+                               _p(zpa), _p(y), FTYPES[yt])
+    if rc:
+        raise ValueError("oracle rejected dequant_int arguments")
+    return y
+
+
+def quant_int_backward(x, xt, gran, axis=0, group_size=0, code="s8", qmin=None, qmax=None,
+                       symmetric=True, scale=None, zp=None, dy=None):
+    x = _check_float(x, xt)
+    dy = _check_float(dy, xt)
+    if qmin is None:
+        qmin, qmax = default_q_range(code, symmetric)
+    dx = np.zeros(x.shape, _storage(xt))
+    zpa = None if zp is None else np.ascontiguousarray(zp).view(np.uint8)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_quant_int_backward(_p(x), FTYPES[xt], x.ndim, _shape_arr(x.shape), g, a,
+                                      ctypes.c_int64(gsz), qmin, qmax,
+                                      _p(np.ascontiguousarray(scale, np.float32)), _p(zpa),
+                                      CODES[code], _p(dy), _p(dx))
+    if rc:
+        raise ValueError("oracle rejected quant_int_backward arguments")
+    return dx
+
+
+def dequant_int_backward(dy, dyt, gran, axis=0, group_size=0, scale=None):
+    dy = _check_float(dy, dyt)
+    dq = np.zeros(dy.shape, _storage(dyt))
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_dequant_int_backward(_p(dy), FTYPES[dyt], dy.ndim, _shape_arr(dy.shape), g, a,
+                                        ctypes.c_int64(gsz),
+                                        _p(np.ascontiguousarray(scale, np.float32)), _p(dq))
+    if rc:
+        raise ValueError("oracle rejected dequant_int_backward arguments")
+    return dq
+
+
+# ----------------------------------------------------------------- FP8
+def quant_fp8_block(x, xt, block_rows, block_cols):
+    x = _check_float(x, xt)
+    rows, cols = x.shape
+    q = np.zeros((rows, cols), np.uint8)
+    s = np.zeros((rows // block_rows, cols // block_cols), np.float32)
+    rc = lib().orc_quant_fp8_block(_p(x), FTYPES[xt], ctypes.c_int64(rows), ctypes.c_int64(cols),
+                                   ctypes.c_int64(block_rows), ctypes.c_int64(block_cols), _p(q), _p(s))
+    if rc:
+        raise ValueError("oracle rejected quant_fp8_block arguments")
+    return q, s
+
+
+def dequant_fp8_block(q, block_rows, block_cols, scale, yt):
+    q = np.ascontiguousarray(q, np.uint8)
+    rows, cols = q.shape
+    y = np.zeros((rows, cols), _storage(yt))
+    rc = lib().orc_dequant_fp8_block(_p(q), ctypes.c_int64(rows), ctypes.c_int64(cols),
+                                     ctypes.c_int64(block_rows), ctypes.c_int64(block_cols),
+                                     _p(np.ascontiguousarray(scale, np.float32)), _p(y), FTYPES[yt])
+    if rc:
+        raise ValueError("oracle rejected dequant_fp8_block arguments")
+    return y
+
+
+def quant_fp8_block_backward(x, xt, block_rows, block_cols, scale, dy):
+    x = _check_float(x, xt)
+    dy = _check_float(dy, xt)
+    rows, cols = x.shape
+    dx = np.zeros((rows, cols), _storage(xt))
+    rc = lib().orc_quant_fp8_block_backward(_p(x), FTYPES[xt], ctypes.c_int64(rows), ctypes.c_int64(cols),
+                                            ctypes.c_int64(block_rows), ctypes.c_int64(block_cols),
+                                            _p(np.ascontiguousarray(scale, np.float32)), _p(dy), _p(dx))
+    if rc:
+        raise ValueError("oracle rejected quant_fp8_block_backward arguments")
+    return dx
+
+
+def dequant_fp8_block_backward(dy, dyt, block_rows, block_cols, scale):
+    dy = _check_float(dy, dyt)
+    rows, cols = dy.shape
+    dq = np.zeros((rows, cols), _storage(dyt))
+    rc = lib().orc_dequant_fp8_block_backward(_p(dy), FTYPES[dyt], ctypes.c_int64(rows), ctypes.c_int64(cols),
+                                              ctypes.c_int64(block_rows), ctypes.c_int64(block_cols),
+                                              _p(np.ascontiguousarray(scale, np.float32)), _p(dq))
+    if rc:
+        raise ValueError("oracle rejected dequant_fp8_block_backward arguments")
+    return dq
+
+
+# ----------------------------------------------------------------- FP4
+def quant_fp4_block(x, xt, kind, static_global=None):
+    """Returns (packed [rows, K/2] u8, block scales [rows, K/gs] u8,
+    global scale float32 (NVFP4; 1.0 for MXFP4))."""
+    x = _check_float(x, xt)
+    rows, k = x.shape
+    gs = FP4_GROUP[kind]
+    packed = np.zeros((rows, k // 2), np.uint8)
+    bs = np.zeros((rows, k // gs), np.uint8)
+    sg = np.array([1.0 if static_global is None else static_global], np.float32)
+    rc = lib().orc_quant_fp4_block(_p(x), FTYPES[xt], ctypes.c_int64(rows), ctypes.c_int64(k),
+                                   FP4_KINDS[kind], _p(packed), _p(bs), _p(sg),
+                                   int(static_global is not None))
+    if rc:
+        raise ValueError("oracle rejected quant_fp4_block arguments")
+    return packed, bs, sg
+
+
+def dequant_fp4_block(packed, bscale, global_scale, kind, yt):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    rows, kb = packed.shape
+    k = kb * 2
+    y = np.zeros((rows, k), _storage(yt))
+    sg = np.asarray([global_scale], np.float32).reshape(1)
+    rc = lib().orc_dequant_fp4_block(_p(packed), _p(np.ascontiguousarray(bscale, np.uint8)), _p(sg),
+                                     ctypes.c_int64(rows), ctypes.c_int64(k), FP4_KINDS[kind], _p(y),
+                                     FTYPES[yt])
+    if rc:
+        raise ValueError("oracle rejected dequant_fp4_block arguments")
+    return y
+
+
+def quant_fp4_block_backward(x, xt, bscale, global_scale, kind, dy):
+    x = _check_float(x, xt)
+    dy = _check_float(dy, xt)
+    rows, k = x.shape
+    dx = np.zeros((rows, k), _storage(xt))
+    sg = np.asarray([global_scale], np.float32).reshape(1)
+    rc = lib().orc_quant_fp4_block_backward(_p(x), FTYPES[xt], _p(np.ascontiguousarray(bscale, np.uint8)),
+                                            _p(sg), ctypes.c_int64(rows), ctypes.c_int64(k),
+                                            FP4_KINDS[kind], _p(dy), _p(dx))
+    if rc:
+        raise ValueError("oracle rejected quant_fp4_block_backward arguments")
+    return dx
+
+
+def dequant_fp4_block_backward(dy, dyt, bscale, global_scale, kind):
+    dy = _check_float(dy, dyt)
+    rows, k = dy.shape
+    dq = np.zeros((rows, k), _storage(dyt))
+    sg = np.asarray([global_scale], np.float32).reshape(1)
+    rc = lib().orc_dequant_fp4_block_backward(_p(dy), FTYPES[dyt], _p(np.ascontiguousarray(bscale, np.uint8)),
+                                              _p(sg), ctypes.c_int64(rows), ctypes.c_int64(k),
+                                              FP4_KINDS[kind], _p(dq))
+    if rc:
+        raise ValueError("oracle rejected dequant_fp4_block_backward arguments")
+    return dq
+
+
+def fp4_transpose_for_gemm(packed, bscale, n, k, gs):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    bscale = np.ascontiguousarray(bscale, np.uint8)
+    pt = np.zeros((k // 2, n), np.uint8)
+    st = np.zeros((k // gs, n), np.uint8)
+    rc = lib().orc_fp4_transpose_for_gemm(_p(packed), _p(bscale), ctypes.c_int64(n), ctypes.c_int64(k),
+                                          ctypes.c_int64(gs), _p(pt), _p(st))
+    if rc:
+        raise ValueError("oracle rejected fp4_transpose_for_gemm arguments")
+    return pt, st
+
+
+# ----------------------------------------------------------------- scalars
+def _map_f32(fn, v, out_dtype):
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.zeros(v.shape, out_dtype)
+    getattr(lib(), fn)(_p(v), ctypes.c_int64(v.size), _p(out))
+    return out
+
+
+def enc_e4m3(v):
+    return _map_f32("orc_enc_e4m3_array", v, np.uint8)
+
+
+def enc_e2m1(v):
+    return _map_f32("orc_enc_e2m1_array", v, np.uint8)
+
+
+def enc_e8m0_mx(amax):
+    return _map_f32("orc_enc_e8m0_mx_array", amax, np.uint8)
+
+
+def narrow_bf16(v):
+    return _map_f32("orc_narrow_bf16_array", v, np.uint16)
+
+
+def narrow_f16(v):
+    return _map_f32("orc_narrow_f16_array", v, np.uint16)
+
+
+def f16_to_f32(h):
+    h = np.ascontiguousarray(h, np.uint16)
+    out = np.zeros(h.shape, np.float32)
+    lib().orc_f16_to_f32_array(_p(h), ctypes.c_int64(h.size), _p(out))
+    return out
+
+
+def bf16_to_f32(h):
+    return (np.ascontiguousarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def dec_e4m3_table():
+    f = lib().orc_dec_e4m3
+    f.restype = ctypes.c_float
+    return np.array([f(ctypes.c_uint8(c)) for c in range(256)], np.float32)
+
+
+def dec_e2m1_table():
+    f = lib().orc_dec_e2m1
+    f.restype = ctypes.c_float
+    return np.array([f(ctypes.c_uint8(c)) for c in range(16)], np.float32)
+
+
+def dec_e8m0(b):
+    f = lib().orc_dec_e8m0
+    f.restype = ctypes.c_float
+    return np.float32(f(ctypes.c_uint8(int(b))))
+
+
+def widen(x, xt):
+    """Float tensor storage -> float32 values (exact)."""
+    if xt == "f32":
+        return np.asarray(x, np.float32)
+    if xt == "bf16":
+        return bf16_to_f32(x)
+    return f16_to_f32(x)
