@@ -1,0 +1,274 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) scaled-quantization library.
+ *
+ * Operations: quantize, dequantize, the straight-through-estimator (STE)
+ * backward of quantize, and the backward of dequantize, for
+ *   - integer codes (s8 / u8 / s4 / u4) at per-tensor, per-channel,
+ *     per-token (per-row) and per-group granularity,
+ *   - FP8 E4M3 with one fp32 scale per block (1x128 activation groups,
+ *     128x128 weight tiles, or any block that tiles the matrix),
+ *   - FP4 E2M1 packed two per byte with NVFP4 (E4M3 block scale per 16 plus
+ *     an fp32 per-tensor scale) or MXFP4 (E8M0 block scale per 32) scales,
+ *   - the FP4 transposes to GEMM layout.
+ *
+ * Sources (page titles and sections):
+ *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
+ *        coverage; per-token and per-group GPTQ-style g=128 families; the STE
+ *        rule dx = (dy / scale) * 1[qmin < q < qmax] with the mask recomputed
+ *        from the saved input), the module list (the *_backward plans of the
+ *        dequantize ops: dq = dy * scale per group), default_q_range.
+ *   [G]  teenygrad granularity.rs -- enum Granularity (PerTensor,
+ *        PerChannel{axis}, Group{axis, group_size}).
+ *   [W]  metrale QuantizedWeight -- fields (packed E2M1 two per byte
+ *        [N, K/2]; block scales E4M3 for NVFP4 / E8M0 for MXFP4; fp32
+ *        per-tensor scale; optional static input scale), transpose_for_gemm
+ *        and transpose_for_gemm_gs.
+ *   [S]  smile.llm.quant package summary -- Fp8BlockGemm (E4M3, one fp32 scale
+ *        per 1x128 activation group and per 128x128 weight tile),
+ *        Fp8BlockDequant, MxFp8 (E8M0 scale per 32 elements).
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless the argument name starts with
+ *     host_.  All buffers are owned by the caller; the library allocates,
+ *     caches and frees nothing and keeps no global state, so calls are
+ *     thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call validates its arguments on the host, enqueues its kernels
+ *     on `stream` and returns without synchronizing.  A non-TQ_OK return
+ *     means nothing was enqueued, except TQ_ERR_HIP, which reports a launch
+ *     failure (hipGetLastError) after an enqueue attempt.
+ *   - Tensors are dense, row-major and contiguous.  Base pointers must be
+ *     16-byte aligned (TQ_ERR_ALIGN otherwise); scale / zero-point arrays need
+ *     only their natural alignment.
+ *   - Float tensors have a tq_ftype (f32, f16, bf16); arithmetic is IEEE
+ *     binary32 with round-to-nearest-even: scale = amax / qmax and
+ *     x / scale are correctly rounded binary32 divisions, f16 / bf16 outputs
+ *     are rounded once from the binary32 result.
+ *   - Integer codes: 8-bit codes take one byte each (s8 as two's
+ *     complement); 4-bit codes are packed two per byte along the LAST
+ *     dimension, the even index in the low nibble, so the last dimension
+ *     must be even.  Zero-points are one byte per group in the code's
+ *     unpacked type (u8 for U8/U4, s8 for S8/S4).
+ *   - Symmetric mode (zero_point == NULL) requires qmin == -qmax and a signed
+ *     code; asymmetric mode requires a zero_point array.
+ *   - The input to a quantize call is never modified.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_ERR_INVALID = 1,     /* bad pointer, shape, dtype, range or group size */
+    TQ_ERR_UNSUPPORTED = 2, /* well-formed request this build does not implement */
+    TQ_ERR_ALIGN = 3,       /* a base pointer is not 16-byte aligned */
+    TQ_ERR_HIP = 4          /* the HIP runtime reported a launch error */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_ftype;
+typedef enum { TQ_S8 = 0, TQ_U8 = 1, TQ_S4 = 2, TQ_U4 = 3 } tq_itype;
+typedef enum { TQ_NVFP4 = 0, TQ_MXFP4 = 1 } tq_fp4_kind;
+
+/* Version of this ABI (bumped on any signature change). */
+int tq_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* tq_status_str(int status);
+
+/* default_q_range ([Q], function default_q_range): S8 -> [-128, 127],
+ * U8 -> [0, 255], S4 -> [-8, 7], U4 -> [0, 15] for asymmetric use; in
+ * symmetric mode the range is [-qmax, qmax] (S8 [-127, 127], S4 [-7, 7]) so
+ * the grid is symmetric about zero.  host_qmin / host_qmax are host
+ * pointers.  TQ_ERR_INVALID for an unknown code or symmetric unsigned code. */
+tq_status tq_default_q_range(int code, int symmetric, int32_t* host_qmin, int32_t* host_qmax);
+
+/* Bytes of device workspace a call needs ([Q] per-tensor scope and the NVFP4
+ * per-tensor scale need a grid-wide reduction).  op: 0 = tq_quant_per_tensor,
+ * 1 = tq_quant_fp4_block with a dynamic global scale.  numel = elements. */
+size_t tq_workspace_bytes(int op, int64_t numel);
+
+/* ===================================================================== */
+/* Integer codes                                                          */
+/* ===================================================================== */
+/*
+ * Quantize ([Q] module overview; [G] Granularity).  For every group of
+ * elements that shares one scale:
+ *   symmetric : scale = amax / qmax              (amax = max |x|)
+ *   asymmetric: mn = min(min x, 0), mx = max(max x, 0),
+ *               scale = (mx - mn) / (qmax - qmin),
+ *               zp = clamp(qmin - rne(mn / scale), qmin, qmax)
+ *   a scale of exactly 0 (all-zero group) is replaced by 1;
+ *   each element: q = clamp(rne(x / scale) + zp, qmin, qmax)
+ * (rne = round to nearest integer, ties to even).  Outputs: q (codes),
+ * scale (fp32, one per group), zero_point (one byte per group, asymmetric
+ * mode only).
+ *
+ * Group layouts and output shapes:
+ *   per_tensor : one group; scale[1], zero_point[1].
+ *   per_channel: x of rank ndim with host_shape; one group per index along
+ *                `axis`; scale[shape[axis]].
+ *   per_token  : x viewed as [rows, cols]; one group per row; scale[rows].
+ *   per_group  : `group_size` consecutive indices along `axis` at fixed
+ *                indices of the other axes (GPTQ weight [N, K] with axis 1
+ *                and group_size 128 -> scale [N, K/128]); the scale tensor
+ *                is x's shape with shape[axis] replaced by
+ *                shape[axis] / group_size.  shape[axis] % group_size == 0.
+ */
+
+/* Per-tensor quantize.  static_scale != 0: scale (and zero_point) are
+ * INPUTS (a static activation scale as in [W] field input_scale) and no
+ * reduction runs.  Otherwise the grid-wide reduction uses `workspace`
+ * (device, >= tq_workspace_bytes(0, numel) bytes, contents ignored). */
+tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel,
+                              int code, int32_t qmin, int32_t qmax, int static_scale,
+                              void* q, float* scale, void* zero_point,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* host_shape: host array of ndim (1..8) extents. */
+tq_status tq_quant_per_channel(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape,
+                               int32_t axis, int code, int32_t qmin, int32_t qmax,
+                               void* q, float* scale, void* zero_point, void* stream);
+
+tq_status tq_quant_per_token(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                             int code, int32_t qmin, int32_t qmax,
+                             void* q, float* scale, void* zero_point, void* stream);
+
+tq_status tq_quant_per_group(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape,
+                             int32_t axis, int64_t group_size, int code, int32_t qmin, int32_t qmax,
+                             void* q, float* scale, void* zero_point, void* stream);
+
+/* Dequantize: y = (q - zp) * scale in binary32, rounded once to y_dtype.
+ * zero_point NULL means zp = 0. */
+tq_status tq_dequant_per_tensor(const void* q, int code, int64_t numel, const float* scale,
+                                const void* zero_point, void* y, int y_dtype, void* stream);
+tq_status tq_dequant_per_channel(const void* q, int code, int32_t ndim, const int64_t* host_shape,
+                                 int32_t axis, const float* scale, const void* zero_point,
+                                 void* y, int y_dtype, void* stream);
+tq_status tq_dequant_per_token(const void* q, int code, int64_t rows, int64_t cols,
+                               const float* scale, const void* zero_point,
+                               void* y, int y_dtype, void* stream);
+tq_status tq_dequant_per_group(const void* q, int code, int32_t ndim, const int64_t* host_shape,
+                               int32_t axis, int64_t group_size, const float* scale,
+                               const void* zero_point, void* y, int y_dtype, void* stream);
+
+/* Quantize backward (STE, [Q] module overview): the code q is recomputed
+ * from the saved input x with the saved scale / zero_point (the amax is not
+ * recomputed), then
+ *   dx = (dy / scale) * (qmin < q < qmax ? 1 : 0)
+ * as a binary32 product (a masked element is a zero carrying the sign of
+ * dy / scale), rounded once to x_dtype.  dy and dx have x's dtype and shape. */
+tq_status tq_quant_per_tensor_backward(const void* x, int x_dtype, int64_t numel,
+                                       int code, int32_t qmin, int32_t qmax,
+                                       const float* scale, const void* zero_point,
+                                       const void* dy, void* dx, void* stream);
+tq_status tq_quant_per_channel_backward(const void* x, int x_dtype, int32_t ndim,
+                                        const int64_t* host_shape, int32_t axis,
+                                        int code, int32_t qmin, int32_t qmax,
+                                        const float* scale, const void* zero_point,
+                                        const void* dy, void* dx, void* stream);
+tq_status tq_quant_per_token_backward(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                      int code, int32_t qmin, int32_t qmax,
+                                      const float* scale, const void* zero_point,
+                                      const void* dy, void* dx, void* stream);
+tq_status tq_quant_per_group_backward(const void* x, int x_dtype, int32_t ndim,
+                                      const int64_t* host_shape, int32_t axis, int64_t group_size,
+                                      int code, int32_t qmin, int32_t qmax,
+                                      const float* scale, const void* zero_point,
+                                      const void* dy, void* dx, void* stream);
+
+/* Dequantize backward ([Q] module list): dq = dy * scale of the element's
+ * group (straight-through in the code), binary32 product rounded once to
+ * dy_dtype; dq has dy's dtype and shape. */
+tq_status tq_dequant_per_tensor_backward(const void* dy, int dy_dtype, int64_t numel,
+                                         const float* scale, void* dq, void* stream);
+tq_status tq_dequant_per_channel_backward(const void* dy, int dy_dtype, int32_t ndim,
+                                          const int64_t* host_shape, int32_t axis,
+                                          const float* scale, void* dq, void* stream);
+tq_status tq_dequant_per_token_backward(const void* dy, int dy_dtype, int64_t rows, int64_t cols,
+                                        const float* scale, void* dq, void* stream);
+tq_status tq_dequant_per_group_backward(const void* dy, int dy_dtype, int32_t ndim,
+                                        const int64_t* host_shape, int32_t axis,
+                                        int64_t group_size, const float* scale, void* dq,
+                                        void* stream);
+
+/* ===================================================================== */
+/* FP8 E4M3 blocks ([S] Fp8BlockGemm, Fp8BlockDequant)                    */
+/* ===================================================================== */
+/* x is [rows, cols]; blocks are block_rows x block_cols (1 x 128 for
+ * activations, 128 x 128 for weights); rows % block_rows == 0 and
+ * cols % block_cols == 0.  scale is [rows/block_rows, cols/block_cols] fp32:
+ *   scale = amax / 448 (1 if that is 0),  q = E4M3(x / scale)
+ * with OCP E4M3 (bias 7, max 448), round to nearest even, saturating at
+ * +-448 and keeping the sign of zero.  q is [rows, cols] bytes. */
+tq_status tq_quant_fp8_block(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                             int32_t block_rows, int32_t block_cols,
+                             uint8_t* q, float* scale, void* stream);
+/* y = val(q) * scale, rounded once to y_dtype. */
+tq_status tq_dequant_fp8_block(const uint8_t* q, int64_t rows, int64_t cols,
+                               int32_t block_rows, int32_t block_cols, const float* scale,
+                               void* y, int y_dtype, void* stream);
+/* STE: dx = (dy / scale) * (-448 < val(q) < 448 ? 1 : 0), q recomputed. */
+tq_status tq_quant_fp8_block_backward(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                      int32_t block_rows, int32_t block_cols, const float* scale,
+                                      const void* dy, void* dx, void* stream);
+/* dq = dy * scale. */
+tq_status tq_dequant_fp8_block_backward(const void* dy, int dy_dtype, int64_t rows, int64_t cols,
+                                        int32_t block_rows, int32_t block_cols,
+                                        const float* scale, void* dq, void* stream);
+
+/* ===================================================================== */
+/* FP4 E2M1 blocks ([W] QuantizedWeight fields; [S] MxFp8 for the E8M0 rule) */
+/* ===================================================================== */
+/* x is [rows, k]; blocks of gs = 16 (NVFP4) or 32 (MXFP4) consecutive
+ * elements along k (k % gs == 0).  Outputs: packed [rows, k/2] (two E2M1
+ * codes per byte, even index in the low nibble), block_scale [rows, k/gs]
+ * bytes, and for NVFP4 the fp32 per-tensor scale global_scale[1].
+ *   NVFP4: s_g = amax_tensor / (6 * 448) (1 if 0), or the caller's value when
+ *          static_global != 0 (global_scale is then an input);
+ *          sb = E4M3(amax_block / (6 * s_g)), replaced by 0x38 (1.0) if it
+ *          encodes to zero; eff = val(sb) * s_g.
+ *   MXFP4: sb = E8M0 byte of 2^(floor(log2 amax_block) - 2) (127 if the block
+ *          is all zero), eff = 2^(sb - 127); global_scale is unused (may be
+ *          NULL).
+ *   every element: q = E2M1(x / eff), round to nearest even, saturating at
+ *          +-6, keeping the sign of zero.
+ * The dynamic NVFP4 scale needs `workspace` (>= tq_workspace_bytes(1, rows*k)
+ * bytes); otherwise workspace may be NULL. */
+tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k, int kind,
+                             uint8_t* packed, uint8_t* block_scale, float* global_scale,
+                             int static_global, void* workspace, size_t workspace_bytes,
+                             void* stream);
+/* y = val(q) * eff, rounded once to y_dtype. */
+tq_status tq_dequant_fp4_block(const uint8_t* packed, const uint8_t* block_scale,
+                               const float* global_scale, int64_t rows, int64_t k, int kind,
+                               void* y, int y_dtype, void* stream);
+/* STE: dx = (dy / eff) * (-6 < val(q) < 6 ? 1 : 0), q recomputed from x. */
+tq_status tq_quant_fp4_block_backward(const void* x, int x_dtype, const uint8_t* block_scale,
+                                      const float* global_scale, int64_t rows, int64_t k, int kind,
+                                      const void* dy, void* dx, void* stream);
+/* dq = dy * eff. */
+tq_status tq_dequant_fp4_block_backward(const void* dy, int dy_dtype, const uint8_t* block_scale,
+                                        const float* global_scale, int64_t rows, int64_t k,
+                                        int kind, void* dq, void* stream);
+
+/* GEMM layout ([W] transpose_for_gemm / transpose_for_gemm_gs): byte
+ * transposes packed [n, k/2] -> packed_t [k/2, n] and block_scale
+ * [n, k/group_size] -> block_scale_t [k/group_size, n] into caller-provided
+ * buffers (the page's version allocates new buffers; here the caller owns
+ * them).  Each byte keeps its two nibbles.  block_scale / block_scale_t may
+ * both be NULL to transpose only the codes. */
+tq_status tq_fp4_transpose_for_gemm(const uint8_t* packed, const uint8_t* block_scale,
+                                    int64_t n, int64_t k, int32_t group_size,
+                                    uint8_t* packed_t, uint8_t* block_scale_t, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,328 @@
+// tq_device.h -- device helpers shared by the gfx950 quantization kernels.
+//
+// Everything here is wave64 CDNA4 code: 16-byte global loads, DPP / bpermute
+// team reductions, v_med3 clamps, and the native FP8 / FP4 / bf16
+// conversion instructions.  Arithmetic follows IEEE binary32 with
+// round-to-nearest-even (the kernels are built with -ffp-contract=off and
+// f32 denormals preserved).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+enum FType { F32 = 0, F16 = 1, BF16 = 2 };
+enum Code { S8 = 0, U8 = 1, S4 = 2, U4 = 3 };
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float as_f(uint32_t b) { return __uint_as_float(b); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------- raw I/O
+// Eight consecutive elements of a float tensor: one 16-byte load for the
+// 2-byte types, two for f32.
+template <int FT> struct Raw8 { uint4 w[FT == F32 ? 2 : 1]; };
+
+template <int FT>
+__device__ __forceinline__ Raw8<FT> load8(const void* base, int64_t e)
+{
+    Raw8<FT> r;
+    if constexpr (FT == F32) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + e);
+        r.w[0] = p[0];
+        r.w[1] = p[1];
+    } else {
+        r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Exact widening to binary32.
+template <int FT>
+__device__ __forceinline__ void widen8(const Raw8<FT>& r, float v[8])
+{
+    if constexpr (FT == F32) {
+        v[0] = as_f(r.w[0].x); v[1] = as_f(r.w[0].y); v[2] = as_f(r.w[0].z); v[3] = as_f(r.w[0].w);
+        v[4] = as_f(r.w[1].x); v[5] = as_f(r.w[1].y); v[6] = as_f(r.w[1].z); v[7] = as_f(r.w[1].w);
+    } else if constexpr (FT == BF16) {
+        const uint32_t w[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = as_f(w[i] << 16);
+            v[2 * i + 1] = as_f(w[i] & 0xffff0000u);
+        }
+    } else {
+        const uint32_t w[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = f16_lo(w[i]);
+            v[2 * i + 1] = f16_hi(w[i]);
+        }
+    }
+}
+
+// Makes v opaque to the optimizer.  Used before every narrowing: without it
+// the backend folds "round(a * b) to f16" into v_fma_mix*_f16 with a zero
+// addend, which rounds the exact product once (not the binary32 product) and
+// turns -0 into +0.
+__device__ __forceinline__ float opaque(float v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ uint16_t to_f16_bits(float v)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)opaque(v));
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float v)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)opaque(v));
+}
+
+// Round-to-nearest-even narrowing of two binary32 values into one packed
+// dword (first value in the low half).
+template <int FT>
+__device__ __forceinline__ uint32_t narrow2(float a, float b)
+{
+    if constexpr (FT == BF16) {
+        bf2v h = __builtin_convertvector((f2v){opaque(a), opaque(b)}, bf2v);
+        return __builtin_bit_cast(uint32_t, h);
+    } else {
+        uint32_t lo = to_f16_bits(a);
+        uint32_t hi = to_f16_bits(b);
+        return lo | (hi << 16);
+    }
+}
+
+// Store eight binary32 values as output type FT at element index e.
+template <int FT>
+__device__ __forceinline__ void store8(void* base, int64_t e, const float v[8])
+{
+    if constexpr (FT == F32) {
+        uint4* p = reinterpret_cast<uint4*>(static_cast<float*>(base) + e);
+        p[0] = make_uint4(as_u(v[0]), as_u(v[1]), as_u(v[2]), as_u(v[3]));
+        p[1] = make_uint4(as_u(v[4]), as_u(v[5]), as_u(v[6]), as_u(v[7]));
+    } else {
+        uint4 w = make_uint4(narrow2<FT>(v[0], v[1]), narrow2<FT>(v[2], v[3]),
+                             narrow2<FT>(v[4], v[5]), narrow2<FT>(v[6], v[7]));
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = w;
+    }
+}
+
+// Scalar element access (generic paths).
+template <int FT>
+__device__ __forceinline__ float load1(const void* base, int64_t e)
+{
+    if constexpr (FT == F32) return static_cast<const float*>(base)[e];
+    else {
+        uint32_t h = static_cast<const uint16_t*>(base)[e];
+        if constexpr (FT == BF16) return as_f(h << 16);
+        else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    }
+}
+
+template <int FT>
+__device__ __forceinline__ void store1(void* base, int64_t e, float v)
+{
+    if constexpr (FT == F32) static_cast<float*>(base)[e] = v;
+    else if constexpr (FT == BF16) static_cast<uint16_t*>(base)[e] = to_bf16_bits(v);
+    else static_cast<uint16_t*>(base)[e] = to_f16_bits(v);
+}
+
+// ---------------------------------------------------------------- division
+// Correctly rounded binary32 x / s from y = RN(1/s) with two FMA
+// corrections (Markstein's division: the first correction makes the
+// quotient faithful, the second, with the correctly rounded reciprocal,
+// makes it correctly rounded; P. Markstein, IBM J. Res. Dev. 34(1), 1990).
+// Written as q + (-r) * y with r = q*s - x so that x = +-0 returns the zero
+// of x's sign, as IEEE division does.
+// Preconditions (no underflow / overflow in the intermediate steps):
+// 2^-40 <= |s| <= 2^40 and 2^-86 <= |x| <= 2^86, or x = +-0.  When |x| is
+// below 2^-86 the result still has x's sign and magnitude below 2^-45,
+// which is all that code selection needs (every code threshold is at
+// least 2^-10); outputs that are values (STE gradients) check |x| first.
+__device__ __forceinline__ float div_fast(float x, float s, float y)
+{
+    float q0 = x * y;
+    float r = __builtin_fmaf(q0, s, -x);
+    float q1 = __builtin_fmaf(-r, y, q0);
+    r = __builtin_fmaf(q1, s, -x);
+    return __builtin_fmaf(-r, y, q1);
+}
+
+__device__ __forceinline__ bool scale_in_fast_range(float s)
+{
+    float a = __builtin_fabsf(s);
+    return a >= 0x1p-40f && a <= 0x1p40f;
+}
+
+__device__ __forceinline__ bool value_in_fast_range(float x)
+{
+    float a = __builtin_fabsf(x);
+    return a >= 0x1p-86f && a <= 0x1p86f;
+}
+
+// ---------------------------------------------------------------- lanes
+// Max / min across a team of T lanes (T = 1..64, power of two) that are
+// contiguous and aligned in the wave: DPP quad permutes and row mirrors
+// within a 16-lane row, ds_bpermute-based shuffles across rows.  Every lane
+// of the team ends with the team's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), CTRL, 0xf, 0xf, false));
+}
+
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+template <int T>
+__device__ __forceinline__ float team_max(float v)
+{
+    if constexpr (T >= 2) v = __builtin_fmaxf(v, dpp<DPP_XOR1>(v));
+    if constexpr (T >= 4) v = __builtin_fmaxf(v, dpp<DPP_XOR2>(v));
+    if constexpr (T >= 8) v = __builtin_fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+    if constexpr (T >= 16) v = __builtin_fmaxf(v, dpp<DPP_MIRROR>(v));
+    if constexpr (T >= 32) v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
+    if constexpr (T >= 64) v = __builtin_fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+template <int T>
+__device__ __forceinline__ float team_min(float v)
+{
+    if constexpr (T >= 2) v = __builtin_fminf(v, dpp<DPP_XOR1>(v));
+    if constexpr (T >= 4) v = __builtin_fminf(v, dpp<DPP_XOR2>(v));
+    if constexpr (T >= 8) v = __builtin_fminf(v, dpp<DPP_HALF_MIRROR>(v));
+    if constexpr (T >= 16) v = __builtin_fminf(v, dpp<DPP_MIRROR>(v));
+    if constexpr (T >= 32) v = __builtin_fminf(v, __shfl_xor(v, 16, 64));
+    if constexpr (T >= 64) v = __builtin_fminf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------- codes
+// Integer codes via the 1.5 * 2^23 trick: for |v| < 2^22, v + M rounds v to
+// an integer with ties to even (the spacing of binary32 in [2^23, 2^24) is
+// 1 and M is even), and the low bits of the sum's pattern hold that
+// integer in two's complement.  Adding the (integer) zero-point and
+// clamping to [M + qmin, M + qmax] stay exact; for |v| >= 2^22 the clamp
+// decides alone.
+constexpr float MAGIC = 12582912.0f;   // 1.5 * 2^23
+
+__device__ __forceinline__ float int_code_f(float v, float zpf, float lo, float hi)
+{
+    return __builtin_amdgcn_fmed3f((v + MAGIC) + zpf, lo, hi);
+}
+
+// Pack the low bytes of four code floats into one dword.
+__device__ __forceinline__ uint32_t pack_bytes4(float a, float b, float c, float d)
+{
+    uint32_t ab = __builtin_amdgcn_perm(as_u(b), as_u(a), 0x0c0c0400u);
+    uint32_t cd = __builtin_amdgcn_perm(as_u(d), as_u(c), 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Pack eight 4-bit codes (low nibbles of the code floats' patterns) into one
+// dword, even index in the low nibble.
+__device__ __forceinline__ uint32_t pack_nibbles8(const float c[8], bool mask_high)
+{
+    uint32_t ev = pack_bytes4(c[0], c[2], c[4], c[6]);
+    uint32_t od = pack_bytes4(c[1], c[3], c[5], c[7]);
+    if (mask_high) {
+        ev &= 0x0f0f0f0fu;
+        od &= 0x0f0f0f0fu;
+    }
+    return ev | (od << 4);
+}
+
+// ---------------------------------------------------------------- FP8 / FP4
+// OCP E4M3 (gfx950's fp8 format): pre-clamped to +-448 so that the result
+// never depends on the instruction's overflow handling; round to nearest
+// even.  Four values -> one dword (first value in the low byte).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ float e4m3_val(uint32_t word, int byte)
+{
+    switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+    }
+}
+
+// OCP E2M1, pre-clamped to +-6.  Eight values -> one dword of nibbles
+// (first value in the low nibble).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float v[8])
+{
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(v[i], -6.0f, 6.0f);
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[0], c[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
+    return w;
+}
+
+// Decode one byte of E2M1 pairs: .x = low nibble, .y = high nibble.
+__device__ __forceinline__ f2v e2m1_val2(uint32_t word, int byte)
+{
+    switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+    }
+}
+
+// E8M0 byte -> 2^(b-127) as binary32 (b = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_val(uint32_t b)
+{
+    return b == 0 ? 0x1p-127f : as_f(b << 23);
+}
+
+// 2^(127-b): the exact reciprocal of e8m0_val(b) (b = 254 gives 2^-127).
+__device__ __forceinline__ float e8m0_inv(uint32_t b)
+{
+    return b == 254 ? 0x1p-127f : as_f((254u - b) << 23);
+}
+
+// Shared scale byte of an MX block with E2M1 elements:
+// floor(log2 amax) - 2 + 127, clamped to [0, 254]; 127 for an all-zero
+// block.  floor(log2) of a normal binary32 is its exponent field - 127;
+// subnormal amax gives byte 0.
+__device__ __forceinline__ uint32_t e8m0_mx_byte(float amax)
+{
+    uint32_t e = as_u(amax) >> 23;         // amax >= 0
+    if (amax == 0.0f) return 127;
+    return e >= 2 ? e - 2 : 0;
+}
+
+}  // namespace tq

@@ -1,0 +1,463 @@
+// tq_fp4.hip -- FP4 E2M1 block quantization with NVFP4 / MXFP4 scales and
+// the transposes to GEMM layout (metrale QuantizedWeight: fields weight,
+// weight_scale, weight_scale_2; transpose_for_gemm, transpose_for_gemm_gs;
+// smile.llm.quant MxFp8 for the E8M0-per-32 scale of the MX family).
+//
+//   NVFP4: s_g = amax / 2688 (6 * 448; 1 if 0) or the caller's static value;
+//          sb = E4M3(amax_16 / (6 * s_g)) (0x38 if it encodes to 0);
+//          eff = val(sb) * s_g;                   q = E2M1(x / eff)
+//   MXFP4: sb = E8M0 byte of 2^(floor(log2 amax_32) - 2) (127 if all zero);
+//          eff = 2^(sb - 127);                   q = E2M1(x * 2^(127 - sb))
+//          (x * 2^(127-sb) is exactly RN(x / eff): one rounding of the same
+//          real number)
+// Codes are packed two per byte along K, even index in the low nibble.
+//
+// Kernels:
+//   k_fp4_quant      one block per lane (16 or 32 elements as 2 or 4 16-byte
+//                    loads), block max in-lane, U blocks per lane in flight.
+//   k_fp4_ew         dequant / STE / dequant-backward, 8 elements per step.
+//   k_transpose_u8   byte transpose through a 64 x 256-byte LDS tile with
+//                    4 x 4 register transposes and 16-byte stores.
+#include "tq_device.h"
+#include "tq_host.h"
+
+namespace tq {
+
+enum { NV = 0, MX = 1 };
+
+// Per-tensor max |x|, pass 1 (block partials into ws).
+template <int FT>
+__global__ __launch_bounds__(256) void k_amax_partial(const void* __restrict__ x, int64_t numel, int64_t chunk,
+                                                      float* __restrict__ ws)
+{
+    __shared__ float sm[4];
+    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < numel ? b0 + chunk : numel;
+    float a = 0.0f;
+    for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8) {
+        float v[8];
+        widen8<FT>(load8<FT>(x, e), v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+    }
+    a = team_max<64>(a);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        ws[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
+}
+
+struct BP {
+    float eff, y;
+    uint32_t sb;
+    bool fast;
+};
+
+__device__ __forceinline__ BP nv_params(float amax, float sg, float six_sg)
+{
+    BP p;
+    const float v = __builtin_amdgcn_fmed3f(amax / six_sg, 0.0f, 448.0f);
+    uint32_t sb = e4m3_pack4(v, 0.0f, 0.0f, 0.0f) & 0xffu;
+    if ((sb & 0x7fu) == 0) sb = 0x38;
+    p.sb = sb;
+    p.eff = e4m3_val(sb, 0) * sg;
+    p.y = 1.0f / p.eff;
+    p.fast = scale_in_fast_range(p.eff);
+    return p;
+}
+
+__device__ __forceinline__ BP mx_params(float amax)
+{
+    BP p;
+    p.sb = e8m0_mx_byte(amax);
+    p.eff = e8m0_val(p.sb);
+    p.y = e8m0_inv(p.sb);
+    p.fast = true;
+    return p;
+}
+
+// Quotients x / eff for 8 values.
+template <int KIND, bool FAST>
+__device__ __forceinline__ void fp4_div8(const float v[8], const BP& p, float t[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (KIND == MX) t[i] = v[i] * p.y;
+        else t[i] = FAST ? div_fast(v[i], p.eff, p.y) : v[i] / p.eff;
+    }
+}
+
+template <int FT, int KIND, int U>
+__global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, int64_t nblocks,
+                                                   const float* __restrict__ ws, int nws, int static_global,
+                                                   float* __restrict__ global_scale, uint8_t* __restrict__ packed,
+                                                   uint8_t* __restrict__ bscale)
+{
+    constexpr int GS = KIND == NV ? 16 : 32;
+    constexpr int NV8 = GS / 8;
+    __shared__ float s_sg;
+    float sg = 1.0f;
+    if constexpr (KIND == NV) {
+        if (threadIdx.x < 64) {
+            float g;
+            if (static_global) {
+                g = global_scale[0];
+            } else {
+                float a = 0.0f;
+                for (int k = threadIdx.x; k < nws; k += 64) a = __builtin_fmaxf(a, ws[k]);
+                a = team_max<64>(a);
+                g = a / 2688.0f;
+                g = (g == 0.0f) ? 1.0f : g;
+                if (blockIdx.x == 0 && threadIdx.x == 0) global_scale[0] = g;
+            }
+            if (threadIdx.x == 0) s_sg = g;
+        }
+        __syncthreads();
+        sg = s_sg;
+    }
+    const float six_sg = 6.0f * sg;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t b0 = wave * (U * 64) + lane;
+    Raw8<FT> raw[U][NV8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = b0 + u * 64;
+#pragma unroll
+        for (int k = 0; k < NV8; ++k) {
+            if (b < nblocks) raw[u][k] = load8<FT>(x, b * GS + k * 8);
+            else raw[u][k] = Raw8<FT>{};
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = b0 + u * 64;
+        if (b >= nblocks) continue;
+        float v[NV8][8];
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV8; ++k) {
+            widen8<FT>(raw[u][k], v[k]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[k][i]));
+        }
+        const BP p = KIND == NV ? nv_params(a, sg, six_sg) : mx_params(a);
+        uint32_t w[NV8];
+#pragma unroll
+        for (int k = 0; k < NV8; ++k) {
+            float t[8];
+            if (p.fast) fp4_div8<KIND, true>(v[k], p, t);
+            else fp4_div8<KIND, false>(v[k], p, t);
+            w[k] = e2m1_pack8(t);
+        }
+        if constexpr (NV8 == 2) *reinterpret_cast<uint2*>(packed + b * 8) = make_uint2(w[0], w[1]);
+        else *reinterpret_cast<uint4*>(packed + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        bscale[b] = (uint8_t)p.sb;
+    }
+}
+
+// ------------------------------------------------------------ elementwise
+enum { OP_DEQ = 0, OP_STE = 1, OP_DQB = 2 };
+
+__device__ __forceinline__ float fp4_eff(int kind, uint32_t sb, float sg)
+{
+    return kind == NV ? e4m3_val(sb, 0) * sg : e8m0_val(sb);
+}
+
+template <int OP, int KIND, int FT>
+__global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, const void* __restrict__ b,
+                                                const uint8_t* __restrict__ bscale,
+                                                const float* __restrict__ global_scale, int64_t nvec,
+                                                void* __restrict__ out)
+{
+    constexpr int GS = KIND == NV ? 16 : 32;
+    const float sg = KIND == NV ? global_scale[0] : 1.0f;
+    for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
+        const int64_t e = vi * 8;
+        const uint32_t sb = bscale[e / GS];
+        float o[8];
+        if constexpr (OP == OP_DEQ) {
+            const float eff = fp4_eff(KIND, sb, sg);
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a) + e / 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f2v d = e2m1_val2(w, i);
+                o[2 * i] = d.x * eff;
+                o[2 * i + 1] = d.y * eff;
+            }
+        } else if constexpr (OP == OP_DQB) {
+            const float eff = fp4_eff(KIND, sb, sg);
+            float d[8];
+            widen8<FT>(load8<FT>(a, e), d);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = d[i] * eff;
+        } else {
+            float xv[8], d[8], t[8], g[8];
+            widen8<FT>(load8<FT>(a, e), xv);
+            widen8<FT>(load8<FT>(b, e), d);
+            if constexpr (KIND == MX) {
+                const float inv = e8m0_inv(sb);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    t[i] = xv[i] * inv;
+                    g[i] = d[i] * inv;
+                }
+            } else {
+                const float eff = fp4_eff(KIND, sb, sg);
+                const float y = 1.0f / eff;
+                bool ok = scale_in_fast_range(eff);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    ok = ok && value_in_fast_range(d[i]) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+                if (ok) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        t[i] = div_fast(xv[i], eff, y);
+                        g[i] = div_fast(d[i], eff, y);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        t[i] = xv[i] / eff;
+                        g[i] = d[i] / eff;
+                    }
+                }
+            }
+            const uint32_t w = e2m1_pack8(t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = g[i] * (((w >> (4 * i)) & 7u) != 7u ? 1.0f : 0.0f);
+        }
+        store8<FT>(out, e, o);
+    }
+}
+
+// ------------------------------------------------------------ transpose
+// dst[c][r] = src[r][c] for a [R, C] byte matrix.  Fast path: R % 16 == 0,
+// C % 16 == 0 and 16-byte aligned bases; a block moves a 64-row x 256-column
+// tile.  Thread (d, m) of the read-out phase owns input columns 4d..4d+3
+// and input rows 16m..16m+15: it reads 16 dwords from LDS, transposes four
+// 4x4 byte blocks in registers and writes 16 bytes to each of 4 output rows.
+constexpr int TR_ROWS = 64, TR_COLS = 256, TR_PITCH = TR_COLS / 4 + 1;   // dwords, padded
+
+__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t o[4])
+{
+    // o[c] byte i = row i byte c
+    const uint32_t t01lo = __builtin_amdgcn_perm(r1, r0, 0x05010400u);   // r0b0 r1b0 r0b1 r1b1
+    const uint32_t t01hi = __builtin_amdgcn_perm(r1, r0, 0x07030602u);   // r0b2 r1b2 r0b3 r1b3
+    const uint32_t t23lo = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+    const uint32_t t23hi = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+    o[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);              // r0b0 r1b0 r2b0 r3b0
+    o[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);              // r0b1 r1b1 r2b1 r3b1
+    o[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
+}
+
+__global__ __launch_bounds__(256) void k_transpose_u8(const uint8_t* __restrict__ src, int64_t R, int64_t C,
+                                                      uint8_t* __restrict__ dst)
+{
+    __shared__ uint32_t tile[TR_ROWS * TR_PITCH];
+    const int t = threadIdx.x;
+    const int64_t R0 = (int64_t)blockIdx.y * TR_ROWS, C0 = (int64_t)blockIdx.x * TR_COLS;
+    // load: 4 rows per wave instruction, 256 contiguous bytes per row
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = t / 16 + 16 * k;
+        const int cq = (t % 16) * 16;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (R0 + r < R && C0 + cq < C)
+            w = *reinterpret_cast<const uint4*>(src + (R0 + r) * C + C0 + cq);
+        uint32_t* row = tile + r * TR_PITCH + cq / 4;
+        row[0] = w.x;
+        row[1] = w.y;
+        row[2] = w.z;
+        row[3] = w.w;
+    }
+    __syncthreads();
+    const int m = t % 4, d = t / 4;        // rows 16m..16m+15, columns 4d..4d+3
+    uint32_t o[4][4];                       // o[c][quad] : output row 4d+c, bytes 4*quad..
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+        const int rb = 16 * m + 4 * qd;
+        uint32_t tr[4];
+        transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d], tile[(rb + 2) * TR_PITCH + d],
+                     tile[(rb + 3) * TR_PITCH + d], tr);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t oc = C0 + 4 * d + c;            // output row = input column
+        const int64_t orr = R0 + 16 * m;              // output column = input row
+        if (oc < C && orr < R)
+            *reinterpret_cast<uint4*>(dst + oc * R + orr) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_transpose_u8_generic(const uint8_t* __restrict__ src, int64_t R, int64_t C,
+                                                              uint8_t* __restrict__ dst)
+{
+    __shared__ uint8_t tile[64][65];
+    const int64_t R0 = (int64_t)blockIdx.y * 64, C0 = (int64_t)blockIdx.x * 64;
+    for (int k = threadIdx.x; k < 64 * 64; k += 256) {
+        const int r = k / 64, c = k % 64;
+        if (R0 + r < R && C0 + c < C) tile[r][c] = src[(R0 + r) * C + C0 + c];
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < 64 * 64; k += 256) {
+        const int c = k / 64, r = k % 64;
+        if (R0 + r < R && C0 + c < C) dst[(C0 + c) * R + R0 + r] = tile[r][c];
+    }
+}
+
+// ============================================================ host side
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static unsigned grid_for(int64_t work, int64_t per_block)
+{
+    int64_t g = cdiv(work, per_block);
+    if (g < 1) g = 1;
+    if (g > (1 << 20)) g = 1 << 20;
+    return (unsigned)g;
+}
+
+#define TQ_FT_SWITCH(ft, ...)                                     \
+    switch (ft) {                                                 \
+    case TQ_F32: { constexpr int FTV = F32; __VA_ARGS__; } break; \
+    case TQ_F16: { constexpr int FTV = F16; __VA_ARGS__; } break; \
+    default: { constexpr int FTV = BF16; __VA_ARGS__; } break;    \
+    }
+
+static tq_status transpose_bytes(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, hipStream_t st)
+{
+    if (R == 0 || C == 0) return TQ_OK;
+    if (R % 16 == 0 && C % 16 == 0 && aligned16(src) && aligned16(dst) && cdiv(R, TR_ROWS) <= 65535) {
+        hipLaunchKernelGGL(k_transpose_u8, dim3((unsigned)cdiv(C, TR_COLS), (unsigned)cdiv(R, TR_ROWS)), dim3(256), 0,
+                           st, src, R, C, dst);
+    } else {
+        if (cdiv(R, 64) > 65535) return TQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k_transpose_u8_generic, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64)), dim3(256), 0,
+                           st, src, R, C, dst);
+    }
+    return launch_status();
+}
+
+static tq_status check_fp4(int64_t rows, int64_t k, int kind)
+{
+    if (kind != TQ_NVFP4 && kind != TQ_MXFP4) return TQ_ERR_INVALID;
+    if (rows < 0 || k < 0) return TQ_ERR_INVALID;
+    if (k % (kind == TQ_NVFP4 ? 16 : 32)) return TQ_ERR_INVALID;
+    return TQ_OK;
+}
+
+template <int OP>
+static tq_status fp4_elementwise(const void* a, const void* b, int ft, const uint8_t* bscale, const float* sg,
+                                 int64_t rows, int64_t k, int kind, void* out, hipStream_t st)
+{
+    const int64_t nvec = rows * k / 8;
+    if (nvec == 0) return TQ_OK;
+    const dim3 grid(grid_for(nvec, 256)), block(256);
+    if (kind == TQ_NVFP4) {
+        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp4_ew<OP, NV, FTV>), grid, block, 0, st, a, b, bscale, sg, nvec, out));
+    } else {
+        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp4_ew<OP, MX, FTV>), grid, block, 0, st, a, b, bscale, sg, nvec, out));
+    }
+    return launch_status();
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k, int kind, uint8_t* packed,
+                             uint8_t* block_scale, float* global_scale, int static_global, void* workspace,
+                             size_t workspace_bytes, void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_fp4(rows, k, kind);
+    if (s) return s;
+    const int64_t numel = rows * k;
+    if (numel == 0) return TQ_OK;
+    if (!x || !packed || !block_scale) return TQ_ERR_INVALID;
+    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(packed)) return TQ_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    int nws = 0;
+    float* ws = static_cast<float*>(workspace);
+    if (kind == TQ_NVFP4 && !static_global) {
+        if (!workspace || workspace_bytes < tq_workspace_bytes(1, numel)) return TQ_ERR_INVALID;
+        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
+        nws = (int)cdiv(numel, chunk);
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_amax_partial<FTV>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws));
+        if (launch_status()) return TQ_ERR_HIP;
+    }
+    constexpr int U = 4;
+    if (kind == TQ_NVFP4) {
+        const int64_t nb = numel / 16;
+        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 64), 4));
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U>), grid, dim3(256), 0, st, x, nb, ws, nws,
+                                                 static_global, global_scale, packed, block_scale));
+    } else {
+        const int64_t nb = numel / 32;
+        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 64), 4));
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U>), grid, dim3(256), 0, st, x, nb, ws, nws,
+                                                 1, global_scale, packed, block_scale));
+    }
+    return launch_status();
+}
+
+tq_status tq_dequant_fp4_block(const uint8_t* packed, const uint8_t* block_scale, const float* global_scale,
+                               int64_t rows, int64_t k, int kind, void* y, int y_dtype, void* stream)
+{
+    if (!valid_ftype(y_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_fp4(rows, k, kind);
+    if (s || rows * k == 0) return s;
+    if (!packed || !block_scale || !y) return TQ_ERR_INVALID;
+    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
+    if (!aligned16(packed) || !aligned16(y)) return TQ_ERR_ALIGN;
+    return fp4_elementwise<OP_DEQ>(packed, nullptr, y_dtype, block_scale, global_scale, rows, k, kind, y,
+                                   as_stream(stream));
+}
+
+tq_status tq_quant_fp4_block_backward(const void* x, int x_dtype, const uint8_t* block_scale,
+                                      const float* global_scale, int64_t rows, int64_t k, int kind, const void* dy,
+                                      void* dx, void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_fp4(rows, k, kind);
+    if (s || rows * k == 0) return s;
+    if (!x || !dy || !dx || !block_scale) return TQ_ERR_INVALID;
+    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return TQ_ERR_ALIGN;
+    return fp4_elementwise<OP_STE>(x, dy, x_dtype, block_scale, global_scale, rows, k, kind, dx, as_stream(stream));
+}
+
+tq_status tq_dequant_fp4_block_backward(const void* dy, int dy_dtype, const uint8_t* block_scale,
+                                        const float* global_scale, int64_t rows, int64_t k, int kind, void* dq,
+                                        void* stream)
+{
+    if (!valid_ftype(dy_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_fp4(rows, k, kind);
+    if (s || rows * k == 0) return s;
+    if (!dy || !dq || !block_scale) return TQ_ERR_INVALID;
+    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
+    if (!aligned16(dy) || !aligned16(dq)) return TQ_ERR_ALIGN;
+    return fp4_elementwise<OP_DQB>(dy, nullptr, dy_dtype, block_scale, global_scale, rows, k, kind, dq,
+                                   as_stream(stream));
+}
+
+tq_status tq_fp4_transpose_for_gemm(const uint8_t* packed, const uint8_t* block_scale, int64_t n, int64_t k,
+                                    int32_t group_size, uint8_t* packed_t, uint8_t* block_scale_t, void* stream)
+{
+    if (n < 0 || k < 0 || (k & 1) || group_size <= 0 || k % group_size) return TQ_ERR_INVALID;
+    if (n == 0 || k == 0) return TQ_OK;
+    if (!packed || !packed_t) return TQ_ERR_INVALID;
+    if ((block_scale == nullptr) != (block_scale_t == nullptr)) return TQ_ERR_INVALID;
+    hipStream_t st = as_stream(stream);
+    tq_status s = transpose_bytes(packed, n, k / 2, packed_t, st);
+    if (s || !block_scale) return s;
+    return transpose_bytes(block_scale, n, k / group_size, block_scale_t, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,381 @@
+// tq_fp8.hip -- FP8 E4M3 block quantization (smile.llm.quant package summary:
+// Fp8BlockGemm's activation quantizer with one fp32 scale per 1x128 group and
+// its weights with one fp32 scale per 128x128 tile; Fp8BlockDequant), with
+// the STE backward and the dequantize backward.
+//
+//   scale = amax / 448 (1 if that is 0),  q = E4M3(x / scale)
+//
+// E4M3 is the OCP format (bias 7, max 448) that gfx950's v_cvt_pk_fp8_f32
+// produces; values are clamped to +-448 before the conversion (saturation),
+// the conversion rounds to nearest even.
+//
+// Kernels:
+//   k_fp8_rows   blocks of 1 x bc (bc = 16..512, power of two): a team of
+//                bc/8 lanes per block, 8 blocks per team per launch row.
+//   k_fp8_tile   blocks of br x bc with bc = 8*T and br = NP * 256/T: one
+//                256-thread workgroup per tile, the tile in registers, the
+//                tile max through DPP, bpermute and LDS.
+//   k_fp8_generic  any block shape: one workgroup per block, two passes.
+//   k_fp8_ew     dequant / STE / dequant-backward, elementwise, 16-byte I/O.
+#include "tq_device.h"
+#include "tq_host.h"
+
+namespace tq {
+
+struct FP {
+    float s, y;
+    bool fast;
+};
+
+__device__ __forceinline__ FP fp8_params(float amax)
+{
+    FP p;
+    float s = amax / 448.0f;
+    p.s = (s == 0.0f) ? 1.0f : s;
+    p.y = 1.0f / p.s;
+    p.fast = scale_in_fast_range(p.s);
+    return p;
+}
+
+template <bool FAST>
+__device__ __forceinline__ uint2 fp8_enc8(const float v[8], const FP& p)
+{
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = FAST ? div_fast(v[i], p.s, p.y) : v[i] / p.s;
+    return make_uint2(e4m3_pack4(t[0], t[1], t[2], t[3]), e4m3_pack4(t[4], t[5], t[6], t[7]));
+}
+
+// ------------------------------------------------------------ 1 x bc rows
+template <int FT, int T, int U>
+__global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, int64_t nblocks,
+                                                  uint8_t* __restrict__ q, float* __restrict__ scale)
+{
+    constexpr int P = 64 / T;
+    constexpr int64_t L = 8 * T;
+    const int lane = threadIdx.x & 63;
+    const int j = lane % T;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t g0 = wave * (U * P) + lane / T;
+    Raw8<FT> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t g = g0 + (int64_t)u * P;
+        if (g < nblocks) raw[u] = load8<FT>(x, g * L + j * 8);
+        else raw[u] = Raw8<FT>{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float v[8];
+        widen8<FT>(raw[u], v);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+        const FP p = fp8_params(team_max<T>(a));
+        const int64_t g = g0 + (int64_t)u * P;
+        if (g >= nblocks) continue;
+        const uint2 c = p.fast ? fp8_enc8<true>(v, p) : fp8_enc8<false>(v, p);
+        *reinterpret_cast<uint2*>(q + g * L + j * 8) = c;
+        if (j == 0) scale[g] = p.s;
+    }
+}
+
+// ------------------------------------------------------------ br x bc tiles
+// Thread t covers columns (t % T) * 8 .. +8 and rows t / T + k * (256 / T),
+// k = 0..NP-1, of its tile.
+template <int FT, int T, int NP>
+__global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, int64_t cols, int64_t nbc,
+                                                  uint8_t* __restrict__ q, float* __restrict__ scale)
+{
+    constexpr int RP = 256 / T;
+    __shared__ float wmax[4];
+    const int64_t tr = blockIdx.y, tc = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t r0 = tr * (RP * NP) + t / T;
+    const int64_t c0 = tc * (8 * T) + (t % T) * 8;
+    Raw8<FT> raw[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) raw[k] = load8<FT>(x, (r0 + (int64_t)k * RP) * cols + c0);
+    float v[NP][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        widen8<FT>(raw[k], v[k]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[k][i]));
+    }
+    a = team_max<64>(a);
+    if ((t & 63) == 0) wmax[t >> 6] = a;
+    __syncthreads();
+    a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    const FP p = fp8_params(a);
+    if (p.fast) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+            *reinterpret_cast<uint2*>(q + (r0 + (int64_t)k * RP) * cols + c0) = fp8_enc8<true>(v[k], p);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NP; ++k)
+            *reinterpret_cast<uint2*>(q + (r0 + (int64_t)k * RP) * cols + c0) = fp8_enc8<false>(v[k], p);
+    }
+    if (t == 0) scale[tr * nbc + tc] = p.s;
+}
+
+// ------------------------------------------------------------ generic blocks
+template <int FT>
+__global__ __launch_bounds__(256) void k_fp8_generic(const void* __restrict__ x, int64_t cols, int64_t br,
+                                                     int64_t bc, int64_t nbc, uint8_t* __restrict__ q,
+                                                     float* __restrict__ scale)
+{
+    __shared__ float wmax[4];
+    const int64_t blk = blockIdx.x;
+    const int64_t r0 = (blk / nbc) * br, c0 = (blk % nbc) * bc;
+    const int64_t n = br * bc;
+    float a = 0.0f;
+    for (int64_t j = threadIdx.x; j < n; j += 256)
+        a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, (r0 + j / bc) * cols + c0 + j % bc)));
+    a = team_max<64>(a);
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    const FP p = fp8_params(a);
+    for (int64_t j = threadIdx.x; j < n; j += 256) {
+        const int64_t e = (r0 + j / bc) * cols + c0 + j % bc;
+        const float t = load1<FT>(x, e) / p.s;
+        q[e] = (uint8_t)e4m3_pack4(t, 0.0f, 0.0f, 0.0f);
+    }
+    if (threadIdx.x == 0) scale[blk] = p.s;
+}
+
+// ------------------------------------------------------------ elementwise
+enum { OP_DEQ = 0, OP_STE = 1, OP_DQB = 2 };
+
+__device__ __forceinline__ int64_t fp8_block_of(int64_t e, int64_t cols, int64_t br, int64_t bc, int64_t nbc)
+{
+    return ((e / cols) / br) * nbc + (e % cols) / bc;
+}
+
+// Vector path (cols % 8 == 0 and bc % 8 == 0: the 8 elements share a block).
+template <int OP, int FT>
+__global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, const void* __restrict__ b,
+                                                int64_t nvec, int64_t cols, int64_t br, int64_t bc, int64_t nbc,
+                                                const float* __restrict__ scale, void* __restrict__ out)
+{
+    for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
+        const int64_t e = vi * 8;
+        const float s = scale[fp8_block_of(e, cols, br, bc, nbc)];
+        float o[8];
+        if constexpr (OP == OP_DEQ) {
+            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = e4m3_val(w.x, i) * s;
+                o[4 + i] = e4m3_val(w.y, i) * s;
+            }
+        } else if constexpr (OP == OP_DQB) {
+            float d[8];
+            widen8<FT>(load8<FT>(a, e), d);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = d[i] * s;
+        } else {
+            float xv[8], d[8];
+            widen8<FT>(load8<FT>(a, e), xv);
+            widen8<FT>(load8<FT>(b, e), d);
+            const float y = 1.0f / s;
+            bool ok = scale_in_fast_range(s);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ok = ok && value_in_fast_range(d[i]) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+            float t[8], g[8];
+            if (ok) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    t[i] = div_fast(xv[i], s, y);
+                    g[i] = div_fast(d[i], s, y);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    t[i] = xv[i] / s;
+                    g[i] = d[i] / s;
+                }
+            }
+            const uint32_t c0 = e4m3_pack4(t[0], t[1], t[2], t[3]);
+            const uint32_t c1 = e4m3_pack4(t[4], t[5], t[6], t[7]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t c = ((i < 4 ? c0 : c1) >> ((i & 3) * 8)) & 0x7fu;
+                o[i] = g[i] * (c < 0x7eu ? 1.0f : 0.0f);
+            }
+        }
+        store8<FT>(out, e, o);
+    }
+}
+
+template <int OP, int FT>
+__global__ __launch_bounds__(256) void k_fp8_ew_generic(const void* __restrict__ a, const void* __restrict__ b,
+                                                        int64_t n, int64_t cols, int64_t br, int64_t bc,
+                                                        int64_t nbc, const float* __restrict__ scale,
+                                                        void* __restrict__ out)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        const float s = scale[fp8_block_of(e, cols, br, bc, nbc)];
+        float o;
+        if constexpr (OP == OP_DEQ) {
+            o = e4m3_val(static_cast<const uint8_t*>(a)[e], 0) * s;
+        } else if constexpr (OP == OP_DQB) {
+            o = load1<FT>(a, e) * s;
+        } else {
+            const uint32_t c = e4m3_pack4(load1<FT>(a, e) / s, 0.0f, 0.0f, 0.0f) & 0x7fu;
+            o = (load1<FT>(b, e) / s) * (c < 0x7eu ? 1.0f : 0.0f);
+        }
+        store1<FT>(out, e, o);
+    }
+}
+
+// ============================================================ host side
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static unsigned grid_for(int64_t work, int64_t per_block)
+{
+    int64_t g = cdiv(work, per_block);
+    if (g < 1) g = 1;
+    if (g > (1 << 20)) g = 1 << 20;
+    return (unsigned)g;
+}
+
+#define TQ_FT_SWITCH(ft, ...)                                     \
+    switch (ft) {                                                 \
+    case TQ_F32: { constexpr int FTV = F32; __VA_ARGS__; } break; \
+    case TQ_F16: { constexpr int FTV = F16; __VA_ARGS__; } break; \
+    default: { constexpr int FTV = BF16; __VA_ARGS__; } break;    \
+    }
+
+template <int FT, int T, int U>
+static void launch_rows(const void* x, int64_t nblocks, uint8_t* q, float* scale, hipStream_t st)
+{
+    constexpr int P = 64 / T;
+    const int64_t waves = cdiv(nblocks, (int64_t)U * P);
+    hipLaunchKernelGGL((k_fp8_rows<FT, T, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st, x, nblocks, q, scale);
+}
+
+template <int FT>
+static bool quant_fast(const void* x, int64_t rows, int64_t cols, int64_t br, int64_t bc, uint8_t* q, float* scale,
+                       hipStream_t st)
+{
+    const int64_t nb = (rows / br) * (cols / bc);
+    if (br == 1) {
+        switch (bc) {
+        case 16: launch_rows<FT, 2, 8>(x, nb, q, scale, st); return true;
+        case 32: launch_rows<FT, 4, 8>(x, nb, q, scale, st); return true;
+        case 64: launch_rows<FT, 8, 8>(x, nb, q, scale, st); return true;
+        case 128: launch_rows<FT, 16, 8>(x, nb, q, scale, st); return true;
+        case 256: launch_rows<FT, 32, 8>(x, nb, q, scale, st); return true;
+        case 512: launch_rows<FT, 64, 8>(x, nb, q, scale, st); return true;
+        default: return false;
+        }
+    }
+    const dim3 grid((unsigned)(cols / bc), (unsigned)(rows / br));
+    if (rows / br > 65535) return false;
+    if (bc == 128 && br == 128) {
+        hipLaunchKernelGGL((k_fp8_tile<FT, 16, 8>), grid, dim3(256), 0, st, x, cols, cols / bc, q, scale);
+        return true;
+    }
+    if (bc == 128 && br == 64) {
+        hipLaunchKernelGGL((k_fp8_tile<FT, 16, 4>), grid, dim3(256), 0, st, x, cols, cols / bc, q, scale);
+        return true;
+    }
+    if (bc == 64 && br == 64) {
+        hipLaunchKernelGGL((k_fp8_tile<FT, 8, 2>), grid, dim3(256), 0, st, x, cols, cols / bc, q, scale);
+        return true;
+    }
+    return false;
+}
+
+static tq_status check_blocks(int64_t rows, int64_t cols, int32_t br, int32_t bc)
+{
+    if (rows < 0 || cols < 0 || br <= 0 || bc <= 0) return TQ_ERR_INVALID;
+    if (rows % br || cols % bc) return TQ_ERR_INVALID;
+    return TQ_OK;
+}
+
+template <int OP>
+static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t rows, int64_t cols, int32_t br,
+                                 int32_t bc, const float* scale, void* out, hipStream_t st)
+{
+    const int64_t n = rows * cols;
+    if (n == 0) return TQ_OK;
+    const int64_t nbc = cols / bc;
+    if (cols % 8 == 0 && bc % 8 == 0) {
+        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256)), dim3(256), 0, st,
+                                            a, b, n / 8, cols, (int64_t)br, (int64_t)bc, nbc, scale, out));
+    } else {
+        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew_generic<OP, FTV>), dim3(grid_for(n, 256)), dim3(256), 0, st,
+                                            a, b, n, cols, (int64_t)br, (int64_t)bc, nbc, scale, out));
+    }
+    return launch_status();
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+tq_status tq_quant_fp8_block(const void* x, int x_dtype, int64_t rows, int64_t cols, int32_t block_rows,
+                             int32_t block_cols, uint8_t* q, float* scale, void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_blocks(rows, cols, block_rows, block_cols);
+    if (s || rows == 0 || cols == 0) return s;
+    if (!x || !q || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    bool done = false;
+    if (cols % 8 == 0) {
+        TQ_FT_SWITCH(x_dtype, done = quant_fast<FTV>(x, rows, cols, block_rows, block_cols, q, scale, st));
+    }
+    if (!done) {
+        const int64_t nb = (rows / block_rows) * (cols / block_cols);
+        if (nb > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp8_generic<FTV>), dim3((unsigned)nb), dim3(256), 0, st, x, cols,
+                                                 (int64_t)block_rows, (int64_t)block_cols, cols / block_cols, q, scale));
+    }
+    return launch_status();
+}
+
+tq_status tq_dequant_fp8_block(const uint8_t* q, int64_t rows, int64_t cols, int32_t block_rows, int32_t block_cols,
+                               const float* scale, void* y, int y_dtype, void* stream)
+{
+    if (!valid_ftype(y_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_blocks(rows, cols, block_rows, block_cols);
+    if (s || rows == 0 || cols == 0) return s;
+    if (!q || !scale || !y) return TQ_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(y)) return TQ_ERR_ALIGN;
+    return fp8_elementwise<OP_DEQ>(q, nullptr, y_dtype, rows, cols, block_rows, block_cols, scale, y, as_stream(stream));
+}
+
+tq_status tq_quant_fp8_block_backward(const void* x, int x_dtype, int64_t rows, int64_t cols, int32_t block_rows,
+                                      int32_t block_cols, const float* scale, const void* dy, void* dx, void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_blocks(rows, cols, block_rows, block_cols);
+    if (s || rows == 0 || cols == 0) return s;
+    if (!x || !dy || !dx || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return TQ_ERR_ALIGN;
+    return fp8_elementwise<OP_STE>(x, dy, x_dtype, rows, cols, block_rows, block_cols, scale, dx, as_stream(stream));
+}
+
+tq_status tq_dequant_fp8_block_backward(const void* dy, int dy_dtype, int64_t rows, int64_t cols, int32_t block_rows,
+                                        int32_t block_cols, const float* scale, void* dq, void* stream)
+{
+    if (!valid_ftype(dy_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_blocks(rows, cols, block_rows, block_cols);
+    if (s || rows == 0 || cols == 0) return s;
+    if (!dy || !dq || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(dy) || !aligned16(dq)) return TQ_ERR_ALIGN;
+    return fp8_elementwise<OP_DQB>(dy, nullptr, dy_dtype, rows, cols, block_rows, block_cols, scale, dq,
+                                   as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// tq_host.h -- host-side helpers shared by the C-ABI entry points:
+// argument validation, the group layout of a granularity, launch checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "tq.h"
+
+namespace tq {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool valid_ftype(int t) { return t == TQ_F32 || t == TQ_F16 || t == TQ_BF16; }
+inline bool valid_code(int c) { return c == TQ_S8 || c == TQ_U8 || c == TQ_S4 || c == TQ_U4; }
+inline int code_bits(int c) { return (c == TQ_S4 || c == TQ_U4) ? 4 : 8; }
+inline bool code_signed(int c) { return c == TQ_S8 || c == TQ_S4; }
+inline int ftype_size(int t) { return t == TQ_F32 ? 4 : 2; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline tq_status launch_status()
+{
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+// Range check of (code, qmin, qmax, symmetric): the range lies inside the
+// code's representable range, qmin < qmax, and symmetric mode uses
+// [-qmax, qmax] with a signed code.
+inline bool valid_range(int code, int32_t qmin, int32_t qmax, bool symmetric)
+{
+    if (!valid_code(code) || qmin >= qmax) return false;
+    int bits = code_bits(code);
+    int32_t lo = code_signed(code) ? -(1 << (bits - 1)) : 0;
+    int32_t hi = code_signed(code) ? (1 << (bits - 1)) - 1 : (1 << bits) - 1;
+    if (qmin < lo || qmax > hi) return false;
+    if (symmetric && (qmin != -qmax || !code_signed(code))) return false;
+    return true;
+}
+
+// Canonical group layout.  The tensor is viewed as [outer, A, inner] around
+// the grouped axis.
+//   KIND_TENSOR : one group.
+//   KIND_CHANNEL: group = index a along A (all outer and inner indices).
+//   KIND_GROUP  : group = g consecutive indices along A at fixed (o, i);
+//                 group id = (o * (A / g) + a / g) * inner + i.
+// Per-token [rows, cols] is KIND_GROUP with outer = rows, A = g = cols,
+// inner = 1.
+enum { KIND_TENSOR = 0, KIND_CHANNEL = 1, KIND_GROUP = 2 };
+
+struct GroupMap {
+    int kind;
+    int64_t outer, A, inner, g;
+    int64_t numel, ngroups;
+};
+
+inline bool make_map(int kind, int32_t ndim, const int64_t* shape, int32_t axis, int64_t g,
+                     GroupMap* m)
+{
+    if (ndim < 1 || ndim > 8 || !shape) return false;
+    int64_t numel = 1;
+    for (int d = 0; d < ndim; ++d) {
+        if (shape[d] < 0) return false;
+        numel *= shape[d];
+    }
+    if (axis < 0 || axis >= ndim) return false;
+    m->kind = kind;
+    m->numel = numel;
+    m->outer = 1;
+    m->inner = 1;
+    m->A = shape[axis];
+    for (int d = 0; d < axis; ++d) m->outer *= shape[d];
+    for (int d = axis + 1; d < ndim; ++d) m->inner *= shape[d];
+    if (kind == KIND_CHANNEL) {
+        m->g = 1;
+        m->ngroups = m->A;
+    } else {
+        if (g <= 0 || m->A % g) return false;
+        m->g = g;
+        m->ngroups = m->outer * (m->A / g) * m->inner;
+    }
+    return true;
+}
+
+inline GroupMap tensor_map(int64_t numel)
+{
+    GroupMap m;
+    m.kind = KIND_TENSOR;
+    m.outer = 1;
+    m.A = numel;
+    m.inner = 1;
+    m.g = numel;
+    m.numel = numel;
+    m.ngroups = 1;
+    return m;
+}
+
+inline GroupMap token_map(int64_t rows, int64_t cols)
+{
+    GroupMap m;
+    m.kind = KIND_GROUP;
+    m.outer = rows;
+    m.A = cols;
+    m.inner = 1;
+    m.g = cols;
+    m.numel = rows * cols;
+    m.ngroups = rows;
+    return m;
+}
+
+}  // namespace tq

@@ -1,0 +1,1186 @@
+// tq_int.hip -- integer codes (s8 / u8 / s4 / u4) at per-tensor, per-channel,
+// per-token and per-group granularity: quantize, dequantize, STE backward
+// and dequantize backward, with their C-ABI entry points.
+//
+// Definitions: docs.rs baracuda_kernels::quantize (module overview: per-token
+// W8A8 rows and GPTQ-style per-group g=128 weights, the STE rule
+// dx = (dy / scale) * 1[qmin < q < qmax] recomputed from the saved input;
+// module list: dequantize backward dq = dy * scale; default_q_range) and
+// teenygrad granularity.rs (enum Granularity).  The readings taken where the
+// pages are silent (symmetric range [-qmax, qmax], the affine zero-point,
+// scale 0 -> 1) are stated in include/tq.h.
+//
+// Kernel map (each group is streamed once, 16-byte loads):
+//   k_quant_team   contiguous groups of L = 8*T*W elements: a team of T
+//                  lanes per group (DPP / bpermute reduction), W vectors of
+//                  8 elements per lane held in registers; per-token rows of
+//                  512..4096 elements use a whole wave, 128-element GPTQ
+//                  groups use 16-lane teams.
+//   k_quant_long   contiguous groups of any length multiple of 8: one wave
+//                  per group, two passes over the group.
+//   k_quant_cols   groups that run down columns ([B, R, C] view: per-channel
+//                  on the last axis, per-group along a non-last axis).
+//   k_*_generic    any layout (index arithmetic per element), the fallback.
+//   k_tensor_*     per-tensor: block partial max, then encode.
+//   k_dequant_vec / k_ste_vec / k_dqb_vec   elementwise streaming.
+#include "tq_device.h"
+#include "tq_host.h"
+
+namespace tq {
+
+// ------------------------------------------------------------ group params
+struct GP {
+    float s;     // scale
+    float y;     // RN(1 / s)
+    float zpf;   // zero-point as a float (0 when symmetric)
+    bool fast;   // s inside the range where div_fast is exact
+};
+
+template <bool SYM>
+__device__ __forceinline__ GP make_gp(float amax, float mn, float mx, float qmin, float qmax)
+{
+    GP p;
+    if constexpr (SYM) {
+        float s = amax / qmax;
+        p.s = (s == 0.0f) ? 1.0f : s;
+        p.zpf = 0.0f;
+    } else {
+        float s = (mx - mn) / (qmax - qmin);
+        s = (s == 0.0f) ? 1.0f : s;
+        float z = qmin - __builtin_rintf(mn / s);
+        p.s = s;
+        p.zpf = __builtin_amdgcn_fmed3f(z, qmin, qmax);
+    }
+    p.y = 1.0f / p.s;
+    p.fast = scale_in_fast_range(p.s);
+    return p;
+}
+
+// Encode 8 values of one group into code floats (MAGIC + code).
+template <bool FAST>
+__device__ __forceinline__ void enc8(const float v[8], const GP& p, float lo, float hi, float c[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float t = FAST ? div_fast(v[i], p.s, p.y) : v[i] / p.s;
+        c[i] = int_code_f(t, p.zpf, lo, hi);
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* q, int64_t e, const float c[8])
+{
+    if constexpr (BITS == 8) {
+        uint2 w = make_uint2(pack_bytes4(c[0], c[1], c[2], c[3]), pack_bytes4(c[4], c[5], c[6], c[7]));
+        *reinterpret_cast<uint2*>(q + e) = w;
+    } else {
+        *reinterpret_cast<uint32_t*>(q + (e >> 1)) = pack_nibbles8(c, true);
+    }
+}
+
+// ------------------------------------------------------------ team kernel
+template <int FT, int BITS, bool SYM, int T, int W, int U>
+__global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, int64_t G, float qmin,
+                                                    float qmax, uint8_t* __restrict__ q,
+                                                    float* __restrict__ scale, uint8_t* __restrict__ zp)
+{
+    constexpr int P = 64 / T;
+    constexpr int64_t L = 8 * T * W;
+    const int lane = threadIdx.x & 63;
+    const int team = lane / T;
+    const int j = lane % T;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t g0 = wave * (U * P) + team;
+
+    Raw8<FT> raw[U][W];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t g = g0 + (int64_t)u * P;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            if (g < G) raw[u][w] = load8<FT>(x, g * L + (int64_t)(w * T + j) * 8);
+            else raw[u][w] = Raw8<FT>{};
+        }
+    }
+    float v[U][W][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int w = 0; w < W; ++w) widen8<FT>(raw[u][w], v[u][w]);
+
+    GP p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (SYM) {
+            float a = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[u][w][i]));
+            p[u] = make_gp<true>(team_max<T>(a), 0.0f, 0.0f, qmin, qmax);
+        } else {
+            float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    mn = __builtin_fminf(mn, v[u][w][i]);
+                    mx = __builtin_fmaxf(mx, v[u][w][i]);
+                }
+            p[u] = make_gp<false>(0.0f, team_min<T>(mn), team_max<T>(mx), qmin, qmax);
+        }
+    }
+
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t g = g0 + (int64_t)u * P;
+        if (g >= G) continue;
+        if (p[u].fast) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                float c[8];
+                enc8<true>(v[u][w], p[u], lo, hi, c);
+                store_codes8<BITS>(q, g * L + (int64_t)(w * T + j) * 8, c);
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                float c[8];
+                enc8<false>(v[u][w], p[u], lo, hi, c);
+                store_codes8<BITS>(q, g * L + (int64_t)(w * T + j) * 8, c);
+            }
+        }
+        if (j == 0) {
+            scale[g] = p[u].s;
+            if constexpr (!SYM) zp[g] = (uint8_t)(int)p[u].zpf;
+        }
+    }
+}
+
+// ------------------------------------------------------------ long groups
+// One wave per group of L elements (L % 8 == 0); the group is read twice
+// (reduce, then encode) in 4-vector strides per lane.
+template <int FT, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, int64_t G, int64_t L,
+                                                    float qmin, float qmax, uint8_t* __restrict__ q,
+                                                    float* __restrict__ scale, uint8_t* __restrict__ zp)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= G) return;
+    const int64_t nvec = L / 8;
+    const int64_t base = g * L;
+    float a = 0.0f, mn = 0.0f, mx = 0.0f;
+    for (int64_t v0 = lane; v0 < nvec; v0 += 256) {
+        Raw8<FT> raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (v0 + k * 64 < nvec) raw[k] = load8<FT>(x, base + (v0 + k * 64) * 8);
+            else raw[k] = Raw8<FT>{};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float v[8];
+            widen8<FT>(raw[k], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+                mn = __builtin_fminf(mn, v[i]);
+                mx = __builtin_fmaxf(mx, v[i]);
+            }
+        }
+    }
+    GP p = SYM ? make_gp<true>(team_max<64>(a), 0.0f, 0.0f, qmin, qmax)
+               : make_gp<false>(0.0f, team_min<64>(mn), team_max<64>(mx), qmin, qmax);
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    for (int64_t v0 = lane; v0 < nvec; v0 += 256) {
+        Raw8<FT> raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (v0 + k * 64 < nvec) raw[k] = load8<FT>(x, base + (v0 + k * 64) * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (v0 + k * 64 >= nvec) continue;
+            float v[8], c[8];
+            widen8<FT>(raw[k], v);
+            if (p.fast) enc8<true>(v, p, lo, hi, c);
+            else enc8<false>(v, p, lo, hi, c);
+            store_codes8<BITS>(q, base + (v0 + k * 64) * 8, c);
+        }
+    }
+    if (lane == 0) {
+        scale[g] = p.s;
+        if constexpr (!SYM) zp[g] = (uint8_t)(int)p.zpf;
+    }
+}
+
+// ------------------------------------------------------------ column groups
+// View [B, R, C] (C % 8 == 0); group (b, c) is column c of slab b, R long.
+// A block covers 512 columns of one slab; its 4 waves split the rows, merge
+// the column partials through LDS, then encode their rows again.  Column
+// scales differ inside a vector, so this path divides with IEEE division.
+template <int FT, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ x, int64_t R, int64_t C,
+                                                    float qmin, float qmax, uint8_t* __restrict__ q,
+                                                    float* __restrict__ scale, uint8_t* __restrict__ zp)
+{
+    __shared__ float red[2][4][64 * 8];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t b = blockIdx.y;
+    const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * 8;
+    const bool active = c0 < C;
+    const int64_t base = b * R * C;
+    float mn[8], mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mn[i] = mx[i] = 0.0f;
+    if (active) {
+        for (int64_t r = wv; r < R; r += 4) {
+            float v[8];
+            widen8<FT>(load8<FT>(x, base + r * C + c0), v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (SYM) {
+                    mx[i] = __builtin_fmaxf(mx[i], __builtin_fabsf(v[i]));
+                } else {
+                    mn[i] = __builtin_fminf(mn[i], v[i]);
+                    mx[i] = __builtin_fmaxf(mx[i], v[i]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        red[0][wv][lane * 8 + i] = mn[i];
+        red[1][wv][lane * 8 + i] = mx[i];
+    }
+    __syncthreads();
+    GP p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float a = red[0][0][lane * 8 + i], m = red[1][0][lane * 8 + i];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) {
+            a = __builtin_fminf(a, red[0][k][lane * 8 + i]);
+            m = __builtin_fmaxf(m, red[1][k][lane * 8 + i]);
+        }
+        p[i] = SYM ? make_gp<true>(m, 0.0f, 0.0f, qmin, qmax) : make_gp<false>(0.0f, a, m, qmin, qmax);
+    }
+    if (!active) return;
+    if (wv == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            scale[b * C + c0 + i] = p[i].s;
+            if constexpr (!SYM) zp[b * C + c0 + i] = (uint8_t)(int)p[i].zpf;
+        }
+    }
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    for (int64_t r = wv; r < R; r += 4) {
+        float v[8], c[8];
+        widen8<FT>(load8<FT>(x, base + r * C + c0), v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = int_code_f(v[i] / p[i].s, p[i].zpf, lo, hi);
+        store_codes8<BITS>(q, base + r * C + c0, c);
+    }
+}
+
+// ------------------------------------------------------------ generic
+struct DMap {
+    int kind;
+    int64_t outer, A, inner, g, numel;
+
+    __device__ int64_t group_of(int64_t e) const
+    {
+        if (kind == KIND_TENSOR) return 0;
+        const int64_t a = (e / inner) % A;
+        if (kind == KIND_CHANNEL) return a;
+        const int64_t i = e % inner, o = e / (inner * A);
+        return (o * (A / g) + a / g) * inner + i;
+    }
+    __device__ int64_t count() const
+    {
+        if (kind == KIND_TENSOR) return numel;
+        if (kind == KIND_CHANNEL) return outer * inner;
+        return g;
+    }
+    __device__ int64_t elem(int64_t gid, int64_t j) const
+    {
+        if (kind == KIND_TENSOR) return j;
+        if (kind == KIND_CHANNEL) return (j / inner) * A * inner + gid * inner + j % inner;
+        const int64_t i = gid % inner, t = gid / inner;
+        const int64_t ab = t % (A / g), o = t / (A / g);
+        return (o * A + ab * g + j) * inner + i;
+    }
+};
+
+static DMap to_dmap(const GroupMap& m)
+{
+    DMap d;
+    d.kind = m.kind;
+    d.outer = m.outer;
+    d.A = m.A;
+    d.inner = m.inner;
+    d.g = m.g;
+    d.numel = m.numel;
+    return d;
+}
+
+// Block-wide max of a non-negative value and min of a non-positive value.
+__device__ __forceinline__ void block_minmax(float& mn, float& mx)
+{
+    __shared__ float smn[4], smx[4];
+    mn = team_min<64>(mn);
+    mx = team_max<64>(mx);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+        smn[wv] = mn;
+        smx[wv] = mx;
+    }
+    __syncthreads();
+    const int nw = (blockDim.x + 63) >> 6;
+    mn = smn[0];
+    mx = smx[0];
+    for (int k = 1; k < nw; ++k) {
+        mn = __builtin_fminf(mn, smn[k]);
+        mx = __builtin_fmaxf(mx, smx[k]);
+    }
+}
+
+template <int FT, bool SYM>
+__global__ __launch_bounds__(256) void k_reduce_generic(const void* __restrict__ x, DMap m, float qmin,
+                                                        float qmax, float* __restrict__ scale,
+                                                        uint8_t* __restrict__ zp)
+{
+    const int64_t gid = blockIdx.x;
+    const int64_t cnt = m.count();
+    float mn = 0.0f, mx = 0.0f;
+    for (int64_t j = threadIdx.x; j < cnt; j += blockDim.x) {
+        float v = load1<FT>(x, m.elem(gid, j));
+        if (SYM) {
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+        } else {
+            mn = __builtin_fminf(mn, v);
+            mx = __builtin_fmaxf(mx, v);
+        }
+    }
+    block_minmax(mn, mx);
+    if (threadIdx.x == 0) {
+        GP p = SYM ? make_gp<true>(mx, 0.0f, 0.0f, qmin, qmax) : make_gp<false>(0.0f, mn, mx, qmin, qmax);
+        scale[gid] = p.s;
+        if (!SYM) zp[gid] = (uint8_t)(int)p.zpf;
+    }
+}
+
+__device__ __forceinline__ float zp_at(const uint8_t* zp, int64_t gid, bool zp_signed)
+{
+    if (!zp) return 0.0f;
+    return zp_signed ? (float)(int8_t)zp[gid] : (float)zp[gid];
+}
+
+// One code, IEEE division (generic path).
+template <int FT>
+__device__ __forceinline__ int code_generic(const void* x, const DMap& m, int64_t e, float qmin,
+                                            float qmax, const float* scale, const uint8_t* zp,
+                                            bool zp_signed)
+{
+    const int64_t gid = m.group_of(e);
+    const float v = load1<FT>(x, e) / scale[gid];
+    const float c = __builtin_amdgcn_fmed3f(__builtin_rintf(v) + zp_at(zp, gid, zp_signed), qmin, qmax);
+    return (int)c;
+}
+
+template <int FT, int BITS>
+__global__ __launch_bounds__(256) void k_encode_generic(const void* __restrict__ x, DMap m, float qmin,
+                                                        float qmax, const float* __restrict__ scale,
+                                                        const uint8_t* __restrict__ zp, bool zp_signed,
+                                                        uint8_t* __restrict__ q, int64_t nbytes)
+{
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nbytes;
+         b += (int64_t)gridDim.x * blockDim.x) {
+        if (BITS == 8) {
+            q[b] = (uint8_t)code_generic<FT>(x, m, b, qmin, qmax, scale, zp, zp_signed);
+        } else {
+            int c0 = code_generic<FT>(x, m, 2 * b, qmin, qmax, scale, zp, zp_signed);
+            int c1 = code_generic<FT>(x, m, 2 * b + 1, qmin, qmax, scale, zp, zp_signed);
+            q[b] = (uint8_t)((c0 & 0xf) | ((c1 & 0xf) << 4));
+        }
+    }
+}
+
+// ------------------------------------------------------------ per tensor
+// Pass 1: each block reduces a contiguous chunk and writes
+// ws[b] = max(max |x| or max x, 0) and ws[nblk + b] = |min(min x, 0)|.
+template <int FT, bool SYM>
+__global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__ x, int64_t numel,
+                                                        int64_t chunk, float* __restrict__ ws)
+{
+    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < numel ? b0 + chunk : numel;
+    float mn = 0.0f, mx = 0.0f;
+    if ((numel & 7) == 0) {
+        for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8) {
+            float v[8];
+            widen8<FT>(load8<FT>(x, e), v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (SYM) {
+                    mx = __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
+                } else {
+                    mn = __builtin_fminf(mn, v[i]);
+                    mx = __builtin_fmaxf(mx, v[i]);
+                }
+            }
+        }
+    } else {
+        for (int64_t e = b0 + threadIdx.x; e < b1; e += 256) {
+            float v = load1<FT>(x, e);
+            if (SYM) {
+                mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+            } else {
+                mn = __builtin_fminf(mn, v);
+                mx = __builtin_fmaxf(mx, v);
+            }
+        }
+    }
+    block_minmax(mn, mx);
+    if (threadIdx.x == 0) {
+        ws[blockIdx.x] = mx;
+        ws[gridDim.x + blockIdx.x] = __builtin_fabsf(mn);
+    }
+}
+
+// Pass 2: every block merges the partials (or reads the static scale),
+// block 0 publishes scale / zero-point, and all blocks encode.
+template <int FT, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ x, int64_t numel,
+                                                       const float* __restrict__ ws, int nblk,
+                                                       int static_scale, float qmin, float qmax,
+                                                       uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                       uint8_t* __restrict__ zp, bool zp_signed)
+{
+    __shared__ GP sp;
+    if (threadIdx.x < 64) {
+        if (static_scale) {
+            if (threadIdx.x == 0) {
+                GP p;
+                p.s = scale[0];
+                p.y = 1.0f / p.s;
+                p.zpf = zp_at(zp, 0, zp_signed);
+                p.fast = scale_in_fast_range(p.s);
+                sp = p;
+            }
+        } else {
+            float mx = 0.0f, nmn = 0.0f;
+            for (int k = threadIdx.x; k < nblk; k += 64) {
+                mx = __builtin_fmaxf(mx, ws[k]);
+                nmn = __builtin_fmaxf(nmn, ws[nblk + k]);
+            }
+            mx = team_max<64>(mx);
+            nmn = team_max<64>(nmn);
+            if (threadIdx.x == 0) {
+                GP p = SYM ? make_gp<true>(mx, 0.0f, 0.0f, qmin, qmax) : make_gp<false>(0.0f, -nmn, mx, qmin, qmax);
+                sp = p;
+                if (blockIdx.x == 0) {
+                    scale[0] = p.s;
+                    if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const GP p = sp;
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if ((numel & 7) == 0) {
+        for (int64_t vi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; vi < numel / 8; vi += stride) {
+            float v[8], c[8];
+            widen8<FT>(load8<FT>(x, vi * 8), v);
+            if (p.fast) enc8<true>(v, p, lo, hi, c);
+            else enc8<false>(v, p, lo, hi, c);
+            store_codes8<BITS>(q, vi * 8, c);
+        }
+    } else {
+        const int64_t nbytes = BITS == 8 ? numel : numel / 2;
+        for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nbytes; b += stride) {
+            if (BITS == 8) {
+                q[b] = (uint8_t)(int)int_code_f(load1<FT>(x, b) / p.s, p.zpf, lo, hi);
+            } else {
+                int c0 = (int)int_code_f(load1<FT>(x, 2 * b) / p.s, p.zpf, lo, hi);
+                int c1 = (int)int_code_f(load1<FT>(x, 2 * b + 1) / p.s, p.zpf, lo, hi);
+                q[b] = (uint8_t)((c0 & 0xf) | ((c1 & 0xf) << 4));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ elementwise
+// Group ids of a vector of 8 elements starting at e (e % 8 == 0):
+//   MAP_CONTIG: groups of L contiguous elements (L % 8 == 0): one group e / L.
+//   MAP_COLS  : [B, R, C] column groups (C % 8 == 0): groups
+//               (e / (R*C)) * C + e % C + i, i = 0..7.
+enum { MAP_CONTIG = 0, MAP_COLS = 1 };
+
+template <int MAPK>
+__device__ __forceinline__ int64_t vec_group(int64_t e, int64_t P1, int64_t P2)
+{
+    if constexpr (MAPK == MAP_CONTIG) return e / P1;
+    else return (e / (P1 * P2)) * P2 + e % P2;
+}
+
+template <int BITS, bool SIGNED>
+__device__ __forceinline__ void load_codes8(const uint8_t* q, int64_t e, int c[8])
+{
+    if constexpr (BITS == 8) {
+        uint2 w = *reinterpret_cast<const uint2*>(q + e);
+        const uint32_t ws[2] = {w.x, w.y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t b = (ws[i >> 2] >> ((i & 3) * 8)) & 0xffu;
+            c[i] = SIGNED ? (int)(int8_t)b : (int)b;
+        }
+    } else {
+        uint32_t w = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t n = (w >> (i * 4)) & 0xfu;
+            c[i] = SIGNED ? (int)((n ^ 8u) - 8u) : (int)n;
+        }
+    }
+}
+
+constexpr int VPT = 4;   // vectors per thread per iteration
+
+template <int MAPK, int YT, int BITS, bool SIGNED>
+__global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__ q, int64_t nvec, int64_t P1,
+                                                     int64_t P2, const float* __restrict__ scale,
+                                                     const uint8_t* __restrict__ zp, void* __restrict__ y)
+{
+    for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi >= nvec) break;
+            const int64_t e = vi * 8;
+            int c[8];
+            load_codes8<BITS, SIGNED>(q, e, c);
+            const int64_t g = vec_group<MAPK>(e, P1, P2);
+            float out[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t gi = MAPK == MAP_CONTIG ? g : g + i;
+                const float z = zp ? (SIGNED ? (float)(int8_t)zp[gi] : (float)zp[gi]) : 0.0f;
+                out[i] = ((float)c[i] - z) * scale[gi];
+            }
+            store8<YT>(y, e, out);
+        }
+    }
+}
+
+template <int MAPK, int FT>
+__global__ __launch_bounds__(256) void k_dqb_vec(const void* __restrict__ dy, int64_t nvec, int64_t P1,
+                                                 int64_t P2, const float* __restrict__ scale,
+                                                 void* __restrict__ dq)
+{
+    for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
+        Raw8<FT> raw[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi < nvec) raw[k] = load8<FT>(dy, vi * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi >= nvec) break;
+            const int64_t e = vi * 8;
+            const int64_t g = vec_group<MAPK>(e, P1, P2);
+            float v[8];
+            widen8<FT>(raw[k], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = v[i] * scale[MAPK == MAP_CONTIG ? g : g + i];
+            store8<FT>(dq, e, v);
+        }
+    }
+}
+
+// STE: q recomputed from x; dx = (dy / s) * 1[qmin < q < qmax].
+template <int MAPK, int FT, bool SIGNED>
+__global__ __launch_bounds__(256) void k_ste_vec(const void* __restrict__ x, const void* __restrict__ dy,
+                                                 int64_t nvec, int64_t P1, int64_t P2, float qmin, float qmax,
+                                                 const float* __restrict__ scale,
+                                                 const uint8_t* __restrict__ zp, void* __restrict__ dx)
+{
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
+        Raw8<FT> rx[VPT], rd[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi < nvec) {
+                rx[k] = load8<FT>(x, vi * 8);
+                rd[k] = load8<FT>(dy, vi * 8);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi >= nvec) break;
+            const int64_t e = vi * 8;
+            const int64_t g = vec_group<MAPK>(e, P1, P2);
+            float xv[8], dv[8], out[8];
+            widen8<FT>(rx[k], xv);
+            widen8<FT>(rd[k], dv);
+            if constexpr (MAPK == MAP_CONTIG) {
+                const float s = scale[g];
+                const float zf = zp ? (SIGNED ? (float)(int8_t)zp[g] : (float)zp[g]) : 0.0f;
+                const float yr = 1.0f / s;
+                bool ok = scale_in_fast_range(s);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ok = ok && value_in_fast_range(dv[i]);
+                if (ok) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float c = int_code_f(div_fast(xv[i], s, yr), zf, lo, hi);
+                        const float m = (c > lo && c < hi) ? 1.0f : 0.0f;
+                        out[i] = div_fast(dv[i], s, yr) * m;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float c = int_code_f(xv[i] / s, zf, lo, hi);
+                        const float m = (c > lo && c < hi) ? 1.0f : 0.0f;
+                        out[i] = (dv[i] / s) * m;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float s = scale[g + i];
+                    const float zf = zp ? (SIGNED ? (float)(int8_t)zp[g + i] : (float)zp[g + i]) : 0.0f;
+                    const float c = int_code_f(xv[i] / s, zf, lo, hi);
+                    const float m = (c > lo && c < hi) ? 1.0f : 0.0f;
+                    out[i] = (dv[i] / s) * m;
+                }
+            }
+            store8<FT>(dx, e, out);
+        }
+    }
+}
+
+// Generic elementwise ops (any group layout, one element per thread step).
+template <int YT, int BITS, bool SIGNED>
+__global__ __launch_bounds__(256) void k_dequant_generic(const uint8_t* __restrict__ q, DMap m,
+                                                         const float* __restrict__ scale,
+                                                         const uint8_t* __restrict__ zp, void* __restrict__ y)
+{
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m.numel;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        int c;
+        if (BITS == 8) {
+            c = SIGNED ? (int)(int8_t)q[e] : (int)q[e];
+        } else {
+            uint32_t n = (e & 1) ? (q[e >> 1] >> 4) : (q[e >> 1] & 0xfu);
+            c = SIGNED ? (int)((n ^ 8u) - 8u) : (int)n;
+        }
+        const int64_t g = m.group_of(e);
+        const float z = zp ? (SIGNED ? (float)(int8_t)zp[g] : (float)zp[g]) : 0.0f;
+        store1<YT>(y, e, ((float)c - z) * scale[g]);
+    }
+}
+
+template <int FT>
+__global__ __launch_bounds__(256) void k_dqb_generic(const void* __restrict__ dy, DMap m,
+                                                     const float* __restrict__ scale, void* __restrict__ dq)
+{
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m.numel;
+         e += (int64_t)gridDim.x * blockDim.x)
+        store1<FT>(dq, e, load1<FT>(dy, e) * scale[m.group_of(e)]);
+}
+
+template <int FT, bool SIGNED>
+__global__ __launch_bounds__(256) void k_ste_generic(const void* __restrict__ x, const void* __restrict__ dy,
+                                                     DMap m, float qmin, float qmax,
+                                                     const float* __restrict__ scale,
+                                                     const uint8_t* __restrict__ zp, void* __restrict__ dx)
+{
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m.numel;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t g = m.group_of(e);
+        const float s = scale[g];
+        const float z = zp ? (SIGNED ? (float)(int8_t)zp[g] : (float)zp[g]) : 0.0f;
+        const float c = int_code_f(load1<FT>(x, e) / s, z, lo, hi);
+        const float mk = (c > lo && c < hi) ? 1.0f : 0.0f;
+        store1<FT>(dx, e, (load1<FT>(dy, e) / s) * mk);
+    }
+}
+
+// ============================================================ host side
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static unsigned grid_for(int64_t work, int64_t per_block)
+{
+    int64_t g = cdiv(work, per_block);
+    if (g < 1) g = 1;
+    if (g > (1 << 20)) g = 1 << 20;
+    return (unsigned)g;
+}
+
+// Dispatch helpers over the runtime (ftype, bits, symmetric) triple.
+#define TQ_FT_SWITCH(ft, ...)                                     \
+    switch (ft) {                                                 \
+    case TQ_F32: { constexpr int FTV = F32; __VA_ARGS__; } break; \
+    case TQ_F16: { constexpr int FTV = F16; __VA_ARGS__; } break; \
+    default: { constexpr int FTV = BF16; __VA_ARGS__; } break;    \
+    }
+
+#define TQ_BITS_SYM_SWITCH(bits, sym, ...)                                                  \
+    if (bits == 8 && sym) { constexpr int BV = 8; constexpr bool SV = true; __VA_ARGS__; }  \
+    else if (bits == 8) { constexpr int BV = 8; constexpr bool SV = false; __VA_ARGS__; }   \
+    else if (sym) { constexpr int BV = 4; constexpr bool SV = true; __VA_ARGS__; }          \
+    else { constexpr int BV = 4; constexpr bool SV = false; __VA_ARGS__; }
+
+template <int FT, int BITS, bool SYM, int T, int W, int U>
+static void launch_team(const void* x, int64_t G, float qmin, float qmax, uint8_t* q, float* scale,
+                        uint8_t* zp, hipStream_t st)
+{
+    constexpr int P = 64 / T;
+    const int64_t waves = cdiv(G, (int64_t)U * P);
+    hipLaunchKernelGGL((k_quant_team<FT, BITS, SYM, T, W, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st,
+                       x, G, qmin, qmax, q, scale, zp);
+}
+
+// Contiguous groups of length L (L % 8 == 0), G groups.
+template <int FT, int BITS, bool SYM>
+static void quant_contig(const void* x, int64_t G, int64_t L, float qmin, float qmax, uint8_t* q,
+                         float* scale, uint8_t* zp, hipStream_t st)
+{
+    switch (L) {
+    case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 128: launch_team<FT, BITS, SYM, 16, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 256: launch_team<FT, BITS, SYM, 32, 1, 4>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 4096: launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, qmin, qmax, q, scale, zp, st); return;
+    default:
+        hipLaunchKernelGGL((k_quant_long<FT, BITS, SYM>), dim3((unsigned)cdiv(G, 4)), dim3(256), 0, st,
+                           x, G, L, qmin, qmax, q, scale, zp);
+    }
+}
+
+// Quantize with a group map; picks the contiguous, column or generic path.
+static tq_status quant_mapped(const void* x, int xt, const GroupMap& m, int code, int32_t qmin, int32_t qmax,
+                              void* q, float* scale, void* zero_point, hipStream_t st)
+{
+    const bool sym = zero_point == nullptr;
+    const int bits = code_bits(code);
+    const float fmin = (float)qmin, fmax = (float)qmax;
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    uint8_t* zb = static_cast<uint8_t*>(zero_point);
+    if (m.numel == 0) return TQ_OK;
+    const int es = ftype_size(xt);
+    // contiguous groups: per-token, per-group on the last axis, per-channel on axis 0
+    int64_t L = -1, G = 0;
+    if (m.kind == KIND_GROUP && m.inner == 1) { L = m.g; G = m.ngroups; }
+    if (m.kind == KIND_CHANNEL && m.outer == 1) { L = m.inner; G = m.A; }
+    if (L > 0 && L % 8 == 0 && (L * es) % 16 == 0) {
+        TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym, quant_contig<FTV, BV, SV>(x, G, L, fmin, fmax, qb, scale, zb, st)));
+        return launch_status();
+    }
+    // column groups: per-channel on the last axis, per-group on a non-last axis
+    int64_t B = 0, R = 0, C = 0;
+    if (m.kind == KIND_CHANNEL && m.inner == 1) { B = 1; R = m.outer; C = m.A; }
+    if (m.kind == KIND_GROUP && m.inner > 1) { B = m.outer * (m.A / m.g); R = m.g; C = m.inner; }
+    if (C > 0 && C % 8 == 0 && (C * es) % 16 == 0 && B <= 65535) {
+        dim3 grid((unsigned)cdiv(C, 512), (unsigned)B);
+        TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym,
+            hipLaunchKernelGGL((k_quant_cols<FTV, BV, SV>), grid, dim3(256), 0, st, x, R, C, fmin, fmax, qb, scale, zb)));
+        return launch_status();
+    }
+    // generic
+    if (m.ngroups > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    const DMap d = to_dmap(m);
+    TQ_FT_SWITCH(xt, {
+        if (sym) hipLaunchKernelGGL((k_reduce_generic<FTV, true>), dim3((unsigned)m.ngroups), dim3(256), 0, st,
+                                    x, d, fmin, fmax, scale, zb);
+        else hipLaunchKernelGGL((k_reduce_generic<FTV, false>), dim3((unsigned)m.ngroups), dim3(256), 0, st,
+                                x, d, fmin, fmax, scale, zb);
+    });
+    const int64_t nbytes = bits == 8 ? m.numel : m.numel / 2;
+    const bool zs = code_signed(code);
+    TQ_FT_SWITCH(xt, {
+        if (bits == 8) hipLaunchKernelGGL((k_encode_generic<FTV, 8>), dim3(grid_for(nbytes, 256)), dim3(256), 0, st,
+                                          x, d, fmin, fmax, scale, zb, zs, qb, nbytes);
+        else hipLaunchKernelGGL((k_encode_generic<FTV, 4>), dim3(grid_for(nbytes, 256)), dim3(256), 0, st,
+                                x, d, fmin, fmax, scale, zb, zs, qb, nbytes);
+    });
+    return launch_status();
+}
+
+// Elementwise ops with a group map.
+enum { OP_DEQ = 0, OP_STE = 1, OP_DQB = 2 };
+
+struct EwArgs {
+    const void* a;      // q (DEQ), x (STE), dy (DQB)
+    const void* b;      // dy (STE)
+    void* out;          // y / dx / dq
+    int in_type;        // ftype of x / dy
+    int out_type;       // ftype of y (DEQ)
+    int code;
+    float qmin, qmax;
+    const float* scale;
+    const uint8_t* zp;
+};
+
+template <int MAPK>
+static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int64_t P2, hipStream_t st)
+{
+    const dim3 grid(grid_for(nvec, 256 * VPT)), block(256);
+    const bool sg = code_signed(a.code);
+    const int bits = code_bits(a.code);
+    const uint8_t* q = static_cast<const uint8_t*>(a.a);
+    if (op == OP_DEQ) {
+        TQ_FT_SWITCH(a.out_type, {
+            if (bits == 8 && sg) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 8, true>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
+            else if (bits == 8) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 8, false>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
+            else if (sg) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 4, true>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
+            else hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 4, false>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
+        });
+    } else if (op == OP_STE) {
+        TQ_FT_SWITCH(a.in_type, {
+            if (sg) hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, true>), grid, block, 0, st, a.a, a.b, nvec, P1, P2, a.qmin, a.qmax, a.scale, a.zp, a.out);
+            else hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, false>), grid, block, 0, st, a.a, a.b, nvec, P1, P2, a.qmin, a.qmax, a.scale, a.zp, a.out);
+        });
+    } else {
+        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), grid, block, 0, st, a.a, nvec, P1, P2, a.scale, a.out));
+    }
+}
+
+static tq_status elementwise_mapped(int op, const EwArgs& a, const GroupMap& m, hipStream_t st)
+{
+    if (m.numel == 0) return TQ_OK;
+    const int64_t nvec = m.numel / 8;
+    const bool vec_ok = m.numel % 8 == 0;
+    int64_t L = -1;
+    if (m.kind == KIND_TENSOR) L = m.numel;
+    if (m.kind == KIND_GROUP && m.inner == 1) L = m.g;
+    if (m.kind == KIND_CHANNEL && m.outer == 1) L = m.inner;
+    if (vec_ok && L > 0 && L % 8 == 0) {
+        launch_ew_vec<MAP_CONTIG>(op, a, nvec, L, 0, st);
+        return launch_status();
+    }
+    int64_t R = 0, C = 0;
+    if (m.kind == KIND_CHANNEL && m.inner == 1) { R = m.outer; C = m.A; }
+    if (m.kind == KIND_GROUP && m.inner > 1) { R = m.g; C = m.inner; }
+    if (vec_ok && C > 0 && C % 8 == 0) {
+        launch_ew_vec<MAP_COLS>(op, a, nvec, R, C, st);
+        return launch_status();
+    }
+    const DMap d = to_dmap(m);
+    const dim3 grid(grid_for(m.numel, 256)), block(256);
+    const bool sg = code_signed(a.code);
+    const uint8_t* q = static_cast<const uint8_t*>(a.a);
+    if (op == OP_DEQ) {
+        const int bits = code_bits(a.code);
+        TQ_FT_SWITCH(a.out_type, {
+            if (bits == 8 && sg) hipLaunchKernelGGL((k_dequant_generic<FTV, 8, true>), grid, block, 0, st, q, d, a.scale, a.zp, a.out);
+            else if (bits == 8) hipLaunchKernelGGL((k_dequant_generic<FTV, 8, false>), grid, block, 0, st, q, d, a.scale, a.zp, a.out);
+            else if (sg) hipLaunchKernelGGL((k_dequant_generic<FTV, 4, true>), grid, block, 0, st, q, d, a.scale, a.zp, a.out);
+            else hipLaunchKernelGGL((k_dequant_generic<FTV, 4, false>), grid, block, 0, st, q, d, a.scale, a.zp, a.out);
+        });
+    } else if (op == OP_STE) {
+        TQ_FT_SWITCH(a.in_type, {
+            if (sg) hipLaunchKernelGGL((k_ste_generic<FTV, true>), grid, block, 0, st, a.a, a.b, d, a.qmin, a.qmax, a.scale, a.zp, a.out);
+            else hipLaunchKernelGGL((k_ste_generic<FTV, false>), grid, block, 0, st, a.a, a.b, d, a.qmin, a.qmax, a.scale, a.zp, a.out);
+        });
+    } else {
+        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_generic<FTV>), grid, block, 0, st, a.a, d, a.scale, a.out));
+    }
+    return launch_status();
+}
+
+// ------------------------------------------------------------ validation
+// With no elements every pointer may be NULL (empty tensors have no
+// storage), so an empty call only needs a range that is valid in some mode.
+static tq_status check_quant_args(const void* x, int xt, int code, int32_t qmin, int32_t qmax, const void* q,
+                                  const float* scale, const void* zp, int64_t last_dim, int64_t numel)
+{
+    if (!valid_ftype(xt)) return TQ_ERR_INVALID;
+    if (!valid_range(code, qmin, qmax, zp == nullptr) && !(numel == 0 && valid_range(code, qmin, qmax, false)))
+        return TQ_ERR_INVALID;
+    if (code_bits(code) == 4 && (last_dim & 1)) return TQ_ERR_INVALID;
+    if (numel == 0) return TQ_OK;
+    if (!x || !q || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
+    return TQ_OK;
+}
+
+static int64_t shape_numel(int32_t ndim, const int64_t* shape)
+{
+    int64_t n = 1;
+    for (int d = 0; d < ndim; ++d) n *= shape[d];
+    return n;
+}
+
+static tq_status check_map_args(int32_t ndim, const int64_t* shape, int32_t axis)
+{
+    if (ndim < 1 || ndim > 8 || !shape) return TQ_ERR_INVALID;
+    for (int d = 0; d < ndim; ++d)
+        if (shape[d] < 0) return TQ_ERR_INVALID;
+    if (axis < 0 || axis >= ndim) return TQ_ERR_INVALID;
+    return TQ_OK;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+// ============================================================ C ABI
+extern "C" {
+
+tq_status tq_quant_per_token(const void* x, int x_dtype, int64_t rows, int64_t cols, int code, int32_t qmin,
+                             int32_t qmax, void* q, float* scale, void* zero_point, void* stream)
+{
+    if (rows < 0 || cols < 0 || (rows > 0 && cols == 0)) return TQ_ERR_INVALID;
+    tq_status s = check_quant_args(x, x_dtype, code, qmin, qmax, q, scale, zero_point, cols, rows * cols);
+    if (s || rows == 0) return s;
+    return quant_mapped(x, x_dtype, token_map(rows, cols), code, qmin, qmax, q, scale, zero_point,
+                        as_stream(stream));
+}
+
+tq_status tq_quant_per_channel(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape, int32_t axis,
+                               int code, int32_t qmin, int32_t qmax, void* q, float* scale, void* zero_point,
+                               void* stream)
+{
+    tq_status s = check_map_args(ndim, host_shape, axis);
+    if (s) return s;
+    const int64_t numel = shape_numel(ndim, host_shape);
+    s = check_quant_args(x, x_dtype, code, qmin, qmax, q, scale, zero_point, host_shape[ndim - 1], numel);
+    if (s || numel == 0) return s;
+    GroupMap m;
+    if (!make_map(KIND_CHANNEL, ndim, host_shape, axis, 1, &m)) return TQ_ERR_INVALID;
+    return quant_mapped(x, x_dtype, m, code, qmin, qmax, q, scale, zero_point, as_stream(stream));
+}
+
+tq_status tq_quant_per_group(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape, int32_t axis,
+                             int64_t group_size, int code, int32_t qmin, int32_t qmax, void* q, float* scale,
+                             void* zero_point, void* stream)
+{
+    tq_status s = check_map_args(ndim, host_shape, axis);
+    if (s) return s;
+    const int64_t numel = shape_numel(ndim, host_shape);
+    s = check_quant_args(x, x_dtype, code, qmin, qmax, q, scale, zero_point, host_shape[ndim - 1], numel);
+    if (s) return s;
+    GroupMap m;
+    if (!make_map(KIND_GROUP, ndim, host_shape, axis, group_size, &m)) return TQ_ERR_INVALID;
+    return quant_mapped(x, x_dtype, m, code, qmin, qmax, q, scale, zero_point, as_stream(stream));
+}
+
+size_t tq_workspace_bytes(int op, int64_t numel)
+{
+    (void)numel;
+    if (op == 0 || op == 1) return 2 * 1024 * sizeof(float);
+    return 0;
+}
+
+tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int code, int32_t qmin, int32_t qmax,
+                              int static_scale, void* q, float* scale, void* zero_point, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    if (numel < 0) return TQ_ERR_INVALID;
+    tq_status s = check_quant_args(x, x_dtype, code, qmin, qmax, q, scale, zero_point, numel, numel);
+    if (s || numel == 0) return s;
+    hipStream_t st = as_stream(stream);
+    const bool sym = zero_point == nullptr;
+    const int bits = code_bits(code);
+    int nblk = 0;
+    if (!static_scale) {
+        if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
+        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
+        nblk = (int)cdiv(numel, chunk);
+        float* ws = static_cast<float*>(workspace);
+        TQ_FT_SWITCH(x_dtype, {
+            if (sym) hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
+            else hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
+        });
+        if (launch_status()) return TQ_ERR_HIP;
+    }
+    const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
+    const dim3 grid(grid_for(work, 256 * 4));
+    const float* ws = static_cast<const float*>(workspace);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    uint8_t* zb = static_cast<uint8_t*>(zero_point);
+    const bool zs = code_signed(code);
+    TQ_FT_SWITCH(x_dtype, TQ_BITS_SYM_SWITCH(bits, sym,
+        hipLaunchKernelGGL((k_tensor_encode<FTV, BV, SV>), grid, dim3(256), 0, st, x, numel, ws, nblk,
+                           static_scale, (float)qmin, (float)qmax, qb, scale, zb, zs)));
+    return launch_status();
+}
+
+// ---------------------------------------------------------------- dequant
+static tq_status dequant_common(const void* q, int code, const GroupMap& m, const float* scale,
+                                const void* zero_point, void* y, int y_dtype, void* stream)
+{
+    if (!valid_code(code) || !valid_ftype(y_dtype)) return TQ_ERR_INVALID;
+    if (m.numel == 0) return TQ_OK;
+    if (!q || !scale || !y) return TQ_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(y)) return TQ_ERR_ALIGN;
+    EwArgs a{};
+    a.a = q;
+    a.out = y;
+    a.out_type = y_dtype;
+    a.code = code;
+    a.scale = scale;
+    a.zp = static_cast<const uint8_t*>(zero_point);
+    return elementwise_mapped(OP_DEQ, a, m, as_stream(stream));
+}
+
+tq_status tq_dequant_per_tensor(const void* q, int code, int64_t numel, const float* scale, const void* zero_point,
+                                void* y, int y_dtype, void* stream)
+{
+    if (numel < 0 || (code_bits(code) == 4 && (numel & 1))) return TQ_ERR_INVALID;
+    return dequant_common(q, code, tensor_map(numel), scale, zero_point, y, y_dtype, stream);
+}
+
+tq_status tq_dequant_per_channel(const void* q, int code, int32_t ndim, const int64_t* host_shape, int32_t axis,
+                                 const float* scale, const void* zero_point, void* y, int y_dtype, void* stream)
+{
+    if (check_map_args(ndim, host_shape, axis)) return TQ_ERR_INVALID;
+    if (code_bits(code) == 4 && (host_shape[ndim - 1] & 1)) return TQ_ERR_INVALID;
+    GroupMap m;
+    if (!make_map(KIND_CHANNEL, ndim, host_shape, axis, 1, &m)) return TQ_ERR_INVALID;
+    return dequant_common(q, code, m, scale, zero_point, y, y_dtype, stream);
+}
+
+tq_status tq_dequant_per_token(const void* q, int code, int64_t rows, int64_t cols, const float* scale,
+                               const void* zero_point, void* y, int y_dtype, void* stream)
+{
+    if (rows < 0 || cols < 0 || (rows > 0 && cols == 0) || (code_bits(code) == 4 && (cols & 1)))
+        return TQ_ERR_INVALID;
+    return dequant_common(q, code, token_map(rows, cols), scale, zero_point, y, y_dtype, stream);
+}
+
+tq_status tq_dequant_per_group(const void* q, int code, int32_t ndim, const int64_t* host_shape, int32_t axis,
+                               int64_t group_size, const float* scale, const void* zero_point, void* y,
+                               int y_dtype, void* stream)
+{
+    if (check_map_args(ndim, host_shape, axis)) return TQ_ERR_INVALID;
+    if (code_bits(code) == 4 && (host_shape[ndim - 1] & 1)) return TQ_ERR_INVALID;
+    GroupMap m;
+    if (!make_map(KIND_GROUP, ndim, host_shape, axis, group_size, &m)) return TQ_ERR_INVALID;
+    return dequant_common(q, code, m, scale, zero_point, y, y_dtype, stream);
+}
+
+// ---------------------------------------------------------------- STE
+static tq_status ste_common(const void* x, int x_dtype, const GroupMap& m, int code, int32_t qmin, int32_t qmax,
+                            const float* scale, const void* zero_point, const void* dy, void* dx, void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    if (m.numel == 0) return valid_code(code) && qmin < qmax ? TQ_OK : TQ_ERR_INVALID;
+    if (!valid_range(code, qmin, qmax, zero_point == nullptr)) return TQ_ERR_INVALID;
+    if (!x || !dy || !dx || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return TQ_ERR_ALIGN;
+    EwArgs a{};
+    a.a = x;
+    a.b = dy;
+    a.out = dx;
+    a.in_type = x_dtype;
+    a.code = code;
+    a.qmin = (float)qmin;
+    a.qmax = (float)qmax;
+    a.scale = scale;
+    a.zp = static_cast<const uint8_t*>(zero_point);
+    return elementwise_mapped(OP_STE, a, m, as_stream(stream));
+}
+
+tq_status tq_quant_per_tensor_backward(const void* x, int x_dtype, int64_t numel, int code, int32_t qmin,
+                                       int32_t qmax, const float* scale, const void* zero_point, const void* dy,
+                                       void* dx, void* stream)
+{
+    if (numel < 0) return TQ_ERR_INVALID;
+    return ste_common(x, x_dtype, tensor_map(numel), code, qmin, qmax, scale, zero_point, dy, dx, stream);
+}
+
+tq_status tq_quant_per_channel_backward(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape,
+                                        int32_t axis, int code, int32_t qmin, int32_t qmax, const float* scale,
+                                        const void* zero_point, const void* dy, void* dx, void* stream)
+{
+    if (check_map_args(ndim, host_shape, axis)) return TQ_ERR_INVALID;
+    GroupMap m;
+    if (!make_map(KIND_CHANNEL, ndim, host_shape, axis, 1, &m)) return TQ_ERR_INVALID;
+    return ste_common(x, x_dtype, m, code, qmin, qmax, scale, zero_point, dy, dx, stream);
+}
+
+tq_status tq_quant_per_token_backward(const void* x, int x_dtype, int64_t rows, int64_t cols, int code,
+                                      int32_t qmin, int32_t qmax, const float* scale, const void* zero_point,
+                                      const void* dy, void* dx, void* stream)
+{
+    if (rows < 0 || cols < 0 || (rows > 0 && cols == 0)) return TQ_ERR_INVALID;
+    return ste_common(x, x_dtype, token_map(rows, cols), code, qmin, qmax, scale, zero_point, dy, dx, stream);
+}
+
+tq_status tq_quant_per_group_backward(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape,
+                                      int32_t axis, int64_t group_size, int code, int32_t qmin, int32_t qmax,
+                                      const float* scale, const void* zero_point, const void* dy, void* dx,
+                                      void* stream)
+{
+    if (check_map_args(ndim, host_shape, axis)) return TQ_ERR_INVALID;
+    GroupMap m;
+    if (!make_map(KIND_GROUP, ndim, host_shape, axis, group_size, &m)) return TQ_ERR_INVALID;
+    return ste_common(x, x_dtype, m, code, qmin, qmax, scale, zero_point, dy, dx, stream);
+}
+
+// ---------------------------------------------------------------- dequant backward
+static tq_status dqb_common(const void* dy, int dy_dtype, const GroupMap& m, const float* scale, void* dq,
+                            void* stream)
+{
+    if (!valid_ftype(dy_dtype)) return TQ_ERR_INVALID;
+    if (m.numel == 0) return TQ_OK;
+    if (!dy || !dq || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(dy) || !aligned16(dq)) return TQ_ERR_ALIGN;
+    EwArgs a{};
+    a.a = dy;
+    a.out = dq;
+    a.in_type = dy_dtype;
+    a.code = TQ_S8;
+    a.scale = scale;
+    return elementwise_mapped(OP_DQB, a, m, as_stream(stream));
+}
+
+tq_status tq_dequant_per_tensor_backward(const void* dy, int dy_dtype, int64_t numel, const float* scale, void* dq,
+                                         void* stream)
+{
+    if (numel < 0) return TQ_ERR_INVALID;
+    return dqb_common(dy, dy_dtype, tensor_map(numel), scale, dq, stream);
+}
+
+tq_status tq_dequant_per_channel_backward(const void* dy, int dy_dtype, int32_t ndim, const int64_t* host_shape,
+                                          int32_t axis, const float* scale, void* dq, void* stream)
+{
+    if (check_map_args(ndim, host_shape, axis)) return TQ_ERR_INVALID;
+    GroupMap m;
+    if (!make_map(KIND_CHANNEL, ndim, host_shape, axis, 1, &m)) return TQ_ERR_INVALID;
+    return dqb_common(dy, dy_dtype, m, scale, dq, stream);
+}
+
+tq_status tq_dequant_per_token_backward(const void* dy, int dy_dtype, int64_t rows, int64_t cols,
+                                        const float* scale, void* dq, void* stream)
+{
+    if (rows < 0 || cols < 0 || (rows > 0 && cols == 0)) return TQ_ERR_INVALID;
+    return dqb_common(dy, dy_dtype, token_map(rows, cols), scale, dq, stream);
+}
+
+tq_status tq_dequant_per_group_backward(const void* dy, int dy_dtype, int32_t ndim, const int64_t* host_shape,
+                                        int32_t axis, int64_t group_size, const float* scale, void* dq,
+                                        void* stream)
+{
+    if (check_map_args(ndim, host_shape, axis)) return TQ_ERR_INVALID;
+    GroupMap m;
+    if (!make_map(KIND_GROUP, ndim, host_shape, axis, group_size, &m)) return TQ_ERR_INVALID;
+    return dqb_common(dy, dy_dtype, m, scale, dq, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/tq.h declares, and rejects malformed arguments on the host
+before anything is enqueued (only calls that fail validation are made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import tensor_quantization_amd as t
+    return t
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(tq):
+    names = _declared()
+    assert {"tq_quant_per_token", "tq_quant_fp4_block", "tq_fp4_transpose_for_gemm"} <= set(names)
+    for n in names:
+        assert hasattr(tq._lib, n), n
+    assert sorted(tq.EXPORTED) == names
+    for n in names:                      # the binding uses the C names
+        assert callable(getattr(tq, n, None)) or n in ("tq_status_str",), n
+
+
+def test_status_and_version(tq):
+    assert tq.tq_abi_version() == 1
+    assert tq._lib.tq_status_str(0) == b"ok"
+    assert tq._lib.tq_status_str(3) == b"misaligned pointer"
+
+
+def test_default_ranges_match_oracle(tq, orc):
+    for code in ("s8", "u8", "s4", "u4"):
+        for sym in (True, False):
+            if code in ("u8", "u4") and sym:
+                with pytest.raises(tq.TQError):
+                    tq.tq_default_q_range(code, sym)
+                continue
+            assert tq.tq_default_q_range(code, sym) == orc.default_q_range(code, sym)
+
+
+P = ctypes.c_void_p
+A = P(0x10000)          # aligned fake device addresses: never dereferenced,
+B = P(0x20000)          # every call below fails validation first
+C = P(0x30000)
+MIS = P(0x10008)
+
+
+def _shape(*s):
+    return (ctypes.c_int64 * len(s))(*s), len(s)
+
+
+def test_integer_validation(tq):
+    L = tq._lib
+    INV, ALIGN = tq.TQ_ERR_INVALID, tq.TQ_ERR_ALIGN
+    # null pointers, bad dtype, bad ranges
+    assert L.tq_quant_per_token(None, 2, 4, 8, 0, -127, 127, B, C, None, None) == INV
+    assert L.tq_quant_per_token(A, 7, 4, 8, 0, -127, 127, B, C, None, None) == INV
+    assert L.tq_quant_per_token(A, 2, 4, 8, 0, -128, 127, B, C, None, None) == INV   # symmetric needs -qmax
+    assert L.tq_quant_per_token(A, 2, 4, 8, 1, 0, 255, B, C, None, None) == INV      # symmetric unsigned
+    assert L.tq_quant_per_token(A, 2, 4, 8, 0, 5, 5, B, C, A, None) == INV           # qmin >= qmax
+    assert L.tq_quant_per_token(A, 2, 4, 8, 3, 0, 16, B, C, A, None) == INV          # beyond u4
+    assert L.tq_quant_per_token(A, 2, 4, 7, 3, 0, 15, B, C, A, None) == INV          # odd last dim, 4-bit
+    assert L.tq_quant_per_token(A, 2, -1, 8, 0, -127, 127, B, C, None, None) == INV
+    assert L.tq_quant_per_token(MIS, 2, 4, 8, 0, -127, 127, B, C, None, None) == ALIGN
+    # group size must divide the axis; axis in range
+    shp, nd = _shape(4, 100)
+    assert L.tq_quant_per_group(A, 1, nd, shp, 1, 128, 3, 0, 15, B, C, A, None) == INV
+    assert L.tq_quant_per_group(A, 1, nd, shp, 2, 4, 3, 0, 15, B, C, A, None) == INV
+    assert L.tq_quant_per_channel(A, 1, nd, shp, -1, 0, -127, 127, B, C, None, None) == INV
+    # per-tensor dynamic scale needs a workspace
+    assert L.tq_quant_per_tensor(A, 0, 64, 0, -127, 127, 0, B, C, None, None, 0, None) == INV
+    # dequant / STE / dequant-backward
+    assert L.tq_dequant_per_token(None, 0, 4, 8, C, None, B, 2, None) == INV
+    assert L.tq_dequant_per_token(A, 0, 4, 8, C, None, B, 9, None) == INV
+    assert L.tq_dequant_per_token(A, 3, 4, 7, C, None, B, 2, None) == INV
+    assert L.tq_quant_per_token_backward(A, 2, 4, 8, 0, -127, 127, C, None, None, B, None) == INV
+    assert L.tq_quant_per_token_backward(A, 2, 4, 8, 0, -127, 127, C, None, MIS, B, None) == ALIGN
+    assert L.tq_dequant_per_token_backward(A, 2, 4, 8, None, B, None) == INV
+
+
+def test_fp8_fp4_validation(tq):
+    L = tq._lib
+    INV, ALIGN = tq.TQ_ERR_INVALID, tq.TQ_ERR_ALIGN
+    assert L.tq_quant_fp8_block(A, 2, 100, 128, 128, 128, B, C, None) == INV     # rows % 128
+    assert L.tq_quant_fp8_block(A, 2, 128, 100, 1, 128, B, C, None) == INV       # cols % 128
+    assert L.tq_quant_fp8_block(A, 2, 128, 128, 0, 128, B, C, None) == INV
+    assert L.tq_quant_fp8_block(MIS, 2, 128, 128, 1, 128, B, C, None) == ALIGN
+    assert L.tq_dequant_fp8_block(A, 128, 128, 1, 128, None, B, 2, None) == INV
+    assert L.tq_quant_fp4_block(A, 2, 4, 24, 0, B, C, A, 1, None, 0, None) == INV   # k % 16
+    assert L.tq_quant_fp4_block(A, 2, 4, 48, 1, B, C, None, 0, None, 0, None) == INV  # k % 32
+    assert L.tq_quant_fp4_block(A, 2, 4, 32, 0, B, C, None, 1, None, 0, None) == INV  # NVFP4 needs s_g
+    assert L.tq_quant_fp4_block(A, 2, 4, 32, 0, B, C, A, 0, None, 0, None) == INV     # dynamic needs ws
+    assert L.tq_quant_fp4_block(A, 2, 4, 32, 5, B, C, A, 1, None, 0, None) == INV     # bad kind
+    assert L.tq_dequant_fp4_block(A, B, None, 4, 32, 0, C, 2, None) == INV
+    assert L.tq_fp4_transpose_for_gemm(A, B, 4, 31, 16, C, A, None) == INV
+    assert L.tq_fp4_transpose_for_gemm(A, B, 4, 32, 16, C, None, None) == INV
+
+
+def test_empty_inputs_enqueue_nothing(tq):
+    L = tq._lib
+    assert L.tq_quant_per_token(A, 2, 0, 8, 0, -127, 127, B, C, None, None) == 0
+    assert L.tq_quant_fp8_block(A, 2, 0, 128, 1, 128, B, C, None) == 0
+    assert L.tq_quant_fp4_block(A, 2, 0, 32, 1, B, C, None, 0, None, 0, None) == 0
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "tensor_quantization_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), os.path.join(dirpath, f)
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        assert "oracle" not in open(os.path.join(ROOT, "include", f)).read().lower()

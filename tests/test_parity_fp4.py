@@ -1,0 +1,120 @@
+"""GPU parity of the FP4 E2M1 family (NVFP4 with dynamic or static per-tensor
+scale, MXFP4; quantize, dequantize, STE, dequantize backward, transpose to
+GEMM layout) against the oracle, bit for bit, plus a dense check of the E2M1
+conversion."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import TORCH, assert_same, from_dev, note, to_dev
+from test_parity_int import nasty
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tq():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import tensor_quantization_amd as t
+    return t
+
+
+def run_fp4(tq, orc, x, xt, kind, static_global=None, dy=None):
+    note("fp4 case", x.shape, xt, kind, "static" if static_global is not None else "dynamic")
+    xd = to_dev(x, xt)
+    sgd = None if static_global is None else torch.tensor([static_global], dtype=torch.float32, device="cuda")
+    p, b, g = tq.tq_quant_fp4_block(xd, kind, global_scale=sgd)
+    op, ob, og = orc.quant_fp4_block(x, xt, kind, static_global=static_global)
+    assert_same(from_dev(p), op, "packed")
+    assert_same(from_dev(b), ob, "block scales")
+    if kind == "nvfp4":
+        assert_same(from_dev(g), og, "global scale")
+    for yt in {xt, "f32"}:
+        y = tq.tq_dequant_fp4_block(p, b, g, kind, out_dtype=TORCH[yt])
+        assert_same(from_dev(y), orc.dequant_fp4_block(op, ob, og[0], kind, yt), "dequant->" + yt)
+    if dy is None:
+        dy = workloads.normal(x.shape, 1.0, 99, xt)
+    dyd = to_dev(dy, xt)
+    dx = tq.tq_quant_fp4_block_backward(xd, dyd, b, g, kind)
+    assert_same(from_dev(dx), orc.quant_fp4_block_backward(x, xt, ob, og[0], kind, dy), "ste")
+    dq = tq.tq_dequant_fp4_block_backward(dyd, b, g, kind)
+    assert_same(from_dev(dq), orc.dequant_fp4_block_backward(dy, xt, ob, og[0], kind), "dq")
+    return p, b
+
+
+@pytest.mark.parametrize("shape,xt,kind", [
+    ((64, 4096), "bf16", "nvfp4"), ((64, 4096), "bf16", "mxfp4"),
+    ((37, 160), "f16", "nvfp4"), ((37, 160), "f32", "mxfp4"),
+    ((3, 32), "bf16", "nvfp4"), ((1, 96), "f16", "mxfp4"),
+    ((300, 48), "f32", "nvfp4"),
+])
+def test_fp4(tq, orc, shape, xt, kind):
+    x = workloads.normal(shape, 0.02, shape[0] + shape[1], xt)
+    run_fp4(tq, orc, x, xt, kind)
+
+
+def test_nvfp4_static_global(tq, orc):
+    x = workloads.normal((48, 512), 0.02, 5, "bf16")
+    run_fp4(tq, orc, x, "bf16", "nvfp4", static_global=np.float32(3.1e-5))
+
+
+@pytest.mark.parametrize("kind", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("xt", ["bf16", "f32"])
+def test_fp4_degenerate_values(tq, orc, kind, xt):
+    x = nasty((32, 256), xt, 21)
+    x[0, :64] = 0
+    x[1, 32:64] = workloads.to_storage(np.full(32, 1e-6, np.float32), xt)
+    run_fp4(tq, orc, x, xt, kind, dy=nasty((32, 256), xt, 22))
+
+
+def test_e2m1_conversion_dense(tq, orc):
+    """MXFP4 blocks whose max |x| lies in [4, 8) get E8M0 byte 127 (scale 1),
+    so their codes are the E2M1 encodings of the inputs: a dense sweep of
+    binary32 values in [2^-8, 7.99] (every 7th pattern), both signs."""
+    lo, hi = np.float32(2.0 ** -8).view(np.uint32), np.float32(7.99).view(np.uint32)
+    v = np.arange(lo, hi, 7, dtype=np.uint32).view(np.float32)
+    v = np.concatenate([v, -v, np.array([0.0, -0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0], np.float32)])
+    n = (v.size + 30) // 31 * 31
+    v = np.concatenate([v, np.zeros(n - v.size, np.float32)]).reshape(-1, 31)
+    x = np.concatenate([np.full((v.shape[0], 1), 4.0, np.float32), v], axis=1)
+    p, b, _ = tq.tq_quant_fp4_block(to_dev(x, "f32"), "mxfp4")
+    assert (from_dev(b) == 127).all()
+    codes = orc.enc_e2m1(x)
+    assert_same(from_dev(p), codes[:, 0::2] | (codes[:, 1::2] << 4), "E2M1 codes")
+
+
+def test_transpose_for_gemm(tq, orc):
+    for (n, k, kind) in [(14336 // 7, 4096, "nvfp4"), (256, 1024, "mxfp4"), (40, 96, "nvfp4"), (24, 64, "mxfp4")]:
+        gs = 16 if kind == "nvfp4" else 32
+        x = workloads.normal((n, k), 0.02, n + k, "bf16")
+        p, b, _ = tq.tq_quant_fp4_block(to_dev(x, "bf16"), kind)
+        pt, bt = tq.tq_fp4_transpose_for_gemm(p, b, n, k, gs)
+        op, ob = orc.fp4_transpose_for_gemm(from_dev(p), from_dev(b), n, k, gs)
+        assert_same(from_dev(pt), op, "packed^T %s" % ((n, k),))
+        assert_same(from_dev(bt), ob, "scales^T %s" % ((n, k),))
+
+
+def test_full_c5_sampled(tq, orc):
+    """Full [14336, 4096] bf16 weight: NVFP4 (dynamic per-tensor scale) and
+    MXFP4, then the GEMM-layout transposes; rows sampled for the oracle.  The
+    per-tensor scale is checked against an independent max |x| / 2688."""
+    w = workloads.make_input("c5_fp4_weight")
+    wd = to_dev(w, "bf16")
+    rows = np.unique(np.concatenate([[0, 14335], np.random.default_rng(4).choice(14336, 48, replace=False)]))
+    ws = np.ascontiguousarray(w[rows])
+    for kind, gs in (("nvfp4", 16), ("mxfp4", 32)):
+        p, b, g = tq.tq_quant_fp4_block(wd, kind)
+        pt, bt = tq.tq_fp4_transpose_for_gemm(p, b, 14336, 4096, gs)
+        sg = None
+        if kind == "nvfp4":
+            amax = np.abs(orc.widen(w, "bf16")).max()
+            sg = np.float32(np.float32(amax) / np.float32(2688.0))
+            assert_same(from_dev(g), np.array([sg], np.float32), "global scale")
+        op, ob, _ = orc.quant_fp4_block(ws, "bf16", kind, static_global=sg)
+        P, B = from_dev(p), from_dev(b)
+        assert_same(P[rows], op, kind + " packed")
+        assert_same(B[rows], ob, kind + " scales")
+        PT, BT = from_dev(pt), from_dev(bt)
+        assert_same(PT[:, rows], op.T, kind + " packed^T")
+        assert_same(BT[:, rows], ob.T, kind + " scales^T")
