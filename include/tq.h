@@ -89,8 +89,10 @@ const char* tq_status_str(int status);
 tq_status tq_default_q_range(int code, int symmetric, int32_t* host_qmin, int32_t* host_qmax);
 
 /* Bytes of device workspace a call needs ([Q] per-tensor scope and the NVFP4
- * per-tensor scale need a grid-wide reduction).  op: 0 = tq_quant_per_tensor,
- * 1 = tq_quant_fp4_block with a dynamic global scale.  numel = elements. */
+ * per-tensor scale need a grid-wide reduction).  op: 0 = tq_quant_per_tensor
+ * with a dynamic scale (0 bytes up to 65536 elements, which one workgroup
+ * reduces and encodes in a single launch), 1 = tq_quant_fp4_block with a
+ * dynamic global scale.  numel = elements. */
 size_t tq_workspace_bytes(int op, int64_t numel);
 
 /* ===================================================================== */
@@ -124,7 +126,8 @@ size_t tq_workspace_bytes(int op, int64_t numel);
 /* Per-tensor quantize.  static_scale != 0: scale (and zero_point) are
  * INPUTS (a static activation scale as in [W] field input_scale) and no
  * reduction runs.  Otherwise the grid-wide reduction uses `workspace`
- * (device, >= tq_workspace_bytes(0, numel) bytes, contents ignored). */
+ * (device, >= tq_workspace_bytes(0, numel) bytes, contents ignored; may be
+ * NULL when that is 0). */
 tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel,
                               int code, int32_t qmin, int32_t qmax, int static_scale,
                               void* q, float* scale, void* zero_point,

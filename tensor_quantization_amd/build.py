@@ -29,21 +29,23 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every csrc/*.hip and link `out`; `extra_flags` (e.g. -D tunables)
+    are appended to every compile line."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     procs, objs = [], []
     for s in srcs:
-        o = os.path.join(BUILD, os.path.basename(s) + ".o")
+        o = os.path.join(build_dir, os.path.basename(s) + ".o")
         objs.append(o)
-        cmd = [HIPCC, *FLAGS, "-c", s, "-o", o]
+        cmd = [HIPCC, *FLAGS, *extra_flags, "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for s, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
         lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip()]
         if p.returncode != 0:
@@ -53,10 +55,10 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write("\n".join(lines) + "\n")
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(os.path.basename(f) for f in failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

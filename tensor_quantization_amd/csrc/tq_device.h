@@ -22,20 +22,60 @@ __device__ __forceinline__ float as_f(uint32_t b) { return __uint_as_float(b); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 
 // ---------------------------------------------------------------- raw I/O
+// Streaming accesses: every input byte is read once and every output byte
+// written once.  Kernels mark an access non-temporal (NT) only when each
+// wave-wide instruction covers whole 128-byte lines: a non-temporal line
+// that an instruction uses only in part is evicted before the next
+// instruction needs the rest.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT = false>
+__device__ __forceinline__ uint4 ld16(const void* p)
+{
+    u32x4 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    else v = *static_cast<const u32x4*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void st16(void* p, uint4 w)
+{
+    const u32x4 v = {w.x, w.y, w.z, w.w};
+    if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+    else *static_cast<u32x4*>(p) = v;
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void st8(void* p, uint2 w)
+{
+    const u32x2 v = {w.x, w.y};
+    if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x2*>(p));
+    else *static_cast<u32x2*>(p) = v;
+}
+
+template <bool NT = false>
+__device__ __forceinline__ void st4(void* p, uint32_t w)
+{
+    if constexpr (NT) __builtin_nontemporal_store(w, static_cast<uint32_t*>(p));
+    else *static_cast<uint32_t*>(p) = w;
+}
+
 // Eight consecutive elements of a float tensor: one 16-byte load for the
 // 2-byte types, two for f32.
 template <int FT> struct Raw8 { uint4 w[FT == F32 ? 2 : 1]; };
 
-template <int FT>
+template <int FT, bool NT = false>
 __device__ __forceinline__ Raw8<FT> load8(const void* base, int64_t e)
 {
     Raw8<FT> r;
     if constexpr (FT == F32) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + e);
-        r.w[0] = p[0];
-        r.w[1] = p[1];
+        const float* p = static_cast<const float*>(base) + e;
+        r.w[0] = ld16<NT>(p);
+        r.w[1] = ld16<NT>(p + 4);
     } else {
-        r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+        r.w[0] = ld16<NT>(static_cast<const uint16_t*>(base) + e);
     }
     return r;
 }
@@ -109,17 +149,17 @@ __device__ __forceinline__ uint32_t narrow2(float a, float b)
 }
 
 // Store eight binary32 values as output type FT at element index e.
-template <int FT>
+template <int FT, bool NT = false>
 __device__ __forceinline__ void store8(void* base, int64_t e, const float v[8])
 {
     if constexpr (FT == F32) {
-        uint4* p = reinterpret_cast<uint4*>(static_cast<float*>(base) + e);
-        p[0] = make_uint4(as_u(v[0]), as_u(v[1]), as_u(v[2]), as_u(v[3]));
-        p[1] = make_uint4(as_u(v[4]), as_u(v[5]), as_u(v[6]), as_u(v[7]));
+        float* p = static_cast<float*>(base) + e;
+        st16<NT>(p, make_uint4(as_u(v[0]), as_u(v[1]), as_u(v[2]), as_u(v[3])));
+        st16<NT>(p + 4, make_uint4(as_u(v[4]), as_u(v[5]), as_u(v[6]), as_u(v[7])));
     } else {
         uint4 w = make_uint4(narrow2<FT>(v[0], v[1]), narrow2<FT>(v[2], v[3]),
                              narrow2<FT>(v[4], v[5]), narrow2<FT>(v[6], v[7]));
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = w;
+        st16<NT>(static_cast<uint16_t*>(base) + e, w);
     }
 }
 
@@ -144,24 +184,32 @@ __device__ __forceinline__ void store1(void* base, int64_t e, float v)
 }
 
 // ---------------------------------------------------------------- division
-// Correctly rounded binary32 x / s from y = RN(1/s) with two FMA
-// corrections (Markstein's division: the first correction makes the
-// quotient faithful, the second, with the correctly rounded reciprocal,
-// makes it correctly rounded; P. Markstein, IBM J. Res. Dev. 34(1), 1990).
-// Written as q + (-r) * y with r = q*s - x so that x = +-0 returns the zero
-// of x's sign, as IEEE division does.
-// Preconditions (no underflow / overflow in the intermediate steps):
-// 2^-40 <= |s| <= 2^40 and 2^-86 <= |x| <= 2^86, or x = +-0.  When |x| is
-// below 2^-86 the result still has x's sign and magnitude below 2^-45,
-// which is all that code selection needs (every code threshold is at
-// least 2^-10); outputs that are values (STE gradients) check |x| first.
-__device__ __forceinline__ float div_fast(float x, float s, float y)
+// Correctly rounded binary32 x / s from y = RN(1/s) by FMA corrections
+// (Markstein's division; P. Markstein, IBM J. Res. Dev. 34(1), 1990):
+//   q0 = x*y,  r = fma(q0, s, -x),  q1 = fma(-r, y, q0)     [one correction]
+//   r  = fma(q1, s, -x),  q2 = fma(-r, y, q1)               [second one]
+// One correction is exact when x is a bf16 or f16 value: every (dividend
+// significand with 7 or 10 fraction bits, binary32 divisor significand)
+// pair was checked against IEEE division, and rounding is scale-invariant
+// while the intermediates stay normal.  Binary32 dividends take both
+// corrections (the first makes the quotient faithful, the second correctly
+// rounded).  Written as q + (-r) * y so that x = +-0 returns the zero of x's
+// sign, as IEEE division does.
+// Exactness range: 2^-40 <= |s| <= 2^40 and 2^-78 <= |x| <= 2^86, or x = 0
+// (all intermediates stay normal).  Below 2^-78 the magnitude is still
+// below 2^-38, far under every code threshold (>= 2^-10), but its sign can
+// be wrong; callers that need that sign restore it with with_sign_of().
+template <int FTX>
+__device__ __forceinline__ float div_q(float x, float s, float y)
 {
     float q0 = x * y;
     float r = __builtin_fmaf(q0, s, -x);
     float q1 = __builtin_fmaf(-r, y, q0);
-    r = __builtin_fmaf(q1, s, -x);
-    return __builtin_fmaf(-r, y, q1);
+    if constexpr (FTX == F32) {
+        r = __builtin_fmaf(q1, s, -x);
+        q1 = __builtin_fmaf(-r, y, q1);
+    }
+    return q1;
 }
 
 __device__ __forceinline__ bool scale_in_fast_range(float s)
@@ -173,7 +221,33 @@ __device__ __forceinline__ bool scale_in_fast_range(float s)
 __device__ __forceinline__ bool value_in_fast_range(float x)
 {
     float a = __builtin_fabsf(x);
-    return a >= 0x1p-86f && a <= 0x1p86f;
+    return a >= 0x1p-78f && a <= 0x1p86f;
+}
+
+// RN(1/s) for 2^-40 <= |s| <= 2^40: v_rcp_f32 and one Newton step.  On
+// gfx950 this equals IEEE 1/s for every binary32 significand (checked
+// exhaustively at several exponents; the step is scale-invariant there).
+__device__ __forceinline__ float rcp_rn(float s)
+{
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, y0, 1.0f);
+    return __builtin_fmaf(e, y0, y0);
+}
+
+// x / c for a divisor c inside the fast range with yc = RN(1/c): the fast
+// sequence when x is in its exact range (or zero), IEEE division otherwise.
+template <int FTX>
+__device__ __forceinline__ float div_by(float x, float c, float yc)
+{
+    if (value_in_fast_range(x) || x == 0.0f) return div_q<FTX>(x, c, yc);
+    return x / c;
+}
+
+// |q| with the sign of x (exact for the fast quotients above, whose sign can
+// only be wrong when |q| < 2^-38).
+__device__ __forceinline__ float with_sign_of(float q, float x)
+{
+    return as_f((as_u(q) & 0x7fffffffu) | (as_u(x) & 0x80000000u));
 }
 
 // ---------------------------------------------------------------- lanes

@@ -34,11 +34,21 @@ __global__ __launch_bounds__(256) void k_amax_partial(const void* __restrict__ x
     const int64_t b0 = (int64_t)blockIdx.x * chunk;
     const int64_t b1 = b0 + chunk < numel ? b0 + chunk : numel;
     float a = 0.0f;
-    for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8) {
-        float v[8];
-        widen8<FT>(load8<FT>(x, e), v);
+    for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8 * 4) {
+        Raw8<FT> r[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+        for (int k = 0; k < 4; ++k) {
+            const int64_t ek = e + k * 256 * 8;
+            if (ek < b1) r[k] = load8<FT>(x, ek);
+            else r[k] = Raw8<FT>{};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float v[8];
+            widen8<FT>(r[k], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+        }
     }
     a = team_max<64>(a);
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
@@ -53,16 +63,21 @@ struct BP {
     bool fast;
 };
 
-__device__ __forceinline__ BP nv_params(float amax, float sg, float six_sg)
+// amax is an element magnitude of type FT (or 0); y6 = RN(1/(6 s_g)) when
+// 6 s_g is inside the fast divisor range, else 0.
+template <int FT>
+__device__ __forceinline__ BP nv_params(float amax, float sg, float six_sg, float y6)
 {
     BP p;
-    const float v = __builtin_amdgcn_fmed3f(amax / six_sg, 0.0f, 448.0f);
+    const float q = (y6 != 0.0f && (value_in_fast_range(amax) || amax == 0.0f)) ? div_q<FT>(amax, six_sg, y6)
+                                                                                  : amax / six_sg;
+    const float v = __builtin_amdgcn_fmed3f(q, 0.0f, 448.0f);
     uint32_t sb = e4m3_pack4(v, 0.0f, 0.0f, 0.0f) & 0xffu;
     if ((sb & 0x7fu) == 0) sb = 0x38;
     p.sb = sb;
     p.eff = e4m3_val(sb, 0) * sg;
-    p.y = 1.0f / p.eff;
     p.fast = scale_in_fast_range(p.eff);
+    p.y = p.fast ? rcp_rn(p.eff) : 0.0f;
     return p;
 }
 
@@ -76,17 +91,22 @@ __device__ __forceinline__ BP mx_params(float amax)
     return p;
 }
 
-// Quotients x / eff for 8 values.
-template <int KIND, bool FAST>
+// Quotients x / eff for 8 values (E2M1 keeps the sign of zero, so a fast
+// quotient gets x's sign back).
+template <int FT, int KIND, bool FAST>
 __device__ __forceinline__ void fp4_div8(const float v[8], const BP& p, float t[8])
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if constexpr (KIND == MX) t[i] = v[i] * p.y;
-        else t[i] = FAST ? div_fast(v[i], p.eff, p.y) : v[i] / p.eff;
+        else t[i] = FAST ? with_sign_of(div_q<FT>(v[i], p.eff, p.y), v[i]) : v[i] / p.eff;
     }
 }
 
+// A team of T = GS/8 lanes per block (2 for NVFP4, 4 for MXFP4): lane j holds
+// elements 8j..8j+7 of its block, so each load instruction of a wave reads
+// 1 KB contiguously and each code store writes 256 bytes contiguously; the
+// block max takes one or two DPP steps.  U rounds of 64/T blocks per wave.
 template <int FT, int KIND, int U>
 __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, int64_t nblocks,
                                                    const float* __restrict__ ws, int nws, int static_global,
@@ -94,7 +114,8 @@ __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, i
                                                    uint8_t* __restrict__ bscale)
 {
     constexpr int GS = KIND == NV ? 16 : 32;
-    constexpr int NV8 = GS / 8;
+    constexpr int T = GS / 8;
+    constexpr int P = 64 / T;
     __shared__ float s_sg;
     float sg = 1.0f;
     if constexpr (KIND == NV) {
@@ -116,43 +137,34 @@ __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, i
         sg = s_sg;
     }
     const float six_sg = 6.0f * sg;
+    const float y6 = scale_in_fast_range(six_sg) ? rcp_rn(six_sg) : 0.0f;
     const int lane = threadIdx.x & 63;
+    const int j = lane % T;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t b0 = wave * (U * 64) + lane;
-    Raw8<FT> raw[U][NV8];
+    const int64_t b0 = wave * (U * P) + lane / T;
+    Raw8<FT> raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t b = b0 + u * 64;
-#pragma unroll
-        for (int k = 0; k < NV8; ++k) {
-            if (b < nblocks) raw[u][k] = load8<FT>(x, b * GS + k * 8);
-            else raw[u][k] = Raw8<FT>{};
-        }
+        const int64_t b = b0 + (int64_t)u * P;
+        if (b < nblocks) raw[u] = load8<FT, true>(x, b * GS + j * 8);
+        else raw[u] = Raw8<FT>{};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t b = b0 + u * 64;
-        if (b >= nblocks) continue;
-        float v[NV8][8];
+        float v[8];
+        widen8<FT>(raw[u], v);
         float a = 0.0f;
 #pragma unroll
-        for (int k = 0; k < NV8; ++k) {
-            widen8<FT>(raw[u][k], v[k]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[k][i]));
-        }
-        const BP p = KIND == NV ? nv_params(a, sg, six_sg) : mx_params(a);
-        uint32_t w[NV8];
-#pragma unroll
-        for (int k = 0; k < NV8; ++k) {
-            float t[8];
-            if (p.fast) fp4_div8<KIND, true>(v[k], p, t);
-            else fp4_div8<KIND, false>(v[k], p, t);
-            w[k] = e2m1_pack8(t);
-        }
-        if constexpr (NV8 == 2) *reinterpret_cast<uint2*>(packed + b * 8) = make_uint2(w[0], w[1]);
-        else *reinterpret_cast<uint4*>(packed + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-        bscale[b] = (uint8_t)p.sb;
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+        a = team_max<T>(a);
+        const int64_t b = b0 + (int64_t)u * P;
+        if (b >= nblocks) continue;
+        const BP p = KIND == NV ? nv_params<FT>(a, sg, six_sg, y6) : mx_params(a);
+        float t[8];
+        if (p.fast) fp4_div8<FT, KIND, true>(v, p, t);
+        else fp4_div8<FT, KIND, false>(v, p, t);
+        st4<true>(packed + ((b * GS + j * 8) >> 1), e2m1_pack8(t));
+        if (j == 0) bscale[b] = (uint8_t)p.sb;
     }
 }
 
@@ -188,13 +200,13 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
         } else if constexpr (OP == OP_DQB) {
             const float eff = fp4_eff(KIND, sb, sg);
             float d[8];
-            widen8<FT>(load8<FT>(a, e), d);
+            widen8<FT>(load8<FT, true>(a, e), d);
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = d[i] * eff;
         } else {
             float xv[8], d[8], t[8], g[8];
-            widen8<FT>(load8<FT>(a, e), xv);
-            widen8<FT>(load8<FT>(b, e), d);
+            widen8<FT>(load8<FT, true>(a, e), xv);
+            widen8<FT>(load8<FT, true>(b, e), d);
             if constexpr (KIND == MX) {
                 const float inv = e8m0_inv(sb);
 #pragma unroll
@@ -204,16 +216,16 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
                 }
             } else {
                 const float eff = fp4_eff(KIND, sb, sg);
-                const float y = 1.0f / eff;
                 bool ok = scale_in_fast_range(eff);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    ok = ok && value_in_fast_range(d[i]) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+                    ok = ok && (value_in_fast_range(d[i]) || d[i] == 0.0f) && __builtin_fabsf(xv[i]) <= 0x1p86f;
                 if (ok) {
+                    const float y = rcp_rn(eff);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        t[i] = div_fast(xv[i], eff, y);
-                        g[i] = div_fast(d[i], eff, y);
+                        t[i] = with_sign_of(div_q<FT>(xv[i], eff, y), xv[i]);
+                        g[i] = div_q<FT>(d[i], eff, y);
                     }
                 } else {
 #pragma unroll
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = g[i] * (((w >> (4 * i)) & 7u) != 7u ? 1.0f : 0.0f);
         }
-        store8<FT>(out, e, o);
+        store8<FT, true>(out, e, o);
     }
 }
 
@@ -392,15 +404,15 @@ tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k
         TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_amax_partial<FTV>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws));
         if (launch_status()) return TQ_ERR_HIP;
     }
-    constexpr int U = 4;
+    constexpr int U = 8;
     if (kind == TQ_NVFP4) {
         const int64_t nb = numel / 16;
-        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 64), 4));
+        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 32), 4));
         TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U>), grid, dim3(256), 0, st, x, nb, ws, nws,
                                                  static_global, global_scale, packed, block_scale));
     } else {
         const int64_t nb = numel / 32;
-        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 64), 4));
+        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 16), 4));
         TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U>), grid, dim3(256), 0, st, x, nb, ws, nws,
                                                  1, global_scale, packed, block_scale));
     }

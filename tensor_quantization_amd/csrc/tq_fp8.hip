@@ -27,55 +27,71 @@ struct FP {
     bool fast;
 };
 
+constexpr float Y448 = 1.0f / 448.0f;   // RN(1/448), folded at compile time
+
+// amax is an element magnitude of type FT (or 0).
+template <int FT>
 __device__ __forceinline__ FP fp8_params(float amax)
 {
     FP p;
-    float s = amax / 448.0f;
+    const float s = div_by<FT>(amax, 448.0f, Y448);
     p.s = (s == 0.0f) ? 1.0f : s;
-    p.y = 1.0f / p.s;
     p.fast = scale_in_fast_range(p.s);
+    p.y = p.fast ? rcp_rn(p.s) : 0.0f;
     return p;
 }
 
-template <bool FAST>
+// E4M3 keeps the sign of zero, so a fast quotient gets x's sign back.
+template <int FT, bool FAST>
 __device__ __forceinline__ uint2 fp8_enc8(const float v[8], const FP& p)
 {
     float t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = FAST ? div_fast(v[i], p.s, p.y) : v[i] / p.s;
+    for (int i = 0; i < 8; ++i) t[i] = FAST ? with_sign_of(div_q<FT>(v[i], p.s, p.y), v[i]) : v[i] / p.s;
     return make_uint2(e4m3_pack4(t[0], t[1], t[2], t[3]), e4m3_pack4(t[4], t[5], t[6], t[7]));
 }
 
 // ------------------------------------------------------------ 1 x bc rows
-template <int FT, int T, int U>
+// Blocks of L = 8*T*W contiguous elements: lane j of a team of T holds
+// vectors w*T + j, so a team's load instruction reads 16*T contiguous bytes.
+template <int FT, int T, int W, int U>
 __global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, int64_t nblocks,
                                                   uint8_t* __restrict__ q, float* __restrict__ scale)
 {
     constexpr int P = 64 / T;
-    constexpr int64_t L = 8 * T;
+    constexpr int64_t L = 8 * T * W;
     const int lane = threadIdx.x & 63;
     const int j = lane % T;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t g0 = wave * (U * P) + lane / T;
-    Raw8<FT> raw[U];
+    Raw8<FT> raw[U][W];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t g = g0 + (int64_t)u * P;
-        if (g < nblocks) raw[u] = load8<FT>(x, g * L + j * 8);
-        else raw[u] = Raw8<FT>{};
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            if (g < nblocks) raw[u][w] = load8<FT, (T >= 8)>(x, g * L + (w * T + j) * 8);
+            else raw[u][w] = Raw8<FT>{};
+        }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        float v[8];
-        widen8<FT>(raw[u], v);
+        float v[W][8];
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-        const FP p = fp8_params(team_max<T>(a));
+        for (int w = 0; w < W; ++w) {
+            widen8<FT>(raw[u][w], v[w]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[w][i]));
+        }
+        const FP p = fp8_params<FT>(team_max<T>(a));
         const int64_t g = g0 + (int64_t)u * P;
         if (g >= nblocks) continue;
-        const uint2 c = p.fast ? fp8_enc8<true>(v, p) : fp8_enc8<false>(v, p);
-        *reinterpret_cast<uint2*>(q + g * L + j * 8) = c;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const uint2 c = p.fast ? fp8_enc8<FT, true>(v[w], p) : fp8_enc8<FT, false>(v[w], p);
+            *reinterpret_cast<uint2*>(q + g * L + (w * T + j) * 8) = c;
+        }
         if (j == 0) scale[g] = p.s;
     }
 }
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, in
     const int64_t c0 = tc * (8 * T) + (t % T) * 8;
     Raw8<FT> raw[NP];
 #pragma unroll
-    for (int k = 0; k < NP; ++k) raw[k] = load8<FT>(x, (r0 + (int64_t)k * RP) * cols + c0);
+    for (int k = 0; k < NP; ++k) raw[k] = load8<FT, (T >= 8)>(x, (r0 + (int64_t)k * RP) * cols + c0);
     float v[NP][8];
     float a = 0.0f;
 #pragma unroll
@@ -108,15 +124,15 @@ __global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, in
     if ((t & 63) == 0) wmax[t >> 6] = a;
     __syncthreads();
     a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-    const FP p = fp8_params(a);
+    const FP p = fp8_params<FT>(a);
     if (p.fast) {
 #pragma unroll
         for (int k = 0; k < NP; ++k)
-            *reinterpret_cast<uint2*>(q + (r0 + (int64_t)k * RP) * cols + c0) = fp8_enc8<true>(v[k], p);
+            st8<(T >= 16)>(q + (r0 + (int64_t)k * RP) * cols + c0, fp8_enc8<FT, true>(v[k], p));
     } else {
 #pragma unroll
         for (int k = 0; k < NP; ++k)
-            *reinterpret_cast<uint2*>(q + (r0 + (int64_t)k * RP) * cols + c0) = fp8_enc8<false>(v[k], p);
+            st8<(T >= 16)>(q + (r0 + (int64_t)k * RP) * cols + c0, fp8_enc8<FT, false>(v[k], p));
     }
     if (t == 0) scale[tr * nbc + tc] = p.s;
 }
@@ -138,7 +154,7 @@ __global__ __launch_bounds__(256) void k_fp8_generic(const void* __restrict__ x,
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
     __syncthreads();
     a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-    const FP p = fp8_params(a);
+    const FP p = fp8_params<FT>(a);
     for (int64_t j = threadIdx.x; j < n; j += 256) {
         const int64_t e = (r0 + j / bc) * cols + c0 + j % bc;
         const float t = load1<FT>(x, e) / p.s;
@@ -174,24 +190,24 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
             }
         } else if constexpr (OP == OP_DQB) {
             float d[8];
-            widen8<FT>(load8<FT>(a, e), d);
+            widen8<FT>(load8<FT, true>(a, e), d);
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = d[i] * s;
         } else {
             float xv[8], d[8];
-            widen8<FT>(load8<FT>(a, e), xv);
-            widen8<FT>(load8<FT>(b, e), d);
-            const float y = 1.0f / s;
+            widen8<FT>(load8<FT, true>(a, e), xv);
+            widen8<FT>(load8<FT, true>(b, e), d);
             bool ok = scale_in_fast_range(s);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                ok = ok && value_in_fast_range(d[i]) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+                ok = ok && (value_in_fast_range(d[i]) || d[i] == 0.0f) && __builtin_fabsf(xv[i]) <= 0x1p86f;
             float t[8], g[8];
             if (ok) {
+                const float y = rcp_rn(s);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    t[i] = div_fast(xv[i], s, y);
-                    g[i] = div_fast(d[i], s, y);
+                    t[i] = with_sign_of(div_q<FT>(xv[i], s, y), xv[i]);
+                    g[i] = div_q<FT>(d[i], s, y);
                 }
             } else {
 #pragma unroll
@@ -208,7 +224,7 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
                 o[i] = g[i] * (c < 0x7eu ? 1.0f : 0.0f);
             }
         }
-        store8<FT>(out, e, o);
+        store8<FT, true>(out, e, o);
     }
 }
 
@@ -251,12 +267,13 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     default: { constexpr int FTV = BF16; __VA_ARGS__; } break;    \
     }
 
-template <int FT, int T, int U>
+template <int FT, int T, int W, int U>
 static void launch_rows(const void* x, int64_t nblocks, uint8_t* q, float* scale, hipStream_t st)
 {
     constexpr int P = 64 / T;
     const int64_t waves = cdiv(nblocks, (int64_t)U * P);
-    hipLaunchKernelGGL((k_fp8_rows<FT, T, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st, x, nblocks, q, scale);
+    hipLaunchKernelGGL((k_fp8_rows<FT, T, W, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st, x, nblocks, q,
+                       scale);
 }
 
 template <int FT>
@@ -266,12 +283,15 @@ static bool quant_fast(const void* x, int64_t rows, int64_t cols, int64_t br, in
     const int64_t nb = (rows / br) * (cols / bc);
     if (br == 1) {
         switch (bc) {
-        case 16: launch_rows<FT, 2, 8>(x, nb, q, scale, st); return true;
-        case 32: launch_rows<FT, 4, 8>(x, nb, q, scale, st); return true;
-        case 64: launch_rows<FT, 8, 8>(x, nb, q, scale, st); return true;
-        case 128: launch_rows<FT, 16, 8>(x, nb, q, scale, st); return true;
-        case 256: launch_rows<FT, 32, 8>(x, nb, q, scale, st); return true;
-        case 512: launch_rows<FT, 64, 8>(x, nb, q, scale, st); return true;
+        case 16: launch_rows<FT, 2, 1, 8>(x, nb, q, scale, st); return true;
+        case 32: launch_rows<FT, 4, 1, 8>(x, nb, q, scale, st); return true;
+        case 64: launch_rows<FT, 8, 1, 8>(x, nb, q, scale, st); return true;
+#ifndef TQ_FP8_U
+#define TQ_FP8_U 1
+#endif
+        case 128: launch_rows<FT, 8, 2, TQ_FP8_U>(x, nb, q, scale, st); return true;
+        case 256: launch_rows<FT, 16, 2, 4>(x, nb, q, scale, st); return true;
+        case 512: launch_rows<FT, 64, 1, 8>(x, nb, q, scale, st); return true;
         default: return false;
         }
     }

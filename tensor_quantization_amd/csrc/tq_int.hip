@@ -31,57 +31,64 @@ namespace tq {
 // ------------------------------------------------------------ group params
 struct GP {
     float s;     // scale
-    float y;     // RN(1 / s)
+    float y;     // RN(1 / s) when fast
     float zpf;   // zero-point as a float (0 when symmetric)
-    bool fast;   // s inside the range where div_fast is exact
+    bool fast;   // s inside the range where the FMA division is exact
 };
 
-template <bool SYM>
-__device__ __forceinline__ GP make_gp(float amax, float mn, float mx, float qmin, float qmax)
+// Scale and zero-point of one group.  yc = RN(1/qmax) (symmetric) or
+// RN(1/(qmax - qmin)) (asymmetric), computed once on the host.  amax and mn
+// are element values of type FT (or 0); the asymmetric range mx - mn is a
+// general binary32 value.
+template <int FT, bool SYM>
+__device__ __forceinline__ GP make_gp(float amax, float mn, float mx, float qmin, float qmax, float yc)
 {
     GP p;
+    float s;
+    if constexpr (SYM) s = div_by<FT>(amax, qmax, yc);
+    else s = div_by<F32>(mx - mn, qmax - qmin, yc);
+    s = (s == 0.0f) ? 1.0f : s;
+    p.s = s;
+    p.fast = scale_in_fast_range(s);
+    p.y = p.fast ? rcp_rn(s) : 0.0f;
     if constexpr (SYM) {
-        float s = amax / qmax;
-        p.s = (s == 0.0f) ? 1.0f : s;
         p.zpf = 0.0f;
     } else {
-        float s = (mx - mn) / (qmax - qmin);
-        s = (s == 0.0f) ? 1.0f : s;
-        float z = qmin - __builtin_rintf(mn / s);
-        p.s = s;
-        p.zpf = __builtin_amdgcn_fmed3f(z, qmin, qmax);
+        const float t = (p.fast && (value_in_fast_range(mn) || mn == 0.0f)) ? div_q<FT>(mn, s, p.y) : mn / s;
+        p.zpf = __builtin_amdgcn_fmed3f(qmin - __builtin_rintf(t), qmin, qmax);
     }
-    p.y = 1.0f / p.s;
-    p.fast = scale_in_fast_range(p.s);
     return p;
 }
 
-// Encode 8 values of one group into code floats (MAGIC + code).
-template <bool FAST>
+// Encode 8 values of one group into code floats (MAGIC + code).  A
+// symmetric dynamic scale s = RN(amax / qmax) keeps |x / s| below qmax + 0.5
+// for every element, so only asymmetric groups (and static scales) clamp.
+template <int FT, bool FAST, bool CLAMP>
 __device__ __forceinline__ void enc8(const float v[8], const GP& p, float lo, float hi, float c[8])
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float t = FAST ? div_fast(v[i], p.s, p.y) : v[i] / p.s;
-        c[i] = int_code_f(t, p.zpf, lo, hi);
+        const float t = FAST ? div_q<FT>(v[i], p.s, p.y) : v[i] / p.s;
+        c[i] = CLAMP ? int_code_f(t, p.zpf, lo, hi) : (t + MAGIC) + p.zpf;
     }
 }
 
-template <int BITS>
+template <int BITS, bool NT = false>
 __device__ __forceinline__ void store_codes8(uint8_t* q, int64_t e, const float c[8])
 {
-    if constexpr (BITS == 8) {
-        uint2 w = make_uint2(pack_bytes4(c[0], c[1], c[2], c[3]), pack_bytes4(c[4], c[5], c[6], c[7]));
-        *reinterpret_cast<uint2*>(q + e) = w;
-    } else {
-        *reinterpret_cast<uint32_t*>(q + (e >> 1)) = pack_nibbles8(c, true);
-    }
+    if constexpr (BITS == 8)
+        st8<NT>(q + e, make_uint2(pack_bytes4(c[0], c[1], c[2], c[3]), pack_bytes4(c[4], c[5], c[6], c[7])));
+    else
+        st4<NT>(q + (e >> 1), pack_nibbles8(c, true));
 }
 
 // ------------------------------------------------------------ team kernel
+// Groups of L = 8*T*W contiguous elements.  Lane j of a team of T lanes
+// holds vectors w*T + j (w < W) of its group, so each load instruction of a
+// team reads 16*T contiguous bytes; a wave runs U rounds of 64/T groups.
 template <int FT, int BITS, bool SYM, int T, int W, int U>
 __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, int64_t G, float qmin,
-                                                    float qmax, uint8_t* __restrict__ q,
+                                                    float qmax, float yc, uint8_t* __restrict__ q,
                                                     float* __restrict__ scale, uint8_t* __restrict__ zp)
 {
     constexpr int P = 64 / T;
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
         const int64_t g = g0 + (int64_t)u * P;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            if (g < G) raw[u][w] = load8<FT>(x, g * L + (int64_t)(w * T + j) * 8);
+            if (g < G) raw[u][w] = load8<FT, (T >= 8)>(x, g * L + (int64_t)(w * T + j) * 8);
             else raw[u][w] = Raw8<FT>{};
         }
     }
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
             for (int w = 0; w < W; ++w)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[u][w][i]));
-            p[u] = make_gp<true>(team_max<T>(a), 0.0f, 0.0f, qmin, qmax);
+            p[u] = make_gp<FT, true>(team_max<T>(a), 0.0f, 0.0f, qmin, qmax, yc);
         } else {
             float mn = 0.0f, mx = 0.0f;
 #pragma unroll
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
                     mn = __builtin_fminf(mn, v[u][w][i]);
                     mx = __builtin_fmaxf(mx, v[u][w][i]);
                 }
-            p[u] = make_gp<false>(0.0f, team_min<T>(mn), team_max<T>(mx), qmin, qmax);
+            p[u] = make_gp<FT, false>(0.0f, team_min<T>(mn), team_max<T>(mx), qmin, qmax, yc);
         }
     }
 
@@ -140,15 +147,15 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
 #pragma unroll
             for (int w = 0; w < W; ++w) {
                 float c[8];
-                enc8<true>(v[u][w], p[u], lo, hi, c);
-                store_codes8<BITS>(q, g * L + (int64_t)(w * T + j) * 8, c);
+                enc8<FT, true, !SYM>(v[u][w], p[u], lo, hi, c);
+                store_codes8<BITS, (T == 64)>(q, g * L + (int64_t)(w * T + j) * 8, c);
             }
         } else {
 #pragma unroll
             for (int w = 0; w < W; ++w) {
                 float c[8];
-                enc8<false>(v[u][w], p[u], lo, hi, c);
-                store_codes8<BITS>(q, g * L + (int64_t)(w * T + j) * 8, c);
+                enc8<FT, false, !SYM>(v[u][w], p[u], lo, hi, c);
+                store_codes8<BITS, (T == 64)>(q, g * L + (int64_t)(w * T + j) * 8, c);
             }
         }
         if (j == 0) {
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
 // (reduce, then encode) in 4-vector strides per lane.
 template <int FT, int BITS, bool SYM>
 __global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, int64_t G, int64_t L,
-                                                    float qmin, float qmax, uint8_t* __restrict__ q,
+                                                    float qmin, float qmax, float yc, uint8_t* __restrict__ q,
                                                     float* __restrict__ scale, uint8_t* __restrict__ zp)
 {
     const int lane = threadIdx.x & 63;
@@ -190,8 +197,8 @@ __global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, 
             }
         }
     }
-    GP p = SYM ? make_gp<true>(team_max<64>(a), 0.0f, 0.0f, qmin, qmax)
-               : make_gp<false>(0.0f, team_min<64>(mn), team_max<64>(mx), qmin, qmax);
+    GP p = SYM ? make_gp<FT, true>(team_max<64>(a), 0.0f, 0.0f, qmin, qmax, yc)
+               : make_gp<FT, false>(0.0f, team_min<64>(mn), team_max<64>(mx), qmin, qmax, yc);
     const float lo = MAGIC + qmin, hi = MAGIC + qmax;
     for (int64_t v0 = lane; v0 < nvec; v0 += 256) {
         Raw8<FT> raw[4];
@@ -203,9 +210,9 @@ __global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, 
             if (v0 + k * 64 >= nvec) continue;
             float v[8], c[8];
             widen8<FT>(raw[k], v);
-            if (p.fast) enc8<true>(v, p, lo, hi, c);
-            else enc8<false>(v, p, lo, hi, c);
-            store_codes8<BITS>(q, base + (v0 + k * 64) * 8, c);
+            if (p.fast) enc8<FT, true, !SYM>(v, p, lo, hi, c);
+            else enc8<FT, false, !SYM>(v, p, lo, hi, c);
+            store_codes8<BITS, true>(q, base + (v0 + k * 64) * 8, c);
         }
     }
     if (lane == 0) {
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, 
 // scales differ inside a vector, so this path divides with IEEE division.
 template <int FT, int BITS, bool SYM>
 __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ x, int64_t R, int64_t C,
-                                                    float qmin, float qmax, uint8_t* __restrict__ q,
+                                                    float qmin, float qmax, float yc, uint8_t* __restrict__ q,
                                                     float* __restrict__ scale, uint8_t* __restrict__ zp)
 {
     __shared__ float red[2][4][64 * 8];
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ x, 
             a = __builtin_fminf(a, red[0][k][lane * 8 + i]);
             m = __builtin_fmaxf(m, red[1][k][lane * 8 + i]);
         }
-        p[i] = SYM ? make_gp<true>(m, 0.0f, 0.0f, qmin, qmax) : make_gp<false>(0.0f, a, m, qmin, qmax);
+        p[i] = SYM ? make_gp<FT, true>(m, 0.0f, 0.0f, qmin, qmax, yc) : make_gp<FT, false>(0.0f, a, m, qmin, qmax, yc);
     }
     if (!active) return;
     if (wv == 0) {
@@ -348,7 +355,7 @@ __device__ __forceinline__ void block_minmax(float& mn, float& mx)
 
 template <int FT, bool SYM>
 __global__ __launch_bounds__(256) void k_reduce_generic(const void* __restrict__ x, DMap m, float qmin,
-                                                        float qmax, float* __restrict__ scale,
+                                                        float qmax, float yc, float* __restrict__ scale,
                                                         uint8_t* __restrict__ zp)
 {
     const int64_t gid = blockIdx.x;
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(256) void k_reduce_generic(const void* __restrict__
     }
     block_minmax(mn, mx);
     if (threadIdx.x == 0) {
-        GP p = SYM ? make_gp<true>(mx, 0.0f, 0.0f, qmin, qmax) : make_gp<false>(0.0f, mn, mx, qmin, qmax);
+        GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc) : make_gp<FT, false>(0.0f, mn, mx, qmin, qmax, yc);
         scale[gid] = p.s;
         if (!SYM) zp[gid] = (uint8_t)(int)p.zpf;
     }
@@ -410,6 +417,43 @@ __global__ __launch_bounds__(256) void k_encode_generic(const void* __restrict__
 // ------------------------------------------------------------ per tensor
 // Pass 1: each block reduces a contiguous chunk and writes
 // ws[b] = max(max |x| or max x, 0) and ws[nblk + b] = |min(min x, 0)|.
+// Four 16-byte loads per thread are in flight per step.
+template <int FT, bool SYM>
+__device__ __forceinline__ void minmax_acc(float v, float& mn, float& mx)
+{
+    if (SYM) {
+        mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
+    } else {
+        mn = __builtin_fminf(mn, v);
+        mx = __builtin_fmaxf(mx, v);
+    }
+}
+
+template <int FT, bool SYM>
+__device__ __forceinline__ void range_minmax(const void* x, int64_t b0, int64_t b1, bool vec, float& mn, float& mx)
+{
+    if (vec) {
+        for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += (int64_t)blockDim.x * 8 * 4) {
+            Raw8<FT> r[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t ek = e + (int64_t)k * blockDim.x * 8;
+                if (ek < b1) r[k] = load8<FT>(x, ek);
+                else r[k] = Raw8<FT>{};
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float v[8];
+                widen8<FT>(r[k], v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) minmax_acc<FT, SYM>(v[i], mn, mx);
+            }
+        }
+    } else {
+        for (int64_t e = b0 + threadIdx.x; e < b1; e += blockDim.x) minmax_acc<FT, SYM>(load1<FT>(x, e), mn, mx);
+    }
+}
+
 template <int FT, bool SYM>
 __global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__ x, int64_t numel,
                                                         int64_t chunk, float* __restrict__ ws)
@@ -417,31 +461,7 @@ __global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__
     const int64_t b0 = (int64_t)blockIdx.x * chunk;
     const int64_t b1 = b0 + chunk < numel ? b0 + chunk : numel;
     float mn = 0.0f, mx = 0.0f;
-    if ((numel & 7) == 0) {
-        for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8) {
-            float v[8];
-            widen8<FT>(load8<FT>(x, e), v);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (SYM) {
-                    mx = __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
-                } else {
-                    mn = __builtin_fminf(mn, v[i]);
-                    mx = __builtin_fmaxf(mx, v[i]);
-                }
-            }
-        }
-    } else {
-        for (int64_t e = b0 + threadIdx.x; e < b1; e += 256) {
-            float v = load1<FT>(x, e);
-            if (SYM) {
-                mx = __builtin_fmaxf(mx, __builtin_fabsf(v));
-            } else {
-                mn = __builtin_fminf(mn, v);
-                mx = __builtin_fmaxf(mx, v);
-            }
-        }
-    }
+    range_minmax<FT, SYM>(x, b0, b1, (numel & 7) == 0, mn, mx);
     block_minmax(mn, mx);
     if (threadIdx.x == 0) {
         ws[blockIdx.x] = mx;
@@ -450,23 +470,36 @@ __global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__
 }
 
 // Pass 2: every block merges the partials (or reads the static scale),
-// block 0 publishes scale / zero-point, and all blocks encode.
+// block 0 publishes scale / zero-point, and all blocks encode.  With
+// nblk == 0 and a dynamic scale the (single) block reduces the whole tensor
+// itself: one launch for small tensors.
 template <int FT, int BITS, bool SYM>
 __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ x, int64_t numel,
                                                        const float* __restrict__ ws, int nblk,
-                                                       int static_scale, float qmin, float qmax,
+                                                       int static_scale, float qmin, float qmax, float yc,
                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
                                                        uint8_t* __restrict__ zp, bool zp_signed)
 {
     __shared__ GP sp;
-    if (threadIdx.x < 64) {
+    if (!static_scale && nblk == 0) {
+        float mn = 0.0f, mx = 0.0f;
+        range_minmax<FT, SYM>(x, 0, numel, (numel & 7) == 0, mn, mx);
+        block_minmax(mn, mx);
+        if (threadIdx.x == 0) {
+            GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
+                       : make_gp<FT, false>(0.0f, mn, mx, qmin, qmax, yc);
+            sp = p;
+            scale[0] = p.s;
+            if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
+        }
+    } else if (threadIdx.x < 64) {
         if (static_scale) {
             if (threadIdx.x == 0) {
                 GP p;
                 p.s = scale[0];
-                p.y = 1.0f / p.s;
-                p.zpf = zp_at(zp, 0, zp_signed);
                 p.fast = scale_in_fast_range(p.s);
+                p.y = p.fast ? rcp_rn(p.s) : 0.0f;
+                p.zpf = zp_at(zp, 0, zp_signed);
                 sp = p;
             }
         } else {
@@ -478,7 +511,8 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
             mx = team_max<64>(mx);
             nmn = team_max<64>(nmn);
             if (threadIdx.x == 0) {
-                GP p = SYM ? make_gp<true>(mx, 0.0f, 0.0f, qmin, qmax) : make_gp<false>(0.0f, -nmn, mx, qmin, qmax);
+                GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
+                           : make_gp<FT, false>(0.0f, -nmn, mx, qmin, qmax, yc);
                 sp = p;
                 if (blockIdx.x == 0) {
                     scale[0] = p.s;
@@ -494,10 +528,16 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
     if ((numel & 7) == 0) {
         for (int64_t vi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; vi < numel / 8; vi += stride) {
             float v[8], c[8];
-            widen8<FT>(load8<FT>(x, vi * 8), v);
-            if (p.fast) enc8<true>(v, p, lo, hi, c);
-            else enc8<false>(v, p, lo, hi, c);
-            store_codes8<BITS>(q, vi * 8, c);
+            widen8<FT>(load8<FT, true>(x, vi * 8), v);
+            // a static scale does not bound |x|: keep x / s from overflowing
+            bool fast = p.fast;
+            if (static_scale) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) fast = fast && __builtin_fabsf(v[i]) <= 0x1p86f;
+            }
+            if (fast) enc8<FT, true, true>(v, p, lo, hi, c);
+            else enc8<FT, false, true>(v, p, lo, hi, c);
+            store_codes8<BITS, true>(q, vi * 8, c);
         }
     } else {
         const int64_t nbytes = BITS == 8 ? numel : numel / 2;
@@ -515,44 +555,45 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
 
 // ------------------------------------------------------------ elementwise
 // Group ids of a vector of 8 elements starting at e (e % 8 == 0):
-//   MAP_CONTIG: groups of L contiguous elements (L % 8 == 0): one group e / L.
+//   MAP_CONTIG: groups of L contiguous elements (L % 8 == 0): one group e / L
+//               (a shift when L is a power of two: sh >= 0).
 //   MAP_COLS  : [B, R, C] column groups (C % 8 == 0): groups
 //               (e / (R*C)) * C + e % C + i, i = 0..7.
 enum { MAP_CONTIG = 0, MAP_COLS = 1 };
 
 template <int MAPK>
-__device__ __forceinline__ int64_t vec_group(int64_t e, int64_t P1, int64_t P2)
+__device__ __forceinline__ int64_t vec_group(int64_t e, int64_t P1, int64_t P2, int sh)
 {
-    if constexpr (MAPK == MAP_CONTIG) return e / P1;
+    if constexpr (MAPK == MAP_CONTIG) return sh >= 0 ? (e >> sh) : e / P1;
     else return (e / (P1 * P2)) * P2 + e % P2;
 }
 
-template <int BITS, bool SIGNED>
-__device__ __forceinline__ void load_codes8(const uint8_t* q, int64_t e, int c[8])
+template <bool SIGNED>
+__device__ __forceinline__ float code_f(uint32_t b, int bits)
 {
-    if constexpr (BITS == 8) {
-        uint2 w = *reinterpret_cast<const uint2*>(q + e);
-        const uint32_t ws[2] = {w.x, w.y};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t b = (ws[i >> 2] >> ((i & 3) * 8)) & 0xffu;
-            c[i] = SIGNED ? (int)(int8_t)b : (int)b;
-        }
-    } else {
-        uint32_t w = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t n = (w >> (i * 4)) & 0xfu;
-            c[i] = SIGNED ? (int)((n ^ 8u) - 8u) : (int)n;
-        }
-    }
+    if (bits == 8) return SIGNED ? (float)(int)(int8_t)b : (float)b;
+    return SIGNED ? (float)(int)((b ^ 8u) - 8u) : (float)b;
 }
 
-constexpr int VPT = 4;   // vectors per thread per iteration
+template <bool SIGNED>
+__device__ __forceinline__ float zp_f(const uint8_t* zp, int64_t g)
+{
+    if (!zp) return 0.0f;
+    return SIGNED ? (float)(int8_t)zp[g] : (float)zp[g];
+}
+
+#ifndef TQ_VPT
+#define TQ_VPT 2
+#endif
+constexpr int VPT = TQ_VPT;   // vectors per thread per iteration
+#ifndef TQ_STE_VPT
+#define TQ_STE_VPT 1
+#endif
+constexpr int SVPT = TQ_STE_VPT;
 
 template <int MAPK, int YT, int BITS, bool SIGNED>
 __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__ q, int64_t nvec, int64_t P1,
-                                                     int64_t P2, const float* __restrict__ scale,
+                                                     int64_t P2, int sh, const float* __restrict__ scale,
                                                      const uint8_t* __restrict__ zp, void* __restrict__ y)
 {
     for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
@@ -561,24 +602,32 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi >= nvec) break;
             const int64_t e = vi * 8;
-            int c[8];
-            load_codes8<BITS, SIGNED>(q, e, c);
-            const int64_t g = vec_group<MAPK>(e, P1, P2);
+            uint32_t cw[2];
+            // plain loads: non-temporal loads of the narrow code stream measured slower
+            if constexpr (BITS == 8) {
+                const uint2 w = *reinterpret_cast<const uint2*>(q + e);
+                cw[0] = w.x;
+                cw[1] = w.y;
+            } else {
+                cw[0] = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
+                cw[1] = 0;
+            }
+            const int64_t g = vec_group<MAPK>(e, P1, P2, sh);
             float out[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t gi = MAPK == MAP_CONTIG ? g : g + i;
-                const float z = zp ? (SIGNED ? (float)(int8_t)zp[gi] : (float)zp[gi]) : 0.0f;
-                out[i] = ((float)c[i] - z) * scale[gi];
+                const uint32_t c = BITS == 8 ? (cw[i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[0] >> (i * 4)) & 0xfu;
+                out[i] = (code_f<SIGNED>(c, BITS) - zp_f<SIGNED>(zp, gi)) * scale[gi];
             }
-            store8<YT>(y, e, out);
+            store8<YT, true>(y, e, out);
         }
     }
 }
 
 template <int MAPK, int FT>
 __global__ __launch_bounds__(256) void k_dqb_vec(const void* __restrict__ dy, int64_t nvec, int64_t P1,
-                                                 int64_t P2, const float* __restrict__ scale,
+                                                 int64_t P2, int sh, const float* __restrict__ scale,
                                                  void* __restrict__ dq)
 {
     for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
@@ -586,63 +635,65 @@ __global__ __launch_bounds__(256) void k_dqb_vec(const void* __restrict__ dy, in
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
-            if (vi < nvec) raw[k] = load8<FT>(dy, vi * 8);
+            if (vi < nvec) raw[k] = load8<FT, true>(dy, vi * 8);
         }
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi >= nvec) break;
             const int64_t e = vi * 8;
-            const int64_t g = vec_group<MAPK>(e, P1, P2);
+            const int64_t g = vec_group<MAPK>(e, P1, P2, sh);
             float v[8];
             widen8<FT>(raw[k], v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = v[i] * scale[MAPK == MAP_CONTIG ? g : g + i];
-            store8<FT>(dq, e, v);
+            store8<FT, true>(dq, e, v);
         }
     }
 }
 
-// STE: q recomputed from x; dx = (dy / s) * 1[qmin < q < qmax].
+// STE: q recomputed from x; dx = (dy / s) * 1[qmin < q < qmax].  The code
+// needs no clamp here: the mask compares the unclamped code with the range.
 template <int MAPK, int FT, bool SIGNED>
 __global__ __launch_bounds__(256) void k_ste_vec(const void* __restrict__ x, const void* __restrict__ dy,
-                                                 int64_t nvec, int64_t P1, int64_t P2, float qmin, float qmax,
-                                                 const float* __restrict__ scale,
+                                                 int64_t nvec, int64_t P1, int64_t P2, int sh, float qmin,
+                                                 float qmax, const float* __restrict__ scale,
                                                  const uint8_t* __restrict__ zp, void* __restrict__ dx)
 {
     const float lo = MAGIC + qmin, hi = MAGIC + qmax;
-    for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
-        Raw8<FT> rx[VPT], rd[VPT];
+    for (int64_t base = (int64_t)blockIdx.x * 256 * SVPT; base < nvec; base += (int64_t)gridDim.x * 256 * SVPT) {
+        Raw8<FT> rx[SVPT], rd[SVPT];
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
+        for (int k = 0; k < SVPT; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi < nvec) {
-                rx[k] = load8<FT>(x, vi * 8);
-                rd[k] = load8<FT>(dy, vi * 8);
+                rx[k] = load8<FT, true>(x, vi * 8);
+                rd[k] = load8<FT, true>(dy, vi * 8);
             }
         }
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
+        for (int k = 0; k < SVPT; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi >= nvec) break;
             const int64_t e = vi * 8;
-            const int64_t g = vec_group<MAPK>(e, P1, P2);
+            const int64_t g = vec_group<MAPK>(e, P1, P2, sh);
             float xv[8], dv[8], out[8];
             widen8<FT>(rx[k], xv);
             widen8<FT>(rd[k], dv);
             if constexpr (MAPK == MAP_CONTIG) {
                 const float s = scale[g];
-                const float zf = zp ? (SIGNED ? (float)(int8_t)zp[g] : (float)zp[g]) : 0.0f;
-                const float yr = 1.0f / s;
+                const float zf = zp_f<SIGNED>(zp, g);
                 bool ok = scale_in_fast_range(s);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ok = ok && value_in_fast_range(dv[i]);
+                for (int i = 0; i < 8; ++i)
+                    ok = ok && (value_in_fast_range(dv[i]) || dv[i] == 0.0f) && __builtin_fabsf(xv[i]) <= 0x1p86f;
                 if (ok) {
+                    const float yr = rcp_rn(s);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const float c = int_code_f(div_fast(xv[i], s, yr), zf, lo, hi);
+                        const float c = (div_q<FT>(xv[i], s, yr) + MAGIC) + zf;
                         const float m = (c > lo && c < hi) ? 1.0f : 0.0f;
-                        out[i] = div_fast(dv[i], s, yr) * m;
+                        out[i] = div_q<FT>(dv[i], s, yr) * m;
                     }
                 } else {
 #pragma unroll
@@ -656,13 +707,12 @@ __global__ __launch_bounds__(256) void k_ste_vec(const void* __restrict__ x, con
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float s = scale[g + i];
-                    const float zf = zp ? (SIGNED ? (float)(int8_t)zp[g + i] : (float)zp[g + i]) : 0.0f;
-                    const float c = int_code_f(xv[i] / s, zf, lo, hi);
+                    const float c = int_code_f(xv[i] / s, zp_f<SIGNED>(zp, g + i), lo, hi);
                     const float m = (c > lo && c < hi) ? 1.0f : 0.0f;
                     out[i] = (dv[i] / s) * m;
                 }
             }
-            store8<FT>(dx, e, out);
+            store8<FT, true>(dx, e, out);
         }
     }
 }
@@ -741,34 +791,50 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     else { constexpr int BV = 4; constexpr bool SV = false; __VA_ARGS__; }
 
 template <int FT, int BITS, bool SYM, int T, int W, int U>
-static void launch_team(const void* x, int64_t G, float qmin, float qmax, uint8_t* q, float* scale,
+static void launch_team(const void* x, int64_t G, float qmin, float qmax, float yc, uint8_t* q, float* scale,
                         uint8_t* zp, hipStream_t st)
 {
     constexpr int P = 64 / T;
     const int64_t waves = cdiv(G, (int64_t)U * P);
     hipLaunchKernelGGL((k_quant_team<FT, BITS, SYM, T, W, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st,
-                       x, G, qmin, qmax, q, scale, zp);
+                       x, G, qmin, qmax, yc, q, scale, zp);
 }
 
-// Contiguous groups of length L (L % 8 == 0), G groups.
+// Contiguous groups of length L (L % 8 == 0), G groups.  Teams of at least
+// 8 lanes read whole 128-byte lines per load instruction; groups of 128 use
+// 8 lanes x 2 vectors so the per-group scale arithmetic is shared by 16
+// elements per lane.
 template <int FT, int BITS, bool SYM>
-static void quant_contig(const void* x, int64_t G, int64_t L, float qmin, float qmax, uint8_t* q,
+static void quant_contig(const void* x, int64_t G, int64_t L, float qmin, float qmax, float yc, uint8_t* q,
                          float* scale, uint8_t* zp, hipStream_t st)
 {
     switch (L) {
-    case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 128: launch_team<FT, BITS, SYM, 16, 1, 8>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 256: launch_team<FT, BITS, SYM, 32, 1, 4>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, qmin, qmax, q, scale, zp, st); return;
-    case 4096: launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, qmin, qmax, q, scale, zp, st); return;
+    case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+#ifndef TQ_G128_U
+#define TQ_G128_U 1
+#endif
+    case 128: launch_team<FT, BITS, SYM, 8, 2, TQ_G128_U>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 256: launch_team<FT, BITS, SYM, 16, 2, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+#ifndef TQ_ROW4096_LONG
+    case 4096: launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+#endif
     default:
         hipLaunchKernelGGL((k_quant_long<FT, BITS, SYM>), dim3((unsigned)cdiv(G, 4)), dim3(256), 0, st,
-                           x, G, L, qmin, qmax, q, scale, zp);
+                           x, G, L, qmin, qmax, yc, q, scale, zp);
     }
+}
+
+// RN(1/qmax) (symmetric) or RN(1/(qmax - qmin)) (asymmetric), on the host
+// in binary32.
+static float range_reciprocal(int32_t qmin, int32_t qmax, bool sym)
+{
+    volatile float one = 1.0f;
+    return sym ? one / (float)qmax : one / (float)(qmax - qmin);
 }
 
 // Quantize with a group map; picks the contiguous, column or generic path.
@@ -778,6 +844,7 @@ static tq_status quant_mapped(const void* x, int xt, const GroupMap& m, int code
     const bool sym = zero_point == nullptr;
     const int bits = code_bits(code);
     const float fmin = (float)qmin, fmax = (float)qmax;
+    const float yc = range_reciprocal(qmin, qmax, sym);
     uint8_t* qb = static_cast<uint8_t*>(q);
     uint8_t* zb = static_cast<uint8_t*>(zero_point);
     if (m.numel == 0) return TQ_OK;
@@ -787,7 +854,7 @@ static tq_status quant_mapped(const void* x, int xt, const GroupMap& m, int code
     if (m.kind == KIND_GROUP && m.inner == 1) { L = m.g; G = m.ngroups; }
     if (m.kind == KIND_CHANNEL && m.outer == 1) { L = m.inner; G = m.A; }
     if (L > 0 && L % 8 == 0 && (L * es) % 16 == 0) {
-        TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym, quant_contig<FTV, BV, SV>(x, G, L, fmin, fmax, qb, scale, zb, st)));
+        TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym, quant_contig<FTV, BV, SV>(x, G, L, fmin, fmax, yc, qb, scale, zb, st)));
         return launch_status();
     }
     // column groups: per-channel on the last axis, per-group on a non-last axis
@@ -797,7 +864,7 @@ static tq_status quant_mapped(const void* x, int xt, const GroupMap& m, int code
     if (C > 0 && C % 8 == 0 && (C * es) % 16 == 0 && B <= 65535) {
         dim3 grid((unsigned)cdiv(C, 512), (unsigned)B);
         TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym,
-            hipLaunchKernelGGL((k_quant_cols<FTV, BV, SV>), grid, dim3(256), 0, st, x, R, C, fmin, fmax, qb, scale, zb)));
+            hipLaunchKernelGGL((k_quant_cols<FTV, BV, SV>), grid, dim3(256), 0, st, x, R, C, fmin, fmax, yc, qb, scale, zb)));
         return launch_status();
     }
     // generic
@@ -805,9 +872,9 @@ static tq_status quant_mapped(const void* x, int xt, const GroupMap& m, int code
     const DMap d = to_dmap(m);
     TQ_FT_SWITCH(xt, {
         if (sym) hipLaunchKernelGGL((k_reduce_generic<FTV, true>), dim3((unsigned)m.ngroups), dim3(256), 0, st,
-                                    x, d, fmin, fmax, scale, zb);
+                                    x, d, fmin, fmax, yc, scale, zb);
         else hipLaunchKernelGGL((k_reduce_generic<FTV, false>), dim3((unsigned)m.ngroups), dim3(256), 0, st,
-                                x, d, fmin, fmax, scale, zb);
+                                x, d, fmin, fmax, yc, scale, zb);
     });
     const int64_t nbytes = bits == 8 ? m.numel : m.numel / 2;
     const bool zs = code_signed(code);
@@ -835,27 +902,37 @@ struct EwArgs {
     const uint8_t* zp;
 };
 
+static int log2_exact(int64_t v)
+{
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int k = 0;
+    while ((int64_t(1) << k) < v) ++k;
+    return k;
+}
+
 template <int MAPK>
 static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int64_t P2, hipStream_t st)
 {
     const dim3 grid(grid_for(nvec, 256 * VPT)), block(256);
     const bool sg = code_signed(a.code);
     const int bits = code_bits(a.code);
+    const int sh = MAPK == MAP_CONTIG ? log2_exact(P1) : -1;
     const uint8_t* q = static_cast<const uint8_t*>(a.a);
     if (op == OP_DEQ) {
         TQ_FT_SWITCH(a.out_type, {
-            if (bits == 8 && sg) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 8, true>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
-            else if (bits == 8) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 8, false>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
-            else if (sg) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 4, true>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
-            else hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 4, false>), grid, block, 0, st, q, nvec, P1, P2, a.scale, a.zp, a.out);
+            if (bits == 8 && sg) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 8, true>), grid, block, 0, st, q, nvec, P1, P2, sh, a.scale, a.zp, a.out);
+            else if (bits == 8) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 8, false>), grid, block, 0, st, q, nvec, P1, P2, sh, a.scale, a.zp, a.out);
+            else if (sg) hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 4, true>), grid, block, 0, st, q, nvec, P1, P2, sh, a.scale, a.zp, a.out);
+            else hipLaunchKernelGGL((k_dequant_vec<MAPK, FTV, 4, false>), grid, block, 0, st, q, nvec, P1, P2, sh, a.scale, a.zp, a.out);
         });
     } else if (op == OP_STE) {
         TQ_FT_SWITCH(a.in_type, {
-            if (sg) hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, true>), grid, block, 0, st, a.a, a.b, nvec, P1, P2, a.qmin, a.qmax, a.scale, a.zp, a.out);
-            else hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, false>), grid, block, 0, st, a.a, a.b, nvec, P1, P2, a.qmin, a.qmax, a.scale, a.zp, a.out);
+            const dim3 sgrid(grid_for(nvec, 256 * SVPT));
+            if (sg) hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, true>), sgrid, block, 0, st, a.a, a.b, nvec, P1, P2, sh, a.qmin, a.qmax, a.scale, a.zp, a.out);
+            else hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, false>), sgrid, block, 0, st, a.a, a.b, nvec, P1, P2, sh, a.qmin, a.qmax, a.scale, a.zp, a.out);
         });
     } else {
-        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), grid, block, 0, st, a.a, nvec, P1, P2, a.scale, a.out));
+        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), grid, block, 0, st, a.a, nvec, P1, P2, sh, a.scale, a.out));
     }
 }
 
@@ -981,8 +1058,8 @@ tq_status tq_quant_per_group(const void* x, int x_dtype, int32_t ndim, const int
 
 size_t tq_workspace_bytes(int op, int64_t numel)
 {
-    (void)numel;
-    if (op == 0 || op == 1) return 2 * 1024 * sizeof(float);
+    if (op == 0) return numel <= 65536 ? 0 : 2 * 1024 * sizeof(float);
+    if (op == 1) return 1024 * sizeof(float);
     return 0;
 }
 
@@ -997,7 +1074,8 @@ tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int cod
     const bool sym = zero_point == nullptr;
     const int bits = code_bits(code);
     int nblk = 0;
-    if (!static_scale) {
+    const bool small = numel <= 65536;
+    if (!static_scale && !small) {
         if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
         const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
         nblk = (int)cdiv(numel, chunk);
@@ -1009,14 +1087,15 @@ tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int cod
         if (launch_status()) return TQ_ERR_HIP;
     }
     const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
-    const dim3 grid(grid_for(work, 256 * 4));
+    const dim3 grid((!static_scale && small) ? 1u : grid_for(work, 256 * 4));
     const float* ws = static_cast<const float*>(workspace);
     uint8_t* qb = static_cast<uint8_t*>(q);
     uint8_t* zb = static_cast<uint8_t*>(zero_point);
     const bool zs = code_signed(code);
     TQ_FT_SWITCH(x_dtype, TQ_BITS_SYM_SWITCH(bits, sym,
         hipLaunchKernelGGL((k_tensor_encode<FTV, BV, SV>), grid, dim3(256), 0, st, x, numel, ws, nblk,
-                           static_scale, (float)qmin, (float)qmax, qb, scale, zb, zs)));
+                           static_scale, (float)qmin, (float)qmax, range_reciprocal(qmin, qmax, sym), qb, scale,
+                           zb, zs)));
     return launch_status();
 }
 

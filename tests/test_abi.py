@@ -77,8 +77,9 @@ def test_integer_validation(tq):
     assert L.tq_quant_per_group(A, 1, nd, shp, 1, 128, 3, 0, 15, B, C, A, None) == INV
     assert L.tq_quant_per_group(A, 1, nd, shp, 2, 4, 3, 0, 15, B, C, A, None) == INV
     assert L.tq_quant_per_channel(A, 1, nd, shp, -1, 0, -127, 127, B, C, None, None) == INV
-    # per-tensor dynamic scale needs a workspace
-    assert L.tq_quant_per_tensor(A, 0, 64, 0, -127, 127, 0, B, C, None, None, 0, None) == INV
+    # a large per-tensor dynamic scale needs a workspace (small tensors reduce in one block)
+    assert L.tq_quant_per_tensor(A, 0, ctypes.c_int64(1 << 20), 0, -127, 127, 0, B, C, None, None, 0, None) == INV
+    assert tq.tq_workspace_bytes(0, 1 << 16) == 0 and tq.tq_workspace_bytes(0, 1 << 20) > 0
     # dequant / STE / dequant-backward
     assert L.tq_dequant_per_token(None, 0, 4, 8, C, None, B, 2, None) == INV
     assert L.tq_dequant_per_token(A, 0, 4, 8, C, None, B, 9, None) == INV
