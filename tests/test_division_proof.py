@@ -1,0 +1,25 @@
+"""The one-correction FMA division used by the quantize kernels for bf16 and
+f16 inputs equals IEEE binary32 division: exhaustive over all dividend
+significands of the input type and all binary32 divisor significands
+(2^30 and 2^33 pairs), on the host's IEEE FMA.  CPU only."""
+import os
+import subprocess
+
+import pytest
+
+HERE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "proofs")
+
+
+@pytest.fixture(scope="module")
+def prog(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("proof") / "division_exhaustive")
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-o", exe,
+                           os.path.join(HERE, "division_exhaustive.c"), "-lm"])
+    return exe
+
+
+@pytest.mark.parametrize("fbits", [7, 10])
+def test_one_correction_division_is_exact(prog, fbits):
+    out = subprocess.run([prog, str(fbits)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert " 0 mismatches" in out.stdout

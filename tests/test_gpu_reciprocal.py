@@ -1,0 +1,20 @@
+"""On gfx950, v_rcp_f32 followed by one Newton step equals the IEEE
+reciprocal for every binary32 significand at several exponents -- the
+per-group reciprocal the kernels use inside their fast range.  Runs the probe
+program that __graft_entry__.build() compiles (tests/proofs/rcp_probe.hip)."""
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "proofs", "rcp_probe")
+
+
+def test_rcp_newton_is_correctly_rounded():
+    assert os.path.exists(EXE), "build the probe with __graft_entry__.build()"
+    print("running", EXE, flush=True)
+    out = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "mismatches: exp0 0 exp-40 0 exp40 0 exp17 0" in out.stdout, out.stdout
