@@ -76,8 +76,17 @@ def P(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
-def nsets_for(set_bytes):
-    return max(4, -(-int(1.2e9) // max(1, set_bytes)))
+LLC_BYTES = 256 << 20
+
+
+def nsets_for(read_bytes, set_bytes, cap_bytes=16 << 30):
+    """Buffer sets to rotate so that a set's inputs are re-read only after at
+    least twice the last-level cache of other reads (non-temporal stores do
+    not allocate there, so reads alone must overflow it), and at least 1.2 GB
+    in total; at most 64 sets (the tiny per-tensor workload is latency-bound
+    and stays cache-resident) and cap_bytes of device memory."""
+    n = max(4, -(-2 * LLC_BYTES // max(1, read_bytes)), -(-int(1.2e9) // max(1, set_bytes)))
+    return max(2, min(n, 64, cap_bytes // max(1, set_bytes)))
 
 
 def check(rc, what):
@@ -122,13 +131,12 @@ def build_step(torch, tq):
     dy = workloads.make_dy("c2_per_token_s8")
     L = tq._lib
     per_set = rows * cols * 2 * 5 + rows * cols + rows * 4
-    nsets = nsets_for(per_set)
+    nsets = nsets_for(rows * cols, per_set)        # smallest read stream: the s8 codes
+    x0, dy0 = dev_bits(x, "bf16", torch), dev_bits(dy, "bf16", torch)
     sets = []
     for i in range(nsets):
-        xd = dev_bits(x, "bf16", torch)
-        dyd = dev_bits(dy, "bf16", torch)
         sets.append(dict(
-            x=xd, dy=dyd,
+            x=x0 if i == 0 else x0.clone(), dy=dy0 if i == 0 else dy0.clone(),
             q=torch.empty((rows, cols), dtype=torch.uint8, device="cuda"),
             s=torch.empty(rows, dtype=torch.float32, device="cuda"),
             y=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"),
@@ -152,24 +160,30 @@ def build_step(torch, tq):
 
 
 def run_step_bench(torch, tq, steps, warmup):
-    """K steps, issued kernel by kernel: K quantize launches (rotating buffer
-    sets), then K dequantize, K STE backward and K dequantize backward
-    launches -- the same work and dependency order as K whole steps.  One HIP
+    """K steps, issued kernel by kernel: K quantize launches, then K dequantize,
+    K STE backward and K dequantize backward launches -- the same work and
+    dependency order as K whole steps.  One launch counter runs through all
+    of them and picks the buffer set, so every launch reads the set touched
+    longest ago (its inputs were last used nsets launches earlier).  One HIP
     event pair brackets each kernel's K back-to-back launches on the launch
     stream, so its mean launch time carries no per-launch event overhead."""
     sets, kernels = build_step(torch, tq)
     names = list(kernels)
     step_bytes = sum(kernels[k][0] for k in names)
+    c = 0
     for i in range(warmup):
         for k in names:
-            kernels[k][1](sets[i % len(sets)])
+            kernels[k][1](sets[c % len(sets)])
+            c += 1
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record()
+    c = 0
     for j, k in enumerate(names):
         for i in range(steps):
-            kernels[k][1](sets[i % len(sets)])
+            kernels[k][1](sets[c % len(sets)])
+            c += 1
         ev[j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -190,11 +204,11 @@ def breakdown(torch, tq, iters=20, only=None):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = []
 
-    def bench_op(name, cfg, nbytes, make_set, launch, set_bytes):
+    def bench_op(name, cfg, nbytes, make_set, launch, set_bytes, read_bytes):
         if only and only != name:
             return
         log("breakdown:", name)
-        sets = [make_set(i) for i in range(nsets_for(set_bytes))]
+        sets = [make_set(i) for i in range(nsets_for(read_bytes, set_bytes))]
         for i in range(3):
             launch(sets[i % len(sets)])
         s_ev = torch.cuda.Event(enable_timing=True)
@@ -223,10 +237,10 @@ def breakdown(torch, tq, iters=20, only=None):
                          ws=E(8192, u8), y=E(n1, f32), dx=E(n1, f32))
     bench_op("quant_per_tensor_s8", "c1 f32 [64,256]", n1 * 4 + n1 + 4, mk1,
              lambda b: check(L.tq_quant_per_tensor(P(b["x"]), 0, n1, 0, -127, 127, 0, P(b["q"]), P(b["s"]), None,
-                                                   P(b["ws"]), 8192, stream), "c1 quant"), n1 * 20)
+                                                   P(b["ws"]), 8192, stream), "c1 quant"), n1 * 20, n1 * 4)
     bench_op("quant_per_tensor_s8_backward", "c1 f32 [64,256]", n1 * 12 + 4, mk1,
              lambda b: check(L.tq_quant_per_tensor_backward(P(b["x"]), 0, n1, 0, -127, 127, P(b["s"]), None,
-                                                            P(b["dy"]), P(b["dx"]), stream), "c1 ste"), n1 * 20)
+                                                            P(b["dy"]), P(b["dx"]), stream), "c1 ste"), n1 * 20, n1 * 8)
 
     # per-group u4 g128 asymmetric, f16 [11008, 4096]
     w3 = workloads.make_input("c3_per_group_u4_g128")
@@ -238,10 +252,10 @@ def breakdown(torch, tq, iters=20, only=None):
                          z=E((N3, K3 // 128), u8), y=E((N3, K3), f16))
     bench_op("quant_per_group_u4_g128", "c3 f16 [11008,4096]", b3, mk3,
              lambda b: check(L.tq_quant_per_group(P(b["x"]), 1, 2, shp3, 1, 128, 3, 0, 15, P(b["q"]), P(b["s"]),
-                                                  P(b["z"]), stream), "c3 quant"), b3 + n3 * 2)
+                                                  P(b["z"]), stream), "c3 quant"), b3 + n3 * 2, n3 * 2)
     bench_op("dequant_per_group_u4_g128", "c3 f16 [11008,4096]", b3, mk3,
              lambda b: check(L.tq_dequant_per_group(P(b["q"]), 3, 2, shp3, 1, 128, P(b["s"]), P(b["z"]), P(b["y"]),
-                                                    1, stream), "c3 dequant"), b3 + n3 * 2)
+                                                    1, stream), "c3 dequant"), b3 + n3 * 2, n3 // 2 + (n3 // 128) * 5)
 
     # FP8 1x128 activations bf16 [4096, 7168]; 128x128 weights bf16 [7168, 7168]
     for key, name in (("c4_fp8_act_1x128", "fp8_1x128"), ("c4_fp8_weight_128x128", "fp8_128x128")):
@@ -256,11 +270,11 @@ def breakdown(torch, tq, iters=20, only=None):
         bench_op("quant_" + name, cfg, nb, mk,
                  lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_quant_fp8_block(P(b["x"]), 2, R, C, br, bc, P(b["q"]),
                                                                               P(b["s"]), stream), "fp8 quant"),
-                 nb + R * C * 2)
+                 nb + R * C * 2, R * C * 2)
         bench_op("dequant_" + name, cfg, nb, mk,
                  lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_dequant_fp8_block(P(b["q"]), R, C, br, bc, P(b["s"]),
                                                                                 P(b["y"]), 2, stream), "fp8 deq"),
-                 nb + R * C * 2)
+                 nb + R * C * 2, R * C + ns * 4)
 
     # FP4: NVFP4 (dynamic and static per-tensor scale), MXFP4, transposes
     w5 = workloads.make_input("c5_fp4_weight")
@@ -275,19 +289,19 @@ def breakdown(torch, tq, iters=20, only=None):
         if kind == "nvfp4":
             bench_op("quant_nvfp4_dynamic_global", cfg, nb, mk,
                      lambda b: check(L.tq_quant_fp4_block(P(b["x"]), 2, N5, K5, 0, P(b["p"]), P(b["b"]), P(b["g"]), 0,
-                                                          P(b["ws"]), 8192, stream), "nvfp4"), nb + n5)
+                                                          P(b["ws"]), 8192, stream), "nvfp4"), nb + n5, n5 * 2)
             bench_op("quant_nvfp4_static_global", cfg, nb, mk,
                      lambda b: check(L.tq_quant_fp4_block(P(b["x"]), 2, N5, K5, 0, P(b["p"]), P(b["b"]), P(b["g"]), 1,
-                                                          None, 0, stream), "nvfp4 static"), nb + n5)
+                                                          None, 0, stream), "nvfp4 static"), nb + n5, n5 * 2)
         else:
             bench_op("quant_mxfp4", cfg, nb, mk,
                      lambda b: check(L.tq_quant_fp4_block(P(b["x"]), 2, N5, K5, 1, P(b["p"]), P(b["b"]), None, 1,
-                                                          None, 0, stream), "mxfp4"), nb + n5)
+                                                          None, 0, stream), "mxfp4"), nb + n5, n5 * 2)
         tb = 2 * (n5 // 2 + n5 // gs)
         bench_op("transpose_for_gemm_" + kind, cfg, tb, mk,
                  lambda b, gs=gs: check(L.tq_fp4_transpose_for_gemm(P(b["p"]), P(b["b"]), N5, K5, gs, P(b["pt"]),
                                                                     P(b["bt"]), stream), "transpose"),
-                 nb + n5)
+                 nb + n5, tb // 2)
     return out
 
 

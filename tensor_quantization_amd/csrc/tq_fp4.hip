@@ -107,7 +107,7 @@ __device__ __forceinline__ void fp4_div8(const float v[8], const BP& p, float t[
 // elements 8j..8j+7 of its block, so each load instruction of a wave reads
 // 1 KB contiguously and each code store writes 256 bytes contiguously; the
 // block max takes one or two DPP steps.  U rounds of 64/T blocks per wave.
-template <int FT, int KIND, int U>
+template <int FT, int KIND, int U, bool NT>
 __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, int64_t nblocks,
                                                    const float* __restrict__ ws, int nws, int static_global,
                                                    float* __restrict__ global_scale, uint8_t* __restrict__ packed,
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, i
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t b = b0 + (int64_t)u * P;
-        if (b < nblocks) raw[u] = load8<FT, true>(x, b * GS + j * 8);
+        if (b < nblocks) raw[u] = load8<FT, NT>(x, b * GS + j * 8);
         else raw[u] = Raw8<FT>{};
     }
 #pragma unroll
@@ -245,11 +245,12 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
 
 // ------------------------------------------------------------ transpose
 // dst[c][r] = src[r][c] for a [R, C] byte matrix.  Fast path: R % 16 == 0,
-// C % 16 == 0 and 16-byte aligned bases; a block moves a 64-row x 256-column
-// tile.  Thread (d, m) of the read-out phase owns input columns 4d..4d+3
-// and input rows 16m..16m+15: it reads 16 dwords from LDS, transposes four
-// 4x4 byte blocks in registers and writes 16 bytes to each of 4 output rows.
-constexpr int TR_ROWS = 64, TR_COLS = 256, TR_PITCH = TR_COLS / 4 + 1;   // dwords, padded
+// C % 16 == 0 and 16-byte aligned bases; tiles of 128 x 128 bytes, so that
+// every wave-wide load and store instruction covers whole 128-byte lines.  Thread (d, m) of the read-out phase owns input columns 4d..4d+3 and
+// input rows 16m..16m+15: it reads 16 dwords from LDS, transposes four 4x4
+// byte blocks in registers and writes 16 bytes to each of 4 output rows; the
+// 8 threads with the same d write one full 128-byte output line per row.
+constexpr int TR = 128, TR_PITCH = TR / 4 + 1;   // dwords per LDS row, padded
 
 __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t o[4])
 {
@@ -264,44 +265,63 @@ __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t 
     o[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
+// A block walks TPB row-tiles of one 128-column strip: the next tile's global
+// loads are issued before the current tile is read out of LDS and stored, so
+// each block overlaps its reads with its writes.
+#ifndef TQ_TPB
+#define TQ_TPB 1
+#endif
+constexpr int TPB = TQ_TPB;
+
 __global__ __launch_bounds__(256) void k_transpose_u8(const uint8_t* __restrict__ src, int64_t R, int64_t C,
                                                       uint8_t* __restrict__ dst)
 {
-    __shared__ uint32_t tile[TR_ROWS * TR_PITCH];
+    __shared__ uint32_t tile[TR * TR_PITCH];
     const int t = threadIdx.x;
-    const int64_t R0 = (int64_t)blockIdx.y * TR_ROWS, C0 = (int64_t)blockIdx.x * TR_COLS;
-    // load: 4 rows per wave instruction, 256 contiguous bytes per row
+    const int64_t C0 = (int64_t)blockIdx.x * TR;
+    const int64_t Rb = (int64_t)blockIdx.y * TR * TPB;
+    uint4 w[4];
+    auto load_tile = [&](int64_t R0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int r = t / 16 + 16 * k;
-        const int cq = (t % 16) * 16;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (R0 + r < R && C0 + cq < C)
-            w = *reinterpret_cast<const uint4*>(src + (R0 + r) * C + C0 + cq);
-        uint32_t* row = tile + r * TR_PITCH + cq / 4;
-        row[0] = w.x;
-        row[1] = w.y;
-        row[2] = w.z;
-        row[3] = w.w;
-    }
-    __syncthreads();
-    const int m = t % 4, d = t / 4;        // rows 16m..16m+15, columns 4d..4d+3
-    uint32_t o[4][4];                       // o[c][quad] : output row 4d+c, bytes 4*quad..
+        for (int k = 0; k < 4; ++k) {
+            const int r = t / 8 + 32 * k;
+            const int cq = (t % 8) * 16;
+            w[k] = make_uint4(0, 0, 0, 0);
+            if (R0 + r < R && C0 + cq < C) w[k] = ld16<true>(src + (R0 + r) * C + C0 + cq);
+        }
+    };
+    load_tile(Rb);
+    const int m = t % 8, d = t / 8;        // read-out: rows 16m..16m+15, columns 4d..4d+3
+    for (int j = 0; j < TPB; ++j) {
+        const int64_t R0 = Rb + (int64_t)j * TR;
+        if (R0 >= R) break;                 // uniform across the block
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-        const int rb = 16 * m + 4 * qd;
-        uint32_t tr[4];
-        transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d], tile[(rb + 2) * TR_PITCH + d],
-                     tile[(rb + 3) * TR_PITCH + d], tr);
+        for (int k = 0; k < 4; ++k) {
+            uint32_t* row = tile + (t / 8 + 32 * k) * TR_PITCH + (t % 8) * 4;
+            row[0] = w[k].x;
+            row[1] = w[k].y;
+            row[2] = w[k].z;
+            row[3] = w[k].w;
+        }
+        __syncthreads();
+        if (j + 1 < TPB && R0 + TR < R) load_tile(R0 + TR);
+        uint32_t o[4][4];                   // o[c][qd]: output row 4d+c, bytes 4*qd.. of this 16-byte piece
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
-    }
+        for (int qd = 0; qd < 4; ++qd) {
+            const int rb = 16 * m + 4 * qd;
+            uint32_t tr[4];
+            transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d],
+                         tile[(rb + 2) * TR_PITCH + d], tile[(rb + 3) * TR_PITCH + d], tr);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int64_t oc = C0 + 4 * d + c;            // output row = input column
-        const int64_t orr = R0 + 16 * m;              // output column = input row
-        if (oc < C && orr < R)
-            *reinterpret_cast<uint4*>(dst + oc * R + orr) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+            for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t oc = C0 + 4 * d + c;        // output row = input column
+            const int64_t orr = R0 + 16 * m;          // output column = input row
+            if (oc < C && orr < R) st16<true>(dst + oc * R + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
+        }
+        __syncthreads();                    // the tile is rewritten next iteration
     }
 }
 
@@ -342,9 +362,9 @@ static unsigned grid_for(int64_t work, int64_t per_block)
 static tq_status transpose_bytes(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, hipStream_t st)
 {
     if (R == 0 || C == 0) return TQ_OK;
-    if (R % 16 == 0 && C % 16 == 0 && aligned16(src) && aligned16(dst) && cdiv(R, TR_ROWS) <= 65535) {
-        hipLaunchKernelGGL(k_transpose_u8, dim3((unsigned)cdiv(C, TR_COLS), (unsigned)cdiv(R, TR_ROWS)), dim3(256), 0,
-                           st, src, R, C, dst);
+    if (R % 16 == 0 && C % 16 == 0 && aligned16(src) && aligned16(dst) && cdiv(R, TR * TPB) <= 65535) {
+        hipLaunchKernelGGL(k_transpose_u8, dim3((unsigned)cdiv(C, TR), (unsigned)cdiv(R, TR * TPB)), dim3(256), 0, st,
+                           src, R, C, dst);
     } else {
         if (cdiv(R, 64) > 65535) return TQ_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(k_transpose_u8_generic, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64)), dim3(256), 0,
@@ -408,13 +428,19 @@ tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k
     if (kind == TQ_NVFP4) {
         const int64_t nb = numel / 16;
         const dim3 grid((unsigned)cdiv(cdiv(nb, U * 32), 4));
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U>), grid, dim3(256), 0, st, x, nb, ws, nws,
-                                                 static_global, global_scale, packed, block_scale));
+        // after the max pre-pass x may still sit in the last-level cache: read it temporally
+        if (static_global) {
+            TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U, true>), grid, dim3(256), 0, st, x, nb, ws,
+                                                     nws, static_global, global_scale, packed, block_scale));
+        } else {
+            TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U, false>), grid, dim3(256), 0, st, x, nb,
+                                                     ws, nws, static_global, global_scale, packed, block_scale));
+        }
     } else {
         const int64_t nb = numel / 32;
         const dim3 grid((unsigned)cdiv(cdiv(nb, U * 16), 4));
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U>), grid, dim3(256), 0, st, x, nb, ws, nws,
-                                                 1, global_scale, packed, block_scale));
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U, true>), grid, dim3(256), 0, st, x, nb, ws,
+                                                 nws, 1, global_scale, packed, block_scale));
     }
     return launch_status();
 }

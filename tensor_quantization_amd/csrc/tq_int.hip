@@ -553,6 +553,64 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
     }
 }
 
+// Small tensors (numel % 8 == 0, numel <= 1024 * 8 * SMALL_V): one launch of
+// 1024 threads; each thread loads its (up to) SMALL_V vectors once, the block
+// reduces through DPP and LDS, and the codes are encoded from registers.
+constexpr int SMALL_V = 4;
+constexpr int64_t SMALL_MAX = 1024 * 8 * SMALL_V;
+
+template <int FT, int BITS, bool SYM>
+__global__ __launch_bounds__(1024) void k_tensor_small(const void* __restrict__ x, int64_t numel, float qmin,
+                                                       float qmax, float yc, uint8_t* __restrict__ q,
+                                                       float* __restrict__ scale, uint8_t* __restrict__ zp)
+{
+    __shared__ float smn[16], smx[16];
+    __shared__ GP sp;
+    const int t = threadIdx.x;
+    const int64_t nvec = numel / 8;
+    float v[SMALL_V][8];
+    float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < SMALL_V; ++k) {
+        const int64_t vi = t + (int64_t)k * 1024;
+        Raw8<FT> r = Raw8<FT>{};
+        if (vi < nvec) r = load8<FT>(x, vi * 8);
+        widen8<FT>(r, v[k]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) minmax_acc<FT, SYM>(v[k][i], mn, mx);
+    }
+    mn = team_min<64>(mn);
+    mx = team_max<64>(mx);
+    if ((t & 63) == 0) {
+        smn[t >> 6] = mn;
+        smx[t >> 6] = mx;
+    }
+    __syncthreads();
+    if (t == 0) {
+        float a = smn[0], b = smx[0];
+        for (int k = 1; k < 16; ++k) {
+            a = __builtin_fminf(a, smn[k]);
+            b = __builtin_fmaxf(b, smx[k]);
+        }
+        GP p = SYM ? make_gp<FT, true>(b, 0.0f, 0.0f, qmin, qmax, yc) : make_gp<FT, false>(0.0f, a, b, qmin, qmax, yc);
+        sp = p;
+        scale[0] = p.s;
+        if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
+    }
+    __syncthreads();
+    const GP p = sp;
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+#pragma unroll
+    for (int k = 0; k < SMALL_V; ++k) {
+        const int64_t vi = t + (int64_t)k * 1024;
+        if (vi >= nvec) break;
+        float c[8];
+        if (p.fast) enc8<FT, true, !SYM>(v[k], p, lo, hi, c);
+        else enc8<FT, false, !SYM>(v[k], p, lo, hi, c);
+        store_codes8<BITS>(q, vi * 8, c);
+    }
+}
+
 // ------------------------------------------------------------ elementwise
 // Group ids of a vector of 8 elements starting at e (e % 8 == 0):
 //   MAP_CONTIG: groups of L contiguous elements (L % 8 == 0): one group e / L
@@ -613,12 +671,25 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
                 cw[1] = 0;
             }
             const int64_t g = vec_group<MAPK>(e, P1, P2, sh);
-            float out[8];
+            float out[8], sv[8], zv[8];
+            if constexpr (MAPK == MAP_CONTIG) {
+                const float s1 = scale[g], z1 = zp_f<SIGNED>(zp, g);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    sv[i] = s1;
+                    zv[i] = z1;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    sv[i] = scale[g + i];
+                    zv[i] = zp_f<SIGNED>(zp, g + i);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int64_t gi = MAPK == MAP_CONTIG ? g : g + i;
                 const uint32_t c = BITS == 8 ? (cw[i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[0] >> (i * 4)) & 0xfu;
-                out[i] = (code_f<SIGNED>(c, BITS) - zp_f<SIGNED>(zp, gi)) * scale[gi];
+                out[i] = (code_f<SIGNED>(c, BITS) - zv[i]) * sv[i];
             }
             store8<YT, true>(y, e, out);
         }
@@ -1073,6 +1144,15 @@ tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int cod
     hipStream_t st = as_stream(stream);
     const bool sym = zero_point == nullptr;
     const int bits = code_bits(code);
+    const float fmin = (float)qmin, fmax = (float)qmax, yc = range_reciprocal(qmin, qmax, sym);
+    if (!static_scale && numel % 8 == 0 && numel <= SMALL_MAX) {
+        uint8_t* qb = static_cast<uint8_t*>(q);
+        uint8_t* zb = static_cast<uint8_t*>(zero_point);
+        TQ_FT_SWITCH(x_dtype, TQ_BITS_SYM_SWITCH(bits, sym,
+            hipLaunchKernelGGL((k_tensor_small<FTV, BV, SV>), dim3(1), dim3(1024), 0, st, x, numel, fmin, fmax, yc, qb,
+                               scale, zb)));
+        return launch_status();
+    }
     int nblk = 0;
     const bool small = numel <= 65536;
     if (!static_scale && !small) {

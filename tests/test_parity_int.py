@@ -160,7 +160,9 @@ def test_per_channel(tq, orc, shape, xt, axis, code, sym):
     run_int_case(tq, orc, x, xt, "channel", axis, 0, code, sym)
 
 
-@pytest.mark.parametrize("numel,xt,code,sym", [(64 * 256, "f32", "s8", True), (1 << 20, "bf16", "s8", True),
+@pytest.mark.parametrize("numel,xt,code,sym", [(64 * 256, "f32", "s8", True), (2048, "f16", "u8", False),
+                                               (32768, "bf16", "s4", True), (32776, "f32", "u4", False),
+                                               (1 << 20, "bf16", "s8", True),
                                                (300_000, "f16", "u8", False), (1001, "f32", "s8", True),
                                                (1002, "bf16", "u4", False), (5 * (1 << 18), "f32", "s4", True)])
 def test_per_tensor(tq, orc, numel, xt, code, sym):
