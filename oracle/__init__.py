@@ -366,3 +366,49 @@ def widen(x, xt):
     if xt == "bf16":
         return bf16_to_f32(x)
     return f16_to_f32(x)
+
+
+# ----------------------------------------------------------------- FP4 layout follow-ons
+def fp4_transpose_concat(parts, k, gs, align=1):
+    """parts: list of (packed [n_i, k/2], block scales [n_i, k/gs]).
+    Returns (packed_t [k/2, stride], scales_t [k/gs, stride], stride)."""
+    n = [int(p.shape[0]) for p, _ in parts]
+    total = sum(n)
+    stride = -(-total // align) * align if align > 1 else total
+    pt = np.zeros((k // 2, stride), np.uint8)
+    st = np.zeros((k // gs, stride), np.uint8)
+    keep = [(np.ascontiguousarray(p, np.uint8), np.ascontiguousarray(b, np.uint8)) for p, b in parts]
+    pp = (ctypes.c_void_p * len(keep))(*[_p(p).value for p, _ in keep])
+    bb = (ctypes.c_void_p * len(keep))(*[_p(b).value for _, b in keep])
+    nn = (ctypes.c_int64 * len(n))(*n)
+    rc = lib().orc_fp4_transpose_concat(len(keep), pp, bb, nn, ctypes.c_int64(k), ctypes.c_int64(gs),
+                                        ctypes.c_int64(stride), _p(pt), _p(st))
+    if rc:
+        raise ValueError("oracle rejected fp4_transpose_concat arguments")
+    return pt, st, stride
+
+
+def fp4_concat_rows(p1, s1, g1, p2, s2, g2, k):
+    p1 = np.ascontiguousarray(p1, np.uint8)
+    p2 = np.ascontiguousarray(p2, np.uint8)
+    n1, n2 = p1.shape[0], p2.shape[0]
+    po = np.zeros((n1 + n2, k // 2), np.uint8)
+    so = np.zeros((n1 + n2, k // 16), np.uint8)
+    rc = lib().orc_fp4_concat_rows(_p(p1), _p(np.ascontiguousarray(s1, np.uint8)), ctypes.c_float(g1), _p(p2),
+                                   _p(np.ascontiguousarray(s2, np.uint8)), ctypes.c_float(g2),
+                                   ctypes.c_int64(n1), ctypes.c_int64(n2), ctypes.c_int64(k), _p(po), _p(so))
+    if rc:
+        raise ValueError("oracle rejected fp4_concat_rows arguments")
+    return po, so
+
+
+def fp4_predequant_to_fp8(packed, bscale, global_scale, kind):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    rows, kb = packed.shape
+    out = np.zeros((rows, kb * 2), np.uint8)
+    rc = lib().orc_fp4_predequant_to_fp8(_p(packed), _p(np.ascontiguousarray(bscale, np.uint8)),
+                                         ctypes.c_float(global_scale), ctypes.c_int64(rows), ctypes.c_int64(kb * 2),
+                                         FP4_KINDS[kind], _p(out))
+    if rc:
+        raise ValueError("oracle rejected fp4_predequant_to_fp8 arguments")
+    return out

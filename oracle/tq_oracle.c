@@ -664,3 +664,66 @@ void orc_f16_to_f32_array(const uint16_t* h, int64_t n, float* out)
 { for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f32(h[i]); }
 void orc_enc_e8m0_mx_array(const float* v, int64_t n, uint8_t* out)
 { for (int64_t i = 0; i < n; ++i) out[i] = orc_enc_e8m0_mx(v[i]); }
+
+/* ------------------------------------------------ FP4 layout follow-ons */
+/* QuantizedWeight::transpose_concat_for_gemm / _gs / _padded: several
+ * weights sharing K, each packed [n_i, K/2] with block scales [n_i, K/gs],
+ * transposed and concatenated along N:
+ *   packed_t[j][off_i + r] = packed_i[r][j],  scale_t[b][off_i + r] = scale_i[r][b]
+ * with off_i = n_0 + ... + n_(i-1), rows of the outputs `stride` bytes long
+ * (stride >= sum n_i; the _padded variant rounds it up to a multiple of
+ * `align`) and the pad columns zero.  An empty list is an error. */
+int orc_fp4_transpose_concat(int nparts, const uint8_t* const* packed, const uint8_t* const* bscale,
+                             const int64_t* n, int64_t k, int64_t gs, int64_t stride,
+                             uint8_t* packed_t, uint8_t* bscale_t)
+{
+    if (nparts <= 0 || k < 0 || (k & 1) || gs <= 0 || k % gs) return ORC_BAD;
+    int64_t total = 0;
+    for (int i = 0; i < nparts; ++i) { if (n[i] < 0) return ORC_BAD; total += n[i]; }
+    if (stride < total) return ORC_BAD;
+    int64_t kb = k / 2, nb = k / gs;
+    memset(packed_t, 0, (size_t)(kb * stride));
+    memset(bscale_t, 0, (size_t)(nb * stride));
+    int64_t off = 0;
+    for (int i = 0; i < nparts; ++i) {
+        for (int64_t r = 0; r < n[i]; ++r) {
+            for (int64_t j = 0; j < kb; ++j) packed_t[j * stride + off + r] = packed[i][r * kb + j];
+            for (int64_t b = 0; b < nb; ++b) bscale_t[b * stride + off + r] = bscale[i][r * nb + b];
+        }
+        off += n[i];
+    }
+    return ORC_OK;
+}
+
+/* QuantizedWeight::concat_rows: [N1, K/2] + [N2, K/2] -> [N1+N2, K/2] (and the
+ * block scales alike) for NVFP4 weights whose per-tensor scales must be
+ * bit-identical, else an error (the result carries one scale for every row). */
+int orc_fp4_concat_rows(const uint8_t* p1, const uint8_t* s1, float g1, const uint8_t* p2, const uint8_t* s2,
+                        float g2, int64_t n1, int64_t n2, int64_t k, uint8_t* pout, uint8_t* sout)
+{
+    if (n1 < 0 || n2 < 0 || k < 0 || k % 16) return ORC_BAD;
+    if (bits_of_f(g1) != bits_of_f(g2)) return ORC_BAD;
+    int64_t kb = k / 2, nb = k / 16;
+    memcpy(pout, p1, (size_t)(n1 * kb));
+    memcpy(pout + n1 * kb, p2, (size_t)(n2 * kb));
+    memcpy(sout, s1, (size_t)(n1 * nb));
+    memcpy(sout + n1 * nb, s2, (size_t)(n2 * nb));
+    return ORC_OK;
+}
+
+/* QuantizedWeight::predequant_to_fp8: the weight dequantized with its
+ * per-tensor scale applied, stored as E4M3:
+ *   out = E4M3(val(q) * eff),  eff = val(sb) * s_g (NVFP4) or 2^(sb-127) (MXFP4)
+ * (binary32 products, one rounding each, then the saturating E4M3 encode). */
+int orc_fp4_predequant_to_fp8(const uint8_t* packed, const uint8_t* bscale, float sg, int64_t rows, int64_t k,
+                              int kind, uint8_t* out)
+{
+    if (fp4_dims(kind, rows, k)) return ORC_BAD;
+    int gs = fp4_gs(kind);
+    for (int64_t e = 0; e < rows * k; ++e) {
+        int64_t r = e / k, b = (e % k) / gs;
+        float eff = fp4_eff(kind, bscale[r * (k / gs) + b], kind == ORC_NVFP4 ? sg : 1.0f);
+        out[e] = orc_enc_e4m3(orc_dec_e2m1(fp4_code_at(packed, e)) * eff);
+    }
+    return ORC_OK;
+}
