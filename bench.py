@@ -302,6 +302,31 @@ def breakdown(torch, tq, iters=20, only=None):
                  lambda b, gs=gs: check(L.tq_fp4_transpose_for_gemm(P(b["p"]), P(b["b"]), N5, K5, gs, P(b["pt"]),
                                                                     P(b["bt"]), stream), "transpose"),
                  nb + n5, tb // 2)
+
+    # FP4 layout follow-ons on the NVFP4 c5 weight: gate + up fused into one
+    # [2048, 28672] GEMM operand, the two stacked by rows, and the FP8 expansion
+    pb, sbb = n5 // 2, n5 // 16
+    mkf = lambda i: dict(p1=E((N5, K5 // 2), u8), b1=E((N5, K5 // 16), u8), p2=E((N5, K5 // 2), u8),
+                         b2=E((N5, K5 // 16), u8), pt=E((K5 // 2, 2 * N5), u8), bt=E((K5 // 16, 2 * N5), u8),
+                         po=E((2 * N5, K5 // 2), u8), bo=E((2 * N5, K5 // 16), u8), f8=E((N5, K5), u8))
+    cfg = "c5 nvfp4 2 x [14336,4096]"
+
+    def concat_t(b):
+        pp = (ctypes.c_void_p * 2)(b["p1"].data_ptr(), b["p2"].data_ptr())
+        bb = (ctypes.c_void_p * 2)(b["b1"].data_ptr(), b["b2"].data_ptr())
+        nn = (ctypes.c_int64 * 2)(N5, N5)
+        check(L.tq_fp4_transpose_concat_for_gemm(2, pp, bb, nn, K5, 16, 128, P(b["pt"]), P(b["bt"]), None,
+                                                 stream), "transpose concat")
+    bench_op("transpose_concat_for_gemm_nvfp4", cfg, 4 * (pb + sbb), mkf, concat_t, 8 * (pb + sbb) + n5,
+             2 * (pb + sbb))
+    bench_op("concat_rows_nvfp4", cfg, 4 * (pb + sbb), mkf,
+             lambda b: check(L.tq_fp4_concat_rows(P(b["p1"]), P(b["b1"]), 1.5e-5, P(b["p2"]), P(b["b2"]), 1.5e-5, N5,
+                                                  N5, K5, P(b["po"]), P(b["bo"]), stream), "concat rows"),
+             8 * (pb + sbb) + n5, 2 * (pb + sbb))
+    bench_op("predequant_to_fp8_nvfp4", "c5 nvfp4 [14336,4096]", pb + sbb + n5, mkf,
+             lambda b: check(L.tq_fp4_predequant_to_fp8(P(b["p1"]), P(b["b1"]), 1.5e-5, N5, K5, 0, P(b["f8"]),
+                                                        stream), "predequant"),
+             8 * (pb + sbb) + n5, pb + sbb)
     return out
 
 
@@ -333,8 +358,8 @@ def cpu_baseline(min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the per-row/per-group/per-tile "
-              "work shards without communication; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (every row, group and tile is "
+              "independent, so the work shards without communication).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import tensor_quantization_amd as tq

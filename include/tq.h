@@ -9,7 +9,8 @@
  *     128x128 weight tiles, or any block that tiles the matrix),
  *   - FP4 E2M1 packed two per byte with NVFP4 (E4M3 block scale per 16 plus
  *     an fp32 per-tensor scale) or MXFP4 (E8M0 block scale per 32) scales,
- *   - the FP4 transposes to GEMM layout.
+ *   - the FP4 transposes to GEMM layout, the concatenations of FP4 weights
+ *     and their expansion to FP8 E4M3.
  *
  * Sources (page titles and sections):
  *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
@@ -21,8 +22,9 @@
  *        PerChannel{axis}, Group{axis, group_size}).
  *   [W]  metrale QuantizedWeight -- fields (packed E2M1 two per byte
  *        [N, K/2]; block scales E4M3 for NVFP4 / E8M0 for MXFP4; fp32
- *        per-tensor scale; optional static input scale), transpose_for_gemm
- *        and transpose_for_gemm_gs.
+ *        per-tensor scale; optional static input scale), transpose_for_gemm,
+ *        transpose_for_gemm_gs, transpose_concat_for_gemm(_gs, _padded),
+ *        concat_rows and predequant_to_fp8.
  *   [S]  smile.llm.quant package summary -- Fp8BlockGemm (E4M3, one fp32 scale
  *        per 1x128 activation group and per 128x128 weight tile),
  *        Fp8BlockDequant, MxFp8 (E8M0 scale per 32 elements).
@@ -66,7 +68,7 @@ extern "C" {
 typedef enum {
     TQ_OK = 0,
     TQ_ERR_INVALID = 1,     /* bad pointer, shape, dtype, range or group size */
-    TQ_ERR_UNSUPPORTED = 2, /* well-formed request this build does not implement */
+    TQ_ERR_UNSUPPORTED = 2, /* well-formed request the library does not implement */
     TQ_ERR_ALIGN = 3,       /* a base pointer is not 16-byte aligned */
     TQ_ERR_HIP = 4          /* the HIP runtime reported a launch error */
 } tq_status;
@@ -269,6 +271,52 @@ tq_status tq_dequant_fp4_block_backward(const void* dy, int dy_dtype, const uint
 tq_status tq_fp4_transpose_for_gemm(const uint8_t* packed, const uint8_t* block_scale,
                                     int64_t n, int64_t k, int32_t group_size,
                                     uint8_t* packed_t, uint8_t* block_scale_t, void* stream);
+
+/* [W] transpose_concat_for_gemm / _gs / _padded: several weights sharing k,
+ * part i packed [n_i, k/2] with block_scale [n_i, k/group_size], transposed
+ * and concatenated along n into one GEMM operand:
+ *   packed_t[j][off_i + r] = packed_i[r][j]      (packed_t is [k/2, stride])
+ *   block_scale_t[b][off_i + r] = block_scale_i[r][b]   ([k/group_size, stride])
+ * with off_i = n_0 + ... + n_(i-1) and stride = n_total rounded up to a
+ * multiple of `align` (align = 1: no padding); columns n_total..stride-1 are
+ * zero.  host_packed / host_block_scale are HOST arrays of nparts DEVICE
+ * pointers, host_n a host array of the n_i; parts need no alignment (16-byte
+ * aligned parts with n_i, off_i and stride multiples of 16 take the tiled
+ * path).  The stride is written to *host_stride when it is not NULL.
+ * block_scale_t == NULL (host_block_scale may then be NULL) transposes only
+ * the codes.  nparts <= 0 (an empty list) or align <= 0 is TQ_ERR_INVALID.
+ * Per-tensor scales are the caller's business: the page's result carries the
+ * first part's and checks nothing. */
+tq_status tq_fp4_transpose_concat_for_gemm(int32_t nparts, const uint8_t* const* host_packed,
+                                           const uint8_t* const* host_block_scale,
+                                           const int64_t* host_n, int64_t k, int32_t group_size,
+                                           int64_t align, uint8_t* packed_t,
+                                           uint8_t* block_scale_t, int64_t* host_stride,
+                                           void* stream);
+
+/* [W] concat_rows: two NVFP4 weights with the same k (k % 16 == 0) stacked
+ * by rows, [n1, k/2] + [n2, k/2] -> packed_out [n1+n2, k/2] and
+ * [n1, k/16] + [n2, k/16] -> block_scale_out [n1+n2, k/16].  The per-tensor
+ * scales (host floats) must be bit-identical, else TQ_ERR_INVALID and nothing
+ * is enqueued: the result has one per-tensor scale (either input's).  Device
+ * to device copies on `stream`; no alignment requirement. */
+tq_status tq_fp4_concat_rows(const uint8_t* packed1, const uint8_t* block_scale1,
+                             float host_global_scale1, const uint8_t* packed2,
+                             const uint8_t* block_scale2, float host_global_scale2, int64_t n1,
+                             int64_t n2, int64_t k, uint8_t* packed_out,
+                             uint8_t* block_scale_out, void* stream);
+
+/* [W] predequant_to_fp8: the FP4 weight [rows, k] expanded to E4M3 bytes
+ * [rows, k] with the per-tensor scale applied:
+ *   fp8_out = E4M3(val(q) * eff),  eff = val(sb) * host_global_scale (NVFP4)
+ *                                  or 2^(sb - 127) (MXFP4; the scale is unused)
+ * each product rounded once to binary32, then encoded round-to-nearest-even,
+ * saturating at +-448, keeping the sign of zero.  packed needs 8-byte
+ * alignment, fp8_out 16-byte.  Asynchronous like every call here (the page's
+ * version synchronizes because it allocates the output). */
+tq_status tq_fp4_predequant_to_fp8(const uint8_t* packed, const uint8_t* block_scale,
+                                   float host_global_scale, int64_t rows, int64_t k, int kind,
+                                   uint8_t* fp8_out, void* stream);
 
 #ifdef __cplusplus
 }

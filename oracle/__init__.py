@@ -8,11 +8,11 @@ arrays.  Float tensors of type f16 / bf16 are passed as ``uint16`` bit
 patterns, f32 as ``float32``.
 
 Every function states the definition it follows in ``tq_oracle.c``; the
-readings taken where the pages are silent are documented there and in
-the design doc.  Functions pinned to outside facts are listed in the tests
-(``tests/test_oracle_*.py``); the choices the pages leave open (NVFP4 scale
-bits, MX clipping, the asymmetric formula, degenerate groups) are pinned only
-by internal invariants -- "parity unpinned" against any outside source.
+readings taken where the pages are silent are documented there.  Functions
+pinned to outside facts are listed in the tests (``tests/test_oracle_*.py``);
+the choices the pages leave open (NVFP4 scale bits, MX clipping, the
+asymmetric formula, degenerate groups) are pinned only by internal
+invariants -- "parity unpinned" against any outside source.
 """
 from __future__ import annotations
 

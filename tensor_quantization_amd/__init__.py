@@ -72,6 +72,10 @@ _SIGS = {
     "tq_quant_fp4_block_backward": ([_P, _I, _P, _P, _I64, _I64, _I, _P, _P, _P], _I),
     "tq_dequant_fp4_block_backward": ([_P, _I, _P, _P, _I64, _I64, _I, _P, _P], _I),
     "tq_fp4_transpose_for_gemm": ([_P, _P, _I64, _I64, _I32, _P, _P, _P], _I),
+    "tq_fp4_transpose_concat_for_gemm": ([_I32, ctypes.POINTER(_P), ctypes.POINTER(_P), _SHAPE, _I64, _I32, _I64,
+                                          _P, _P, ctypes.POINTER(_I64), _P], _I),
+    "tq_fp4_concat_rows": ([_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _I64, _I64, _I64, _P, _P, _P], _I),
+    "tq_fp4_predequant_to_fp8": ([_P, _P, ctypes.c_float, _I64, _I64, _I, _P, _P], _I),
 }
 
 for _name, (_args, _ret) in _SIGS.items():
@@ -444,3 +448,49 @@ def tq_fp4_transpose_for_gemm(packed, block_scale, n, k, group_size):
           None if block_scale is None else _ptr(block_scale.contiguous()), n, k, group_size, _ptr(pt), _ptr(st),
           _stream(packed.device))
     return pt, st
+
+
+def tq_fp4_transpose_concat_for_gemm(parts, k, group_size, align=1):
+    """parts: [(packed [n_i, k/2], block_scale [n_i, k/gs] or None), ...].
+    Returns (packed_t [k/2, stride], block_scale_t [k/gs, stride] or None,
+    stride) with stride = sum(n_i) rounded up to a multiple of ``align``."""
+    if not parts:
+        raise TQError("tq_fp4_transpose_concat_for_gemm", TQ_ERR_INVALID)
+    dev = parts[0][0].device
+    packed = [p.contiguous() for p, _ in parts]
+    with_scales = all(b is not None for _, b in parts)
+    scales = [b.contiguous() for _, b in parts] if with_scales else None
+    n = [int(p.shape[0]) for p in packed]
+    stride = -(-sum(n) // align) * align if align > 0 else 0
+    pt = torch.empty((k // 2, stride), dtype=torch.uint8, device=dev)
+    st = torch.empty((k // group_size, stride), dtype=torch.uint8, device=dev) if with_scales else None
+    pp = (_P * len(packed))(*[p.data_ptr() for p in packed])
+    bb = (_P * len(packed))(*[b.data_ptr() for b in scales]) if with_scales else None
+    got = _I64(0)
+    _call("tq_fp4_transpose_concat_for_gemm", len(packed), pp, bb, (_I64 * len(n))(*n), k, group_size, align, _ptr(pt),
+          _ptr(st), ctypes.byref(got), _stream(dev))
+    assert got.value == stride
+    return pt, st, stride
+
+
+def tq_fp4_concat_rows(packed1, block_scale1, global_scale1, packed2, block_scale2, global_scale2, k):
+    """Stack two NVFP4 weights by rows; the per-tensor scales are host floats
+    that must be bit-identical."""
+    n1, n2 = int(packed1.shape[0]), int(packed2.shape[0])
+    dev = packed1.device
+    po = torch.empty((n1 + n2, k // 2), dtype=torch.uint8, device=dev)
+    so = torch.empty((n1 + n2, k // 16), dtype=torch.uint8, device=dev)
+    _call("tq_fp4_concat_rows", _ptr(packed1.contiguous()), _ptr(block_scale1.contiguous()), float(global_scale1),
+          _ptr(packed2.contiguous()), _ptr(block_scale2.contiguous()), float(global_scale2), n1, n2, k, _ptr(po),
+          _ptr(so), _stream(dev))
+    return po, so
+
+
+def tq_fp4_predequant_to_fp8(packed, block_scale, global_scale=1.0, kind="nvfp4"):
+    """packed [rows, k/2] -> E4M3 bytes [rows, k] (uint8) with the per-tensor
+    scale (a host float) applied."""
+    rows, kb = packed.shape
+    out = torch.empty((rows, kb * 2), dtype=torch.uint8, device=packed.device)
+    _call("tq_fp4_predequant_to_fp8", _ptr(packed.contiguous()), _ptr(block_scale.contiguous()), float(global_scale),
+          rows, kb * 2, FP4_KIND[kind], _ptr(out), _stream(packed.device))
+    return out

@@ -40,6 +40,15 @@ __device__ __forceinline__ uint4 ld16(const void* p)
 }
 
 template <bool NT = false>
+__device__ __forceinline__ uint2 ld8(const void* p)
+{
+    u32x2 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+    else v = *static_cast<const u32x2*>(p);
+    return make_uint2(v.x, v.y);
+}
+
+template <bool NT = false>
 __device__ __forceinline__ void st16(void* p, uint4 w)
 {
     const u32x4 v = {w.x, w.y, w.z, w.w};

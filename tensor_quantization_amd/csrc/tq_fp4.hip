@@ -21,6 +21,8 @@
 #include "tq_device.h"
 #include "tq_host.h"
 
+#include <string.h>
+
 namespace tq {
 
 enum { NV = 0, MX = 1 };
@@ -244,8 +246,10 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
 }
 
 // ------------------------------------------------------------ transpose
-// dst[c][r] = src[r][c] for a [R, C] byte matrix.  Fast path: R % 16 == 0,
-// C % 16 == 0 and 16-byte aligned bases; tiles of 128 x 128 bytes, so that
+// dst[c * ldd + off + r] = src[r][c] for a [R, C] byte matrix: the transpose
+// written into columns off..off+R-1 of a [C, ldd] matrix (ldd = R, off = 0 for
+// a plain transpose).  Fast path: R, C, ldd and off multiples of 16 and
+// 16-byte aligned bases; tiles of 128 x 128 bytes, so that
 // every wave-wide load and store instruction covers whole 128-byte lines.  Thread (d, m) of the read-out phase owns input columns 4d..4d+3 and
 // input rows 16m..16m+15: it reads 16 dwords from LDS, transposes four 4x4
 // byte blocks in registers and writes 16 bytes to each of 4 output rows; the
@@ -274,7 +278,7 @@ __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t 
 constexpr int TPB = TQ_TPB;
 
 __global__ __launch_bounds__(256) void k_transpose_u8(const uint8_t* __restrict__ src, int64_t R, int64_t C,
-                                                      uint8_t* __restrict__ dst)
+                                                      uint8_t* __restrict__ dst, int64_t ldd)
 {
     __shared__ uint32_t tile[TR * TR_PITCH];
     const int t = threadIdx.x;
@@ -319,14 +323,14 @@ __global__ __launch_bounds__(256) void k_transpose_u8(const uint8_t* __restrict_
         for (int c = 0; c < 4; ++c) {
             const int64_t oc = C0 + 4 * d + c;        // output row = input column
             const int64_t orr = R0 + 16 * m;          // output column = input row
-            if (oc < C && orr < R) st16<true>(dst + oc * R + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
+            if (oc < C && orr < R) st16<true>(dst + oc * ldd + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
         }
         __syncthreads();                    // the tile is rewritten next iteration
     }
 }
 
 __global__ __launch_bounds__(256) void k_transpose_u8_generic(const uint8_t* __restrict__ src, int64_t R, int64_t C,
-                                                              uint8_t* __restrict__ dst)
+                                                              uint8_t* __restrict__ dst, int64_t ldd)
 {
     __shared__ uint8_t tile[64][65];
     const int64_t R0 = (int64_t)blockIdx.y * 64, C0 = (int64_t)blockIdx.x * 64;
@@ -337,7 +341,60 @@ __global__ __launch_bounds__(256) void k_transpose_u8_generic(const uint8_t* __r
     __syncthreads();
     for (int k = threadIdx.x; k < 64 * 64; k += 256) {
         const int c = k / 64, r = k % 64;
-        if (R0 + r < R && C0 + c < C) dst[(C0 + c) * R + R0 + r] = tile[r][c];
+        if (R0 + r < R && C0 + c < C) dst[(C0 + c) * ldd + R0 + r] = tile[r][c];
+    }
+}
+
+// Zero columns c0..c1-1 of each of `rows` rows of a byte matrix with row
+// stride ld (the pad of a concatenated transpose).
+__global__ __launch_bounds__(256) void k_zero_cols(uint8_t* __restrict__ dst, int64_t rows, int64_t ld, int64_t c0,
+                                                   int64_t c1)
+{
+    const int64_t w = c1 - c0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * w; i += (int64_t)gridDim.x * 256)
+        dst[(i / w) * ld + c0 + i % w] = 0;
+}
+
+// ------------------------------------------------------------ FP4 -> FP8
+// out = E4M3(val(q) * eff) per element, eff as in dequantization.  One lane
+// per 16 elements: an 8-byte code load (a wave reads 512 contiguous bytes) and
+// one 16-byte E4M3 store (1 KB per wave instruction).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_fp4_to_fp8(const uint8_t* __restrict__ packed,
+                                                    const uint8_t* __restrict__ bscale, float sg, int64_t n16,
+                                                    uint8_t* __restrict__ out)
+{
+    constexpr int U = 2;
+    const int64_t base = (int64_t)blockIdx.x * (256 * U) + threadIdx.x;
+    uint2 w[U];
+    uint32_t sb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = base + u * 256;
+        w[u] = make_uint2(0, 0);
+        sb[u] = 0;
+        if (i < n16) {
+            w[u] = ld8<true>(packed + i * 8);
+            sb[u] = bscale[KIND == NV ? i : i / 2];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = base + u * 256;
+        if (i >= n16) break;
+        const float eff = fp4_eff(KIND, sb[u], sg);
+        float d[16];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f2v lo = e2m1_val2(w[u].x, b), hi = e2m1_val2(w[u].y, b);
+            d[2 * b] = lo.x * eff;
+            d[2 * b + 1] = lo.y * eff;
+            d[8 + 2 * b] = hi.x * eff;
+            d[8 + 2 * b + 1] = hi.y * eff;
+        }
+        st16<true>(out + i * 16, make_uint4(e4m3_pack4(d[0], d[1], d[2], d[3]), e4m3_pack4(d[4], d[5], d[6], d[7]),
+                                            e4m3_pack4(d[8], d[9], d[10], d[11]),
+                                            e4m3_pack4(d[12], d[13], d[14], d[15])));
     }
 }
 
@@ -359,16 +416,20 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     default: { constexpr int FTV = BF16; __VA_ARGS__; } break;    \
     }
 
-static tq_status transpose_bytes(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, hipStream_t st)
+// dst points at column `off` of the destination already (callers pass
+// base + off); fast only when that address and ldd keep 16-byte alignment.
+static tq_status transpose_bytes(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, int64_t ldd,
+                                 hipStream_t st)
 {
     if (R == 0 || C == 0) return TQ_OK;
-    if (R % 16 == 0 && C % 16 == 0 && aligned16(src) && aligned16(dst) && cdiv(R, TR * TPB) <= 65535) {
+    if (R % 16 == 0 && C % 16 == 0 && ldd % 16 == 0 && aligned16(src) && aligned16(dst) &&
+        cdiv(R, TR * TPB) <= 65535) {
         hipLaunchKernelGGL(k_transpose_u8, dim3((unsigned)cdiv(C, TR), (unsigned)cdiv(R, TR * TPB)), dim3(256), 0, st,
-                           src, R, C, dst);
+                           src, R, C, dst, ldd);
     } else {
         if (cdiv(R, 64) > 65535) return TQ_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(k_transpose_u8_generic, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64)), dim3(256), 0,
-                           st, src, R, C, dst);
+                           st, src, R, C, dst, ldd);
     }
     return launch_status();
 }
@@ -493,9 +554,95 @@ tq_status tq_fp4_transpose_for_gemm(const uint8_t* packed, const uint8_t* block_
     if (!packed || !packed_t) return TQ_ERR_INVALID;
     if ((block_scale == nullptr) != (block_scale_t == nullptr)) return TQ_ERR_INVALID;
     hipStream_t st = as_stream(stream);
-    tq_status s = transpose_bytes(packed, n, k / 2, packed_t, st);
+    tq_status s = transpose_bytes(packed, n, k / 2, packed_t, n, st);
     if (s || !block_scale) return s;
-    return transpose_bytes(block_scale, n, k / group_size, block_scale_t, st);
+    return transpose_bytes(block_scale, n, k / group_size, block_scale_t, n, st);
+}
+
+tq_status tq_fp4_transpose_concat_for_gemm(int32_t nparts, const uint8_t* const* host_packed,
+                                           const uint8_t* const* host_block_scale, const int64_t* host_n,
+                                           int64_t k, int32_t group_size, int64_t align, uint8_t* packed_t,
+                                           uint8_t* block_scale_t, int64_t* host_stride, void* stream)
+{
+    if (nparts <= 0 || !host_packed || !host_n || k < 0 || (k & 1) || group_size <= 0 || k % group_size ||
+        align <= 0)
+        return TQ_ERR_INVALID;
+    int64_t total = 0;
+    for (int32_t i = 0; i < nparts; ++i) {
+        if (host_n[i] < 0 || host_n[i] > (INT64_MAX >> 2) - total) return TQ_ERR_INVALID;
+        total += host_n[i];
+    }
+    const int64_t stride = cdiv(total, align) * align;
+    if (host_stride) *host_stride = stride;
+    const bool scales = block_scale_t != nullptr;
+    if (scales && !host_block_scale) return TQ_ERR_INVALID;
+    if (stride == 0 || k == 0) return TQ_OK;
+    if (!packed_t) return TQ_ERR_INVALID;
+    for (int32_t i = 0; i < nparts; ++i) {
+        if (host_n[i] == 0) continue;
+        if (!host_packed[i] || (scales && !host_block_scale[i])) return TQ_ERR_INVALID;
+    }
+    hipStream_t st = as_stream(stream);
+    const int64_t kb = k / 2, nb = k / group_size;
+    int64_t off = 0;
+    for (int32_t i = 0; i < nparts; ++i) {
+        tq_status s = transpose_bytes(host_packed[i], host_n[i], kb, packed_t + off, stride, st);
+        if (!s && scales) s = transpose_bytes(host_block_scale[i], host_n[i], nb, block_scale_t + off, stride, st);
+        if (s) return s;
+        off += host_n[i];
+    }
+    if (stride > total) {
+        hipLaunchKernelGGL(k_zero_cols, dim3(grid_for(kb * (stride - total), 256)), dim3(256), 0, st, packed_t, kb,
+                           stride, total, stride);
+        if (scales)
+            hipLaunchKernelGGL(k_zero_cols, dim3(grid_for(nb * (stride - total), 256)), dim3(256), 0, st,
+                               block_scale_t, nb, stride, total, stride);
+        return launch_status();
+    }
+    return TQ_OK;
+}
+
+tq_status tq_fp4_concat_rows(const uint8_t* packed1, const uint8_t* block_scale1, float host_global_scale1,
+                             const uint8_t* packed2, const uint8_t* block_scale2, float host_global_scale2,
+                             int64_t n1, int64_t n2, int64_t k, uint8_t* packed_out, uint8_t* block_scale_out,
+                             void* stream)
+{
+    if (n1 < 0 || n2 < 0 || k < 0 || k % 16) return TQ_ERR_INVALID;
+    uint32_t g1, g2;
+    memcpy(&g1, &host_global_scale1, 4);
+    memcpy(&g2, &host_global_scale2, 4);
+    if (g1 != g2) return TQ_ERR_INVALID;
+    const int64_t kb = k / 2, nb = k / 16;
+    if ((n1 + n2) * k == 0) return TQ_OK;
+    if (!packed_out || !block_scale_out) return TQ_ERR_INVALID;
+    if (n1 > 0 && (!packed1 || !block_scale1)) return TQ_ERR_INVALID;
+    if (n2 > 0 && (!packed2 || !block_scale2)) return TQ_ERR_INVALID;
+    hipStream_t st = as_stream(stream);
+    const struct { const uint8_t* src; uint8_t* dst; int64_t bytes; } cp[4] = {
+        {packed1, packed_out, n1 * kb}, {packed2, packed_out + n1 * kb, n2 * kb},
+        {block_scale1, block_scale_out, n1 * nb}, {block_scale2, block_scale_out + n1 * nb, n2 * nb}};
+    for (const auto& c : cp)
+        if (c.bytes > 0 && hipMemcpyAsync(c.dst, c.src, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return TQ_ERR_HIP;
+    return TQ_OK;
+}
+
+tq_status tq_fp4_predequant_to_fp8(const uint8_t* packed, const uint8_t* block_scale, float host_global_scale,
+                                   int64_t rows, int64_t k, int kind, uint8_t* fp8_out, void* stream)
+{
+    tq_status s = check_fp4(rows, k, kind);
+    if (s || rows * k == 0) return s;
+    if (!packed || !block_scale || !fp8_out) return TQ_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(packed) & 7) || !aligned16(fp8_out)) return TQ_ERR_ALIGN;
+    const int64_t n16 = rows * k / 16;
+    const dim3 grid((unsigned)cdiv(n16, 512)), block(256);
+    if (cdiv(n16, 512) > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    hipStream_t st = as_stream(stream);
+    if (kind == TQ_NVFP4)
+        hipLaunchKernelGGL(k_fp4_to_fp8<NV>, grid, block, 0, st, packed, block_scale, host_global_scale, n16, fp8_out);
+    else
+        hipLaunchKernelGGL(k_fp4_to_fp8<MX>, grid, block, 0, st, packed, block_scale, 1.0f, n16, fp8_out);
+    return launch_status();
 }
 
 }  // extern "C"

@@ -118,3 +118,119 @@ def test_full_c5_sampled(tq, orc):
         PT, BT = from_dev(pt), from_dev(bt)
         assert_same(PT[:, rows], op.T, kind + " packed^T")
         assert_same(BT[:, rows], ob.T, kind + " scales^T")
+
+
+def _quant_parts(tq, ns, k, kind, seed0):
+    parts = []
+    for i, n in enumerate(ns):
+        x = workloads.normal((n, k), 0.02, seed0 + i, "bf16")
+        sg = torch.tensor([2e-5], dtype=torch.float32, device="cuda") if kind == "nvfp4" else None
+        p, b, _ = tq.tq_quant_fp4_block(to_dev(x, "bf16"), kind, global_scale=sg)
+        parts.append((p, b))
+    return parts
+
+
+@pytest.mark.parametrize("ns,k,kind,align", [
+    ([2048, 512, 512], 4096, "nvfp4", 1),       # fused QKV-like: tiled path, no pad
+    ([256, 128], 1024, "mxfp4", 512),           # tiled path, 128 pad columns
+    ([1001], 256, "nvfp4", 16),                 # odd N: generic path, 7 pad columns
+    ([40, 24, 33], 96, "nvfp4", 64),            # ragged parts
+    ([0, 48, 0, 16], 64, "mxfp4", 1),           # empty parts
+])
+def test_transpose_concat_for_gemm(tq, orc, ns, k, kind, align):
+    note("transpose_concat", ns, k, kind, align)
+    gs = 16 if kind == "nvfp4" else 32
+    parts = _quant_parts(tq, ns, k, kind, 700 + k)
+    pt, bt, stride = tq.tq_fp4_transpose_concat_for_gemm(parts, k, gs, align)
+    host = [(from_dev(p), from_dev(b)) for p, b in parts]
+    op, ob, ostride = orc.fp4_transpose_concat(host, k, gs, align)
+    assert stride == ostride
+    assert_same(from_dev(pt), op, "packed^T concat")
+    assert_same(from_dev(bt), ob, "scales^T concat")
+    # codes only
+    pt2, bt2, _ = tq.tq_fp4_transpose_concat_for_gemm([(p, None) for p, _ in parts], k, gs, align)
+    assert bt2 is None
+    assert_same(from_dev(pt2), op, "packed^T concat, codes only")
+
+
+def test_transpose_concat_rejects_empty_list(tq):
+    with pytest.raises(tq.TQError):
+        tq.tq_fp4_transpose_concat_for_gemm([], 64, 16)
+
+
+def test_transpose_concat_full_size_sampled(tq, orc):
+    """[14336, 4096] gate and up projections fused into one [2048, 28672]
+    NVFP4 GEMM operand (tiled path); sampled columns against the oracle."""
+    note("transpose_concat full size")
+    w = workloads.make_input("c5_fp4_weight")
+    p, b, g = tq.tq_quant_fp4_block(to_dev(w, "bf16"), "nvfp4")
+    up = (torch.flip(p, [0]).contiguous(), torch.flip(b, [0]).contiguous())   # a second weight, same shape
+    pt, bt, stride = tq.tq_fp4_transpose_concat_for_gemm([(p, b), up], 4096, 16, 128)
+    assert stride == 28672
+    P, B = from_dev(p), from_dev(b)
+    cols = np.unique(np.concatenate([[0, 14335, 14336, 28671], np.random.default_rng(9).choice(28672, 64, False)]))
+    PT, BT = from_dev(pt), from_dev(bt)
+    src = lambda A, c: A[c] if c < 14336 else A[14336 - 1 - (c - 14336)]   # noqa: E731
+    for c in cols:
+        assert_same(PT[:, c], src(P, c), "packed^T column %d" % c)
+        assert_same(BT[:, c], src(B, c), "scales^T column %d" % c)
+
+
+def test_concat_rows(tq, orc):
+    note("concat_rows")
+    k = 4096
+    parts = _quant_parts(tq, [96, 40], k, "nvfp4", 800)
+    (p1, b1), (p2, b2) = parts
+    g = np.float32(2e-5)
+    po, bo = tq.tq_fp4_concat_rows(p1, b1, g, p2, b2, g, k)
+    op, ob = orc.fp4_concat_rows(from_dev(p1), from_dev(b1), g, from_dev(p2), from_dev(b2), g, k)
+    assert_same(from_dev(po), op, "rows packed")
+    assert_same(from_dev(bo), ob, "rows scales")
+    with pytest.raises(tq.TQError):
+        tq.tq_fp4_concat_rows(p1, b1, g, p2, b2, np.nextafter(g, np.float32(1)), k)
+    with pytest.raises(tq.TQError):
+        tq.tq_fp4_concat_rows(p1, b1, 0.0, p2, b2, -0.0, k)
+
+
+@pytest.mark.parametrize("shape,kind,scale_x", [((64, 4096), "nvfp4", 1.0), ((64, 4096), "mxfp4", 1.0),
+                                                ((37, 160), "nvfp4", 50.0), ((3, 96), "mxfp4", 1e4),
+                                                ((1, 16), "nvfp4", 1.0)])
+def test_predequant_to_fp8(tq, orc, shape, kind, scale_x):
+    note("predequant_to_fp8", shape, kind, scale_x)
+    x = workloads.normal(shape, 0.02 * scale_x, shape[0] * 7 + shape[1], "f32")
+    x[0, :16] = 0.0
+    p, b, g = tq.tq_quant_fp4_block(to_dev(x, "f32"), kind)
+    gh = float(from_dev(g)[0]) if kind == "nvfp4" else 1.0
+    out = tq.tq_fp4_predequant_to_fp8(p, b, gh, kind)
+    assert_same(from_dev(out), orc.fp4_predequant_to_fp8(from_dev(p), from_dev(b), np.float32(gh), kind), "e4m3")
+
+
+def test_predequant_degenerate_scales(tq, orc):
+    """Every E4M3 block-scale byte with each of a few per-tensor scales
+    (products that saturate, fall in the E4M3 subnormals or underflow),
+    every E2M1 code pair."""
+    note("predequant degenerate")
+    codes = np.arange(256, dtype=np.uint8)
+    packed = np.tile(codes[None, :], (256, 1))          # row r: every code pair; k = 512
+    bscale = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 512 // 16, axis=1)
+    bscale[(bscale & 0x7F) == 0x7F] = 0x38                                  # no NaN scales
+    for sg in (1.0, 2.0 ** -20, 3.0e3, 7.1e-3):
+        out = tq.tq_fp4_predequant_to_fp8(to_dev(packed), to_dev(bscale), sg, "nvfp4")
+        assert_same(from_dev(out), orc.fp4_predequant_to_fp8(packed, bscale, np.float32(sg), "nvfp4"),
+                    "e4m3 sg=%g" % sg)
+    mx = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 512 // 32, axis=1)
+    mx[mx == 255] = 127                                                       # 0xFF is the E8M0 NaN
+    out = tq.tq_fp4_predequant_to_fp8(to_dev(packed), to_dev(mx), 1.0, "mxfp4")
+    assert_same(from_dev(out), orc.fp4_predequant_to_fp8(packed, mx, np.float32(1.0), "mxfp4"), "e4m3 mx")
+
+
+def test_predequant_full_size_sampled(tq, orc):
+    note("predequant full size")
+    w = workloads.make_input("c5_fp4_weight")
+    rows = np.unique(np.concatenate([[0, 14335], np.random.default_rng(5).choice(14336, 32, replace=False)]))
+    for kind in ("nvfp4", "mxfp4"):
+        p, b, g = tq.tq_quant_fp4_block(to_dev(w, "bf16"), kind)
+        gh = float(from_dev(g)[0]) if kind == "nvfp4" else 1.0
+        out = from_dev(tq.tq_fp4_predequant_to_fp8(p, b, gh, kind))
+        P, B = from_dev(p), from_dev(b)
+        assert_same(out[rows], orc.fp4_predequant_to_fp8(P[rows], B[rows], np.float32(gh), kind), kind + " e4m3")
