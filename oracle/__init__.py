@@ -412,3 +412,63 @@ def fp4_predequant_to_fp8(packed, bscale, global_scale, kind):
     if rc:
         raise ValueError("oracle rejected fp4_predequant_to_fp8 arguments")
     return out
+
+
+# ----------------------------------------------------------------- fake quantization / dynamic range
+def fake_quant_per_tensor(x, xt, code="s8", qmin=None, qmax=None, symmetric=True, scale=None, zp=None):
+    """Per-tensor round trip y = (q - zp) * scale in x's type.  Returns
+    (y, scale float32[1], zp int8/uint8[1] or None); pass ``scale`` (and
+    ``zp``) for static parameters."""
+    x = _check_float(x, xt)
+    if qmin is None:
+        qmin, qmax = default_q_range(code, symmetric)
+    static = scale is not None
+    s = np.ascontiguousarray(scale, np.float32).reshape(1).copy() if static else np.zeros(1, np.float32)
+    z = None
+    if not symmetric:
+        z = np.ascontiguousarray(zp).view(np.uint8).reshape(1).copy() if static else np.zeros(1, np.uint8)
+    y = np.zeros(x.shape, _storage(xt))
+    rc = lib().orc_fake_quant_per_tensor(_p(x), FTYPES[xt], ctypes.c_int64(x.size), CODES[code], qmin, qmax,
+                                         int(bool(symmetric)), int(static), _p(s), _p(z), _p(y))
+    if rc:
+        raise ValueError("oracle rejected fake_quant_per_tensor arguments")
+    if z is not None and code in ("s8", "s4"):
+        z = z.view(np.int8)
+    return y, s, z
+
+
+def fake_quant_per_tensor_backward(x, xt, dy, scale, zp=None, code="s8", qmin=None, qmax=None, symmetric=True):
+    x = _check_float(x, xt)
+    dy = _check_float(dy, xt)
+    if qmin is None:
+        qmin, qmax = default_q_range(code, symmetric)
+    dx = np.zeros(x.shape, _storage(xt))
+    zpa = None if zp is None else np.ascontiguousarray(zp).view(np.uint8)
+    rc = lib().orc_fake_quant_per_tensor_backward(_p(x), FTYPES[xt], ctypes.c_int64(x.size), CODES[code], qmin,
+                                                  qmax, _p(np.ascontiguousarray(scale, np.float32)), _p(zpa),
+                                                  _p(dy), _p(dx))
+    if rc:
+        raise ValueError("oracle rejected fake_quant_per_tensor_backward arguments")
+    return dx
+
+
+RANGE_MODES = {"symmetric": 0, "asymmetric": 1}
+RANGE_SCOPES = {"tensor": 0, "token": 1, "channel": 2}
+
+
+def dynamic_range_quantize(x, xt, mode, scope, code, axis=0):
+    """Returns (q, scale, zp or None) with the code's default range for the
+    mode and the scale tensor of the scope."""
+    x = _check_float(x, xt)
+    gran = {"tensor": "tensor", "token": "token", "channel": "channel"}[scope]
+    sshape = scale_shape(x.shape, gran, axis)
+    q = np.zeros(packed_shape(x.shape, code), np.uint8)
+    s = np.zeros(sshape, np.float32)
+    z = None if mode == "symmetric" else np.zeros(sshape, np.uint8)
+    rc = lib().orc_dynamic_range_quantize(_p(x), FTYPES[xt], x.ndim, _shape_arr(x.shape), RANGE_MODES[mode],
+                                          RANGE_SCOPES[scope], int(axis), CODES[code], _p(q), _p(s), _p(z))
+    if rc:
+        raise ValueError("oracle rejected dynamic_range_quantize arguments")
+    if z is not None and code in ("s8", "s4"):
+        z = z.view(np.int8)
+    return q, s, z

@@ -727,3 +727,73 @@ int orc_fp4_predequant_to_fp8(const uint8_t* packed, const uint8_t* bscale, floa
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------ fake quantization */
+/* fake_quantize (per-tensor floating-point round trip): every element is
+ * quantized with the tensor's scale / zero-point and dequantized at once,
+ *   y = narrow_xt((float)(q - zp) * scale),  q = clamp(rne(x / scale) + zp),
+ * with scale / zp derived from the data exactly as for per-tensor quantize,
+ * or given (static_scale).  y has x's type. */
+int orc_fake_quant_per_tensor(const void* x, int xt, int64_t numel, int code, int qmin, int qmax, int symmetric,
+                              int static_scale, float* scale, void* zp, void* y)
+{
+    if (numel < 0 || qmin >= qmax || (symmetric && qmin != -qmax) || (!symmetric && !zp)) return ORC_BAD;
+    float s;
+    int z;
+    if (static_scale) {
+        s = *scale;
+        z = symmetric ? 0 : get_zp(zp, code, 0);
+    } else {
+        float amax = 0.0f, mn = 0.0f, mx = 0.0f;
+        for (int64_t e = 0; e < numel; ++e) {
+            float v = widen(x, xt, e);
+            if (fabsf(v) > amax) amax = fabsf(v);
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        group_params(amax, mn, mx, symmetric, qmin, qmax, &s, &z);
+        *scale = s;
+        if (!symmetric) put_zp(zp, 0, z);
+    }
+    for (int64_t e = 0; e < numel; ++e) {
+        int q = encode_int(widen(x, xt, e), s, z, qmin, qmax);
+        store_float(y, xt, e, (float)(q - z) * s);
+    }
+    return ORC_OK;
+}
+
+/* fake_quantize backward, straight-through (reading): the round trip passes
+ * the gradient unchanged where the code is strictly inside the range and
+ * blocks it at the clamp bounds, q recomputed from the saved x, scale, zp:
+ *   dx = narrow_xt(dy * (qmin < q < qmax ? 1 : 0))   (a zero keeps dy's sign). */
+int orc_fake_quant_per_tensor_backward(const void* x, int xt, int64_t numel, int code, int qmin, int qmax,
+                                       const float* scale, const void* zp, const void* dy, void* dx)
+{
+    if (numel < 0 || qmin >= qmax) return ORC_BAD;
+    int z = get_zp(zp, code, 0);
+    for (int64_t e = 0; e < numel; ++e) {
+        int q = encode_int(widen(x, xt, e), *scale, z, qmin, qmax);
+        float mask = (qmin < q && q < qmax) ? 1.0f : 0.0f;
+        store_float(dx, xt, e, widen(dy, xt, e) * mask);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------ dynamic range quantize */
+/* dynamic_range_quantize (compose op; reading of DynamicRangeMode /
+ * DynamicRangeScope): the range is taken from the data at the chosen scope
+ * and the matching quantize runs with the code's default range for the
+ * mode:  mode 0 = symmetric ([-qmax, qmax]), 1 = asymmetric (full range,
+ * zero-point);  scope 0 = per tensor, 1 = per token (rows = product of the
+ * leading dims), 2 = per channel along `axis`. */
+int orc_dynamic_range_quantize(const void* x, int xt, int ndim, const int64_t* shape, int mode, int scope, int axis,
+                               int code, void* q, float* scale, void* zp)
+{
+    int qmin, qmax;
+    if (mode != 0 && mode != 1) return ORC_BAD;
+    if (orc_default_q_range(code, mode == 0, &qmin, &qmax)) return ORC_BAD;
+    int gran = scope == 0 ? ORC_TENSOR : scope == 1 ? ORC_TOKEN : scope == 2 ? ORC_CHANNEL : -1;
+    if (gran < 0) return ORC_BAD;
+    return orc_quant_int(x, xt, ndim, shape, gran, scope == 2 ? axis : 0, 0, code, qmin, qmax, mode == 0, 0, q,
+                         scale, mode == 0 ? NULL : zp);
+}
