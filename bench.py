@@ -242,6 +242,26 @@ def breakdown(torch, tq, iters=20, only=None):
              lambda b: check(L.tq_quant_per_tensor_backward(P(b["x"]), 0, n1, 0, -127, 127, P(b["s"]), None,
                                                             P(b["dy"]), P(b["dx"]), stream), "c1 ste"), n1 * 20, n1 * 8)
 
+    # per-tensor fake quantization (round trip) and its backward on the c2
+    # activations bf16 [8192, 4096]: dynamic scale (reduce + round trip),
+    # static scale (one pass), straight-through backward
+    x2 = workloads.make_input("c2_per_token_s8")
+    dy2 = workloads.make_dy("c2_per_token_s8")
+    n2 = x2.size
+    mkf2 = lambda i: dict(x=dev_bits(x2, "bf16", torch), dy=dev_bits(dy2, "bf16", torch), y=E(n2, bf16),
+                          s=torch.full((1,), 0.03, dtype=f32, device="cuda"), ws=E(8192, u8), dx=E(n2, bf16))
+    cfg2 = "c2 bf16 [8192,4096] per-tensor s8"
+    bench_op("fake_quant_per_tensor_s8_dynamic", cfg2, n2 * 4 + 4, mkf2,
+             lambda b: check(L.tq_fake_quant_per_tensor(P(b["x"]), 2, n2, 0, -127, 127, 0, P(b["y"]), P(b["s"]), None,
+                                                        P(b["ws"]), 8192, stream), "fake dyn"), n2 * 8, n2 * 2)
+    bench_op("fake_quant_per_tensor_s8_static", cfg2, n2 * 4 + 4, mkf2,
+             lambda b: check(L.tq_fake_quant_per_tensor(P(b["x"]), 2, n2, 0, -127, 127, 1, P(b["y"]), P(b["s"]), None,
+                                                        None, 0, stream), "fake static"), n2 * 8, n2 * 2)
+    bench_op("fake_quant_per_tensor_s8_backward", cfg2, n2 * 6 + 4, mkf2,
+             lambda b: check(L.tq_fake_quant_per_tensor_backward(P(b["x"]), 2, n2, 0, -127, 127, P(b["s"]), None,
+                                                                 P(b["dy"]), P(b["dx"]), stream), "fake bwd"),
+             n2 * 8, n2 * 4)
+
     # per-group u4 g128 asymmetric, f16 [11008, 4096]
     w3 = workloads.make_input("c3_per_group_u4_g128")
     N3, K3 = w3.shape

@@ -10,14 +10,18 @@
  *   - FP4 E2M1 packed two per byte with NVFP4 (E4M3 block scale per 16 plus
  *     an fp32 per-tensor scale) or MXFP4 (E8M0 block scale per 32) scales,
  *   - the FP4 transposes to GEMM layout, the concatenations of FP4 weights
- *     and their expansion to FP8 E4M3.
+ *     and their expansion to FP8 E4M3,
+ *   - per-tensor fake quantization (round trip) and its backward, and
+ *     dynamic-range quantization by mode and scope.
  *
  * Sources (page titles and sections):
  *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
  *        coverage; per-token and per-group GPTQ-style g=128 families; the STE
  *        rule dx = (dy / scale) * 1[qmin < q < qmax] with the mask recomputed
  *        from the saved input), the module list (the *_backward plans of the
- *        dequantize ops: dq = dy * scale per group), default_q_range.
+ *        dequantize ops: dq = dy * scale per group; fake_quantize and its
+ *        backward; dynamic_range_quantize), the re-exports (DynamicRangeMode,
+ *        DynamicRangeScope), default_q_range.
  *   [G]  teenygrad granularity.rs -- enum Granularity (PerTensor,
  *        PerChannel{axis}, Group{axis, group_size}).
  *   [W]  metrale QuantizedWeight -- fields (packed E2M1 two per byte
@@ -76,6 +80,8 @@ typedef enum {
 typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_ftype;
 typedef enum { TQ_S8 = 0, TQ_U8 = 1, TQ_S4 = 2, TQ_U4 = 3 } tq_itype;
 typedef enum { TQ_NVFP4 = 0, TQ_MXFP4 = 1 } tq_fp4_kind;
+typedef enum { TQ_RANGE_SYMMETRIC = 0, TQ_RANGE_ASYMMETRIC = 1 } tq_range_mode;
+typedef enum { TQ_SCOPE_TENSOR = 0, TQ_SCOPE_TOKEN = 1, TQ_SCOPE_CHANNEL = 2 } tq_range_scope;
 
 /* Version of this ABI (bumped on any signature change). */
 int tq_abi_version(void);
@@ -201,6 +207,43 @@ tq_status tq_dequant_per_group_backward(const void* dy, int dy_dtype, int32_t nd
                                         const int64_t* host_shape, int32_t axis,
                                         int64_t group_size, const float* scale, void* dq,
                                         void* stream);
+
+/* Fake quantization ([Q] module list: fake_quantize, "per-tensor, FP round
+ * trip", and fake_quantize_backward "via STE").  Per-tensor scale and
+ * zero-point exactly as tq_quant_per_tensor (dynamic, using `workspace` of
+ * tq_workspace_bytes(0, numel) bytes, or static inputs when static_scale != 0),
+ * and every element quantized and dequantized at once:
+ *   y = (q - zp) * scale,  q = clamp(rne(x / scale) + zp, qmin, qmax)
+ * in binary32, rounded once to x_dtype; y has x's dtype and shape, no code is
+ * stored.  `code` fixes the allowed range and the zero-point byte's type. */
+tq_status tq_fake_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int code,
+                                   int32_t qmin, int32_t qmax, int static_scale, void* y,
+                                   float* scale, void* zero_point, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+/* Straight-through backward of the round trip (reading: the round trip is
+ * the identity inside the range, so dy passes unscaled):
+ *   dx = dy * (qmin < q < qmax ? 1 : 0)
+ * with q recomputed from the saved x, scale and zero_point; a masked element
+ * is a zero with dy's sign.  dy and dx have x's dtype and shape. */
+tq_status tq_fake_quant_per_tensor_backward(const void* x, int x_dtype, int64_t numel, int code,
+                                            int32_t qmin, int32_t qmax, const float* scale,
+                                            const void* zero_point, const void* dy, void* dx,
+                                            void* stream);
+
+/* Dynamic-range quantize ([Q] module list: dynamic_range_quantize, a compose
+ * op, with DynamicRangeMode and DynamicRangeScope).  Reading: the range is
+ * derived from the data at the scope and the matching quantize above runs
+ * with tq_default_q_range(code, mode == TQ_RANGE_SYMMETRIC):
+ *   TQ_SCOPE_TENSOR  -> tq_quant_per_tensor (dynamic; workspace as there),
+ *   TQ_SCOPE_TOKEN   -> tq_quant_per_token, rows = product of the leading
+ *                       extents, cols = the last,
+ *   TQ_SCOPE_CHANNEL -> tq_quant_per_channel along `axis` (ignored otherwise).
+ * TQ_RANGE_ASYMMETRIC needs zero_point; TQ_RANGE_SYMMETRIC ignores it and
+ * rejects unsigned codes.  Outputs as for the routed call. */
+tq_status tq_dynamic_range_quantize(const void* x, int x_dtype, int32_t ndim,
+                                    const int64_t* host_shape, int mode, int scope, int32_t axis,
+                                    int code, void* q, float* scale, void* zero_point,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ===================================================================== */
 /* FP8 E4M3 blocks ([S] Fp8BlockGemm, Fp8BlockDequant)                    */

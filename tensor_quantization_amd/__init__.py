@@ -76,6 +76,9 @@ _SIGS = {
                                           _P, _P, ctypes.POINTER(_I64), _P], _I),
     "tq_fp4_concat_rows": ([_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _I64, _I64, _I64, _P, _P, _P], _I),
     "tq_fp4_predequant_to_fp8": ([_P, _P, ctypes.c_float, _I64, _I64, _I, _P, _P], _I),
+    "tq_fake_quant_per_tensor": ([_P, _I, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "tq_fake_quant_per_tensor_backward": ([_P, _I, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
+    "tq_dynamic_range_quantize": ([_P, _I, _I32, _SHAPE, _I, _I, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
 }
 
 for _name, (_args, _ret) in _SIGS.items():
@@ -494,3 +497,56 @@ def tq_fp4_predequant_to_fp8(packed, block_scale, global_scale=1.0, kind="nvfp4"
     _call("tq_fp4_predequant_to_fp8", _ptr(packed.contiguous()), _ptr(block_scale.contiguous()), float(global_scale),
           rows, kb * 2, FP4_KIND[kind], _ptr(out), _stream(packed.device))
     return out
+
+
+# ------------------------------------------------------------ fake quantization / dynamic range
+def tq_fake_quant_per_tensor(x, code="s8", qmin=None, qmax=None, symmetric=True, scale=None, zero_point=None):
+    """Per-tensor round trip y = (q - zp) * scale in x's dtype.  Returns
+    (y, scale float32[1], zero_point[1] or None); passing ``scale`` (and
+    ``zero_point``) makes them static inputs."""
+    x = _dev_float(x, "x")
+    qmin, qmax = _range(code, qmin, qmax, symmetric)
+    static = scale is not None
+    s = torch.empty(1, dtype=torch.float32, device=x.device)
+    z = None if symmetric else torch.empty(1, dtype=_zp_dtype(code), device=x.device)
+    if static:
+        s = scale.to(device=x.device, dtype=torch.float32).reshape(1).contiguous()
+        if not symmetric:
+            z = zero_point.to(device=x.device, dtype=_zp_dtype(code)).reshape(1).contiguous()
+    y = torch.empty_like(x)
+    ws = torch.empty(max(1, tq_workspace_bytes(0, x.numel())), dtype=torch.uint8, device=x.device)
+    _call("tq_fake_quant_per_tensor", _ptr(x), _ft(x), x.numel(), CODE[code], qmin, qmax, int(static), _ptr(y),
+          _ptr(s), _ptr(z), _ptr(ws), ws.numel(), _stream(x.device))
+    return y, s, z
+
+
+def tq_fake_quant_per_tensor_backward(x, dy, scale, zero_point=None, code="s8", qmin=None, qmax=None):
+    x, dy, dx = _ste_prep(x, dy)
+    qmin, qmax = _range(code, qmin, qmax, zero_point is None)
+    _call("tq_fake_quant_per_tensor_backward", _ptr(x), _ft(x), x.numel(), CODE[code], qmin, qmax, _ptr(scale),
+          _ptr(zero_point), _ptr(dy), _ptr(dx), _stream(x.device))
+    return dx
+
+
+RANGE_MODE = {"symmetric": 0, "asymmetric": 1}
+RANGE_SCOPE = {"tensor": 0, "token": 1, "channel": 2}
+
+
+def tq_dynamic_range_quantize(x, mode="symmetric", scope="token", code="s8", axis=0):
+    """Quantize with the range taken from the data at ``scope`` ('tensor',
+    'token' or 'channel' along ``axis``) and the code's default range for
+    ``mode``.  Returns (q, scale, zero_point or None)."""
+    x = _dev_float(x, "x")
+    sym = mode == "symmetric"
+    if scope == "tensor":
+        sshape = (1,)
+    elif scope == "token":
+        sshape = (x.numel() // x.shape[-1] if x.shape[-1] else 0,)
+    else:
+        sshape = (x.shape[axis],)
+    q, s, z = _outputs(x, code, sshape, sym)
+    shp, nd = _shape(x.shape)
+    ws = torch.empty(max(1, tq_workspace_bytes(0, x.numel())), dtype=torch.uint8, device=x.device)
+    _call("tq_dynamic_range_quantize", _ptr(x), _ft(x), nd, shp, RANGE_MODE[mode], RANGE_SCOPE[scope], axis,
+          CODE[code], _ptr(q), _ptr(s), _ptr(z), _ptr(ws), ws.numel(), _stream(x.device))
+    return q, s, z

@@ -82,6 +82,23 @@ __device__ __forceinline__ void store_codes8(uint8_t* q, int64_t e, const float 
         st4<NT>(q + (e >> 1), pack_nibbles8(c, true));
 }
 
+// Fake quantization writes the round trip instead of the code:
+// y = (q - zp) * s, with q - zp = (c - MAGIC) - zp exact (small integers), one
+// binary32 rounding for the product, then one for the narrowing to FT.
+__device__ __forceinline__ float fake_value(float c, const GP& p)
+{
+    return ((c - MAGIC) - p.zpf) * p.s;
+}
+
+template <int FT>
+__device__ __forceinline__ void store_fake8(void* y, int64_t e, const float c[8], const GP& p)
+{
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = fake_value(c[i], p);
+    store8<FT, true>(y, e, o);
+}
+
 // ------------------------------------------------------------ team kernel
 // Groups of L = 8*T*W contiguous elements.  Lane j of a team of T lanes
 // holds vectors w*T + j (w < W) of its group, so each load instruction of a
@@ -473,13 +490,14 @@ __global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__
 // block 0 publishes scale / zero-point, and all blocks encode.  With
 // nblk == 0 and a dynamic scale the (single) block reduces the whole tensor
 // itself: one launch for small tensors.
-template <int FT, int BITS, bool SYM>
+template <int FT, int BITS, bool SYM, bool FAKE = false>
 __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ x, int64_t numel,
                                                        const float* __restrict__ ws, int nblk,
                                                        int static_scale, float qmin, float qmax, float yc,
-                                                       uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                       void* __restrict__ out, float* __restrict__ scale,
                                                        uint8_t* __restrict__ zp, bool zp_signed)
 {
+    uint8_t* const q = static_cast<uint8_t*>(out);
     __shared__ GP sp;
     if (!static_scale && nblk == 0) {
         float mn = 0.0f, mx = 0.0f;
@@ -537,12 +555,16 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
             }
             if (fast) enc8<FT, true, true>(v, p, lo, hi, c);
             else enc8<FT, false, true>(v, p, lo, hi, c);
-            store_codes8<BITS, true>(q, vi * 8, c);
+            if constexpr (FAKE) store_fake8<FT>(out, vi * 8, c, p);
+            else store_codes8<BITS, true>(q, vi * 8, c);
         }
     } else {
-        const int64_t nbytes = BITS == 8 ? numel : numel / 2;
+        const int64_t nbytes = FAKE ? numel : BITS == 8 ? numel : numel / 2;
         for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nbytes; b += stride) {
-            if (BITS == 8) {
+            if (FAKE) {
+                const float c = int_code_f(load1<FT>(x, b) / p.s, p.zpf, lo, hi);
+                store1<FT>(out, b, fake_value(c, p));
+            } else if (BITS == 8) {
                 q[b] = (uint8_t)(int)int_code_f(load1<FT>(x, b) / p.s, p.zpf, lo, hi);
             } else {
                 int c0 = (int)int_code_f(load1<FT>(x, 2 * b) / p.s, p.zpf, lo, hi);
@@ -559,11 +581,12 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
 constexpr int SMALL_V = 4;
 constexpr int64_t SMALL_MAX = 1024 * 8 * SMALL_V;
 
-template <int FT, int BITS, bool SYM>
+template <int FT, int BITS, bool SYM, bool FAKE = false>
 __global__ __launch_bounds__(1024) void k_tensor_small(const void* __restrict__ x, int64_t numel, float qmin,
-                                                       float qmax, float yc, uint8_t* __restrict__ q,
+                                                       float qmax, float yc, void* __restrict__ out,
                                                        float* __restrict__ scale, uint8_t* __restrict__ zp)
 {
+    uint8_t* const q = static_cast<uint8_t*>(out);
     __shared__ float smn[16], smx[16];
     __shared__ GP sp;
     const int t = threadIdx.x;
@@ -607,7 +630,8 @@ __global__ __launch_bounds__(1024) void k_tensor_small(const void* __restrict__ 
         float c[8];
         if (p.fast) enc8<FT, true, !SYM>(v[k], p, lo, hi, c);
         else enc8<FT, false, !SYM>(v[k], p, lo, hi, c);
-        store_codes8<BITS>(q, vi * 8, c);
+        if constexpr (FAKE) store_fake8<FT>(out, vi * 8, c, p);
+        else store_codes8<BITS>(q, vi * 8, c);
     }
 }
 
@@ -784,6 +808,45 @@ __global__ __launch_bounds__(256) void k_ste_vec(const void* __restrict__ x, con
                 }
             }
             store8<FT, true>(dx, e, out);
+        }
+    }
+}
+
+// Fake-quantize backward (per-tensor): q recomputed from x with the saved
+// scale / zero-point, dx = dy * 1[qmin < q < qmax] (dy itself, or a zero with
+// dy's sign).  VEC: numel % 8 == 0, 8 elements per thread step.
+template <int FT, bool VEC>
+__global__ __launch_bounds__(256) void k_fake_ste(const void* __restrict__ x, const void* __restrict__ dy,
+                                                  int64_t numel, float qmin, float qmax,
+                                                  const float* __restrict__ scale, const uint8_t* __restrict__ zp,
+                                                  bool zp_signed, void* __restrict__ dx)
+{
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    const float s = scale[0];
+    const float zf = zp_at(zp, 0, zp_signed);
+    const bool sfast = scale_in_fast_range(s);
+    const float yr = sfast ? rcp_rn(s) : 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if constexpr (VEC) {
+        for (int64_t vi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; vi < numel / 8; vi += stride) {
+            float xv[8], dv[8], out[8];
+            widen8<FT>(load8<FT, true>(x, vi * 8), xv);
+            widen8<FT>(load8<FT, true>(dy, vi * 8), dv);
+            bool ok = sfast;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ok = ok && __builtin_fabsf(xv[i]) <= 0x1p86f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float t = ok ? div_q<FT>(xv[i], s, yr) : xv[i] / s;
+                const float c = int_code_f(t, zf, lo, hi);
+                out[i] = dv[i] * ((c > lo && c < hi) ? 1.0f : 0.0f);
+            }
+            store8<FT, true>(dx, vi * 8, out);
+        }
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < numel; e += stride) {
+            const float c = int_code_f(load1<FT>(x, e) / s, zf, lo, hi);
+            store1<FT>(dx, e, load1<FT>(dy, e) * ((c > lo && c < hi) ? 1.0f : 0.0f));
         }
     }
 }
@@ -1177,6 +1240,104 @@ tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int cod
                            static_scale, (float)qmin, (float)qmax, range_reciprocal(qmin, qmax, sym), qb, scale,
                            zb, zs)));
     return launch_status();
+}
+
+tq_status tq_fake_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int code, int32_t qmin,
+                                   int32_t qmax, int static_scale, void* y, float* scale, void* zero_point,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (numel < 0) return TQ_ERR_INVALID;
+    tq_status s = check_quant_args(x, x_dtype, code, qmin, qmax, y, scale, zero_point, 0, numel);
+    if (s || numel == 0) return s;
+    hipStream_t st = as_stream(stream);
+    const bool sym = zero_point == nullptr;
+    const float fmin = (float)qmin, fmax = (float)qmax, yc = range_reciprocal(qmin, qmax, sym);
+    uint8_t* zb = static_cast<uint8_t*>(zero_point);
+    if (!static_scale && numel % 8 == 0 && numel <= SMALL_MAX) {
+        TQ_FT_SWITCH(x_dtype, {
+            if (sym) hipLaunchKernelGGL((k_tensor_small<FTV, 8, true, true>), dim3(1), dim3(1024), 0, st, x, numel,
+                                        fmin, fmax, yc, y, scale, zb);
+            else hipLaunchKernelGGL((k_tensor_small<FTV, 8, false, true>), dim3(1), dim3(1024), 0, st, x, numel,
+                                    fmin, fmax, yc, y, scale, zb);
+        });
+        return launch_status();
+    }
+    int nblk = 0;
+    const bool small = numel <= 65536;
+    if (!static_scale && !small) {
+        if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
+        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
+        nblk = (int)cdiv(numel, chunk);
+        float* ws = static_cast<float*>(workspace);
+        TQ_FT_SWITCH(x_dtype, {
+            if (sym) hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
+            else hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
+        });
+        if (launch_status()) return TQ_ERR_HIP;
+    }
+    const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
+    const dim3 grid((!static_scale && small) ? 1u : grid_for(work, 256 * 4));
+    const float* ws = static_cast<const float*>(workspace);
+    const bool zs = code_signed(code);
+    TQ_FT_SWITCH(x_dtype, {
+        if (sym) hipLaunchKernelGGL((k_tensor_encode<FTV, 8, true, true>), grid, dim3(256), 0, st, x, numel, ws, nblk,
+                                    static_scale, fmin, fmax, yc, y, scale, zb, zs);
+        else hipLaunchKernelGGL((k_tensor_encode<FTV, 8, false, true>), grid, dim3(256), 0, st, x, numel, ws, nblk,
+                                static_scale, fmin, fmax, yc, y, scale, zb, zs);
+    });
+    return launch_status();
+}
+
+tq_status tq_fake_quant_per_tensor_backward(const void* x, int x_dtype, int64_t numel, int code, int32_t qmin,
+                                            int32_t qmax, const float* scale, const void* zero_point,
+                                            const void* dy, void* dx, void* stream)
+{
+    if (numel < 0) return TQ_ERR_INVALID;
+    tq_status s = check_quant_args(x, x_dtype, code, qmin, qmax, dx, scale, zero_point, 0, numel);
+    if (s || numel == 0) return s;
+    if (!dy) return TQ_ERR_INVALID;
+    if (!aligned16(dy)) return TQ_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    const uint8_t* zb = static_cast<const uint8_t*>(zero_point);
+    const bool zs = code_signed(code);
+    const bool vec = numel % 8 == 0;
+    const dim3 grid(grid_for(vec ? numel / 8 : numel, 256 * 2));
+    TQ_FT_SWITCH(x_dtype, {
+        if (vec) hipLaunchKernelGGL((k_fake_ste<FTV, true>), grid, dim3(256), 0, st, x, dy, numel, (float)qmin,
+                                    (float)qmax, scale, zb, zs, dx);
+        else hipLaunchKernelGGL((k_fake_ste<FTV, false>), grid, dim3(256), 0, st, x, dy, numel, (float)qmin,
+                                (float)qmax, scale, zb, zs, dx);
+    });
+    return launch_status();
+}
+
+tq_status tq_dynamic_range_quantize(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape, int mode,
+                                    int scope, int32_t axis, int code, void* q, float* scale, void* zero_point,
+                                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (mode != TQ_RANGE_SYMMETRIC && mode != TQ_RANGE_ASYMMETRIC) return TQ_ERR_INVALID;
+    const bool sym = mode == TQ_RANGE_SYMMETRIC;
+    int32_t qmin, qmax;
+    if (tq_default_q_range(code, sym, &qmin, &qmax) != TQ_OK) return TQ_ERR_INVALID;
+    tq_status s = check_map_args(ndim, host_shape, scope == TQ_SCOPE_CHANNEL ? axis : 0);
+    if (s) return s;
+    const int64_t numel = shape_numel(ndim, host_shape);
+    if (!sym && !zero_point && numel > 0) return TQ_ERR_INVALID;
+    void* zp = sym ? nullptr : zero_point;
+    switch (scope) {
+    case TQ_SCOPE_TENSOR:
+        return tq_quant_per_tensor(x, x_dtype, numel, code, qmin, qmax, 0, q, scale, zp, workspace, workspace_bytes,
+                                   stream);
+    case TQ_SCOPE_TOKEN: {
+        const int64_t cols = host_shape[ndim - 1];
+        const int64_t rows = shape_numel(ndim - 1, host_shape);
+        return tq_quant_per_token(x, x_dtype, rows, cols, code, qmin, qmax, q, scale, zp, stream);
+    }
+    case TQ_SCOPE_CHANNEL:
+        return tq_quant_per_channel(x, x_dtype, ndim, host_shape, axis, code, qmin, qmax, q, scale, zp, stream);
+    default:
+        return TQ_ERR_INVALID;
+    }
 }
 
 // ---------------------------------------------------------------- dequant

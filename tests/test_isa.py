@@ -14,8 +14,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "tensor_quantization_amd", "csrc")
 
 
+def _build_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_tq_hipbuild", os.path.join(ROOT, "tensor_quantization_amd",
+                                                                                "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def _asm(src, tmp):
-    from tensor_quantization_amd import build as b
+    b = _build_module()
     out = os.path.join(tmp, os.path.basename(src) + ".s")
     subprocess.check_call([b.HIPCC, *b.FLAGS, "-S", "--cuda-device-only", src, "-o", out],
                           stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
