@@ -472,3 +472,51 @@ def dynamic_range_quantize(x, xt, mode, scope, code, axis=0):
     if z is not None and code in ("s8", "s4"):
         z = z.view(np.int8)
     return q, s, z
+
+
+# ----------------------------------------------------------------- MXFP8
+def enc_e8m0_mx8(v):
+    """Shared MX scale byte for E4M3 elements: floor(log2 amax) - 8 + 127."""
+    return _map_f32("orc_enc_e8m0_mx8_array", v, np.uint8)
+
+
+def quant_mxfp8(x, xt):
+    """Returns (q [rows, k] E4M3 bytes, block scales [rows, k/32] E8M0 bytes)."""
+    x = _check_float(x, xt)
+    rows, k = x.shape
+    q = np.zeros((rows, k), np.uint8)
+    s = np.zeros((rows, k // 32), np.uint8)
+    if lib().orc_quant_mxfp8(_p(x), FTYPES[xt], ctypes.c_int64(rows), ctypes.c_int64(k), _p(q), _p(s)):
+        raise ValueError("oracle rejected quant_mxfp8 arguments")
+    return q, s
+
+
+def dequant_mxfp8(q, bscale, yt="f32"):
+    q = np.ascontiguousarray(q, np.uint8)
+    rows, k = q.shape
+    y = np.zeros((rows, k), _storage(yt))
+    if lib().orc_dequant_mxfp8(_p(q), _p(np.ascontiguousarray(bscale, np.uint8)), ctypes.c_int64(rows),
+                               ctypes.c_int64(k), _p(y), FTYPES[yt]):
+        raise ValueError("oracle rejected dequant_mxfp8 arguments")
+    return y
+
+
+def quant_mxfp8_backward(x, xt, bscale, dy):
+    x = _check_float(x, xt)
+    dy = _check_float(dy, xt)
+    rows, k = x.shape
+    dx = np.zeros(x.shape, _storage(xt))
+    if lib().orc_quant_mxfp8_backward(_p(x), FTYPES[xt], _p(np.ascontiguousarray(bscale, np.uint8)),
+                                      ctypes.c_int64(rows), ctypes.c_int64(k), _p(dy), _p(dx)):
+        raise ValueError("oracle rejected quant_mxfp8_backward arguments")
+    return dx
+
+
+def dequant_mxfp8_backward(dy, dyt, bscale):
+    dy = _check_float(dy, dyt)
+    rows, k = dy.shape
+    dq = np.zeros(dy.shape, _storage(dyt))
+    if lib().orc_dequant_mxfp8_backward(_p(dy), FTYPES[dyt], _p(np.ascontiguousarray(bscale, np.uint8)),
+                                        ctypes.c_int64(rows), ctypes.c_int64(k), _p(dq)):
+        raise ValueError("oracle rejected dequant_mxfp8_backward arguments")
+    return dq

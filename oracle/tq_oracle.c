@@ -797,3 +797,73 @@ int orc_dynamic_range_quantize(const void* x, int xt, int ndim, const int64_t* s
     return orc_quant_int(x, xt, ndim, shape, gran, scope == 2 ? axis : 0, 0, code, qmin, qmax, mode == 0, 0, q,
                          scale, mode == 0 ? NULL : zp);
 }
+
+/* ------------------------------------------------------------ MXFP8 */
+/* MXFP8 (smile.llm.quant MxFp8: E4M3 elements, one E8M0 scale per 32
+ * consecutive elements along the reduction dimension).  Shared scale by the
+ * OCP MX v1.0 rule with the element format's largest exponent (8 for E4M3):
+ *   X = 2^(floor(log2 amax) - 8), byte = that exponent + 127 clamped to
+ *   [0, 254]; reading for an all-zero block: byte 127 (X = 1);
+ *   q = E4M3(x / X), saturating at +-448 (amax / X lies in [256, 512)).
+ * Row-major [rows, K], K % 32 == 0; q [rows, K] bytes, scales [rows, K/32]. */
+uint8_t orc_enc_e8m0_mx8(float amax)
+{
+    if (amax == 0.0f) return 127;
+    int e;
+    frexp((double)amax, &e);                     /* amax in [2^(e-1), 2^e) */
+    int b = (e - 1) - 8 + 127;
+    if (b < 0) b = 0;
+    if (b > 254) b = 254;
+    return (uint8_t)b;
+}
+
+static int mx8_dims(int64_t rows, int64_t k) { return (rows < 0 || k < 0 || k % 32) ? ORC_BAD : ORC_OK; }
+
+int orc_quant_mxfp8(const void* x, int xt, int64_t rows, int64_t k, uint8_t* q, uint8_t* bscale)
+{
+    if (mx8_dims(rows, k)) return ORC_BAD;
+    for (int64_t b = 0; b < rows * k / 32; ++b) {
+        float amax = 0.0f;
+        for (int j = 0; j < 32; ++j) {
+            float a = fabsf(widen(x, xt, b * 32 + j));
+            if (a > amax) amax = a;
+        }
+        uint8_t sb = orc_enc_e8m0_mx8(amax);
+        bscale[b] = sb;
+        float X = orc_dec_e8m0(sb);
+        for (int j = 0; j < 32; ++j) q[b * 32 + j] = orc_enc_e4m3(widen(x, xt, b * 32 + j) / X);
+    }
+    return ORC_OK;
+}
+
+/* y = val(q) * X, rounded once to y's type. */
+int orc_dequant_mxfp8(const uint8_t* q, const uint8_t* bscale, int64_t rows, int64_t k, void* y, int yt)
+{
+    if (mx8_dims(rows, k)) return ORC_BAD;
+    for (int64_t e = 0; e < rows * k; ++e) store_float(y, yt, e, orc_dec_e4m3(q[e]) * orc_dec_e8m0(bscale[e / 32]));
+    return ORC_OK;
+}
+
+/* STE: dx = (dy / X) * (-448 < val(q) < 448 ? 1 : 0), q recomputed from x. */
+int orc_quant_mxfp8_backward(const void* x, int xt, const uint8_t* bscale, int64_t rows, int64_t k,
+                             const void* dy, void* dx)
+{
+    if (mx8_dims(rows, k)) return ORC_BAD;
+    for (int64_t e = 0; e < rows * k; ++e) {
+        float X = orc_dec_e8m0(bscale[e / 32]);
+        float qv = orc_dec_e4m3(orc_enc_e4m3(widen(x, xt, e) / X));
+        float mask = (-448.0f < qv && qv < 448.0f) ? 1.0f : 0.0f;
+        store_float(dx, xt, e, (widen(dy, xt, e) / X) * mask);
+    }
+    return ORC_OK;
+}
+
+/* dq = dy * X. */
+int orc_dequant_mxfp8_backward(const void* dy, int dyt, const uint8_t* bscale, int64_t rows, int64_t k, void* dq)
+{
+    if (mx8_dims(rows, k)) return ORC_BAD;
+    for (int64_t e = 0; e < rows * k; ++e) store_float(dq, dyt, e, widen(dy, dyt, e) * orc_dec_e8m0(bscale[e / 32]));
+    return ORC_OK;
+}
+void orc_enc_e8m0_mx8_array(const float* v, int64_t n, uint8_t* out)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_enc_e8m0_mx8(v[i]); }
