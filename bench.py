@@ -296,6 +296,20 @@ def breakdown(torch, tq, iters=20, only=None):
                                                                                 P(b["y"]), 2, stream), "fp8 deq"),
                  nb + R * C * 2, R * C + ns * 4)
 
+    # MXFP8 on the c4 activations bf16 [4096, 7168]: E4M3 + E8M0 per 32
+    xm = workloads.make_input("c4_fp8_act_1x128")
+    Rm, Cm = xm.shape
+    nm = xm.size
+    bm = nm * 2 + nm + nm // 32
+    mkm = lambda i: dict(x=dev_bits(xm, "bf16", torch), q=E((Rm, Cm), u8), b=E((Rm, Cm // 32), u8),
+                         y=E((Rm, Cm), bf16))
+    bench_op("quant_mxfp8", "c4 bf16 [4096,7168] MXFP8", bm, mkm,
+             lambda b: check(L.tq_quant_mxfp8(P(b["x"]), 2, Rm, Cm, P(b["q"]), P(b["b"]), stream), "mxfp8"),
+             bm + nm * 2, nm * 2)
+    bench_op("dequant_mxfp8", "c4 bf16 [4096,7168] MXFP8", bm, mkm,
+             lambda b: check(L.tq_dequant_mxfp8(P(b["q"]), P(b["b"]), Rm, Cm, P(b["y"]), 2, stream), "mxfp8 deq"),
+             bm + nm * 2, nm + nm // 32)
+
     # FP4: NVFP4 (dynamic and static per-tensor scale), MXFP4, transposes
     w5 = workloads.make_input("c5_fp4_weight")
     N5, K5 = w5.shape

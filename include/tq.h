@@ -6,7 +6,8 @@
  *   - integer codes (s8 / u8 / s4 / u4) at per-tensor, per-channel,
  *     per-token (per-row) and per-group granularity,
  *   - FP8 E4M3 with one fp32 scale per block (1x128 activation groups,
- *     128x128 weight tiles, or any block that tiles the matrix),
+ *     128x128 weight tiles, or any block that tiles the matrix), and MXFP8
+ *     (E4M3 with an E8M0 scale per 32 elements),
  *   - FP4 E2M1 packed two per byte with NVFP4 (E4M3 block scale per 16 plus
  *     an fp32 per-tensor scale) or MXFP4 (E8M0 block scale per 32) scales,
  *   - the FP4 transposes to GEMM layout, the concatenations of FP4 weights
@@ -269,6 +270,26 @@ tq_status tq_quant_fp8_block_backward(const void* x, int x_dtype, int64_t rows, 
 tq_status tq_dequant_fp8_block_backward(const void* dy, int dy_dtype, int64_t rows, int64_t cols,
                                         int32_t block_rows, int32_t block_cols,
                                         const float* scale, void* dq, void* stream);
+
+/* MXFP8 ([S] MxFp8: E4M3 elements with one shared E8M0 scale per 32
+ * consecutive elements along the reduction dimension).  x is [rows, k],
+ * k % 32 == 0; q is [rows, k] E4M3 bytes, block_scale [rows, k/32] bytes.
+ * Shared scale by the OCP MX v1.0 rule with E4M3's largest exponent 8:
+ *   sb = floor(log2 amax) - 8 + 127 clamped to [0, 254] (127 for an all-zero
+ *   block), X = 2^(sb - 127);  q = E4M3(x / X), round to nearest even,
+ *   saturating at +-448 (amax / X lies in [256, 512)), keeping the sign of
+ *   zero. */
+tq_status tq_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t k, uint8_t* q,
+                         uint8_t* block_scale, void* stream);
+/* y = val(q) * X, rounded once to y_dtype. */
+tq_status tq_dequant_mxfp8(const uint8_t* q, const uint8_t* block_scale, int64_t rows, int64_t k,
+                           void* y, int y_dtype, void* stream);
+/* STE: dx = (dy / X) * (-448 < val(q) < 448 ? 1 : 0), q recomputed from x. */
+tq_status tq_quant_mxfp8_backward(const void* x, int x_dtype, const uint8_t* block_scale,
+                                  int64_t rows, int64_t k, const void* dy, void* dx, void* stream);
+/* dq = dy * X. */
+tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t* block_scale,
+                                    int64_t rows, int64_t k, void* dq, void* stream);
 
 /* ===================================================================== */
 /* FP4 E2M1 blocks ([W] QuantizedWeight fields; [S] MxFp8 for the E8M0 rule) */

@@ -79,6 +79,10 @@ _SIGS = {
     "tq_fake_quant_per_tensor": ([_P, _I, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "tq_fake_quant_per_tensor_backward": ([_P, _I, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
     "tq_dynamic_range_quantize": ([_P, _I, _I32, _SHAPE, _I, _I, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "tq_quant_mxfp8": ([_P, _I, _I64, _I64, _P, _P, _P], _I),
+    "tq_dequant_mxfp8": ([_P, _P, _I64, _I64, _P, _I, _P], _I),
+    "tq_quant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
+    "tq_dequant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P], _I),
 }
 
 for _name, (_args, _ret) in _SIGS.items():
@@ -550,3 +554,40 @@ def tq_dynamic_range_quantize(x, mode="symmetric", scope="token", code="s8", axi
     _call("tq_dynamic_range_quantize", _ptr(x), _ft(x), nd, shp, RANGE_MODE[mode], RANGE_SCOPE[scope], axis,
           CODE[code], _ptr(q), _ptr(s), _ptr(z), _ptr(ws), ws.numel(), _stream(x.device))
     return q, s, z
+
+
+# ------------------------------------------------------------ MXFP8
+def tq_quant_mxfp8(x):
+    """Returns (q [rows, k] E4M3 bytes as uint8, block scales [rows, k/32]
+    E8M0 bytes)."""
+    x = _dev_float(x, "x")
+    rows, k = x.shape
+    q = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    bs = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    _call("tq_quant_mxfp8", _ptr(x), _ft(x), rows, k, _ptr(q), _ptr(bs), _stream(x.device))
+    return q, bs
+
+
+def tq_dequant_mxfp8(q, block_scale, out_dtype=torch.bfloat16):
+    rows, k = q.shape
+    y = torch.empty((rows, k), dtype=out_dtype, device=q.device)
+    _call("tq_dequant_mxfp8", _ptr(q.contiguous()), _ptr(block_scale.contiguous()), rows, k, _ptr(y),
+          FTYPE[out_dtype], _stream(q.device))
+    return y
+
+
+def tq_quant_mxfp8_backward(x, dy, block_scale):
+    x, dy, dx = _ste_prep(x, dy)
+    rows, k = x.shape
+    _call("tq_quant_mxfp8_backward", _ptr(x), _ft(x), _ptr(block_scale.contiguous()), rows, k, _ptr(dy), _ptr(dx),
+          _stream(x.device))
+    return dx
+
+
+def tq_dequant_mxfp8_backward(dy, block_scale):
+    dy = _dev_float(dy, "dy")
+    dq = torch.empty_like(dy)
+    rows, k = dy.shape
+    _call("tq_dequant_mxfp8_backward", _ptr(dy), _ft(dy), _ptr(block_scale.contiguous()), rows, k, _ptr(dq),
+          _stream(dy.device))
+    return dq

@@ -397,6 +397,16 @@ __device__ __forceinline__ float e8m0_inv(uint32_t b)
     return b == 254 ? 0x1p-127f : as_f((254u - b) << 23);
 }
 
+// Shared scale byte of an MX block with E4M3 elements (largest exponent 8):
+// floor(log2 amax) - 8 + 127, clamped below at 0 (the top clamp at 254 is
+// unreachable from a finite binary32 amax); 127 for an all-zero block.
+__device__ __forceinline__ uint32_t e8m0_mx8_byte(float amax)
+{
+    const uint32_t e = as_u(amax) >> 23;   // amax >= 0
+    if (amax == 0.0f) return 127;
+    return e >= 8 ? e - 8 : 0;
+}
+
 // Shared scale byte of an MX block with E2M1 elements:
 // floor(log2 amax) - 2 + 127, clamped to [0, 254]; 127 for an all-zero
 // block.  floor(log2) of a normal binary32 is its exponent field - 127;

@@ -17,6 +17,13 @@
 //                tile max through DPP, bpermute and LDS.
 //   k_fp8_generic  any block shape: one workgroup per block, two passes.
 //   k_fp8_ew     dequant / STE / dequant-backward, elementwise, 16-byte I/O.
+//
+// MXFP8 (smile.llm.quant MxFp8; OCP MX v1.0): E4M3 elements with one E8M0
+// scale X = 2^(floor(log2 amax) - 8) per 32 consecutive elements along K;
+// q = E4M3(x * 2^(127 - sb)), which is exactly RN(x / X).
+//   k_mxfp8_quant  a team of 4 lanes per block (8 elements each): each load
+//                  instruction of a wave reads 1 KB, each code store 512 B.
+//   k_mxfp8_ew     dequant / STE / dequant-backward, 8 elements per step.
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -249,6 +256,86 @@ __global__ __launch_bounds__(256) void k_fp8_ew_generic(const void* __restrict__
     }
 }
 
+// ------------------------------------------------------------ MXFP8
+template <int FT, int U>
+__global__ __launch_bounds__(256) void k_mxfp8_quant(const void* __restrict__ x, int64_t nblocks,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ bscale)
+{
+    constexpr int T = 4, P = 64 / T;
+    const int lane = threadIdx.x & 63;
+    const int j = lane % T;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t b0 = wave * (U * P) + lane / T;
+    Raw8<FT> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t b = b0 + (int64_t)u * P;
+        if (b < nblocks) raw[u] = load8<FT, true>(x, b * 32 + j * 8);
+        else raw[u] = Raw8<FT>{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float v[8];
+        widen8<FT>(raw[u], v);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+        a = team_max<T>(a);
+        const int64_t b = b0 + (int64_t)u * P;
+        if (b >= nblocks) continue;
+        const uint32_t sb = e8m0_mx8_byte(a);
+        const float inv = e8m0_inv(sb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= inv;
+        st8<true>(q + b * 32 + j * 8, make_uint2(e4m3_pack4(v[0], v[1], v[2], v[3]), e4m3_pack4(v[4], v[5], v[6], v[7])));
+        if (j == 0) bscale[b] = (uint8_t)sb;
+    }
+}
+
+// X = 2^(sb - 127) and its exact reciprocal: dequant multiplies by X, the
+// STE's dy / X is dy * 2^(127 - sb) (the same correctly rounded quotient).
+template <int OP, int FT>
+__global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, const void* __restrict__ b,
+                                                  const uint8_t* __restrict__ bscale, int64_t nvec,
+                                                  void* __restrict__ out)
+{
+    for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
+        const int64_t e = vi * 8;
+        const uint32_t sb = bscale[e / 32];
+        float o[8];
+        if constexpr (OP == OP_DEQ) {
+            const float X = e8m0_val(sb);
+            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = e4m3_val(w.x, i) * X;
+                o[4 + i] = e4m3_val(w.y, i) * X;
+            }
+        } else if constexpr (OP == OP_DQB) {
+            const float X = e8m0_val(sb);
+            float d[8];
+            widen8<FT>(load8<FT, true>(a, e), d);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = d[i] * X;
+        } else {
+            const float inv = e8m0_inv(sb);
+            float t[8], d[8];
+            widen8<FT>(load8<FT, true>(a, e), t);
+            widen8<FT>(load8<FT, true>(b, e), d);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] *= inv;
+            const uint32_t c0 = e4m3_pack4(t[0], t[1], t[2], t[3]);
+            const uint32_t c1 = e4m3_pack4(t[4], t[5], t[6], t[7]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t c = ((i < 4 ? c0 : c1) >> ((i & 3) * 8)) & 0x7fu;
+                o[i] = (d[i] * inv) * (c < 0x7eu ? 1.0f : 0.0f);
+            }
+        }
+        store8<FT, true>(out, e, o);
+    }
+}
+
 // ============================================================ host side
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -336,6 +423,22 @@ static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t r
     return launch_status();
 }
 
+// ---------------------------------------------------------------- MXFP8
+static tq_status check_mx8(int64_t rows, int64_t k)
+{
+    return (rows < 0 || k < 0 || k % 32) ? TQ_ERR_INVALID : TQ_OK;
+}
+
+template <int OP>
+static tq_status mx8_elementwise(const void* a, const void* b, int ft, const uint8_t* bscale, int64_t rows, int64_t k,
+                                 void* out, hipStream_t st)
+{
+    const int64_t nvec = rows * k / 8;
+    const dim3 grid(grid_for(nvec, 256)), block(256);
+    TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_mxfp8_ew<OP, FTV>), grid, block, 0, st, a, b, bscale, nvec, out));
+    return launch_status();
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -396,6 +499,56 @@ tq_status tq_dequant_fp8_block_backward(const void* dy, int dy_dtype, int64_t ro
     if (!aligned16(dy) || !aligned16(dq)) return TQ_ERR_ALIGN;
     return fp8_elementwise<OP_DQB>(dy, nullptr, dy_dtype, rows, cols, block_rows, block_cols, scale, dq,
                                    as_stream(stream));
+}
+
+tq_status tq_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t k, uint8_t* q, uint8_t* block_scale,
+                         void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_mx8(rows, k);
+    if (s || rows * k == 0) return s;
+    if (!x || !q || !block_scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
+    constexpr int U = 8;
+    const int64_t nb = rows * k / 32;
+    const int64_t grid = cdiv(cdiv(nb, U * 16), 4);
+    if (grid > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_mxfp8_quant<FTV, U>), dim3((unsigned)grid), dim3(256), 0,
+                                             as_stream(stream), x, nb, q, block_scale));
+    return launch_status();
+}
+
+tq_status tq_dequant_mxfp8(const uint8_t* q, const uint8_t* block_scale, int64_t rows, int64_t k, void* y,
+                           int y_dtype, void* stream)
+{
+    if (!valid_ftype(y_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_mx8(rows, k);
+    if (s || rows * k == 0) return s;
+    if (!q || !block_scale || !y) return TQ_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(y)) return TQ_ERR_ALIGN;
+    return mx8_elementwise<OP_DEQ>(q, nullptr, y_dtype, block_scale, rows, k, y, as_stream(stream));
+}
+
+tq_status tq_quant_mxfp8_backward(const void* x, int x_dtype, const uint8_t* block_scale, int64_t rows, int64_t k,
+                                  const void* dy, void* dx, void* stream)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_mx8(rows, k);
+    if (s || rows * k == 0) return s;
+    if (!x || !dy || !dx || !block_scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return TQ_ERR_ALIGN;
+    return mx8_elementwise<OP_STE>(x, dy, x_dtype, block_scale, rows, k, dx, as_stream(stream));
+}
+
+tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t* block_scale, int64_t rows,
+                                    int64_t k, void* dq, void* stream)
+{
+    if (!valid_ftype(dy_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_mx8(rows, k);
+    if (s || rows * k == 0) return s;
+    if (!dy || !dq || !block_scale) return TQ_ERR_INVALID;
+    if (!aligned16(dy) || !aligned16(dq)) return TQ_ERR_ALIGN;
+    return mx8_elementwise<OP_DQB>(dy, nullptr, dy_dtype, block_scale, rows, k, dq, as_stream(stream));
 }
 
 }  // extern "C"
