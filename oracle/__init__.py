@@ -186,7 +186,7 @@ def quant_fp8_block(x, xt, block_rows, block_cols):
     x = _check_float(x, xt)
     rows, cols = x.shape
     q = np.zeros((rows, cols), np.uint8)
-    s = np.zeros((rows // block_rows, cols // block_cols), np.float32)
+    s = np.zeros((-(-rows // block_rows), -(-cols // block_cols)), np.float32)
     rc = lib().orc_quant_fp8_block(_p(x), FTYPES[xt], ctypes.c_int64(rows), ctypes.c_int64(cols),
                                    ctypes.c_int64(block_rows), ctypes.c_int64(block_cols), _p(q), _p(s))
     if rc:

@@ -434,12 +434,16 @@ int orc_dequant_int_backward(const void* dy, int dyt, int ndim, const int64_t* s
 
 /* ------------------------------------------------------ FP8 E4M3 blocks */
 /* Blocks of br x bc elements of a row-major [rows, cols] tensor (1x128 for
- * activations, 128x128 for weights); scales are [rows/br, cols/bc] fp32.
+ * activations, 128x128 for weights); scales are [ceil(rows/br),
+ * ceil(cols/bc)] fp32, block (i, j) holding element (r, c) with i = r / br,
+ * j = c / bc.  Reading for shapes the blocks do not tile: the blocks on the
+ * last row / column of blocks are partial and cover only the elements that
+ * exist (their amax is over those elements).
  *   scale = amax / 448 (1 if that is 0),  q = E4M3(x / scale). */
 static int fp8_dims(int64_t rows, int64_t cols, int64_t br, int64_t bc, int64_t* nbc)
 {
-    if (rows < 0 || cols < 0 || br <= 0 || bc <= 0 || rows % br || cols % bc) return ORC_BAD;
-    *nbc = cols / bc;
+    if (rows < 0 || cols < 0 || br <= 0 || bc <= 0) return ORC_BAD;
+    *nbc = (cols + bc - 1) / bc;
     return ORC_OK;
 }
 
@@ -448,7 +452,7 @@ int orc_quant_fp8_block(const void* x, int xt, int64_t rows, int64_t cols, int64
 {
     int64_t nbc;
     if (fp8_dims(rows, cols, br, bc, &nbc)) return ORC_BAD;
-    int64_t nb = (rows / br) * nbc;
+    int64_t nb = ((rows + br - 1) / br) * nbc;
     float* amax = (float*)calloc(nb ? nb : 1, sizeof(float));
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {

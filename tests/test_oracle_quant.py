@@ -445,3 +445,30 @@ def test_zero_point_represents_zero_exactly(orc):
     lo = (0 - z.astype(np.float64)) * s
     hi = (15 - z.astype(np.float64)) * s
     assert (xv.min(axis=2) >= lo - s / 2).all() and (xv.max(axis=2) <= hi + s / 2).all()
+
+
+@pytest.mark.parametrize("shape,block,xt", [((5, 300), (1, 128), "bf16"), ((200, 130), (128, 128), "f32"),
+                                            ((7, 9), (4, 4), "f16")])
+def test_bruteforce_fp8_partial_tiles(orc, shape, block, xt):
+    """Shapes the blocks do not tile: the edge blocks cover only the
+    elements that exist; scales are [ceil(rows/br), ceil(cols/bc)]."""
+    x = workloads.normal(shape, 3.0, 78, xt)
+    q, s = orc.quant_fp8_block(x, xt, *block)
+    xv = _values(x, xt)
+    mags = bf.e4m3_magnitudes()
+    br, bc = block
+    nbr, nbc = -(-shape[0] // br), -(-shape[1] // bc)
+    assert s.shape == (nbr, nbc)
+    for i in range(nbr):
+        for j in range(nbc):
+            blk = xv[i * br:min((i + 1) * br, shape[0]), j * bc:min((j + 1) * bc, shape[1])]
+            sc = bf.div32(np.abs(blk).max(), 448)
+            sc = np.float32(1) if sc == 0 else sc
+            assert s[i, j].view(np.uint32) == sc.view(np.uint32)
+            want = bf.nearest_code(bf.div32(blk, sc), mags, 0x80)
+            assert (q[i * br:(i + 1) * br, j * bc:(j + 1) * bc] == want).all()
+    srep = np.repeat(np.repeat(s, br, 0), bc, 1)[:shape[0], :shape[1]]
+    y = orc.dequant_fp8_block(q, br, bc, s, "f32")
+    dec = np.zeros(256, np.float32)
+    dec[:127], dec[128:255] = mags, -mags
+    assert (y == bf.mul32(dec[q], srep)).all()
