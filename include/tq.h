@@ -250,8 +250,10 @@ tq_status tq_dynamic_range_quantize(const void* x, int x_dtype, int32_t ndim,
 /* FP8 E4M3 blocks ([S] Fp8BlockGemm, Fp8BlockDequant)                    */
 /* ===================================================================== */
 /* x is [rows, cols]; blocks are block_rows x block_cols (1 x 128 for
- * activations, 128 x 128 for weights); rows % block_rows == 0 and
- * cols % block_cols == 0.  scale is [rows/block_rows, cols/block_cols] fp32:
+ * activations, 128 x 128 for weights).  scale is [ceil(rows/block_rows),
+ * ceil(cols/block_cols)] fp32; when the blocks do not tile the shape, the
+ * blocks of the last block row / column are partial and cover only the
+ * elements that exist (tiling shapes take the fast kernels):
  *   scale = amax / 448 (1 if that is 0),  q = E4M3(x / scale)
  * with OCP E4M3 (bias 7, max 448), round to nearest even, saturating at
  * +-448 and keeping the sign of zero.  q is [rows, cols] bytes. */

@@ -369,7 +369,7 @@ def tq_quant_fp8_block(x, block_rows=1, block_cols=128):
     x = _dev_float(x, "x")
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
-    s = torch.empty((rows // block_rows, cols // block_cols), dtype=torch.float32, device=x.device)
+    s = torch.empty((-(-rows // block_rows), -(-cols // block_cols)), dtype=torch.float32, device=x.device)
     _call("tq_quant_fp8_block", _ptr(x), _ft(x), rows, cols, block_rows, block_cols, _ptr(q), _ptr(s),
           _stream(x.device))
     return q, s

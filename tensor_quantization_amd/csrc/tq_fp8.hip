@@ -15,7 +15,8 @@
 //   k_fp8_tile   blocks of br x bc with bc = 8*T and br = NP * 256/T: one
 //                256-thread workgroup per tile, the tile in registers, the
 //                tile max through DPP, bpermute and LDS.
-//   k_fp8_generic  any block shape: one workgroup per block, two passes.
+//   k_fp8_generic  any block shape, partial edge blocks included: one
+//                  workgroup per block, two passes.
 //   k_fp8_ew     dequant / STE / dequant-backward, elementwise, 16-byte I/O.
 //
 // MXFP8 (smile.llm.quant MxFp8; OCP MX v1.0): E4M3 elements with one E8M0
@@ -145,25 +146,29 @@ __global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, in
 }
 
 // ------------------------------------------------------------ generic blocks
+// One workgroup per block, two passes over it; blocks on the last block row /
+// column may be partial (hb x wb of the br x bc that the shape leaves).
 template <int FT>
-__global__ __launch_bounds__(256) void k_fp8_generic(const void* __restrict__ x, int64_t cols, int64_t br,
-                                                     int64_t bc, int64_t nbc, uint8_t* __restrict__ q,
+__global__ __launch_bounds__(256) void k_fp8_generic(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                     int64_t br, int64_t bc, int64_t nbc, uint8_t* __restrict__ q,
                                                      float* __restrict__ scale)
 {
     __shared__ float wmax[4];
     const int64_t blk = blockIdx.x;
     const int64_t r0 = (blk / nbc) * br, c0 = (blk % nbc) * bc;
-    const int64_t n = br * bc;
+    const int64_t hb = rows - r0 < br ? rows - r0 : br;
+    const int64_t wb = cols - c0 < bc ? cols - c0 : bc;
+    const int64_t n = hb * wb;
     float a = 0.0f;
     for (int64_t j = threadIdx.x; j < n; j += 256)
-        a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, (r0 + j / bc) * cols + c0 + j % bc)));
+        a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, (r0 + j / wb) * cols + c0 + j % wb)));
     a = team_max<64>(a);
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
     __syncthreads();
     a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
     const FP p = fp8_params<FT>(a);
     for (int64_t j = threadIdx.x; j < n; j += 256) {
-        const int64_t e = (r0 + j / bc) * cols + c0 + j % bc;
+        const int64_t e = (r0 + j / wb) * cols + c0 + j % wb;
         const float t = load1<FT>(x, e) / p.s;
         q[e] = (uint8_t)e4m3_pack4(t, 0.0f, 0.0f, 0.0f);
     }
@@ -399,10 +404,10 @@ static bool quant_fast(const void* x, int64_t rows, int64_t cols, int64_t br, in
     return false;
 }
 
+// Any positive block shape; blocks that the shape does not fill are partial.
 static tq_status check_blocks(int64_t rows, int64_t cols, int32_t br, int32_t bc)
 {
     if (rows < 0 || cols < 0 || br <= 0 || bc <= 0) return TQ_ERR_INVALID;
-    if (rows % br || cols % bc) return TQ_ERR_INVALID;
     return TQ_OK;
 }
 
@@ -412,7 +417,7 @@ static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t r
 {
     const int64_t n = rows * cols;
     if (n == 0) return TQ_OK;
-    const int64_t nbc = cols / bc;
+    const int64_t nbc = cdiv(cols, bc);
     if (cols % 8 == 0 && bc % 8 == 0) {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256)), dim3(256), 0, st,
                                             a, b, n / 8, cols, (int64_t)br, (int64_t)bc, nbc, scale, out));
@@ -455,14 +460,15 @@ tq_status tq_quant_fp8_block(const void* x, int x_dtype, int64_t rows, int64_t c
     if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
     hipStream_t st = as_stream(stream);
     bool done = false;
-    if (cols % 8 == 0) {
+    if (cols % 8 == 0 && rows % block_rows == 0 && cols % block_cols == 0) {
         TQ_FT_SWITCH(x_dtype, done = quant_fast<FTV>(x, rows, cols, block_rows, block_cols, q, scale, st));
     }
     if (!done) {
-        const int64_t nb = (rows / block_rows) * (cols / block_cols);
+        const int64_t nbc = cdiv(cols, block_cols);
+        const int64_t nb = cdiv(rows, block_rows) * nbc;
         if (nb > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp8_generic<FTV>), dim3((unsigned)nb), dim3(256), 0, st, x, cols,
-                                                 (int64_t)block_rows, (int64_t)block_cols, cols / block_cols, q, scale));
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp8_generic<FTV>), dim3((unsigned)nb), dim3(256), 0, st, x, rows,
+                                                 cols, (int64_t)block_rows, (int64_t)block_cols, nbc, q, scale));
     }
     return launch_status();
 }

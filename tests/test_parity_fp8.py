@@ -111,3 +111,14 @@ def test_full_c4_weight_sampled(tq, orc):
         assert_same(q[r0:r0 + 128], oq, "q slab %d" % tr)
         assert_same(s[tr:tr + 1], os_, "scale slab %d" % tr)
         assert_same(y[r0:r0 + 128], orc.dequant_fp8_block(oq, 128, 128, os_, "bf16"), "dequant slab %d" % tr)
+
+
+@pytest.mark.parametrize("shape,xt,block", [
+    ((5, 7000), "bf16", (1, 128)),        # ragged K: last 1x128 group has 88 elements
+    ((200, 330), "f32", (128, 128)),      # partial tiles on both edges
+    ((130, 256), "bf16", (128, 128)),     # one partial block row
+    ((7, 9), "f16", (4, 4)),              # odd everything (scalar element path)
+    ((3, 100), "bf16", (8, 64)),          # block taller than the tensor
+])
+def test_fp8_partial_tiles(tq, orc, shape, xt, block):
+    run_fp8(tq, orc, workloads.normal(shape, 2.0, shape[0] * 7 + shape[1], xt), xt, *block)
