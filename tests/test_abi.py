@@ -92,9 +92,10 @@ def test_integer_validation(tq):
 def test_fp8_fp4_validation(tq):
     L = tq._lib
     INV, ALIGN = tq.TQ_ERR_INVALID, tq.TQ_ERR_ALIGN
-    assert L.tq_quant_fp8_block(A, 2, 100, 128, 128, 128, B, C, None) == INV     # rows % 128
-    assert L.tq_quant_fp8_block(A, 2, 128, 100, 1, 128, B, C, None) == INV       # cols % 128
-    assert L.tq_quant_fp8_block(A, 2, 128, 128, 0, 128, B, C, None) == INV
+    assert L.tq_quant_fp8_block(A, 2, 128, 128, 0, 128, B, C, None) == INV       # block rows 0
+    assert L.tq_quant_fp8_block(A, 2, 128, 128, 1, -128, B, C, None) == INV      # negative block
+    assert L.tq_quant_fp8_block(A, 2, -1, 128, 1, 128, B, C, None) == INV
+    assert L.tq_quant_fp8_block(A, 7, 128, 128, 1, 128, B, C, None) == INV       # bad dtype
     assert L.tq_quant_fp8_block(MIS, 2, 128, 128, 1, 128, B, C, None) == ALIGN
     assert L.tq_dequant_fp8_block(A, 128, 128, 1, 128, None, B, 2, None) == INV
     assert L.tq_quant_fp4_block(A, 2, 4, 24, 0, B, C, A, 1, None, 0, None) == INV   # k % 16
@@ -105,6 +106,37 @@ def test_fp8_fp4_validation(tq):
     assert L.tq_dequant_fp4_block(A, B, None, 4, 32, 0, C, 2, None) == INV
     assert L.tq_fp4_transpose_for_gemm(A, B, 4, 31, 16, C, A, None) == INV
     assert L.tq_fp4_transpose_for_gemm(A, B, 4, 32, 16, C, None, None) == INV
+    assert L.tq_quant_mxfp8(A, 2, 4, 48, B, C, None) == INV                       # k % 32
+    assert L.tq_quant_mxfp8(MIS, 2, 4, 64, B, C, None) == ALIGN
+    assert L.tq_dequant_mxfp8(A, None, 4, 64, B, 2, None) == INV
+
+
+def test_follow_on_validation(tq):
+    L = tq._lib
+    INV = tq.TQ_ERR_INVALID
+    P2 = (ctypes.c_void_p * 2)(A.value, B.value)
+    N2 = (ctypes.c_int64 * 2)(16, 16)
+    stride = ctypes.c_int64(-1)
+    assert L.tq_fp4_transpose_concat_for_gemm(0, P2, P2, N2, 32, 16, 1, C, C, None, None) == INV   # empty list
+    assert L.tq_fp4_transpose_concat_for_gemm(2, P2, P2, N2, 32, 16, 0, C, C, None, None) == INV   # align 0
+    assert L.tq_fp4_transpose_concat_for_gemm(2, P2, P2, N2, 31, 16, 1, C, C, None, None) == INV   # odd k
+    assert L.tq_fp4_transpose_concat_for_gemm(2, P2, P2, N2, 0, 16, 48, C, C, ctypes.byref(stride),
+                                              None) == tq.TQ_OK                                   # k = 0: no work
+    assert stride.value == 48
+    assert L.tq_fp4_concat_rows(A, B, 1.0, A, B, 2.0, 4, 4, 32, C, C, None) == INV     # scales differ
+    assert L.tq_fp4_concat_rows(A, B, 0.0, A, B, -0.0, 4, 4, 32, C, C, None) == INV    # +0 vs -0
+    assert L.tq_fp4_concat_rows(A, B, 1.0, A, B, 1.0, 4, 4, 24, C, C, None) == INV     # k % 16
+    assert L.tq_fp4_predequant_to_fp8(A, B, 1.0, 4, 24, 0, C, None) == INV             # k % 16
+    assert L.tq_fp4_predequant_to_fp8(A, B, 1.0, 4, 32, 3, C, None) == INV             # bad kind
+    assert L.tq_fake_quant_per_tensor(A, 2, 64, 1, -127, 127, 0, B, C, None, None, 0, None) == INV  # u8 sym
+    assert L.tq_fake_quant_per_tensor(A, 2, -1, 0, -127, 127, 0, B, C, None, None, 0, None) == INV
+    assert L.tq_fake_quant_per_tensor_backward(A, 2, 64, 0, -127, 127, C, None, None, B, None) == INV  # no dy
+    shp = (ctypes.c_int64 * 2)(4, 8)
+    assert L.tq_dynamic_range_quantize(A, 2, 2, shp, 2, 1, 0, 0, B, C, None, None, 0, None) == INV  # bad mode
+    assert L.tq_dynamic_range_quantize(A, 2, 2, shp, 0, 3, 0, 0, B, C, None, None, 0, None) == INV  # bad scope
+    assert L.tq_dynamic_range_quantize(A, 2, 2, shp, 0, 1, 0, 1, B, C, None, None, 0, None) == INV  # u8 sym
+    assert L.tq_dynamic_range_quantize(A, 2, 2, shp, 1, 1, 0, 1, B, C, None, None, 0, None) == INV  # no zp
+    assert L.tq_dynamic_range_quantize(A, 2, 2, shp, 0, 2, 5, 0, B, C, None, None, 0, None) == INV  # bad axis
 
 
 def test_empty_inputs_enqueue_nothing(tq):
