@@ -520,3 +520,15 @@ def dequant_mxfp8_backward(dy, dyt, bscale):
                                         ctypes.c_int64(rows), ctypes.c_int64(k), _p(dq)):
         raise ValueError("oracle rejected dequant_mxfp8_backward arguments")
     return dq
+
+
+def quant_fp8_per_tensor(x, xt, scale=None):
+    """Returns (q E4M3 bytes of x's shape, scale float32[1]); ``scale`` makes
+    the scale a static input."""
+    x = _check_float(x, xt)
+    static = scale is not None
+    s = np.ascontiguousarray(scale, np.float32).reshape(1).copy() if static else np.zeros(1, np.float32)
+    q = np.zeros(x.shape, np.uint8)
+    if lib().orc_quant_fp8_per_tensor(_p(x), FTYPES[xt], ctypes.c_int64(x.size), int(static), _p(s), _p(q)):
+        raise ValueError("oracle rejected quant_fp8_per_tensor arguments")
+    return q, s

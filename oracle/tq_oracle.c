@@ -871,3 +871,28 @@ int orc_dequant_mxfp8_backward(const void* dy, int dyt, const uint8_t* bscale, i
 }
 void orc_enc_e8m0_mx8_array(const float* v, int64_t n, uint8_t* out)
 { for (int64_t i = 0; i < n; ++i) out[i] = orc_enc_e8m0_mx8(v[i]); }
+
+/* ------------------------------------------------ FP8 per-tensor */
+/* FP8 E4M3 with one fp32 scale for the whole tensor (smile.llm.quant
+ * Fp8KvCodec: FP8 KV store / load with per-tensor scales):
+ *   scale = amax / 448 (1 if that is 0), or the caller's (static) value;
+ *   q = E4M3(x / scale).  Load is the block dequantize with one block. */
+int orc_quant_fp8_per_tensor(const void* x, int xt, int64_t numel, int static_scale, float* scale, uint8_t* q)
+{
+    if (numel < 0) return ORC_BAD;
+    float s;
+    if (static_scale) {
+        s = *scale;
+    } else {
+        float amax = 0.0f;
+        for (int64_t e = 0; e < numel; ++e) {
+            float a = fabsf(widen(x, xt, e));
+            if (a > amax) amax = a;
+        }
+        s = amax / 448.0f;
+        if (s == 0.0f) s = 1.0f;
+        *scale = s;
+    }
+    for (int64_t e = 0; e < numel; ++e) q[e] = orc_enc_e4m3(widen(x, xt, e) / s);
+    return ORC_OK;
+}

@@ -472,3 +472,24 @@ def test_bruteforce_fp8_partial_tiles(orc, shape, block, xt):
     dec = np.zeros(256, np.float32)
     dec[:127], dec[128:255] = mags, -mags
     assert (y == bf.mul32(dec[q], srep)).all()
+
+
+@pytest.mark.parametrize("xt,static", [("bf16", None), ("f32", None), ("f16", 0.004), ("bf16", 1e-3)])
+def test_fp8_per_tensor(orc, xt, static):
+    """Per-tensor FP8: a dynamic scale equals the single-block FP8 result
+    (one 1 x numel block); every code is the brute-force nearest E4M3 value
+    of x / scale, saturating (static scales drive many codes to +-448)."""
+    x = workloads.normal((12, 40), 1.0, 91, xt)
+    q, s = orc.quant_fp8_per_tensor(x, xt, None if static is None else np.float32(static))
+    xv = _values(x, xt)
+    if static is None:
+        want_s = bf.div32(np.abs(xv).max(), 448)
+        assert s[0].view(np.uint32) == want_s.view(np.uint32)
+        qb, sb = orc.quant_fp8_block(x.reshape(1, -1), xt, 1, x.size)
+        assert (qb.reshape(q.shape) == q).all() and sb.ravel()[0] == s[0]
+    else:
+        assert s[0] == np.float32(static)
+    want = bf.nearest_code(bf.div32(xv, s[0]), bf.e4m3_magnitudes(), 0x80)
+    assert (q == want).all()
+    if static is not None:
+        assert ((q & 0x7F) == 0x7E).sum() > 10
