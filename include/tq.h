@@ -6,7 +6,8 @@
  *   - integer codes (s8 / u8 / s4 / u4) at per-tensor, per-channel,
  *     per-token (per-row) and per-group granularity,
  *   - FP8 E4M3 with one fp32 scale per block (1x128 activation groups,
- *     128x128 weight tiles, or any block that tiles the matrix), and MXFP8
+ *     128x128 weight tiles, or any block shape, partial edge blocks
+ *     included), per-tensor FP8 with a dynamic or static scale, and MXFP8
  *     (E4M3 with an E8M0 scale per 32 elements),
  *   - FP4 E2M1 packed two per byte with NVFP4 (E4M3 block scale per 16 plus
  *     an fp32 per-tensor scale) or MXFP4 (E8M0 block scale per 32) scales,
@@ -100,8 +101,10 @@ tq_status tq_default_q_range(int code, int symmetric, int32_t* host_qmin, int32_
 /* Bytes of device workspace a call needs ([Q] per-tensor scope and the NVFP4
  * per-tensor scale need a grid-wide reduction).  op: 0 = tq_quant_per_tensor
  * with a dynamic scale (0 bytes up to 65536 elements, which one workgroup
- * reduces and encodes in a single launch), 1 = tq_quant_fp4_block with a
- * dynamic global scale.  numel = elements. */
+ * reduces and encodes in a single launch; tq_fake_quant_per_tensor and the
+ * TQ_SCOPE_TENSOR dynamic-range call likewise), 1 = tq_quant_fp4_block with
+ * a dynamic global scale, 2 = tq_quant_fp8_per_tensor with a dynamic scale
+ * (0 bytes up to 65536 elements).  numel = elements. */
 size_t tq_workspace_bytes(int op, int64_t numel);
 
 /* ===================================================================== */
@@ -272,6 +275,21 @@ tq_status tq_quant_fp8_block_backward(const void* x, int x_dtype, int64_t rows, 
 tq_status tq_dequant_fp8_block_backward(const void* dy, int dy_dtype, int64_t rows, int64_t cols,
                                         int32_t block_rows, int32_t block_cols,
                                         const float* scale, void* dq, void* stream);
+
+/* FP8 E4M3 with one fp32 scale for the whole tensor ([S] Fp8KvCodec: FP8
+ * KV store / load with per-tensor scales).  x has numel elements (any
+ * shape, contiguous); q has numel E4M3 bytes.
+ *   scale = amax / 448 (1 if that is 0), or when static_scale != 0 the
+ *   caller's value in scale[0] (an input; no reduction runs);
+ *   q = E4M3(x / scale) as in the block calls.
+ * The dynamic scale needs `workspace` of tq_workspace_bytes(2, numel) bytes
+ * (may be NULL when that is 0). */
+tq_status tq_quant_fp8_per_tensor(const void* x, int x_dtype, int64_t numel, int static_scale,
+                                  uint8_t* q, float* scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+/* Load: y = val(q) * scale[0], rounded once to y_dtype. */
+tq_status tq_dequant_fp8_per_tensor(const uint8_t* q, int64_t numel, const float* scale, void* y,
+                                    int y_dtype, void* stream);
 
 /* MXFP8 ([S] MxFp8: E4M3 elements with one shared E8M0 scale per 32
  * consecutive elements along the reduction dimension).  x is [rows, k],

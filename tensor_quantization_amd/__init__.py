@@ -80,6 +80,8 @@ _SIGS = {
     "tq_fake_quant_per_tensor_backward": ([_P, _I, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
     "tq_dynamic_range_quantize": ([_P, _I, _I32, _SHAPE, _I, _I, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "tq_quant_mxfp8": ([_P, _I, _I64, _I64, _P, _P, _P], _I),
+    "tq_quant_fp8_per_tensor": ([_P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
+    "tq_dequant_fp8_per_tensor": ([_P, _I64, _P, _P, _I, _P], _I),
     "tq_dequant_mxfp8": ([_P, _P, _I64, _I64, _P, _I, _P], _I),
     "tq_quant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
     "tq_dequant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P], _I),
@@ -591,3 +593,25 @@ def tq_dequant_mxfp8_backward(dy, block_scale):
     _call("tq_dequant_mxfp8_backward", _ptr(dy), _ft(dy), _ptr(block_scale.contiguous()), rows, k, _ptr(dq),
           _stream(dy.device))
     return dq
+
+
+# ------------------------------------------------------------ FP8 per tensor
+def tq_quant_fp8_per_tensor(x, scale=None):
+    """Returns (q E4M3 bytes of x's shape as uint8, scale float32[1]);
+    passing ``scale`` makes it a static input."""
+    x = _dev_float(x, "x")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    static = scale is not None
+    s = (scale.to(device=x.device, dtype=torch.float32).reshape(1).clone() if static
+         else torch.empty(1, dtype=torch.float32, device=x.device))
+    ws = torch.empty(max(1, tq_workspace_bytes(2, x.numel())), dtype=torch.uint8, device=x.device)
+    _call("tq_quant_fp8_per_tensor", _ptr(x), _ft(x), x.numel(), int(static), _ptr(q), _ptr(s), _ptr(ws),
+          ws.numel(), _stream(x.device))
+    return q, s
+
+
+def tq_dequant_fp8_per_tensor(q, scale, out_dtype=torch.bfloat16):
+    y = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _call("tq_dequant_fp8_per_tensor", _ptr(q.contiguous()), q.numel(), _ptr(scale), _ptr(y), FTYPE[out_dtype],
+          _stream(q.device))
+    return y

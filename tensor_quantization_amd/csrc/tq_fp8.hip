@@ -261,6 +261,94 @@ __global__ __launch_bounds__(256) void k_fp8_ew_generic(const void* __restrict__
     }
 }
 
+// ------------------------------------------------------------ per tensor
+// Pass 1: max |x| of each chunk into ws.  VEC: numel % 8 == 0.
+template <int FT, bool VEC>
+__global__ __launch_bounds__(256) void k_fp8_tensor_amax(const void* __restrict__ x, int64_t numel, int64_t chunk,
+                                                         float* __restrict__ ws)
+{
+    __shared__ float sm[4];
+    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t b1 = b0 + chunk < numel ? b0 + chunk : numel;
+    float a = 0.0f;
+    if constexpr (VEC) {
+        for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8 * 4) {
+            Raw8<FT> r[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t ek = e + k * 256 * 8;
+                r[k] = ek < b1 ? load8<FT>(x, ek) : Raw8<FT>{};
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float v[8];
+                widen8<FT>(r[k], v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+            }
+        }
+    } else {
+        for (int64_t e = b0 + threadIdx.x; e < b1; e += 256) a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, e)));
+    }
+    a = team_max<64>(a);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        ws[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
+}
+
+// Pass 2: every block merges the partials (or reads the static scale; with
+// nws == 0 and a dynamic scale the single block reduces the tensor itself),
+// block 0 publishes the scale, and all blocks encode.
+template <int FT, bool VEC>
+__global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restrict__ x, int64_t numel,
+                                                           const float* __restrict__ ws, int nws, int static_scale,
+                                                           float* __restrict__ scale, uint8_t* __restrict__ q)
+{
+    __shared__ float sm[4];
+    __shared__ FP sp;
+    float a = 0.0f;
+    if (!static_scale) {
+        if (nws == 0) {
+            for (int64_t e = threadIdx.x; e < numel; e += 256) a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, e)));
+        } else {
+            for (int k = threadIdx.x; k < nws; k += 256) a = __builtin_fmaxf(a, ws[k]);
+        }
+        a = team_max<64>(a);
+        if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        FP p;
+        if (static_scale) {
+            p.s = scale[0];
+            p.fast = scale_in_fast_range(p.s);
+            p.y = p.fast ? rcp_rn(p.s) : 0.0f;
+        } else {
+            p = fp8_params<FT>(__builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3])));
+            if (blockIdx.x == 0) scale[0] = p.s;
+        }
+        sp = p;
+    }
+    __syncthreads();
+    const FP p = sp;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if constexpr (VEC) {
+        for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < numel / 8; vi += stride) {
+            float v[8];
+            widen8<FT>(load8<FT, true>(x, vi * 8), v);
+            // a static scale does not bound |x|: keep x / s from overflowing on the fast path
+            bool fast = p.fast;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fast = fast && __builtin_fabsf(v[i]) <= 0x1p86f;
+            st8<true>(q + vi * 8, fast ? fp8_enc8<FT, true>(v, p) : fp8_enc8<FT, false>(v, p));
+        }
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < numel; e += stride)
+            q[e] = (uint8_t)e4m3_pack4(load1<FT>(x, e) / p.s, 0.0f, 0.0f, 0.0f);
+    }
+}
+
 // ------------------------------------------------------------ MXFP8
 template <int FT, int U>
 __global__ __launch_bounds__(256) void k_mxfp8_quant(const void* __restrict__ x, int64_t nblocks,
@@ -412,18 +500,18 @@ static tq_status check_blocks(int64_t rows, int64_t cols, int32_t br, int32_t bc
 }
 
 template <int OP>
-static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t rows, int64_t cols, int32_t br,
-                                 int32_t bc, const float* scale, void* out, hipStream_t st)
+static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t rows, int64_t cols, int64_t br,
+                                 int64_t bc, const float* scale, void* out, hipStream_t st)
 {
     const int64_t n = rows * cols;
     if (n == 0) return TQ_OK;
     const int64_t nbc = cdiv(cols, bc);
     if (cols % 8 == 0 && bc % 8 == 0) {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256)), dim3(256), 0, st,
-                                            a, b, n / 8, cols, (int64_t)br, (int64_t)bc, nbc, scale, out));
+                                            a, b, n / 8, cols, br, bc, nbc, scale, out));
     } else {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew_generic<OP, FTV>), dim3(grid_for(n, 256)), dim3(256), 0, st,
-                                            a, b, n, cols, (int64_t)br, (int64_t)bc, nbc, scale, out));
+                                            a, b, n, cols, br, bc, nbc, scale, out));
     }
     return launch_status();
 }
@@ -555,6 +643,49 @@ tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t*
     if (!dy || !dq || !block_scale) return TQ_ERR_INVALID;
     if (!aligned16(dy) || !aligned16(dq)) return TQ_ERR_ALIGN;
     return mx8_elementwise<OP_DQB>(dy, nullptr, dy_dtype, block_scale, rows, k, dq, as_stream(stream));
+}
+
+tq_status tq_quant_fp8_per_tensor(const void* x, int x_dtype, int64_t numel, int static_scale, uint8_t* q,
+                                  float* scale, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!valid_ftype(x_dtype) || numel < 0) return TQ_ERR_INVALID;
+    if (numel == 0) return TQ_OK;
+    if (!x || !q || !scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    const bool vec = numel % 8 == 0;
+    int nws = 0;
+    const bool small = numel <= 65536;
+    if (!static_scale && !small) {
+        if (!workspace || workspace_bytes < tq_workspace_bytes(2, numel)) return TQ_ERR_INVALID;
+        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
+        nws = (int)cdiv(numel, chunk);
+        float* ws = static_cast<float*>(workspace);
+        TQ_FT_SWITCH(x_dtype, {
+            if (vec) hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, true>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws);
+            else hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, false>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws);
+        });
+        if (launch_status()) return TQ_ERR_HIP;
+    }
+    const dim3 grid((!static_scale && small) ? 1u : grid_for(vec ? numel / 8 : numel, 256 * 4));
+    const float* ws = static_cast<const float*>(workspace);
+    TQ_FT_SWITCH(x_dtype, {
+        if (vec) hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, true>), grid, dim3(256), 0, st, x, numel, ws, nws,
+                                    static_scale, scale, q);
+        else hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, false>), grid, dim3(256), 0, st, x, numel, ws, nws,
+                                static_scale, scale, q);
+    });
+    return launch_status();
+}
+
+tq_status tq_dequant_fp8_per_tensor(const uint8_t* q, int64_t numel, const float* scale, void* y, int y_dtype,
+                                    void* stream)
+{
+    if (!valid_ftype(y_dtype) || numel < 0) return TQ_ERR_INVALID;
+    if (numel == 0) return TQ_OK;
+    if (!q || !scale || !y) return TQ_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(y)) return TQ_ERR_ALIGN;
+    return fp8_elementwise<OP_DEQ>(q, nullptr, y_dtype, 1, numel, 1, numel, scale, y, as_stream(stream));
 }
 
 }  // extern "C"

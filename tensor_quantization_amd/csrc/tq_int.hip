@@ -1194,6 +1194,7 @@ size_t tq_workspace_bytes(int op, int64_t numel)
 {
     if (op == 0) return numel <= 65536 ? 0 : 2 * 1024 * sizeof(float);
     if (op == 1) return 1024 * sizeof(float);
+    if (op == 2) return numel <= 65536 ? 0 : 1024 * sizeof(float);
     return 0;
 }
 

@@ -122,3 +122,34 @@ def test_full_c4_weight_sampled(tq, orc):
 ])
 def test_fp8_partial_tiles(tq, orc, shape, xt, block):
     run_fp8(tq, orc, workloads.normal(shape, 2.0, shape[0] * 7 + shape[1], xt), xt, *block)
+
+
+@pytest.mark.parametrize("shape,xt,static", [
+    ((64, 256), "bf16", None),             # one launch (<= 65536 elements)
+    ((4096, 7168), "bf16", None),          # two passes (c4 activation size)
+    ((333, 777), "f16", None),             # scalar path, two passes
+    ((16, 1024), "f32", 0.004),            # static: many saturated codes
+    ((5, 7), "bf16", 1e-3),                # static, scalar path
+])
+def test_fp8_per_tensor(tq, orc, shape, xt, static):
+    note("fp8 per tensor", shape, xt, static)
+    x = workloads.normal(shape, 1.0, shape[0] + 3 * shape[1], xt)
+    sd = None if static is None else torch.tensor([static], dtype=torch.float32, device="cuda")
+    q, s = tq.tq_quant_fp8_per_tensor(to_dev(x, xt), sd)
+    oq, os_ = orc.quant_fp8_per_tensor(x, xt, None if static is None else np.float32(static))
+    assert_same(from_dev(s), os_, "scale")
+    assert_same(from_dev(q), oq, "codes")
+    for yt in {xt, "f32"}:
+        y = tq.tq_dequant_fp8_per_tensor(q, s, out_dtype=TORCH[yt])
+        want = orc.dequant_fp8_block(oq.reshape(1, -1), 1, oq.size, os_.reshape(1, 1), yt).reshape(shape)
+        assert_same(from_dev(y), want, "load->" + yt)
+
+
+def test_fp8_per_tensor_degenerate(tq, orc):
+    x = nasty((40, 100), "f32", 44)
+    for static in (None, np.float32(2.5e-3)):
+        sd = None if static is None else torch.tensor([static], device="cuda")
+        q, s = tq.tq_quant_fp8_per_tensor(to_dev(x, "f32"), sd)
+        oq, os_ = orc.quant_fp8_per_tensor(x, "f32", static)
+        assert_same(from_dev(q), oq, "codes")
+        assert_same(from_dev(s), os_, "scale")
