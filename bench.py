@@ -94,10 +94,16 @@ def check(rc, what):
         raise RuntimeError("%s failed with status %d" % (what, rc))
 
 
+# The step's kernels (per-token quantize, dequantize, STE, dequantize
+# backward) are built from these sources only; a counter summary taken from
+# other versions of them is stale.
+STEP_SOURCES = ("tq_int.hip", "tq_device.h", "tq_host.h")
+
+
 def source_digest():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tensor_quantization_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in STEP_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

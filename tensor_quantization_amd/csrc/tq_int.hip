@@ -182,6 +182,69 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
     }
 }
 
+// ------------------------------------------------------------ row groups
+// One workgroup of NW waves per group of L = 512 * NW * W contiguous
+// elements: thread t holds vectors w * 64 * NW + t (w < W), so every load
+// instruction of a wave reads 1 KB contiguously and each thread keeps only W
+// loads in flight; the group max / min goes through DPP within a wave and
+// LDS across the NW waves.
+template <int FT, int BITS, bool SYM, int NW, int W>
+__global__ __launch_bounds__(64 * NW) void k_quant_rows(const void* __restrict__ x, float qmin, float qmax,
+                                                        float yc, uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale, uint8_t* __restrict__ zp)
+{
+    constexpr int NT = 64 * NW;
+    constexpr int64_t L = 8 * NT * W;
+    __shared__ float smx[NW], smn[NW];
+    const int64_t g = blockIdx.x;
+    const int t = threadIdx.x;
+    Raw8<FT> raw[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) raw[w] = load8<FT, true>(x, g * L + (int64_t)(w * NT + t) * 8);
+    float v[W][8];
+    float mn = 0.0f, mx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        widen8<FT>(raw[w], v[w]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (SYM) {
+                mx = __builtin_fmaxf(mx, __builtin_fabsf(v[w][i]));
+            } else {
+                mn = __builtin_fminf(mn, v[w][i]);
+                mx = __builtin_fmaxf(mx, v[w][i]);
+            }
+        }
+    }
+    mx = team_max<64>(mx);
+    if constexpr (!SYM) mn = team_min<64>(mn);
+    if ((t & 63) == 0) {
+        smx[t >> 6] = mx;
+        smn[t >> 6] = mn;
+    }
+    __syncthreads();
+    mx = smx[0];
+    mn = smn[0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) {
+        mx = __builtin_fmaxf(mx, smx[k]);
+        mn = __builtin_fminf(mn, smn[k]);
+    }
+    const GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc) : make_gp<FT, false>(0.0f, mn, mx, qmin, qmax, yc);
+    const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        float c[8];
+        if (p.fast) enc8<FT, true, !SYM>(v[w], p, lo, hi, c);
+        else enc8<FT, false, !SYM>(v[w], p, lo, hi, c);
+        store_codes8<BITS, true>(q, g * L + (int64_t)(w * NT + t) * 8, c);
+    }
+    if (t == 0) {
+        scale[g] = p.s;
+        if constexpr (!SYM) zp[g] = (uint8_t)(int)p.zpf;
+    }
+}
+
 // ------------------------------------------------------------ long groups
 // One wave per group of L elements (L % 8 == 0); the group is read twice
 // (reduce, then encode) in 4-vector strides per lane.
@@ -665,13 +728,21 @@ __device__ __forceinline__ float zp_f(const uint8_t* zp, int64_t g)
 }
 
 #ifndef TQ_VPT
-#define TQ_VPT 2
+#define TQ_VPT 1
 #endif
 constexpr int VPT = TQ_VPT;   // vectors per thread per iteration
 #ifndef TQ_STE_VPT
 #define TQ_STE_VPT 1
 #endif
 constexpr int SVPT = TQ_STE_VPT;
+#ifndef TQ_DEQ_NT
+#define TQ_DEQ_NT 1
+#endif
+constexpr bool DEQ_NT = TQ_DEQ_NT != 0;
+#ifndef TQ_DQB_VPT
+#define TQ_DQB_VPT 1
+#endif
+constexpr int DVPT = TQ_DQB_VPT;
 
 template <int MAPK, int YT, int BITS, bool SIGNED>
 __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__ q, int64_t nvec, int64_t P1,
@@ -685,13 +756,13 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
             if (vi >= nvec) break;
             const int64_t e = vi * 8;
             uint32_t cw[2];
-            // plain loads: non-temporal loads of the narrow code stream measured slower
             if constexpr (BITS == 8) {
-                const uint2 w = *reinterpret_cast<const uint2*>(q + e);
+                const uint2 w = DEQ_NT ? ld8<true>(q + e) : *reinterpret_cast<const uint2*>(q + e);
                 cw[0] = w.x;
                 cw[1] = w.y;
             } else {
-                cw[0] = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
+                cw[0] = DEQ_NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + (e >> 1)))
+                               : *reinterpret_cast<const uint32_t*>(q + (e >> 1));
                 cw[1] = 0;
             }
             const int64_t g = vec_group<MAPK>(e, P1, P2, sh);
@@ -725,15 +796,15 @@ __global__ __launch_bounds__(256) void k_dqb_vec(const void* __restrict__ dy, in
                                                  int64_t P2, int sh, const float* __restrict__ scale,
                                                  void* __restrict__ dq)
 {
-    for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
-        Raw8<FT> raw[VPT];
+    for (int64_t base = (int64_t)blockIdx.x * 256 * DVPT; base < nvec; base += (int64_t)gridDim.x * 256 * DVPT) {
+        Raw8<FT> raw[DVPT];
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
+        for (int k = 0; k < DVPT; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi < nvec) raw[k] = load8<FT, true>(dy, vi * 8);
         }
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
+        for (int k = 0; k < DVPT; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi >= nvec) break;
             const int64_t e = vi * 8;
@@ -954,9 +1025,20 @@ static void quant_contig(const void* x, int64_t G, int64_t L, float qmin, float 
     case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
     case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
     case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
-#ifndef TQ_ROW4096_LONG
-    case 4096: launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+#ifndef TQ_ROW4096
+#define TQ_ROW4096 4
 #endif
+    case 4096:
+        if (TQ_ROW4096 == 4 && G <= 0x7fffffff) {
+            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 4, 2>), dim3((unsigned)G), dim3(256), 0, st, x, qmin, qmax,
+                               yc, q, scale, zp);
+        } else if (TQ_ROW4096 == 8 && G <= 0x7fffffff) {
+            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 8, 1>), dim3((unsigned)G), dim3(512), 0, st, x, qmin, qmax,
+                               yc, q, scale, zp);
+        } else {
+            launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, qmin, qmax, yc, q, scale, zp, st);
+        }
+        return;
     default:
         hipLaunchKernelGGL((k_quant_long<FT, BITS, SYM>), dim3((unsigned)cdiv(G, 4)), dim3(256), 0, st,
                            x, G, L, qmin, qmax, yc, q, scale, zp);
@@ -1044,10 +1126,19 @@ static int log2_exact(int64_t v)
     return k;
 }
 
+#ifndef TQ_EW_GRID
+#define TQ_EW_GRID 0
+#endif
+static unsigned ew_grid(int64_t nvec, int64_t per_block)
+{
+    const unsigned g = grid_for(nvec, per_block);
+    return (TQ_EW_GRID > 0 && g > (unsigned)TQ_EW_GRID) ? (unsigned)TQ_EW_GRID : g;
+}
+
 template <int MAPK>
 static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int64_t P2, hipStream_t st)
 {
-    const dim3 grid(grid_for(nvec, 256 * VPT)), block(256);
+    const dim3 grid(ew_grid(nvec, 256 * VPT)), block(256);
     const bool sg = code_signed(a.code);
     const int bits = code_bits(a.code);
     const int sh = MAPK == MAP_CONTIG ? log2_exact(P1) : -1;
@@ -1061,12 +1152,12 @@ static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int
         });
     } else if (op == OP_STE) {
         TQ_FT_SWITCH(a.in_type, {
-            const dim3 sgrid(grid_for(nvec, 256 * SVPT));
+            const dim3 sgrid(ew_grid(nvec, 256 * SVPT));
             if (sg) hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, true>), sgrid, block, 0, st, a.a, a.b, nvec, P1, P2, sh, a.qmin, a.qmax, a.scale, a.zp, a.out);
             else hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, false>), sgrid, block, 0, st, a.a, a.b, nvec, P1, P2, sh, a.qmin, a.qmax, a.scale, a.zp, a.out);
         });
     } else {
-        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), grid, block, 0, st, a.a, nvec, P1, P2, sh, a.scale, a.out));
+        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), dim3(ew_grid(nvec, 256 * DVPT)), block, 0, st, a.a, nvec, P1, P2, sh, a.scale, a.out));
     }
 }
 

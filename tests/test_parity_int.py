@@ -103,7 +103,10 @@ TOKEN_CASES = [
     (9, 512, "bf16", "s8", True),
     (7, 1024, "f32", "u8", False),
     (5, 2048, "bf16", "s4", True),
-    (65, 4096, "bf16", "s8", True),
+    (65, 4096, "bf16", "s8", True),      # row-group kernel: 4 waves per 4096-element row
+    (12, 4096, "f16", "u8", False),
+    (10, 4096, "f32", "u4", False),
+    (3, 4096, "bf16", "s4", True),
     (6, 7168, "bf16", "s8", True),
     (3, 4104, "f16", "u4", False),
     (11, 100, "f32", "s8", True),
