@@ -1020,7 +1020,11 @@ static void quant_contig(const void* x, int64_t G, int64_t L, float qmin, float 
 #ifndef TQ_G128_U
 #define TQ_G128_U 1
 #endif
-    case 128: launch_team<FT, BITS, SYM, 8, 2, TQ_G128_U>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+#ifndef TQ_G128_T
+#define TQ_G128_T 8
+#endif
+    case 128: launch_team<FT, BITS, SYM, TQ_G128_T, 16 / TQ_G128_T, TQ_G128_U>(x, G, qmin, qmax, yc, q, scale, zp, st);
+        return;
     case 256: launch_team<FT, BITS, SYM, 16, 2, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
     case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
     case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
