@@ -13,11 +13,15 @@
 // Codes are packed two per byte along K, even index in the low nibble.
 //
 // Kernels:
-//   k_fp4_quant      one block per lane (16 or 32 elements as 2 or 4 16-byte
-//                    loads), block max in-lane, U blocks per lane in flight.
+//   k_amax_partial + k_nv_global_scale   dynamic NVFP4 s_g: chunk maxima, then
+//                    one workgroup publishes s_g into global_scale.
+//   k_fp4_quant      a team of 2 (NVFP4) / 4 (MXFP4) lanes per block, block max
+//                    through DPP, U rounds per wave; reads s_g from global_scale.
 //   k_fp4_ew         dequant / STE / dequant-backward, 8 elements per step.
-//   k_transpose_u8   byte transpose through a 64 x 256-byte LDS tile with
-//                    4 x 4 register transposes and 16-byte stores.
+//   k_transpose_u8   byte transpose through a 128 x 128-byte LDS tile with
+//                    4 x 4 register transposes and 16-byte stores, into a
+//                    destination of any row stride (concatenation, padding).
+//   k_fp4_to_fp8     FP4 -> E4M3 with the per-tensor scale folded in.
 #include "tq_device.h"
 #include "tq_host.h"
 
@@ -33,7 +37,8 @@ __global__ __launch_bounds__(256) void k_amax_partial(const void* __restrict__ x
                                                       float* __restrict__ ws)
 {
     __shared__ float sm[4];
-    const int64_t b0 = (int64_t)blockIdx.x * chunk;
+    const int64_t blk = blockIdx.x;
+    const int64_t b0 = blk * chunk;
     const int64_t b1 = b0 + chunk < numel ? b0 + chunk : numel;
     float a = 0.0f;
     for (int64_t e = b0 + (int64_t)threadIdx.x * 8; e < b1; e += 256 * 8 * 4) {
@@ -55,8 +60,26 @@ __global__ __launch_bounds__(256) void k_amax_partial(const void* __restrict__ x
     a = team_max<64>(a);
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
     __syncthreads();
-    if (threadIdx.x == 0)
-        ws[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
+    if (threadIdx.x == 0) ws[blk] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
+}
+
+// Pass 1b: one workgroup merges the partials and publishes
+// s_g = amax / 2688 (1 if 0); the encode pass then reads s_g like a static
+// scale instead of every workgroup merging the partials again.
+__global__ __launch_bounds__(256) void k_nv_global_scale(const float* __restrict__ ws, int nws,
+                                                         float* __restrict__ global_scale)
+{
+    __shared__ float sm[4];
+    float a = 0.0f;
+    for (int k = threadIdx.x; k < nws; k += 256) a = __builtin_fmaxf(a, ws[k]);
+    a = team_max<64>(a);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
+        const float g = a / 2688.0f;
+        global_scale[0] = (g == 0.0f) ? 1.0f : g;
+    }
 }
 
 struct BP {
@@ -109,35 +132,15 @@ __device__ __forceinline__ void fp4_div8(const float v[8], const BP& p, float t[
 // elements 8j..8j+7 of its block, so each load instruction of a wave reads
 // 1 KB contiguously and each code store writes 256 bytes contiguously; the
 // block max takes one or two DPP steps.  U rounds of 64/T blocks per wave.
-template <int FT, int KIND, int U, bool NT>
+template <int FT, int KIND, int U>
 __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, int64_t nblocks,
-                                                   const float* __restrict__ ws, int nws, int static_global,
-                                                   float* __restrict__ global_scale, uint8_t* __restrict__ packed,
-                                                   uint8_t* __restrict__ bscale)
+                                                   const float* __restrict__ global_scale,
+                                                   uint8_t* __restrict__ packed, uint8_t* __restrict__ bscale)
 {
     constexpr int GS = KIND == NV ? 16 : 32;
     constexpr int T = GS / 8;
     constexpr int P = 64 / T;
-    __shared__ float s_sg;
-    float sg = 1.0f;
-    if constexpr (KIND == NV) {
-        if (threadIdx.x < 64) {
-            float g;
-            if (static_global) {
-                g = global_scale[0];
-            } else {
-                float a = 0.0f;
-                for (int k = threadIdx.x; k < nws; k += 64) a = __builtin_fmaxf(a, ws[k]);
-                a = team_max<64>(a);
-                g = a / 2688.0f;
-                g = (g == 0.0f) ? 1.0f : g;
-                if (blockIdx.x == 0 && threadIdx.x == 0) global_scale[0] = g;
-            }
-            if (threadIdx.x == 0) s_sg = g;
-        }
-        __syncthreads();
-        sg = s_sg;
-    }
+    const float sg = KIND == NV ? global_scale[0] : 1.0f;
     const float six_sg = 6.0f * sg;
     const float y6 = scale_in_fast_range(six_sg) ? rcp_rn(six_sg) : 0.0f;
     const int lane = threadIdx.x & 63;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, i
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t b = b0 + (int64_t)u * P;
-        if (b < nblocks) raw[u] = load8<FT, NT>(x, b * GS + j * 8);
+        if (b < nblocks) raw[u] = load8<FT, true>(x, b * GS + j * 8);
         else raw[u] = Raw8<FT>{};
     }
 #pragma unroll
@@ -487,21 +490,20 @@ tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k
     }
     constexpr int U = 8;
     if (kind == TQ_NVFP4) {
+        if (!static_global) {
+            hipLaunchKernelGGL(k_nv_global_scale, dim3(1), dim3(256), 0, st, ws, nws, global_scale);
+            if (launch_status()) return TQ_ERR_HIP;
+        }
         const int64_t nb = numel / 16;
         const dim3 grid((unsigned)cdiv(cdiv(nb, U * 32), 4));
-        // after the max pre-pass x may still sit in the last-level cache: read it temporally
-        if (static_global) {
-            TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U, true>), grid, dim3(256), 0, st, x, nb, ws,
-                                                     nws, static_global, global_scale, packed, block_scale));
-        } else {
-            TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U, false>), grid, dim3(256), 0, st, x, nb,
-                                                     ws, nws, static_global, global_scale, packed, block_scale));
-        }
+        // s_g is in global_scale now (the caller's, or just published)
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U>), grid, dim3(256), 0, st, x, nb, global_scale,
+                                                 packed, block_scale));
     } else {
         const int64_t nb = numel / 32;
         const dim3 grid((unsigned)cdiv(cdiv(nb, U * 16), 4));
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U, true>), grid, dim3(256), 0, st, x, nb, ws,
-                                                 nws, 1, global_scale, packed, block_scale));
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U>), grid, dim3(256), 0, st, x, nb, global_scale,
+                                                 packed, block_scale));
     }
     return launch_status();
 }

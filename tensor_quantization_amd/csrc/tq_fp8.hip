@@ -297,23 +297,34 @@ __global__ __launch_bounds__(256) void k_fp8_tensor_amax(const void* __restrict_
         ws[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
 }
 
-// Pass 2: every block merges the partials (or reads the static scale; with
-// nws == 0 and a dynamic scale the single block reduces the tensor itself),
-// block 0 publishes the scale, and all blocks encode.
+// Pass 1b: one workgroup merges the partials and publishes the scale.
+template <int FT>
+__global__ __launch_bounds__(256) void k_fp8_tensor_finalize(const float* __restrict__ ws, int nws,
+                                                             float* __restrict__ scale)
+{
+    __shared__ float sm[4];
+    float a = 0.0f;
+    for (int k = threadIdx.x; k < nws; k += 256) a = __builtin_fmaxf(a, ws[k]);
+    a = team_max<64>(a);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        scale[0] = fp8_params<FT>(__builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]))).s;
+}
+
+// Pass 2: with a static (or already published) scale every block reads it
+// and encodes; with a dynamic scale the single block of a small tensor
+// (<= 65536 elements) reduces it itself first.
 template <int FT, bool VEC>
 __global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restrict__ x, int64_t numel,
-                                                           const float* __restrict__ ws, int nws, int static_scale,
-                                                           float* __restrict__ scale, uint8_t* __restrict__ q)
+                                                           int static_scale, float* __restrict__ scale,
+                                                           uint8_t* __restrict__ q)
 {
     __shared__ float sm[4];
     __shared__ FP sp;
-    float a = 0.0f;
     if (!static_scale) {
-        if (nws == 0) {
-            for (int64_t e = threadIdx.x; e < numel; e += 256) a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, e)));
-        } else {
-            for (int k = threadIdx.x; k < nws; k += 256) a = __builtin_fmaxf(a, ws[k]);
-        }
+        float a = 0.0f;
+        for (int64_t e = threadIdx.x; e < numel; e += 256) a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, e)));
         a = team_max<64>(a);
         if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
     }
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restric
             p.y = p.fast ? rcp_rn(p.s) : 0.0f;
         } else {
             p = fp8_params<FT>(__builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3])));
-            if (blockIdx.x == 0) scale[0] = p.s;
+            scale[0] = p.s;
         }
         sp = p;
     }
@@ -654,26 +665,26 @@ tq_status tq_quant_fp8_per_tensor(const void* x, int x_dtype, int64_t numel, int
     if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
     hipStream_t st = as_stream(stream);
     const bool vec = numel % 8 == 0;
-    int nws = 0;
     const bool small = numel <= 65536;
     if (!static_scale && !small) {
         if (!workspace || workspace_bytes < tq_workspace_bytes(2, numel)) return TQ_ERR_INVALID;
         const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
-        nws = (int)cdiv(numel, chunk);
+        const int nws = (int)cdiv(numel, chunk);
         float* ws = static_cast<float*>(workspace);
         TQ_FT_SWITCH(x_dtype, {
             if (vec) hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, true>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws);
             else hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, false>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws);
+            hipLaunchKernelGGL((k_fp8_tensor_finalize<FTV>), dim3(1), dim3(256), 0, st, ws, nws, scale);
         });
         if (launch_status()) return TQ_ERR_HIP;
     }
-    const dim3 grid((!static_scale && small) ? 1u : grid_for(vec ? numel / 8 : numel, 256 * 4));
-    const float* ws = static_cast<const float*>(workspace);
+    const int eff_static = static_scale || !small;   // the scale is known before the encode
+    const dim3 grid(eff_static ? grid_for(vec ? numel / 8 : numel, 256 * 4) : 1u);
     TQ_FT_SWITCH(x_dtype, {
-        if (vec) hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, true>), grid, dim3(256), 0, st, x, numel, ws, nws,
-                                    static_scale, scale, q);
-        else hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, false>), grid, dim3(256), 0, st, x, numel, ws, nws,
-                                static_scale, scale, q);
+        if (vec) hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, true>), grid, dim3(256), 0, st, x, numel, eff_static,
+                                    scale, q);
+        else hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, false>), grid, dim3(256), 0, st, x, numel, eff_static,
+                                scale, q);
     });
     return launch_status();
 }

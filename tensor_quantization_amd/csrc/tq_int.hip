@@ -21,7 +21,8 @@
 //   k_quant_cols   groups that run down columns ([B, R, C] view: per-channel
 //                  on the last axis, per-group along a non-last axis).
 //   k_*_generic    any layout (index arithmetic per element), the fallback.
-//   k_tensor_*     per-tensor: block partial max, then encode.
+//   k_tensor_*     per-tensor: block partial max, one workgroup publishing the
+//                  scale, then encode (small tensors: one single-block launch).
 //   k_dequant_vec / k_ste_vec / k_dqb_vec   elementwise streaming.
 #include "tq_device.h"
 #include "tq_host.h"
@@ -549,20 +550,49 @@ __global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__
     }
 }
 
-// Pass 2: every block merges the partials (or reads the static scale),
-// block 0 publishes scale / zero-point, and all blocks encode.  With
-// nblk == 0 and a dynamic scale the (single) block reduces the whole tensor
-// itself: one launch for small tensors.
+// Pass 1b: one workgroup merges the partials and publishes scale (and
+// zero-point); the encode pass then reads them like a static scale instead of
+// every workgroup merging the partials again.
+template <int FT, bool SYM>
+__global__ __launch_bounds__(256) void k_tensor_finalize(const float* __restrict__ ws, int nblk, float qmin,
+                                                         float qmax, float yc, float* __restrict__ scale,
+                                                         uint8_t* __restrict__ zp)
+{
+    __shared__ float smx[4], smn[4];
+    float mx = 0.0f, nmn = 0.0f;
+    for (int k = threadIdx.x; k < nblk; k += 256) {
+        mx = __builtin_fmaxf(mx, ws[k]);
+        nmn = __builtin_fmaxf(nmn, ws[nblk + k]);
+    }
+    mx = team_max<64>(mx);
+    nmn = team_max<64>(nmn);
+    if ((threadIdx.x & 63) == 0) {
+        smx[threadIdx.x >> 6] = mx;
+        smn[threadIdx.x >> 6] = nmn;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        mx = __builtin_fmaxf(__builtin_fmaxf(smx[0], smx[1]), __builtin_fmaxf(smx[2], smx[3]));
+        nmn = __builtin_fmaxf(__builtin_fmaxf(smn[0], smn[1]), __builtin_fmaxf(smn[2], smn[3]));
+        const GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
+                         : make_gp<FT, false>(0.0f, -nmn, mx, qmin, qmax, yc);
+        scale[0] = p.s;
+        if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
+    }
+}
+
+// Pass 2: with a static (or already published) scale every block reads
+// scale / zero-point and encodes; with a dynamic scale the single block of a
+// small tensor (<= 65536 elements) reduces it itself first: one launch.
 template <int FT, int BITS, bool SYM, bool FAKE = false>
 __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ x, int64_t numel,
-                                                       const float* __restrict__ ws, int nblk,
                                                        int static_scale, float qmin, float qmax, float yc,
                                                        void* __restrict__ out, float* __restrict__ scale,
                                                        uint8_t* __restrict__ zp, bool zp_signed)
 {
     uint8_t* const q = static_cast<uint8_t*>(out);
     __shared__ GP sp;
-    if (!static_scale && nblk == 0) {
+    if (!static_scale) {
         float mn = 0.0f, mx = 0.0f;
         range_minmax<FT, SYM>(x, 0, numel, (numel & 7) == 0, mn, mx);
         block_minmax(mn, mx);
@@ -573,34 +603,13 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
             scale[0] = p.s;
             if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
         }
-    } else if (threadIdx.x < 64) {
-        if (static_scale) {
-            if (threadIdx.x == 0) {
-                GP p;
-                p.s = scale[0];
-                p.fast = scale_in_fast_range(p.s);
-                p.y = p.fast ? rcp_rn(p.s) : 0.0f;
-                p.zpf = zp_at(zp, 0, zp_signed);
-                sp = p;
-            }
-        } else {
-            float mx = 0.0f, nmn = 0.0f;
-            for (int k = threadIdx.x; k < nblk; k += 64) {
-                mx = __builtin_fmaxf(mx, ws[k]);
-                nmn = __builtin_fmaxf(nmn, ws[nblk + k]);
-            }
-            mx = team_max<64>(mx);
-            nmn = team_max<64>(nmn);
-            if (threadIdx.x == 0) {
-                GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
-                           : make_gp<FT, false>(0.0f, -nmn, mx, qmin, qmax, yc);
-                sp = p;
-                if (blockIdx.x == 0) {
-                    scale[0] = p.s;
-                    if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
-                }
-            }
-        }
+    } else if (threadIdx.x == 0) {
+        GP p;
+        p.s = scale[0];
+        p.fast = scale_in_fast_range(p.s);
+        p.y = p.fast ? rcp_rn(p.s) : 0.0f;
+        p.zpf = zp_at(zp, 0, zp_signed);
+        sp = p;
     }
     __syncthreads();
     const GP p = sp;
@@ -1240,6 +1249,30 @@ static tq_status check_map_args(int32_t ndim, const int64_t* shape, int32_t axis
     return TQ_OK;
 }
 
+// Per-tensor dynamic scale of a large tensor: block partials (pass 1), then
+// one workgroup publishes scale / zero-point (pass 1b).
+static tq_status tensor_scale_passes(const void* x, int xt, int64_t numel, bool sym, float qmin, float qmax,
+                                     float yc, void* workspace, size_t workspace_bytes, float* scale, uint8_t* zp,
+                                     hipStream_t st)
+{
+    if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
+    const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
+    const int nblk = (int)cdiv(numel, chunk);
+    float* ws = static_cast<float*>(workspace);
+    TQ_FT_SWITCH(xt, {
+        if (sym) {
+            hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
+            hipLaunchKernelGGL((k_tensor_finalize<FTV, true>), dim3(1), dim3(256), 0, st, ws, nblk, qmin, qmax, yc,
+                               scale, zp);
+        } else {
+            hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
+            hipLaunchKernelGGL((k_tensor_finalize<FTV, false>), dim3(1), dim3(256), 0, st, ws, nblk, qmin, qmax, yc,
+                               scale, zp);
+        }
+    });
+    return launch_status();
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -1312,29 +1345,20 @@ tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int cod
                                scale, zb)));
         return launch_status();
     }
-    int nblk = 0;
     const bool small = numel <= 65536;
-    if (!static_scale && !small) {
-        if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
-        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
-        nblk = (int)cdiv(numel, chunk);
-        float* ws = static_cast<float*>(workspace);
-        TQ_FT_SWITCH(x_dtype, {
-            if (sym) hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
-            else hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
-        });
-        if (launch_status()) return TQ_ERR_HIP;
-    }
-    const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
-    const dim3 grid((!static_scale && small) ? 1u : grid_for(work, 256 * 4));
-    const float* ws = static_cast<const float*>(workspace);
     uint8_t* qb = static_cast<uint8_t*>(q);
     uint8_t* zb = static_cast<uint8_t*>(zero_point);
+    if (!static_scale && !small) {
+        s = tensor_scale_passes(x, x_dtype, numel, sym, fmin, fmax, yc, workspace, workspace_bytes, scale, zb, st);
+        if (s) return s;
+    }
+    const int eff_static = static_scale || !small;   // the scale is known before the encode
+    const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
+    const dim3 grid(eff_static ? grid_for(work, 256 * 4) : 1u);
     const bool zs = code_signed(code);
     TQ_FT_SWITCH(x_dtype, TQ_BITS_SYM_SWITCH(bits, sym,
-        hipLaunchKernelGGL((k_tensor_encode<FTV, BV, SV>), grid, dim3(256), 0, st, x, numel, ws, nblk,
-                           static_scale, (float)qmin, (float)qmax, range_reciprocal(qmin, qmax, sym), qb, scale,
-                           zb, zs)));
+        hipLaunchKernelGGL((k_tensor_encode<FTV, BV, SV>), grid, dim3(256), 0, st, x, numel, eff_static, fmin, fmax,
+                           yc, qb, scale, zb, zs)));
     return launch_status();
 }
 
@@ -1358,28 +1382,20 @@ tq_status tq_fake_quant_per_tensor(const void* x, int x_dtype, int64_t numel, in
         });
         return launch_status();
     }
-    int nblk = 0;
     const bool small = numel <= 65536;
     if (!static_scale && !small) {
-        if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
-        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
-        nblk = (int)cdiv(numel, chunk);
-        float* ws = static_cast<float*>(workspace);
-        TQ_FT_SWITCH(x_dtype, {
-            if (sym) hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
-            else hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
-        });
-        if (launch_status()) return TQ_ERR_HIP;
+        s = tensor_scale_passes(x, x_dtype, numel, sym, fmin, fmax, yc, workspace, workspace_bytes, scale, zb, st);
+        if (s) return s;
     }
+    const int eff_static = static_scale || !small;
     const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
-    const dim3 grid((!static_scale && small) ? 1u : grid_for(work, 256 * 4));
-    const float* ws = static_cast<const float*>(workspace);
+    const dim3 grid(eff_static ? grid_for(work, 256 * 4) : 1u);
     const bool zs = code_signed(code);
     TQ_FT_SWITCH(x_dtype, {
-        if (sym) hipLaunchKernelGGL((k_tensor_encode<FTV, 8, true, true>), grid, dim3(256), 0, st, x, numel, ws, nblk,
-                                    static_scale, fmin, fmax, yc, y, scale, zb, zs);
-        else hipLaunchKernelGGL((k_tensor_encode<FTV, 8, false, true>), grid, dim3(256), 0, st, x, numel, ws, nblk,
-                                static_scale, fmin, fmax, yc, y, scale, zb, zs);
+        if (sym) hipLaunchKernelGGL((k_tensor_encode<FTV, 8, true, true>), grid, dim3(256), 0, st, x, numel,
+                                    eff_static, fmin, fmax, yc, y, scale, zb, zs);
+        else hipLaunchKernelGGL((k_tensor_encode<FTV, 8, false, true>), grid, dim3(256), 0, st, x, numel, eff_static,
+                                fmin, fmax, yc, y, scale, zb, zs);
     });
     return launch_status();
 }
