@@ -18,7 +18,7 @@
 //   k_fp4_quant      a team of 2 (NVFP4) / 4 (MXFP4) lanes per block, block max
 //                    through DPP, U rounds per wave; reads s_g from global_scale.
 //   k_fp4_ew         dequant / STE / dequant-backward, 8 elements per step.
-//   k_transpose_u8   byte transpose through a 128 x 128-byte LDS tile with
+//   k_transpose_jobs byte transposes through 128 x 128-byte LDS tiles with
 //                    4 x 4 register transposes and 16-byte stores, into a
 //                    destination of any row stride (concatenation, padding).
 //   k_fp4_to_fp8     FP4 -> E4M3 with the per-tensor scale folded in.
@@ -272,64 +272,74 @@ __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t 
     o[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-// A block walks TPB row-tiles of one 128-column strip: the next tile's global
-// loads are issued before the current tile is read out of LDS and stored, so
-// each block overlaps its reads with its writes.
-#ifndef TQ_TPB
-#define TQ_TPB 1
-#endif
-constexpr int TPB = TQ_TPB;
+// One 128 x 128-byte tile (rows R0.., columns C0.. of src) through LDS.
+__device__ __forceinline__ void transpose_tile(const uint8_t* __restrict__ src, int64_t R, int64_t C,
+                                               uint8_t* __restrict__ dst, int64_t ldd, int64_t R0, int64_t C0,
+                                               uint32_t* tile)
+{
+    const int t = threadIdx.x;
+    uint4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = t / 8 + 32 * k;
+        const int cq = (t % 8) * 16;
+        w[k] = make_uint4(0, 0, 0, 0);
+        if (R0 + r < R && C0 + cq < C) w[k] = ld16<true>(src + (R0 + r) * C + C0 + cq);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t* row = tile + (t / 8 + 32 * k) * TR_PITCH + (t % 8) * 4;
+        row[0] = w[k].x;
+        row[1] = w[k].y;
+        row[2] = w[k].z;
+        row[3] = w[k].w;
+    }
+    __syncthreads();
+    const int m = t % 8, d = t / 8;        // read-out: rows 16m..16m+15, columns 4d..4d+3
+    uint32_t o[4][4];                       // o[c][qd]: output row 4d+c, bytes 4*qd.. of this 16-byte piece
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+        const int rb = 16 * m + 4 * qd;
+        uint32_t tr[4];
+        transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d], tile[(rb + 2) * TR_PITCH + d],
+                     tile[(rb + 3) * TR_PITCH + d], tr);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t oc = C0 + 4 * d + c;        // output row = input column
+        const int64_t orr = R0 + 16 * m;          // output column = input row
+        if (oc < C && orr < R) st16<true>(dst + oc * ldd + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
+    }
+}
 
-__global__ __launch_bounds__(256) void k_transpose_u8(const uint8_t* __restrict__ src, int64_t R, int64_t C,
-                                                      uint8_t* __restrict__ dst, int64_t ldd)
+// Several transposes in one launch (codes and block scales of a weight, every
+// part of a concatenation): block b does tile b - tile0 of the job whose
+// range holds b, so small matrices (the block scales) fill the chip together
+// with the large ones instead of running as a separate under-occupied launch.
+struct TJob {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t R, C, ldd;
+    int64_t tile0, tiles_c;
+};
+constexpr int MAX_TJOBS = 8;
+struct TJobs {
+    TJob j[MAX_TJOBS];
+    int n;
+};
+
+__global__ __launch_bounds__(256) void k_transpose_jobs(const TJobs jobs)
 {
     __shared__ uint32_t tile[TR * TR_PITCH];
-    const int t = threadIdx.x;
-    const int64_t C0 = (int64_t)blockIdx.x * TR;
-    const int64_t Rb = (int64_t)blockIdx.y * TR * TPB;
-    uint4 w[4];
-    auto load_tile = [&](int64_t R0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = t / 8 + 32 * k;
-            const int cq = (t % 8) * 16;
-            w[k] = make_uint4(0, 0, 0, 0);
-            if (R0 + r < R && C0 + cq < C) w[k] = ld16<true>(src + (R0 + r) * C + C0 + cq);
-        }
-    };
-    load_tile(Rb);
-    const int m = t % 8, d = t / 8;        // read-out: rows 16m..16m+15, columns 4d..4d+3
-    for (int j = 0; j < TPB; ++j) {
-        const int64_t R0 = Rb + (int64_t)j * TR;
-        if (R0 >= R) break;                 // uniform across the block
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t* row = tile + (t / 8 + 32 * k) * TR_PITCH + (t % 8) * 4;
-            row[0] = w[k].x;
-            row[1] = w[k].y;
-            row[2] = w[k].z;
-            row[3] = w[k].w;
-        }
-        __syncthreads();
-        if (j + 1 < TPB && R0 + TR < R) load_tile(R0 + TR);
-        uint32_t o[4][4];                   // o[c][qd]: output row 4d+c, bytes 4*qd.. of this 16-byte piece
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const int rb = 16 * m + 4 * qd;
-            uint32_t tr[4];
-            transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d],
-                         tile[(rb + 2) * TR_PITCH + d], tile[(rb + 3) * TR_PITCH + d], tr);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int64_t oc = C0 + 4 * d + c;        // output row = input column
-            const int64_t orr = R0 + 16 * m;          // output column = input row
-            if (oc < C && orr < R) st16<true>(dst + oc * ldd + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
-        }
-        __syncthreads();                    // the tile is rewritten next iteration
-    }
+    const int64_t b = blockIdx.x;
+    int k = 0;
+    for (int i = 1; i < jobs.n; ++i)
+        if (b >= jobs.j[i].tile0) k = i;
+    const TJob J = jobs.j[k];
+    const int64_t tl = b - J.tile0;
+    transpose_tile(J.src, J.R, J.C, J.dst, J.ldd, (tl / J.tiles_c) * TR, (tl % J.tiles_c) * TR, tile);
 }
 
 __global__ __launch_bounds__(256) void k_transpose_u8_generic(const uint8_t* __restrict__ src, int64_t R, int64_t C,
@@ -419,23 +429,58 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     default: { constexpr int FTV = BF16; __VA_ARGS__; } break;    \
     }
 
-// dst points at column `off` of the destination already (callers pass
-// base + off); fast only when that address and ldd keep 16-byte alignment.
-static tq_status transpose_bytes(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, int64_t ldd,
-                                 hipStream_t st)
-{
-    if (R == 0 || C == 0) return TQ_OK;
-    if (R % 16 == 0 && C % 16 == 0 && ldd % 16 == 0 && aligned16(src) && aligned16(dst) &&
-        cdiv(R, TR * TPB) <= 65535) {
-        hipLaunchKernelGGL(k_transpose_u8, dim3((unsigned)cdiv(C, TR), (unsigned)cdiv(R, TR * TPB)), dim3(256), 0, st,
-                           src, R, C, dst, ldd);
-    } else {
-        if (cdiv(R, 64) > 65535) return TQ_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(k_transpose_u8_generic, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64)), dim3(256), 0,
-                           st, src, R, C, dst, ldd);
+// Transposes dst[c * ldd + r] = src[r][c] collected into job launches.  A
+// job takes the tiled kernel when R, C and ldd are multiples of 16 and both
+// bases 16-byte aligned (dst already points at the job's column offset);
+// others run the generic kernel at once.  flush() launches what is queued.
+struct TransposeBatch {
+    TJobs jobs{};
+    int64_t tiles = 0;
+    hipStream_t st;
+    tq_status err = TQ_OK;
+    explicit TransposeBatch(hipStream_t s) : st(s) { jobs.n = 0; }
+    void flush()
+    {
+        if (jobs.n == 0 || err) return;
+        if (tiles > 0x7fffffff) {
+            err = TQ_ERR_UNSUPPORTED;
+            return;
+        }
+        hipLaunchKernelGGL(k_transpose_jobs, dim3((unsigned)tiles), dim3(256), 0, st, jobs);
+        err = launch_status();
+        jobs.n = 0;
+        tiles = 0;
     }
-    return launch_status();
-}
+    void add(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, int64_t ldd)
+    {
+        if (R == 0 || C == 0 || err) return;
+        if (R % 16 == 0 && C % 16 == 0 && ldd % 16 == 0 && aligned16(src) && aligned16(dst)) {
+            if (jobs.n == MAX_TJOBS) flush();
+            TJob& j = jobs.j[jobs.n++];
+            j.src = src;
+            j.dst = dst;
+            j.R = R;
+            j.C = C;
+            j.ldd = ldd;
+            j.tile0 = tiles;
+            j.tiles_c = cdiv(C, TR);
+            tiles += j.tiles_c * cdiv(R, TR);
+        } else {
+            if (cdiv(R, 64) > 65535) {
+                err = TQ_ERR_UNSUPPORTED;
+                return;
+            }
+            hipLaunchKernelGGL(k_transpose_u8_generic, dim3((unsigned)cdiv(C, 64), (unsigned)cdiv(R, 64)), dim3(256), 0,
+                               st, src, R, C, dst, ldd);
+            err = launch_status();
+        }
+    }
+    tq_status finish()
+    {
+        flush();
+        return err;
+    }
+};
 
 static tq_status check_fp4(int64_t rows, int64_t k, int kind)
 {
@@ -555,10 +600,10 @@ tq_status tq_fp4_transpose_for_gemm(const uint8_t* packed, const uint8_t* block_
     if (n == 0 || k == 0) return TQ_OK;
     if (!packed || !packed_t) return TQ_ERR_INVALID;
     if ((block_scale == nullptr) != (block_scale_t == nullptr)) return TQ_ERR_INVALID;
-    hipStream_t st = as_stream(stream);
-    tq_status s = transpose_bytes(packed, n, k / 2, packed_t, n, st);
-    if (s || !block_scale) return s;
-    return transpose_bytes(block_scale, n, k / group_size, block_scale_t, n, st);
+    TransposeBatch tb(as_stream(stream));
+    tb.add(packed, n, k / 2, packed_t, n);
+    if (block_scale) tb.add(block_scale, n, k / group_size, block_scale_t, n);
+    return tb.finish();
 }
 
 tq_status tq_fp4_transpose_concat_for_gemm(int32_t nparts, const uint8_t* const* host_packed,
@@ -586,13 +631,15 @@ tq_status tq_fp4_transpose_concat_for_gemm(int32_t nparts, const uint8_t* const*
     }
     hipStream_t st = as_stream(stream);
     const int64_t kb = k / 2, nb = k / group_size;
+    TransposeBatch tb(st);
     int64_t off = 0;
     for (int32_t i = 0; i < nparts; ++i) {
-        tq_status s = transpose_bytes(host_packed[i], host_n[i], kb, packed_t + off, stride, st);
-        if (!s && scales) s = transpose_bytes(host_block_scale[i], host_n[i], nb, block_scale_t + off, stride, st);
-        if (s) return s;
+        tb.add(host_packed[i], host_n[i], kb, packed_t + off, stride);
+        if (scales) tb.add(host_block_scale[i], host_n[i], nb, block_scale_t + off, stride);
         off += host_n[i];
     }
+    tq_status s = tb.finish();
+    if (s) return s;
     if (stride > total) {
         hipLaunchKernelGGL(k_zero_cols, dim3(grid_for(kb * (stride - total), 256)), dim3(256), 0, st, packed_t, kb,
                            stride, total, stride);
