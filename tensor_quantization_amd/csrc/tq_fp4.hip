@@ -368,6 +368,36 @@ __global__ __launch_bounds__(256) void k_zero_cols(uint8_t* __restrict__ dst, in
         dst[(i / w) * ld + c0 + i % w] = 0;
 }
 
+// ------------------------------------------------------------ row concat
+// Up to four byte ranges copied in one launch; each range moves in the widest
+// unit (16, 8 or 1 bytes) that its source, destination and length allow.
+// Block b copies 256 units of the range whose block span holds b.
+struct CSeg {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t units;
+    int64_t block0;
+    int32_t unit;
+};
+struct CSegs {
+    CSeg s[4];
+    int n;
+};
+
+__global__ __launch_bounds__(256) void k_copy_segments(const CSegs segs)
+{
+    const int64_t b = blockIdx.x;
+    int k = 0;
+    for (int i = 1; i < segs.n; ++i)
+        if (b >= segs.s[i].block0) k = i;
+    const CSeg S = segs.s[k];
+    const int64_t i = (b - S.block0) * 256 + threadIdx.x;
+    if (i >= S.units) return;
+    if (S.unit == 16) st16<true>(S.dst + i * 16, ld16<true>(S.src + i * 16));
+    else if (S.unit == 8) st8<true>(S.dst + i * 8, ld8<true>(S.src + i * 8));
+    else S.dst[i] = S.src[i];
+}
+
 // ------------------------------------------------------------ FP4 -> FP8
 // out = E4M3(val(q) * eff) per element, eff as in dequantization.  One lane
 // per 16 elements: an 8-byte code load (a wave reads 512 contiguous bytes) and
@@ -666,14 +696,25 @@ tq_status tq_fp4_concat_rows(const uint8_t* packed1, const uint8_t* block_scale1
     if (!packed_out || !block_scale_out) return TQ_ERR_INVALID;
     if (n1 > 0 && (!packed1 || !block_scale1)) return TQ_ERR_INVALID;
     if (n2 > 0 && (!packed2 || !block_scale2)) return TQ_ERR_INVALID;
-    hipStream_t st = as_stream(stream);
     const struct { const uint8_t* src; uint8_t* dst; int64_t bytes; } cp[4] = {
         {packed1, packed_out, n1 * kb}, {packed2, packed_out + n1 * kb, n2 * kb},
         {block_scale1, block_scale_out, n1 * nb}, {block_scale2, block_scale_out + n1 * nb, n2 * nb}};
-    for (const auto& c : cp)
-        if (c.bytes > 0 && hipMemcpyAsync(c.dst, c.src, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
-            return TQ_ERR_HIP;
-    return TQ_OK;
+    CSegs segs{};
+    int64_t blocks = 0;
+    for (const auto& c : cp) {
+        if (c.bytes <= 0) continue;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(c.src) | reinterpret_cast<uintptr_t>(c.dst) | (uintptr_t)c.bytes;
+        CSeg& g = segs.s[segs.n++];
+        g.unit = (a % 16 == 0) ? 16 : (a % 8 == 0) ? 8 : 1;
+        g.src = c.src;
+        g.dst = c.dst;
+        g.units = c.bytes / g.unit;
+        g.block0 = blocks;
+        blocks += cdiv(g.units, 256);
+    }
+    if (blocks > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_copy_segments, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream), segs);
+    return launch_status();
 }
 
 tq_status tq_fp4_predequant_to_fp8(const uint8_t* packed, const uint8_t* block_scale, float host_global_scale,

@@ -176,10 +176,14 @@ def test_transpose_concat_full_size_sampled(tq, orc):
         assert_same(BT[:, c], src(B, c), "scales^T column %d" % c)
 
 
-def test_concat_rows(tq, orc):
-    note("concat_rows")
-    k = 4096
-    parts = _quant_parts(tq, [96, 40], k, "nvfp4", 800)
+@pytest.mark.parametrize("n1,n2,k", [(96, 40, 4096), (3, 5, 48), (7, 0, 32)])
+def test_concat_rows(tq, orc, n1, n2, k):
+    """16-byte units (aligned rows), 8-byte and 1-byte units (rows of 24 code
+    bytes and 3 scale bytes put the second part at unaligned offsets)."""
+    note("concat_rows", n1, n2, k)
+    parts = _quant_parts(tq, [n1, max(n2, 1)], k, "nvfp4", 800)
+    if n2 == 0:
+        parts[1] = (parts[1][0][:0], parts[1][1][:0])
     (p1, b1), (p2, b2) = parts
     g = np.float32(2e-5)
     po, bo = tq.tq_fp4_concat_rows(p1, b1, g, p2, b2, g, k)
