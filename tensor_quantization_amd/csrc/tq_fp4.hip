@@ -175,6 +175,10 @@ __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, i
 
 // ------------------------------------------------------------ elementwise
 enum { OP_DEQ = 0, OP_STE = 1, OP_DQB = 2 };
+#ifndef TQ_EW_NT
+#define TQ_EW_NT 0
+#endif
+constexpr bool EW_NT = TQ_EW_NT != 0;   // non-temporal code loads in the dequantizer
 
 __device__ __forceinline__ float fp4_eff(int kind, uint32_t sb, float sg)
 {
@@ -195,7 +199,9 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
         float o[8];
         if constexpr (OP == OP_DEQ) {
             const float eff = fp4_eff(KIND, sb, sg);
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a) + e / 2);
+            const uint32_t w = EW_NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+                                           static_cast<const uint8_t*>(a) + e / 2))
+                                     : *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a) + e / 2);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f2v d = e2m1_val2(w, i);
@@ -563,7 +569,10 @@ tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k
         TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_amax_partial<FTV>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws));
         if (launch_status()) return TQ_ERR_HIP;
     }
-    constexpr int U = 8;
+#ifndef TQ_FP4_U
+#define TQ_FP4_U 2
+#endif
+    constexpr int U = TQ_FP4_U;
     if (kind == TQ_NVFP4) {
         if (!static_global) {
             hipLaunchKernelGGL(k_nv_global_scale, dim3(1), dim3(256), 0, st, ws, nws, global_scale);

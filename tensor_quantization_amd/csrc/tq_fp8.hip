@@ -177,6 +177,10 @@ __global__ __launch_bounds__(256) void k_fp8_generic(const void* __restrict__ x,
 
 // ------------------------------------------------------------ elementwise
 enum { OP_DEQ = 0, OP_STE = 1, OP_DQB = 2 };
+#ifndef TQ_EW_NT
+#define TQ_EW_NT 0
+#endif
+constexpr bool EW_NT = TQ_EW_NT != 0;   // non-temporal code loads in the dequantizers
 
 __device__ __forceinline__ int64_t fp8_block_of(int64_t e, int64_t cols, int64_t br, int64_t bc, int64_t nbc)
 {
@@ -184,17 +188,20 @@ __device__ __forceinline__ int64_t fp8_block_of(int64_t e, int64_t cols, int64_t
 }
 
 // Vector path (cols % 8 == 0 and bc % 8 == 0: the 8 elements share a block).
+// SHIFT >= 0: 1 x bc blocks with cols % bc == 0 and bc = 2^SHIFT, so the
+// block of element e is e >> SHIFT (no 64-bit divisions per vector).
 template <int OP, int FT>
 __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, const void* __restrict__ b,
                                                 int64_t nvec, int64_t cols, int64_t br, int64_t bc, int64_t nbc,
-                                                const float* __restrict__ scale, void* __restrict__ out)
+                                                int shift, const float* __restrict__ scale, void* __restrict__ out)
 {
     for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
         const int64_t e = vi * 8;
-        const float s = scale[fp8_block_of(e, cols, br, bc, nbc)];
+        const float s = scale[shift >= 0 ? (e >> shift) : fp8_block_of(e, cols, br, bc, nbc)];
         float o[8];
         if constexpr (OP == OP_DEQ) {
-            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
+            const uint2 w = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + e)
+                                  : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 o[i] = e4m3_val(w.x, i) * s;
@@ -409,7 +416,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, co
         float o[8];
         if constexpr (OP == OP_DEQ) {
             const float X = e8m0_val(sb);
-            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
+            const uint2 w = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + e)
+                                  : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 o[i] = e4m3_val(w.x, i) * X;
@@ -518,8 +526,11 @@ static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t r
     if (n == 0) return TQ_OK;
     const int64_t nbc = cdiv(cols, bc);
     if (cols % 8 == 0 && bc % 8 == 0) {
+        int shift = -1;
+        if (br == 1 && cols % bc == 0 && (bc & (bc - 1)) == 0)
+            for (shift = 0; ((int64_t)1 << shift) < bc; ++shift) {}
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256)), dim3(256), 0, st,
-                                            a, b, n / 8, cols, br, bc, nbc, scale, out));
+                                            a, b, n / 8, cols, br, bc, nbc, shift, scale, out));
     } else {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew_generic<OP, FTV>), dim3(grid_for(n, 256)), dim3(256), 0, st,
                                             a, b, n, cols, br, bc, nbc, scale, out));
@@ -614,7 +625,10 @@ tq_status tq_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t k, ui
     if (s || rows * k == 0) return s;
     if (!x || !q || !block_scale) return TQ_ERR_INVALID;
     if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
-    constexpr int U = 8;
+#ifndef TQ_MX8_U
+#define TQ_MX8_U 2
+#endif
+    constexpr int U = TQ_MX8_U;
     const int64_t nb = rows * k / 32;
     const int64_t grid = cdiv(cdiv(nb, U * 16), 4);
     if (grid > 0x7fffffff) return TQ_ERR_UNSUPPORTED;

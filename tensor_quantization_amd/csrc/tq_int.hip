@@ -739,7 +739,9 @@ __device__ __forceinline__ float zp_f(const uint8_t* zp, int64_t g)
 #ifndef TQ_VPT
 #define TQ_VPT 1
 #endif
-constexpr int VPT = TQ_VPT;   // vectors per thread per iteration
+#ifndef TQ_VPT4
+#define TQ_VPT4 TQ_VPT
+#endif
 #ifndef TQ_STE_VPT
 #define TQ_STE_VPT 1
 #endif
@@ -758,9 +760,10 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
                                                      int64_t P2, int sh, const float* __restrict__ scale,
                                                      const uint8_t* __restrict__ zp, void* __restrict__ y)
 {
-    for (int64_t base = (int64_t)blockIdx.x * 256 * VPT; base < nvec; base += (int64_t)gridDim.x * 256 * VPT) {
+    constexpr int DQV = BITS == 4 ? TQ_VPT4 : TQ_VPT;   // vectors per thread per iteration
+    for (int64_t base = (int64_t)blockIdx.x * 256 * DQV; base < nvec; base += (int64_t)gridDim.x * 256 * DQV) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
+        for (int k = 0; k < DQV; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
             if (vi >= nvec) break;
             const int64_t e = vi * 8;
@@ -1151,7 +1154,7 @@ static unsigned ew_grid(int64_t nvec, int64_t per_block)
 template <int MAPK>
 static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int64_t P2, hipStream_t st)
 {
-    const dim3 grid(ew_grid(nvec, 256 * VPT)), block(256);
+    const dim3 grid(ew_grid(nvec, 256 * (code_bits(a.code) == 4 ? TQ_VPT4 : TQ_VPT))), block(256);
     const bool sg = code_signed(a.code);
     const int bits = code_bits(a.code);
     const int sh = MAPK == MAP_CONTIG ? log2_exact(P1) : -1;
