@@ -233,6 +233,31 @@ __device__ __forceinline__ bool value_in_fast_range(float x)
     return a >= 0x1p-78f && a <= 0x1p86f;
 }
 
+// Range guards over a vector of 8 values, reduced branch-free through
+// max / min (short-circuit && chains compile into nested exec-mask branches).
+// Every |v| <= 2^86 (quotients that only feed a code):
+__device__ __forceinline__ bool codes_fast8(const float v[8])
+{
+    float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])), __builtin_fabsf(v[2]));
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(v[3])), __builtin_fabsf(v[4]));
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(v[5])), __builtin_fabsf(v[6]));
+    m = __builtin_fmaxf(m, __builtin_fabsf(v[7]));
+    return m <= 0x1p86f;
+}
+
+// Every v zero or 2^-78 <= |v| <= 2^86 (quotients that are output values):
+__device__ __forceinline__ bool values_fast8(const float v[8])
+{
+    float hi = 0.0f, lo = __builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        hi = __builtin_fmaxf(hi, a);
+        lo = __builtin_fminf(lo, a == 0.0f ? __builtin_inff() : a);
+    }
+    return (hi <= 0x1p86f) & (lo >= 0x1p-78f);
+}
+
 // RN(1/s) for 2^-40 <= |s| <= 2^40: v_rcp_f32 and one Newton step.  On
 // gfx950 this equals IEEE 1/s for every binary32 significand (checked
 // exhaustively at several exponents; the step is scale-invariant there).

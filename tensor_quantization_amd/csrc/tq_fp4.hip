@@ -227,10 +227,7 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
                 }
             } else {
                 const float eff = fp4_eff(KIND, sb, sg);
-                bool ok = scale_in_fast_range(eff);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    ok = ok && (value_in_fast_range(d[i]) || d[i] == 0.0f) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+                const bool ok = scale_in_fast_range(eff) & values_fast8(d) & codes_fast8(xv);
                 if (ok) {
                     const float y = rcp_rn(eff);
 #pragma unroll

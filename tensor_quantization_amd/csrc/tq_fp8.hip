@@ -216,10 +216,7 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
             float xv[8], d[8];
             widen8<FT>(load8<FT, true>(a, e), xv);
             widen8<FT>(load8<FT, true>(b, e), d);
-            bool ok = scale_in_fast_range(s);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                ok = ok && (value_in_fast_range(d[i]) || d[i] == 0.0f) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+            const bool ok = scale_in_fast_range(s) & values_fast8(d) & codes_fast8(xv);
             float t[8], g[8];
             if (ok) {
                 const float y = rcp_rn(s);
@@ -356,9 +353,7 @@ __global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restric
             float v[8];
             widen8<FT>(load8<FT, true>(x, vi * 8), v);
             // a static scale does not bound |x|: keep x / s from overflowing on the fast path
-            bool fast = p.fast;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) fast = fast && __builtin_fabsf(v[i]) <= 0x1p86f;
+            const bool fast = p.fast & codes_fast8(v);
             st8<true>(q + vi * 8, fast ? fp8_enc8<FT, true>(v, p) : fp8_enc8<FT, false>(v, p));
         }
     } else {

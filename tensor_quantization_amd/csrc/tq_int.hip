@@ -620,11 +620,7 @@ __global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ 
             float v[8], c[8];
             widen8<FT>(load8<FT, true>(x, vi * 8), v);
             // a static scale does not bound |x|: keep x / s from overflowing
-            bool fast = p.fast;
-            if (static_scale) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) fast = fast && __builtin_fabsf(v[i]) <= 0x1p86f;
-            }
+            const bool fast = p.fast & (!static_scale | codes_fast8(v));
             if (fast) enc8<FT, true, true>(v, p, lo, hi, c);
             else enc8<FT, false, true>(v, p, lo, hi, c);
             if constexpr (FAKE) store_fake8<FT>(out, vi * 8, c, p);
@@ -861,10 +857,7 @@ __global__ __launch_bounds__(256) void k_ste_vec(const void* __restrict__ x, con
             if constexpr (MAPK == MAP_CONTIG) {
                 const float s = scale[g];
                 const float zf = zp_f<SIGNED>(zp, g);
-                bool ok = scale_in_fast_range(s);
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    ok = ok && (value_in_fast_range(dv[i]) || dv[i] == 0.0f) && __builtin_fabsf(xv[i]) <= 0x1p86f;
+                const bool ok = scale_in_fast_range(s) & values_fast8(dv) & codes_fast8(xv);
                 if (ok) {
                     const float yr = rcp_rn(s);
 #pragma unroll
@@ -915,9 +908,7 @@ __global__ __launch_bounds__(256) void k_fake_ste(const void* __restrict__ x, co
             float xv[8], dv[8], out[8];
             widen8<FT>(load8<FT, true>(x, vi * 8), xv);
             widen8<FT>(load8<FT, true>(dy, vi * 8), dv);
-            bool ok = sfast;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ok = ok && __builtin_fabsf(xv[i]) <= 0x1p86f;
+            const bool ok = sfast & codes_fast8(xv);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float t = ok ? div_q<FT>(xv[i], s, yr) : xv[i] / s;
