@@ -532,3 +532,66 @@ def quant_fp8_per_tensor(x, xt, scale=None):
     if lib().orc_quant_fp8_per_tensor(_p(x), FTYPES[xt], ctypes.c_int64(x.size), int(static), _p(s), _p(q)):
         raise ValueError("oracle rejected quant_fp8_per_tensor arguments")
     return q, s
+
+
+# ----------------------------------------------------------------- binary64 inputs
+def quant_f64(x, gran, axis=0, group_size=0, code="s8", qmin=None, qmax=None, symmetric=True, scale=None, zp=None):
+    """Binary64 quantize: x float64; returns (q, scale float64, zp or None)."""
+    x = np.ascontiguousarray(x, np.float64)
+    if qmin is None:
+        qmin, qmax = default_q_range(code, symmetric)
+    sshape = scale_shape(x.shape, gran, axis, group_size)
+    static = scale is not None
+    q = np.zeros(packed_shape(x.shape, code), np.uint8)
+    s = np.ascontiguousarray(scale, np.float64).copy() if static else np.zeros(sshape, np.float64)
+    z = None
+    if not symmetric:
+        z = np.ascontiguousarray(zp).view(np.uint8).copy() if static else np.zeros(sshape, np.uint8)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_quant_f64(_p(x), x.ndim, _shape_arr(x.shape), g, a, ctypes.c_int64(gsz), CODES[code], qmin, qmax,
+                             int(bool(symmetric)), int(static), _p(q), _p(s), _p(z))
+    if rc:
+        raise ValueError("oracle rejected quant_f64 arguments")
+    if z is not None and code in ("s8", "s4"):
+        z = z.view(np.int8)
+    return q, s, z
+
+
+def dequant_f64(q, code, shape, gran, axis=0, group_size=0, scale=None, zp=None):
+    q = np.ascontiguousarray(q, np.uint8)
+    y = np.zeros(tuple(shape), np.float64)
+    zpa = None if zp is None else np.ascontiguousarray(zp).view(np.uint8)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_dequant_f64(_p(q), CODES[code], len(shape), _shape_arr(shape), g, a, ctypes.c_int64(gsz),
+                               _p(np.ascontiguousarray(scale, np.float64)), _p(zpa), _p(y))
+    if rc:
+        raise ValueError("oracle rejected dequant_f64 arguments")
+    return y
+
+
+def quant_f64_backward(x, gran, axis=0, group_size=0, code="s8", qmin=None, qmax=None, symmetric=True, scale=None,
+                       zp=None, dy=None):
+    x = np.ascontiguousarray(x, np.float64)
+    dy = np.ascontiguousarray(dy, np.float64)
+    if qmin is None:
+        qmin, qmax = default_q_range(code, symmetric)
+    dx = np.zeros(x.shape, np.float64)
+    zpa = None if zp is None else np.ascontiguousarray(zp).view(np.uint8)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_quant_f64_backward(_p(x), x.ndim, _shape_arr(x.shape), g, a, ctypes.c_int64(gsz), CODES[code],
+                                      qmin, qmax, _p(np.ascontiguousarray(scale, np.float64)), _p(zpa), _p(dy),
+                                      _p(dx))
+    if rc:
+        raise ValueError("oracle rejected quant_f64_backward arguments")
+    return dx
+
+
+def dequant_f64_backward(dy, gran, axis=0, group_size=0, scale=None):
+    dy = np.ascontiguousarray(dy, np.float64)
+    dq = np.zeros(dy.shape, np.float64)
+    g, a, gsz = _gran_args(gran, axis, group_size)
+    rc = lib().orc_dequant_f64_backward(_p(dy), dy.ndim, _shape_arr(dy.shape), g, a, ctypes.c_int64(gsz),
+                                        _p(np.ascontiguousarray(scale, np.float64)), _p(dq))
+    if rc:
+        raise ValueError("oracle rejected dequant_f64_backward arguments")
+    return dq

@@ -896,3 +896,108 @@ int orc_quant_fp8_per_tensor(const void* x, int xt, int64_t numel, int static_sc
     for (int64_t e = 0; e < numel; ++e) q[e] = orc_enc_e4m3(widen(x, xt, e) / s);
     return ORC_OK;
 }
+
+/* ------------------------------------------------ binary64 inputs */
+/* docs.rs quantize overview lists f64 among the input types.  Reading: an
+ * f64 input is computed in binary64 throughout -- the same definitions as
+ * the binary32 family above with every division, product and rounding done
+ * in binary64, scales stored as binary64, outputs (dequantized values and
+ * gradients) in binary64:
+ *   symmetric : scale = amax / qmax;  asymmetric: mn = min(min x, 0),
+ *               mx = max(max x, 0), scale = (mx - mn) / (qmax - qmin),
+ *               zp = clamp(qmin - rne(mn / scale), qmin, qmax);  0 -> 1
+ *   q  = clamp(rne(x / scale) + zp, qmin, qmax)
+ *   y  = (q - zp) * scale
+ *   dx = (dy / scale) * 1[qmin < q < qmax]
+ *   dq = dy * scale */
+static int encode_int64(double x, double scale, int zp, int qmin, int qmax)
+{
+    double r = rne(x / scale) + (double)zp;
+    if (r < qmin) r = qmin;
+    if (r > qmax) r = qmax;
+    return (int)r;
+}
+
+int orc_quant_f64(const double* x, int ndim, const int64_t* shape, int gran, int axis, int64_t group_size, int code,
+                  int qmin, int qmax, int symmetric, int static_scale, void* q, double* scale, void* zp)
+{
+    orc_groups G;
+    if (make_groups(ndim, shape, gran, axis, group_size, &G)) return ORC_BAD;
+    if (code_bits(code) == 4 && (shape[ndim - 1] & 1)) return ORC_BAD;
+    if (qmin >= qmax || (symmetric && qmin != -qmax) || (!symmetric && !zp)) return ORC_BAD;
+    int64_t ng = G.ngroups ? G.ngroups : 1;
+    int* z = (int*)calloc(ng, sizeof(int));
+    if (static_scale) {
+        for (int64_t gi = 0; gi < G.ngroups; ++gi) z[gi] = symmetric ? 0 : get_zp(zp, code, gi);
+    } else {
+        double* amax = (double*)calloc(ng, sizeof(double));
+        double* mn = (double*)calloc(ng, sizeof(double));
+        double* mx = (double*)calloc(ng, sizeof(double));
+        for (int64_t e = 0; e < G.numel; ++e) {
+            int64_t gi = group_of(&G, e);
+            if (fabs(x[e]) > amax[gi]) amax[gi] = fabs(x[e]);
+            if (x[e] < mn[gi]) mn[gi] = x[e];
+            if (x[e] > mx[gi]) mx[gi] = x[e];
+        }
+        for (int64_t gi = 0; gi < G.ngroups; ++gi) {
+            double s;
+            if (symmetric) {
+                s = amax[gi] / (double)qmax;
+                if (s == 0.0) s = 1.0;
+                z[gi] = 0;
+            } else {
+                s = (mx[gi] - mn[gi]) / (double)(qmax - qmin);
+                if (s == 0.0) s = 1.0;
+                double zz = (double)qmin - rne(mn[gi] / s);
+                if (zz < qmin) zz = qmin;
+                if (zz > qmax) zz = qmax;
+                z[gi] = (int)zz;
+                put_zp(zp, gi, z[gi]);
+            }
+            scale[gi] = s;
+        }
+        free(amax); free(mn); free(mx);
+    }
+    for (int64_t e = 0; e < G.numel; ++e) {
+        int64_t gi = group_of(&G, e);
+        put_code(q, code, e, encode_int64(x[e], scale[gi], z[gi], qmin, qmax));
+    }
+    free(z);
+    return ORC_OK;
+}
+
+int orc_dequant_f64(const void* q, int code, int ndim, const int64_t* shape, int gran, int axis, int64_t group_size,
+                    const double* scale, const void* zp, double* y)
+{
+    orc_groups G;
+    if (make_groups(ndim, shape, gran, axis, group_size, &G)) return ORC_BAD;
+    for (int64_t e = 0; e < G.numel; ++e) {
+        int64_t gi = group_of(&G, e);
+        y[e] = (double)(get_code(q, code, e) - get_zp(zp, code, gi)) * scale[gi];
+    }
+    return ORC_OK;
+}
+
+int orc_quant_f64_backward(const double* x, int ndim, const int64_t* shape, int gran, int axis, int64_t group_size,
+                           int code, int qmin, int qmax, const double* scale, const void* zp, const double* dy,
+                           double* dx)
+{
+    orc_groups G;
+    if (make_groups(ndim, shape, gran, axis, group_size, &G)) return ORC_BAD;
+    for (int64_t e = 0; e < G.numel; ++e) {
+        int64_t gi = group_of(&G, e);
+        int qv = encode_int64(x[e], scale[gi], get_zp(zp, code, gi), qmin, qmax);
+        double mask = (qmin < qv && qv < qmax) ? 1.0 : 0.0;
+        dx[e] = (dy[e] / scale[gi]) * mask;
+    }
+    return ORC_OK;
+}
+
+int orc_dequant_f64_backward(const double* dy, int ndim, const int64_t* shape, int gran, int axis,
+                             int64_t group_size, const double* scale, double* dq)
+{
+    orc_groups G;
+    if (make_groups(ndim, shape, gran, axis, group_size, &G)) return ORC_BAD;
+    for (int64_t e = 0; e < G.numel; ++e) dq[e] = dy[e] * scale[group_of(&G, e)];
+    return ORC_OK;
+}
