@@ -268,6 +268,19 @@ def breakdown(torch, tq, iters=20, only=None):
                                                                  P(b["dy"]), P(b["dx"]), stream), "fake bwd"),
              n2 * 8, n2 * 4)
 
+    # binary64 inputs: the per-token workload's shape in f64 (N(0,1) values)
+    xf = np.random.default_rng(211).standard_normal((8192, 4096))
+    shpf = (ctypes.c_int64 * 2)(8192, 4096)
+    mkd = lambda i: dict(x=torch.from_numpy(xf).cuda(), q=E(n2, u8), s=E(8192, torch.float64),
+                         y=E((8192, 4096), torch.float64))
+    bench_op("quant_f64_per_token_s8", "f64 [8192,4096] per-token s8", n2 * 9 + 8192 * 8, mkd,
+             lambda b: check(L.tq_quant_f64(P(b["x"]), 2, shpf, 2, 0, 0, 0, -127, 127, 0, P(b["q"]), P(b["s"]), None,
+                                            None, 0, stream), "f64 quant"), n2 * 17, n2 * 8)
+    bench_op("dequant_f64_per_token_s8", "f64 [8192,4096] per-token s8", n2 * 9 + 8192 * 8, mkd,
+             lambda b: check(L.tq_dequant_f64(P(b["q"]), 0, 2, shpf, 2, 0, 0, P(b["s"]), None, P(b["y"]), stream),
+                             "f64 dequant"), n2 * 17, n2)
+    del xf
+
     # per-group u4 g128 asymmetric, f16 [11008, 4096]
     w3 = workloads.make_input("c3_per_group_u4_g128")
     N3, K3 = w3.shape

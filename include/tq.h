@@ -14,7 +14,8 @@
  *   - the FP4 transposes to GEMM layout, the concatenations of FP4 weights
  *     and their expansion to FP8 E4M3,
  *   - per-tensor fake quantization (round trip) and its backward, and
- *     dynamic-range quantization by mode and scope.
+ *     dynamic-range quantization by mode and scope,
+ *   - integer codes of binary64 inputs computed in binary64.
  *
  * Sources (page titles and sections):
  *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
@@ -83,6 +84,7 @@ typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_ftype;
 typedef enum { TQ_S8 = 0, TQ_U8 = 1, TQ_S4 = 2, TQ_U4 = 3 } tq_itype;
 typedef enum { TQ_NVFP4 = 0, TQ_MXFP4 = 1 } tq_fp4_kind;
 typedef enum { TQ_RANGE_SYMMETRIC = 0, TQ_RANGE_ASYMMETRIC = 1 } tq_range_mode;
+typedef enum { TQ_GRAN_TENSOR = 0, TQ_GRAN_CHANNEL = 1, TQ_GRAN_TOKEN = 2, TQ_GRAN_GROUP = 3 } tq_granularity;
 typedef enum { TQ_SCOPE_TENSOR = 0, TQ_SCOPE_TOKEN = 1, TQ_SCOPE_CHANNEL = 2 } tq_range_scope;
 
 /* Version of this ABI (bumped on any signature change). */
@@ -104,7 +106,8 @@ tq_status tq_default_q_range(int code, int symmetric, int32_t* host_qmin, int32_
  * reduces and encodes in a single launch; tq_fake_quant_per_tensor and the
  * TQ_SCOPE_TENSOR dynamic-range call likewise), 1 = tq_quant_fp4_block with
  * a dynamic global scale, 2 = tq_quant_fp8_per_tensor with a dynamic scale
- * (0 bytes up to 65536 elements).  numel = elements. */
+ * (0 bytes up to 65536 elements), 3 = tq_quant_f64 at TQ_GRAN_TENSOR with a
+ * dynamic scale (16 KiB).  numel = elements. */
 size_t tq_workspace_bytes(int op, int64_t numel);
 
 /* ===================================================================== */
@@ -248,6 +251,35 @@ tq_status tq_dynamic_range_quantize(const void* x, int x_dtype, int32_t ndim,
                                     const int64_t* host_shape, int mode, int scope, int32_t axis,
                                     int code, void* q, float* scale, void* zero_point,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Binary64 inputs ([Q] module overview: f64 among the input types).
+ * Reading: an f64 input is computed in binary64 throughout -- the integer-code
+ * definitions above with every division, product and rounding a binary64
+ * operation, `scale` arrays of binary64, and binary64 dequantized values and
+ * gradients.  One call per operation with the granularity as an argument:
+ * gran = TQ_GRAN_TENSOR, TQ_GRAN_TOKEN (rows = product of the leading extents),
+ * TQ_GRAN_CHANNEL (along `axis`) or TQ_GRAN_GROUP (`group_size` along `axis`);
+ * scale / zero_point have the shapes of the binary32 calls.  Codes, zero-points,
+ * ranges and symmetric mode as above.  Pointers need only their natural
+ * alignment.  A dynamic TQ_GRAN_TENSOR scale needs `workspace` of
+ * tq_workspace_bytes(3, numel) bytes; otherwise it may be NULL. */
+tq_status tq_quant_f64(const double* x, int32_t ndim, const int64_t* host_shape, int gran,
+                       int32_t axis, int64_t group_size, int code, int32_t qmin, int32_t qmax,
+                       int static_scale, void* q, double* scale, void* zero_point,
+                       void* workspace, size_t workspace_bytes, void* stream);
+/* y = (q - zp) * scale (binary64). */
+tq_status tq_dequant_f64(const void* q, int code, int32_t ndim, const int64_t* host_shape,
+                         int gran, int32_t axis, int64_t group_size, const double* scale,
+                         const void* zero_point, double* y, void* stream);
+/* dx = (dy / scale) * (qmin < q < qmax ? 1 : 0), q recomputed from x. */
+tq_status tq_quant_f64_backward(const double* x, int32_t ndim, const int64_t* host_shape, int gran,
+                                int32_t axis, int64_t group_size, int code, int32_t qmin,
+                                int32_t qmax, const double* scale, const void* zero_point,
+                                const double* dy, double* dx, void* stream);
+/* dq = dy * scale. */
+tq_status tq_dequant_f64_backward(const double* dy, int32_t ndim, const int64_t* host_shape,
+                                  int gran, int32_t axis, int64_t group_size, const double* scale,
+                                  double* dq, void* stream);
 
 /* ===================================================================== */
 /* FP8 E4M3 blocks ([S] Fp8BlockGemm, Fp8BlockDequant)                    */

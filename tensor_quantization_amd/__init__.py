@@ -82,6 +82,10 @@ _SIGS = {
     "tq_quant_mxfp8": ([_P, _I, _I64, _I64, _P, _P, _P], _I),
     "tq_quant_fp8_per_tensor": ([_P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
     "tq_dequant_fp8_per_tensor": ([_P, _I64, _P, _P, _I, _P], _I),
+    "tq_quant_f64": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "tq_dequant_f64": ([_P, _I, _I32, _SHAPE, _I, _I32, _I64, _P, _P, _P, _P], _I),
+    "tq_quant_f64_backward": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
+    "tq_dequant_f64_backward": ([_P, _I32, _SHAPE, _I, _I32, _I64, _P, _P, _P], _I),
     "tq_dequant_mxfp8": ([_P, _P, _I64, _I64, _P, _I, _P], _I),
     "tq_quant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
     "tq_dequant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P], _I),
@@ -615,3 +619,75 @@ def tq_dequant_fp8_per_tensor(q, scale, out_dtype=torch.bfloat16):
     _call("tq_dequant_fp8_per_tensor", _ptr(q.contiguous()), q.numel(), _ptr(scale), _ptr(y), FTYPE[out_dtype],
           _stream(q.device))
     return y
+
+
+# ------------------------------------------------------------ binary64 inputs
+GRAN = {"tensor": 0, "channel": 1, "token": 2, "group": 3}
+
+
+def _f64_scale_shape(shape, gran, axis, group_size):
+    if gran == "tensor":
+        return (1,)
+    if gran == "token":
+        rows = 1
+        for d in shape[:-1]:
+            rows *= int(d)
+        return (rows,)
+    if gran == "channel":
+        return (shape[axis],)
+    return _scale_shape(shape, axis, group_size)
+
+
+def _f64(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float64:
+        raise TypeError("%s must be a float64 CUDA (HIP) tensor" % name)
+    return t.contiguous()
+
+
+def tq_quant_f64(x, gran="token", axis=0, group_size=0, code="s8", qmin=None, qmax=None, symmetric=True,
+                 scale=None, zero_point=None):
+    """Binary64 quantize; returns (q, scale float64, zero_point or None)."""
+    x = _f64(x, "x")
+    qmin, qmax = _range(code, qmin, qmax, symmetric)
+    sshape = _f64_scale_shape(tuple(x.shape), gran, axis, group_size)
+    q = torch.empty(_packed_shape(x.shape, code), dtype=torch.uint8, device=x.device)
+    static = scale is not None
+    s = (scale.to(device=x.device, dtype=torch.float64).reshape(sshape).contiguous() if static
+         else torch.empty(sshape, dtype=torch.float64, device=x.device))
+    z = None
+    if not symmetric:
+        z = (zero_point.to(device=x.device, dtype=_zp_dtype(code)).reshape(sshape).contiguous() if static
+             else torch.empty(sshape, dtype=_zp_dtype(code), device=x.device))
+    shp, nd = _shape(x.shape)
+    ws = torch.empty(max(1, tq_workspace_bytes(3, x.numel())), dtype=torch.uint8, device=x.device)
+    _call("tq_quant_f64", _ptr(x), nd, shp, GRAN[gran], axis, group_size, CODE[code], qmin, qmax, int(static),
+          _ptr(q), _ptr(s), _ptr(z), _ptr(ws), ws.numel(), _stream(x.device))
+    return q, s, z
+
+
+def tq_dequant_f64(q, shape, scale, zero_point=None, gran="token", axis=0, group_size=0, code="s8"):
+    y = torch.empty(tuple(shape), dtype=torch.float64, device=q.device)
+    shp, nd = _shape(shape)
+    _call("tq_dequant_f64", _ptr(q.contiguous()), CODE[code], nd, shp, GRAN[gran], axis, group_size, _ptr(scale),
+          _ptr(zero_point), _ptr(y), _stream(q.device))
+    return y
+
+
+def tq_quant_f64_backward(x, dy, scale, zero_point=None, gran="token", axis=0, group_size=0, code="s8", qmin=None,
+                          qmax=None):
+    x, dy = _f64(x, "x"), _f64(dy, "dy")
+    qmin, qmax = _range(code, qmin, qmax, zero_point is None)
+    dx = torch.empty_like(x)
+    shp, nd = _shape(x.shape)
+    _call("tq_quant_f64_backward", _ptr(x), nd, shp, GRAN[gran], axis, group_size, CODE[code], qmin, qmax,
+          _ptr(scale), _ptr(zero_point), _ptr(dy), _ptr(dx), _stream(x.device))
+    return dx
+
+
+def tq_dequant_f64_backward(dy, scale, gran="token", axis=0, group_size=0):
+    dy = _f64(dy, "dy")
+    dq = torch.empty_like(dy)
+    shp, nd = _shape(dy.shape)
+    _call("tq_dequant_f64_backward", _ptr(dy), nd, shp, GRAN[gran], axis, group_size, _ptr(scale), _ptr(dq),
+          _stream(dy.device))
+    return dq

@@ -108,4 +108,46 @@ inline GroupMap token_map(int64_t rows, int64_t cols)
     return m;
 }
 
+// Device copy of a group layout: group id of element e, group size, and the
+// j-th element of group gid (index arithmetic for any layout).
+struct DMap {
+    int kind;
+    int64_t outer, A, inner, g, numel;
+
+    __device__ int64_t group_of(int64_t e) const
+    {
+        if (kind == KIND_TENSOR) return 0;
+        const int64_t a = (e / inner) % A;
+        if (kind == KIND_CHANNEL) return a;
+        const int64_t i = e % inner, o = e / (inner * A);
+        return (o * (A / g) + a / g) * inner + i;
+    }
+    __device__ int64_t count() const
+    {
+        if (kind == KIND_TENSOR) return numel;
+        if (kind == KIND_CHANNEL) return outer * inner;
+        return g;
+    }
+    __device__ int64_t elem(int64_t gid, int64_t j) const
+    {
+        if (kind == KIND_TENSOR) return j;
+        if (kind == KIND_CHANNEL) return (j / inner) * A * inner + gid * inner + j % inner;
+        const int64_t i = gid % inner, t = gid / inner;
+        const int64_t ab = t % (A / g), o = t / (A / g);
+        return (o * A + ab * g + j) * inner + i;
+    }
+};
+
+inline DMap to_dmap(const GroupMap& m)
+{
+    DMap d;
+    d.kind = m.kind;
+    d.outer = m.outer;
+    d.A = m.A;
+    d.inner = m.inner;
+    d.g = m.g;
+    d.numel = m.numel;
+    return d;
+}
+
 }  // namespace tq

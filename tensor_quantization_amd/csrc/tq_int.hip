@@ -372,46 +372,6 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void* __restrict__ x, 
 }
 
 // ------------------------------------------------------------ generic
-struct DMap {
-    int kind;
-    int64_t outer, A, inner, g, numel;
-
-    __device__ int64_t group_of(int64_t e) const
-    {
-        if (kind == KIND_TENSOR) return 0;
-        const int64_t a = (e / inner) % A;
-        if (kind == KIND_CHANNEL) return a;
-        const int64_t i = e % inner, o = e / (inner * A);
-        return (o * (A / g) + a / g) * inner + i;
-    }
-    __device__ int64_t count() const
-    {
-        if (kind == KIND_TENSOR) return numel;
-        if (kind == KIND_CHANNEL) return outer * inner;
-        return g;
-    }
-    __device__ int64_t elem(int64_t gid, int64_t j) const
-    {
-        if (kind == KIND_TENSOR) return j;
-        if (kind == KIND_CHANNEL) return (j / inner) * A * inner + gid * inner + j % inner;
-        const int64_t i = gid % inner, t = gid / inner;
-        const int64_t ab = t % (A / g), o = t / (A / g);
-        return (o * A + ab * g + j) * inner + i;
-    }
-};
-
-static DMap to_dmap(const GroupMap& m)
-{
-    DMap d;
-    d.kind = m.kind;
-    d.outer = m.outer;
-    d.A = m.A;
-    d.inner = m.inner;
-    d.g = m.g;
-    d.numel = m.numel;
-    return d;
-}
-
 // Block-wide max of a non-negative value and min of a non-positive value.
 __device__ __forceinline__ void block_minmax(float& mn, float& mx)
 {
@@ -1317,6 +1277,7 @@ size_t tq_workspace_bytes(int op, int64_t numel)
     if (op == 0) return numel <= 65536 ? 0 : 2 * 1024 * sizeof(float);
     if (op == 1) return 1024 * sizeof(float);
     if (op == 2) return numel <= 65536 ? 0 : 1024 * sizeof(float);
+    if (op == 3) return numel <= 0 ? 0 : 2 * 1024 * sizeof(double);
     return 0;
 }
 
