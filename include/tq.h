@@ -46,7 +46,8 @@
  *     on `stream` and returns without synchronizing.  A non-TQ_OK return
  *     means nothing was enqueued, except TQ_ERR_HIP, which reports a launch
  *     failure (hipGetLastError) after an enqueue attempt.
- *   - Tensors are dense, row-major and contiguous.  Base pointers must be
+ *   - Tensors are dense, row-major and contiguous (the *_strided calls take a
+ *     row stride for their input).  Base pointers must be
  *     16-byte aligned (TQ_ERR_ALIGN otherwise); scale / zero-point arrays need
  *     only their natural alignment.
  *   - Float tensors have a tq_ftype (f32, f16, bf16); arithmetic is IEEE
@@ -156,6 +157,16 @@ tq_status tq_quant_per_channel(const void* x, int x_dtype, int32_t ndim, const i
 tq_status tq_quant_per_token(const void* x, int x_dtype, int64_t rows, int64_t cols,
                              int code, int32_t qmin, int32_t qmax,
                              void* q, float* scale, void* zero_point, void* stream);
+
+/* Per-token quantize of a row-strided input: row r of x starts x_row_stride
+ * elements after row r-1 (x_row_stride >= cols; a column slice of a wider
+ * matrix); q, scale and zero_point are dense as in tq_quant_per_token, and
+ * the results are those of tq_quant_per_token on the dense rows.  Needs
+ * cols % 8 == 0 (TQ_ERR_UNSUPPORTED otherwise) and 16-byte aligned rows:
+ * x aligned, cols and x_row_stride multiples of 16 bytes (TQ_ERR_ALIGN). */
+tq_status tq_quant_per_token_strided(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                     int64_t x_row_stride, int code, int32_t qmin, int32_t qmax,
+                                     void* q, float* scale, void* zero_point, void* stream);
 
 tq_status tq_quant_per_group(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape,
                              int32_t axis, int64_t group_size, int code, int32_t qmin, int32_t qmax,
@@ -295,6 +306,15 @@ tq_status tq_dequant_f64_backward(const double* dy, int32_t ndim, const int64_t*
 tq_status tq_quant_fp8_block(const void* x, int x_dtype, int64_t rows, int64_t cols,
                              int32_t block_rows, int32_t block_cols,
                              uint8_t* q, float* scale, void* stream);
+/* FP8 1 x block_cols quantize of a row-strided input (row r starts
+ * x_row_stride elements after row r-1, x_row_stride >= cols); q and scale are
+ * dense ([rows, cols] and [rows, cols/block_cols]) and equal those of
+ * tq_quant_fp8_block(…, 1, block_cols, …) on the dense rows.  block_cols is
+ * 16, 32, 64, 128, 256 or 512 (TQ_ERR_UNSUPPORTED otherwise) and must divide
+ * cols; rows need 16-byte alignment as for tq_quant_per_token_strided. */
+tq_status tq_quant_fp8_rows_strided(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                    int64_t x_row_stride, int32_t block_cols, uint8_t* q,
+                                    float* scale, void* stream);
 /* y = val(q) * scale, rounded once to y_dtype. */
 tq_status tq_dequant_fp8_block(const uint8_t* q, int64_t rows, int64_t cols,
                                int32_t block_rows, int32_t block_cols, const float* scale,

@@ -82,6 +82,8 @@ _SIGS = {
     "tq_quant_mxfp8": ([_P, _I, _I64, _I64, _P, _P, _P], _I),
     "tq_quant_fp8_per_tensor": ([_P, _I, _I64, _I, _P, _P, _P, _SZ, _P], _I),
     "tq_dequant_fp8_per_tensor": ([_P, _I64, _P, _P, _I, _P], _I),
+    "tq_quant_per_token_strided": ([_P, _I, _I64, _I64, _I64, _I, _I32, _I32, _P, _P, _P, _P], _I),
+    "tq_quant_fp8_rows_strided": ([_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P], _I),
     "tq_quant_f64": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "tq_dequant_f64": ([_P, _I, _I32, _SHAPE, _I, _I32, _I64, _P, _P, _P, _P], _I),
     "tq_quant_f64_backward": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
@@ -691,3 +693,33 @@ def tq_dequant_f64_backward(dy, scale, gran="token", axis=0, group_size=0):
     _call("tq_dequant_f64_backward", _ptr(dy), nd, shp, GRAN[gran], axis, group_size, _ptr(scale), _ptr(dq),
           _stream(dy.device))
     return dq
+
+
+# ------------------------------------------------------------ row-strided inputs
+def _row_strided(x, name):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise TypeError("%s must be a 2-D CUDA (HIP) tensor with unit column stride" % name)
+    _ft(x)
+    return x
+
+
+def tq_quant_per_token_strided(x, code="s8", qmin=None, qmax=None, symmetric=True):
+    """Per-token quantize of a 2-D view whose rows are strided (e.g. a column
+    slice); the view is read in place."""
+    x = _row_strided(x, "x")
+    qmin, qmax = _range(code, qmin, qmax, symmetric)
+    rows, cols = x.shape
+    q, s, z = _outputs(x, code, (rows,), symmetric)
+    _call("tq_quant_per_token_strided", _ptr(x), _ft(x), rows, cols, x.stride(0), CODE[code], qmin, qmax, _ptr(q),
+          _ptr(s), _ptr(z), _stream(x.device))
+    return q, s, z
+
+
+def tq_quant_fp8_rows_strided(x, block_cols=128):
+    x = _row_strided(x, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, cols // block_cols), dtype=torch.float32, device=x.device)
+    _call("tq_quant_fp8_rows_strided", _ptr(x), _ft(x), rows, cols, x.stride(0), block_cols, _ptr(q), _ptr(s),
+          _stream(x.device))
+    return q, s

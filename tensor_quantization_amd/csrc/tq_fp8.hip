@@ -62,9 +62,11 @@ __device__ __forceinline__ uint2 fp8_enc8(const float v[8], const FP& p)
 // ------------------------------------------------------------ 1 x bc rows
 // Blocks of L = 8*T*W contiguous elements: lane j of a team of T holds
 // vectors w*T + j, so a team's load instruction reads 16*T contiguous bytes.
-template <int FT, int T, int W, int U>
-__global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, int64_t nblocks,
-                                                  uint8_t* __restrict__ q, float* __restrict__ scale)
+// STRIDED: input rows start every ldx elements (nbc blocks per row); codes
+// and scales stay dense.
+template <int FT, int T, int W, int U, bool STRIDED = false>
+__global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, int64_t nblocks, int64_t nbc,
+                                                  int64_t ldx, uint8_t* __restrict__ q, float* __restrict__ scale)
 {
     constexpr int P = 64 / T;
     constexpr int64_t L = 8 * T * W;
@@ -78,7 +80,8 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, in
         const int64_t g = g0 + (int64_t)u * P;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            if (g < nblocks) raw[u][w] = load8<FT, (T >= 8)>(x, g * L + (w * T + j) * 8);
+            const int64_t xb = STRIDED ? (g / nbc) * ldx + (g % nbc) * L : g * L;
+            if (g < nblocks) raw[u][w] = load8<FT, (T >= 8)>(x, xb + (w * T + j) * 8);
             else raw[u][w] = Raw8<FT>{};
         }
     }
@@ -462,12 +465,34 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     }
 
 template <int FT, int T, int W, int U>
-static void launch_rows(const void* x, int64_t nblocks, uint8_t* q, float* scale, hipStream_t st)
+static void launch_rows(const void* x, int64_t nblocks, uint8_t* q, float* scale, hipStream_t st, int64_t nbc = 1,
+                        int64_t ldx = 0)
 {
     constexpr int P = 64 / T;
     const int64_t waves = cdiv(nblocks, (int64_t)U * P);
-    hipLaunchKernelGGL((k_fp8_rows<FT, T, W, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st, x, nblocks, q,
-                       scale);
+    if (ldx)
+        hipLaunchKernelGGL((k_fp8_rows<FT, T, W, U, true>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st, x,
+                           nblocks, nbc, ldx, q, scale);
+    else
+        hipLaunchKernelGGL((k_fp8_rows<FT, T, W, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st, x, nblocks,
+                           nbc, ldx, q, scale);
+}
+
+// 1 x bc blocks of a row-strided input (ldx elements between row starts).
+template <int FT>
+static bool quant_rows_strided(const void* x, int64_t rows, int64_t cols, int64_t ldx, int64_t bc, uint8_t* q,
+                               float* scale, hipStream_t st)
+{
+    const int64_t nbc = cols / bc, nb = rows * nbc;
+    switch (bc) {
+    case 16: launch_rows<FT, 2, 1, 8>(x, nb, q, scale, st, nbc, ldx); return true;
+    case 32: launch_rows<FT, 4, 1, 8>(x, nb, q, scale, st, nbc, ldx); return true;
+    case 64: launch_rows<FT, 8, 1, 8>(x, nb, q, scale, st, nbc, ldx); return true;
+    case 128: launch_rows<FT, 8, 2, 1>(x, nb, q, scale, st, nbc, ldx); return true;
+    case 256: launch_rows<FT, 16, 2, 4>(x, nb, q, scale, st, nbc, ldx); return true;
+    case 512: launch_rows<FT, 64, 1, 8>(x, nb, q, scale, st, nbc, ldx); return true;
+    default: return false;
+    }
 }
 
 template <int FT>
@@ -706,6 +731,23 @@ tq_status tq_dequant_fp8_per_tensor(const uint8_t* q, int64_t numel, const float
     if (!q || !scale || !y) return TQ_ERR_INVALID;
     if (!aligned16(q) || !aligned16(y)) return TQ_ERR_ALIGN;
     return fp8_elementwise<OP_DEQ>(q, nullptr, y_dtype, 1, numel, 1, numel, scale, y, as_stream(stream));
+}
+
+tq_status tq_quant_fp8_rows_strided(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+                                    int32_t block_cols, uint8_t* q, float* scale, void* stream)
+{
+    if (!valid_ftype(x_dtype) || rows < 0 || cols < 0 || block_cols <= 0 || x_row_stride < cols)
+        return TQ_ERR_INVALID;
+    if (cols % block_cols) return TQ_ERR_INVALID;
+    if (rows == 0 || cols == 0) return TQ_OK;
+    if (!x || !q || !scale) return TQ_ERR_INVALID;
+    const int es = ftype_size(x_dtype);
+    if (!aligned16(x) || !aligned16(q) || (x_row_stride * es) % 16 || (cols * es) % 16) return TQ_ERR_ALIGN;
+    bool done = false;
+    TQ_FT_SWITCH(x_dtype, done = quant_rows_strided<FTV>(x, rows, cols, x_row_stride, block_cols, q, scale,
+                                                         as_stream(stream)));
+    if (!done) return TQ_ERR_UNSUPPORTED;
+    return launch_status();
 }
 
 }  // extern "C"

@@ -105,8 +105,8 @@ __device__ __forceinline__ void store_fake8(void* y, int64_t e, const float c[8]
 // holds vectors w*T + j (w < W) of its group, so each load instruction of a
 // team reads 16*T contiguous bytes; a wave runs U rounds of 64/T groups.
 template <int FT, int BITS, bool SYM, int T, int W, int U>
-__global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, int64_t G, float qmin,
-                                                    float qmax, float yc, uint8_t* __restrict__ q,
+__global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, int64_t G, int64_t ldx,
+                                                    float qmin, float qmax, float yc, uint8_t* __restrict__ q,
                                                     float* __restrict__ scale, uint8_t* __restrict__ zp)
 {
     constexpr int P = 64 / T;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
         const int64_t g = g0 + (int64_t)u * P;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            if (g < G) raw[u][w] = load8<FT, (T >= 8)>(x, g * L + (int64_t)(w * T + j) * 8);
+            if (g < G) raw[u][w] = load8<FT, (T >= 8)>(x, g * ldx + (int64_t)(w * T + j) * 8);
             else raw[u][w] = Raw8<FT>{};
         }
     }
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
 // loads in flight; the group max / min goes through DPP within a wave and
 // LDS across the NW waves.
 template <int FT, int BITS, bool SYM, int NW, int W>
-__global__ __launch_bounds__(64 * NW) void k_quant_rows(const void* __restrict__ x, float qmin, float qmax,
-                                                        float yc, uint8_t* __restrict__ q,
+__global__ __launch_bounds__(64 * NW) void k_quant_rows(const void* __restrict__ x, int64_t ldx, float qmin,
+                                                        float qmax, float yc, uint8_t* __restrict__ q,
                                                         float* __restrict__ scale, uint8_t* __restrict__ zp)
 {
     constexpr int NT = 64 * NW;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64 * NW) void k_quant_rows(const void* __restrict__
     const int t = threadIdx.x;
     Raw8<FT> raw[W];
 #pragma unroll
-    for (int w = 0; w < W; ++w) raw[w] = load8<FT, true>(x, g * L + (int64_t)(w * NT + t) * 8);
+    for (int w = 0; w < W; ++w) raw[w] = load8<FT, true>(x, g * ldx + (int64_t)(w * NT + t) * 8);
     float v[W][8];
     float mn = 0.0f, mx = 0.0f;
 #pragma unroll
@@ -251,14 +251,15 @@ __global__ __launch_bounds__(64 * NW) void k_quant_rows(const void* __restrict__
 // (reduce, then encode) in 4-vector strides per lane.
 template <int FT, int BITS, bool SYM>
 __global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, int64_t G, int64_t L,
-                                                    float qmin, float qmax, float yc, uint8_t* __restrict__ q,
-                                                    float* __restrict__ scale, uint8_t* __restrict__ zp)
+                                                    int64_t ldx, float qmin, float qmax, float yc,
+                                                    uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                    uint8_t* __restrict__ zp)
 {
     const int lane = threadIdx.x & 63;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (g >= G) return;
     const int64_t nvec = L / 8;
-    const int64_t base = g * L;
+    const int64_t base = g * ldx;      // input row; codes go to g * L
     float a = 0.0f, mn = 0.0f, mx = 0.0f;
     for (int64_t v0 = lane; v0 < nvec; v0 += 256) {
         Raw8<FT> raw[4];
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(256) void k_quant_long(const void* __restrict__ x, 
             widen8<FT>(raw[k], v);
             if (p.fast) enc8<FT, true, !SYM>(v, p, lo, hi, c);
             else enc8<FT, false, !SYM>(v, p, lo, hi, c);
-            store_codes8<BITS, true>(q, base + (v0 + k * 64) * 8, c);
+            store_codes8<BITS, true>(q, g * L + (v0 + k * 64) * 8, c);
         }
     }
     if (lane == 0) {
@@ -959,13 +960,13 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     else { constexpr int BV = 4; constexpr bool SV = false; __VA_ARGS__; }
 
 template <int FT, int BITS, bool SYM, int T, int W, int U>
-static void launch_team(const void* x, int64_t G, float qmin, float qmax, float yc, uint8_t* q, float* scale,
-                        uint8_t* zp, hipStream_t st)
+static void launch_team(const void* x, int64_t G, int64_t ldx, float qmin, float qmax, float yc, uint8_t* q,
+                        float* scale, uint8_t* zp, hipStream_t st)
 {
     constexpr int P = 64 / T;
     const int64_t waves = cdiv(G, (int64_t)U * P);
     hipLaunchKernelGGL((k_quant_team<FT, BITS, SYM, T, W, U>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, st,
-                       x, G, qmin, qmax, yc, q, scale, zp);
+                       x, G, ldx, qmin, qmax, yc, q, scale, zp);
 }
 
 // Contiguous groups of length L (L % 8 == 0), G groups.  Teams of at least
@@ -973,42 +974,43 @@ static void launch_team(const void* x, int64_t G, float qmin, float qmax, float 
 // 8 lanes x 2 vectors so the per-group scale arithmetic is shared by 16
 // elements per lane.
 template <int FT, int BITS, bool SYM>
-static void quant_contig(const void* x, int64_t G, int64_t L, float qmin, float qmax, float yc, uint8_t* q,
-                         float* scale, uint8_t* zp, hipStream_t st)
+static void quant_contig(const void* x, int64_t G, int64_t L, int64_t ldx, float qmin, float qmax, float yc,
+                         uint8_t* q, float* scale, uint8_t* zp, hipStream_t st)
 {
     switch (L) {
-    case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
-    case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
-    case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
+    case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
+    case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
 #ifndef TQ_G128_U
 #define TQ_G128_U 1
 #endif
 #ifndef TQ_G128_T
 #define TQ_G128_T 8
 #endif
-    case 128: launch_team<FT, BITS, SYM, TQ_G128_T, 16 / TQ_G128_T, TQ_G128_U>(x, G, qmin, qmax, yc, q, scale, zp, st);
+    case 128: launch_team<FT, BITS, SYM, TQ_G128_T, 16 / TQ_G128_T, TQ_G128_U>(x, G, ldx, qmin, qmax, yc, q, scale, zp,
+                                                                             st);
         return;
-    case 256: launch_team<FT, BITS, SYM, 16, 2, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
-    case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
-    case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
-    case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, qmin, qmax, yc, q, scale, zp, st); return;
+    case 256: launch_team<FT, BITS, SYM, 16, 2, 4>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
+    case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
+    case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
+    case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
 #ifndef TQ_ROW4096
 #define TQ_ROW4096 4
 #endif
     case 4096:
         if (TQ_ROW4096 == 4 && G <= 0x7fffffff) {
-            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 4, 2>), dim3((unsigned)G), dim3(256), 0, st, x, qmin, qmax,
-                               yc, q, scale, zp);
+            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 4, 2>), dim3((unsigned)G), dim3(256), 0, st, x, ldx, qmin,
+                               qmax, yc, q, scale, zp);
         } else if (TQ_ROW4096 == 8 && G <= 0x7fffffff) {
-            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 8, 1>), dim3((unsigned)G), dim3(512), 0, st, x, qmin, qmax,
-                               yc, q, scale, zp);
+            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 8, 1>), dim3((unsigned)G), dim3(512), 0, st, x, ldx, qmin,
+                               qmax, yc, q, scale, zp);
         } else {
-            launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, qmin, qmax, yc, q, scale, zp, st);
+            launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st);
         }
         return;
     default:
         hipLaunchKernelGGL((k_quant_long<FT, BITS, SYM>), dim3((unsigned)cdiv(G, 4)), dim3(256), 0, st,
-                           x, G, L, qmin, qmax, yc, q, scale, zp);
+                           x, G, L, ldx, qmin, qmax, yc, q, scale, zp);
     }
 }
 
@@ -1037,7 +1039,7 @@ static tq_status quant_mapped(const void* x, int xt, const GroupMap& m, int code
     if (m.kind == KIND_GROUP && m.inner == 1) { L = m.g; G = m.ngroups; }
     if (m.kind == KIND_CHANNEL && m.outer == 1) { L = m.inner; G = m.A; }
     if (L > 0 && L % 8 == 0 && (L * es) % 16 == 0) {
-        TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym, quant_contig<FTV, BV, SV>(x, G, L, fmin, fmax, yc, qb, scale, zb, st)));
+        TQ_FT_SWITCH(xt, TQ_BITS_SYM_SWITCH(bits, sym, quant_contig<FTV, BV, SV>(x, G, L, L, fmin, fmax, yc, qb, scale, zb, st)));
         return launch_status();
     }
     // column groups: per-channel on the last axis, per-group on a non-last axis
@@ -1242,6 +1244,27 @@ tq_status tq_quant_per_token(const void* x, int x_dtype, int64_t rows, int64_t c
     if (s || rows == 0) return s;
     return quant_mapped(x, x_dtype, token_map(rows, cols), code, qmin, qmax, q, scale, zero_point,
                         as_stream(stream));
+}
+
+tq_status tq_quant_per_token_strided(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+                                     int code, int32_t qmin, int32_t qmax, void* q, float* scale, void* zero_point,
+                                     void* stream)
+{
+    if (rows < 0 || cols < 0 || (rows > 0 && cols == 0) || x_row_stride < cols) return TQ_ERR_INVALID;
+    tq_status s = check_quant_args(x, x_dtype, code, qmin, qmax, q, scale, zero_point, cols, rows * cols);
+    if (s || rows == 0) return s;
+    const int es = ftype_size(x_dtype);
+    if (cols % 8) return TQ_ERR_UNSUPPORTED;
+    if ((cols * es) % 16 || (x_row_stride * es) % 16) return TQ_ERR_ALIGN;
+    const bool sym = zero_point == nullptr;
+    const int bits = code_bits(code);
+    const float fmin = (float)qmin, fmax = (float)qmax, yc = range_reciprocal(qmin, qmax, sym);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    uint8_t* zb = static_cast<uint8_t*>(zero_point);
+    hipStream_t st = as_stream(stream);
+    TQ_FT_SWITCH(x_dtype, TQ_BITS_SYM_SWITCH(bits, sym, quant_contig<FTV, BV, SV>(x, rows, cols, x_row_stride, fmin,
+                                                                                   fmax, yc, qb, scale, zb, st)));
+    return launch_status();
 }
 
 tq_status tq_quant_per_channel(const void* x, int x_dtype, int32_t ndim, const int64_t* host_shape, int32_t axis,
