@@ -289,10 +289,19 @@ __device__ __forceinline__ float with_sign_of(float q, float x)
 // contiguous and aligned in the wave: DPP quad permutes and row mirrors
 // within a 16-lane row, ds_bpermute-based shuffles across rows.  Every lane
 // of the team ends with the team's result.
+//
+// The reductions run on bit patterns.  Every team_max caller reduces values
+// >= 0, whose unsigned order is their float order; every team_min caller
+// reduces values <= 0 (a minimum that starts at 0), whose float minimum is
+// the unsigned maximum (sign bit set, larger magnitude wins; -0 may win over
+// +0, which no caller can tell apart).  An integer max needs no NaN
+// canonicalization and fuses with the DPP move into one instruction.
+// Every control used here reads a valid lane for every lane, so the old
+// value is irrelevant (bound_ctrl) and the move folds into the max.
 template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
-    return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), CTRL, 0xf, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true);
 }
 
 constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -301,27 +310,29 @@ constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_MIRROR = 0x140;
 
 template <int T>
-__device__ __forceinline__ float team_max(float v)
+__device__ __forceinline__ uint32_t team_umax(uint32_t u)
 {
-    if constexpr (T >= 2) v = __builtin_fmaxf(v, dpp<DPP_XOR1>(v));
-    if constexpr (T >= 4) v = __builtin_fmaxf(v, dpp<DPP_XOR2>(v));
-    if constexpr (T >= 8) v = __builtin_fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
-    if constexpr (T >= 16) v = __builtin_fmaxf(v, dpp<DPP_MIRROR>(v));
-    if constexpr (T >= 32) v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
-    if constexpr (T >= 64) v = __builtin_fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    if constexpr (T >= 2) u = max(u, dpp<DPP_XOR1>(u));
+    if constexpr (T >= 4) u = max(u, dpp<DPP_XOR2>(u));
+    if constexpr (T >= 8) u = max(u, dpp<DPP_HALF_MIRROR>(u));
+    if constexpr (T >= 16) u = max(u, dpp<DPP_MIRROR>(u));
+    if constexpr (T >= 32) u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+    if constexpr (T >= 64) u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+    return u;
 }
 
+// max over the team of values >= 0
+template <int T>
+__device__ __forceinline__ float team_max(float v)
+{
+    return as_f(team_umax<T>(as_u(v)));
+}
+
+// min over the team of values <= 0
 template <int T>
 __device__ __forceinline__ float team_min(float v)
 {
-    if constexpr (T >= 2) v = __builtin_fminf(v, dpp<DPP_XOR1>(v));
-    if constexpr (T >= 4) v = __builtin_fminf(v, dpp<DPP_XOR2>(v));
-    if constexpr (T >= 8) v = __builtin_fminf(v, dpp<DPP_HALF_MIRROR>(v));
-    if constexpr (T >= 16) v = __builtin_fminf(v, dpp<DPP_MIRROR>(v));
-    if constexpr (T >= 32) v = __builtin_fminf(v, __shfl_xor(v, 16, 64));
-    if constexpr (T >= 64) v = __builtin_fminf(v, __shfl_xor(v, 32, 64));
-    return v;
+    return as_f(team_umax<T>(as_u(v)));
 }
 
 // ---------------------------------------------------------------- codes
