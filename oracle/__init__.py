@@ -595,3 +595,21 @@ def dequant_f64_backward(dy, gran, axis=0, group_size=0, scale=None):
     if rc:
         raise ValueError("oracle rejected dequant_f64_backward arguments")
     return dq
+
+
+# ----------------------------------------------------------------- FP8 block GEMM
+def fp8_block_gemm(qa, sa, qw, sw):
+    """qa [M, K] E4M3, sa [M, K/128] f32, qw [N, K] E4M3, sw [N/128, K/128] f32.
+    Returns (y [M, N] float64, yabs [M, N] float64)."""
+    qa = np.ascontiguousarray(qa, np.uint8)
+    qw = np.ascontiguousarray(qw, np.uint8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = np.zeros((M, N), np.float64)
+    ya = np.zeros((M, N), np.float64)
+    rc = lib().orc_fp8_block_gemm(_p(qa), _p(np.ascontiguousarray(sa, np.float32)), _p(qw),
+                                  _p(np.ascontiguousarray(sw, np.float32)), ctypes.c_int64(M), ctypes.c_int64(N),
+                                  ctypes.c_int64(K), _p(y), _p(ya))
+    if rc:
+        raise ValueError("oracle rejected fp8_block_gemm arguments")
+    return y, ya

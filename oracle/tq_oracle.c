@@ -1001,3 +1001,37 @@ int orc_dequant_f64_backward(const double* dy, int ndim, const int64_t* shape, i
     for (int64_t e = 0; e < G.numel; ++e) dq[e] = dy[e] * scale[group_of(&G, e)];
     return ORC_OK;
 }
+
+/* ------------------------------------------------ FP8 block GEMM */
+/* smile.llm.quant Fp8BlockGemm: activations in E4M3 with one fp32 scale per
+ * 1 x 128 group, weights in E4M3 with one fp32 scale per 128 x 128 tile;
+ * out = x W^T.  With qa [M, K], sa [M, K/128], qw [N, K], sw [N/128, K/128]:
+ *   y[m][n] = sum over K-blocks kb of (sa[m][kb] * sw[n/128][kb]) *
+ *             sum_{k in kb} val(qa[m][k]) * val(qw[n][k])
+ * evaluated in binary64 (each block's sum of fp8 products is exact there).
+ * yabs receives the same sum with every product and scale taken in magnitude
+ * (the scale of the rounding error of any binary32 evaluation order). */
+int orc_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, int64_t M, int64_t N,
+                       int64_t K, double* y, double* yabs)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 128 || N % 128) return ORC_BAD;
+    int64_t nkb = K / 128;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t kb = 0; kb < nkb; ++kb) {
+                double s = 0.0, sabs = 0.0;
+                for (int64_t k = kb * 128; k < kb * 128 + 128; ++k) {
+                    double p = (double)orc_dec_e4m3(qa[m * K + k]) * (double)orc_dec_e4m3(qw[n * K + k]);
+                    s += p;
+                    sabs += fabs(p);
+                }
+                double c = (double)sa[m * nkb + kb] * (double)sw[(n / 128) * nkb + kb];
+                acc += c * s;
+                aacc += fabs(c) * sabs;
+            }
+            y[m * N + n] = acc;
+            if (yabs) yabs[m * N + n] = aacc;
+        }
+    return ORC_OK;
+}
