@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0      # dense fp8 matrix-core peak
 METRIC = "quantize GB/s (bytes in+out) & % HBM peak: per-token s8, g128 4-bit, FP4"
 
 
@@ -210,7 +211,7 @@ def breakdown(torch, tq, iters=20, only=None):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = []
 
-    def bench_op(name, cfg, nbytes, make_set, launch, set_bytes, read_bytes):
+    def bench_op(name, cfg, nbytes, make_set, launch, set_bytes, read_bytes, flops=None):
         if only and only != name:
             return
         log("breakdown:", name)
@@ -227,8 +228,13 @@ def breakdown(torch, tq, iters=20, only=None):
         torch.cuda.synchronize()
         us = 1000.0 * s_ev.elapsed_time(e_ev) / iters
         gbps = nbytes / (us * 1e-6) / 1e9
-        out.append({"op": name, "workload": cfg, "bytes": nbytes, "us": round(us, 3), "GBps": round(gbps, 1),
-                    "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        if flops is None:
+            out.append({"op": name, "workload": cfg, "bytes": nbytes, "us": round(us, 3), "GBps": round(gbps, 1),
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        else:
+            tf = flops / (us * 1e-6) / 1e12
+            out.append({"op": name, "workload": cfg, "flops": flops, "us": round(us, 3), "TFLOPs": round(tf, 1),
+                        "frac": round(tf / FP8_PEAK_TFLOPS, 4), "bound": "mfma"})
         del sets
         torch.cuda.empty_cache()
 
@@ -380,6 +386,24 @@ def breakdown(torch, tq, iters=20, only=None):
              lambda b: check(L.tq_fp4_predequant_to_fp8(P(b["p1"]), P(b["b1"]), 1.5e-5, N5, K5, 0, P(b["f8"]),
                                                         stream), "predequant"),
              8 * (pb + sbb) + n5, pb + sbb)
+
+    # block-scaled FP8 GEMM: the c4 activations [4096, 7168] (1 x 128) times the
+    # c4 weight [7168, 7168] (128 x 128), bf16 out; 2 M N K flops on the fp8 peak
+    if not only or only == "fp8_block_gemm":
+        Mg, Kg = 4096, 7168
+        Ng = Kg
+        xa = torch.from_numpy(workloads.make_input("c4_fp8_act_1x128").view(np.int16)).view(bf16).cuda()
+        xw = torch.from_numpy(workloads.make_input("c4_fp8_weight_128x128").view(np.int16)).view(bf16).cuda()
+        qa0, sa0 = tq.tq_quant_fp8_block(xa, 1, 128)
+        qw0, sw0 = tq.tq_quant_fp8_block(xw, 128, 128)
+        del xa, xw
+        mkg = lambda i: dict(qa=qa0.clone(), sa=sa0.clone(), qw=qw0.clone(), sw=sw0.clone(), y=E((Mg, Ng), bf16))
+        gb = Mg * Kg + Ng * Kg + 2 * Mg * Ng + 4 * (Mg * Kg // 128 + Ng * Kg // 16384)
+        bench_op("fp8_block_gemm", "c4 fp8 [4096,7168] x [7168,7168]^T bf16 out", gb, mkg,
+                 lambda b: check(L.tq_fp8_block_gemm(P(b["qa"]), P(b["sa"]), P(b["qw"]), P(b["sw"]), Mg, Ng, Kg,
+                                                     P(b["y"]), 2, stream), "fp8 gemm"),
+                 gb, Mg * Kg + Ng * Kg, flops=2 * Mg * Ng * Kg)
+        del qa0, sa0, qw0, sw0
     return out
 
 

@@ -15,7 +15,8 @@
  *     and their expansion to FP8 E4M3,
  *   - per-tensor fake quantization (round trip) and its backward, and
  *     dynamic-range quantization by mode and scope,
- *   - integer codes of binary64 inputs computed in binary64.
+ *   - integer codes of binary64 inputs computed in binary64,
+ *   - the block-scaled FP8 GEMM that consumes the FP8 activations and weights.
  *
  * Sources (page titles and sections):
  *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
@@ -362,6 +363,28 @@ tq_status tq_quant_mxfp8_backward(const void* x, int x_dtype, const uint8_t* blo
 /* dq = dy * X. */
 tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t* block_scale,
                                     int64_t rows, int64_t k, void* dq, void* stream);
+
+/* Block-scaled FP8 GEMM ([S] Fp8BlockGemm: activations E4M3 with one fp32
+ * scale per 1 x 128 group, weights E4M3 with one fp32 scale per 128 x 128
+ * tile; out = x W^T).  qa [M, K] with sa [M, K/128] (tq_quant_fp8_block with
+ * 1 x 128 blocks), qw [N, K] with sw [N/128, K/128] (128 x 128 blocks):
+ *   y[m][n] = sum_kb (sa[m][kb] * sw[n/128][kb]) *
+ *             sum_{k in kb} val(qa[m][k]) * val(qw[n][k])
+ * computed on the matrix cores: each 128-wide K block is two E4M3 matrix-core
+ * steps of 64 products; the block sum is scaled by sa * sw and accumulated in
+ * binary32, and the total is rounded once to y_dtype (y is [M, N]).  The
+ * matrix core does not add exactly: within each group of 8 consecutive K it
+ * cuts every product toward zero to a multiple of 2^(E - 13), E the group's
+ * largest operand exponent sum, and it keeps about 24 bits when it combines
+ * the group sums and converts toward zero.  So the result is within
+ * sum_kb |sa sw| (those cuts) + about 2^-18 of the magnitude sum
+ * sum |sa sw val val| of the exact value, not bit-equal to it.  K and N
+ * multiples of 128 (TQ_ERR_INVALID otherwise), M a multiple of 128
+ * (TQ_ERR_UNSUPPORTED otherwise); qa, qw 16-byte aligned.  K = 0 writes
+ * zeros (the operand pointers may then be null); M = 0 or N = 0 does
+ * nothing.  Launches only; no allocation. */
+tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                            int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* stream);
 
 /* ===================================================================== */
 /* FP4 E2M1 blocks ([W] QuantizedWeight fields; [S] MxFp8 for the E8M0 rule) */

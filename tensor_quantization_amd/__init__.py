@@ -84,6 +84,7 @@ _SIGS = {
     "tq_dequant_fp8_per_tensor": ([_P, _I64, _P, _P, _I, _P], _I),
     "tq_quant_per_token_strided": ([_P, _I, _I64, _I64, _I64, _I, _I32, _I32, _P, _P, _P, _P], _I),
     "tq_quant_fp8_rows_strided": ([_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P], _I),
+    "tq_fp8_block_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "tq_quant_f64": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "tq_dequant_f64": ([_P, _I, _I32, _SHAPE, _I, _I32, _I64, _P, _P, _P, _P], _I),
     "tq_quant_f64_backward": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
@@ -723,3 +724,15 @@ def tq_quant_fp8_rows_strided(x, block_cols=128):
     _call("tq_quant_fp8_rows_strided", _ptr(x), _ft(x), rows, cols, x.stride(0), block_cols, _ptr(q), _ptr(s),
           _stream(x.device))
     return q, s
+
+
+# ------------------------------------------------------------ FP8 block GEMM
+def tq_fp8_block_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16):
+    """y = x W^T from E4M3 activations qa [M, K] (scales sa [M, K/128]) and
+    E4M3 weights qw [N, K] (scales sw [N/128, K/128])."""
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=qa.device)
+    _call("tq_fp8_block_gemm", _ptr(qa.contiguous()), _ptr(sa.contiguous()), _ptr(qw.contiguous()),
+          _ptr(sw.contiguous()), M, N, K, _ptr(y), FTYPE[out_dtype], _stream(qa.device))
+    return y
