@@ -28,6 +28,10 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# per-file extras: the GEMM keeps its matrix-core results in ordinary VGPRs,
+# so the scale-and-accumulate step reads them without accumulator moves
+FILE_FLAGS = {"tq_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD) -> str:
     """Compile every csrc/*.hip and link `out`; `extra_flags` (e.g. -D tunables)
@@ -38,7 +42,7 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str 
     for s in srcs:
         o = os.path.join(build_dir, os.path.basename(s) + ".o")
         objs.append(o)
-        cmd = [HIPCC, *FLAGS, *extra_flags, "-c", s, "-o", o]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), *extra_flags, "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -4,141 +4,152 @@
 //
 //   y[m][n] = sum_kb (sa[m][kb] * sw[n/128][kb]) * sum_{k in kb} val(qa[m][k]) val(qw[n][k])
 //
-// Each 128-wide K block is one unit: its fp8 dot products come out of two
-// v_mfma_scale_f32_32x32x64_f8f6f4 steps (E8M0 operand scales fixed at 1),
-// then the block sum is scaled by sa * sw and added to the binary32 total.
-// Scaling per block keeps the matrix core's own summation short: inside a
-// step it cuts products toward zero 13 bits below the largest exponent of
-// each group of eight K, and keeps about 24 bits across groups, so its
-// error is bounded per block and never grows with K.
+// Each 128-wide K block is one unit: its fp8 dot products come out of one
+// v_mfma_scale_f32_16x16x128_f8f6f4 step per 16 x 16 tile (E8M0 operand
+// scales fixed at 1), then the block sum is scaled by sa * sw and added to
+// the binary32 total.  Scaling per block keeps the matrix core's own
+// summation short: inside a step it cuts products toward zero 13 bits below
+// the largest exponent of each group of eight consecutive K, and keeps about
+// 24 bits across groups, so its error is bounded per block and never grows
+// with K.
 //
 // k_fp8_gemm: a 256-thread workgroup owns a 128 x 128 output tile; wave w
-// computes the 64 x 64 quarter (w / 2, w % 2) as 2 x 2 MFMA tiles of 32 x 32.
-// The A and B K-slices (128 x 128 bytes each) move through double-buffered
-// LDS: the next slice is fetched into registers while the current one feeds
-// the matrix cores.  LDS rows are 128 bytes whose eight 16-byte chunks are
-// XOR-swizzled by (row % 8), so both the 8-lanes-per-row fills and the
-// 32-rows-per-instruction operand reads spread over all banks.
+// computes the 64 x 64 quarter (w / 2, w % 2) as 4 x 4 tiles of 16 x 16,
+// sixteen independent products per block, so the scale-and-accumulate of
+// one tile overlaps the products of the next.  Lane l holds row l % 16 of A
+// (column l % 16 of B) and bytes 32 (l / 16) .. + 31 of the block; result
+// element r of lane l is D[4 (l / 16) + r][l % 16], so a lane meets 16
+// distinct rows per block (16 scale products).
 //
-// MFMA lane layout (32 x 32 x 64): lane l holds row l % 32 of A (column
-// l % 32 of B) and 32 of its 64 K values -- here bytes 32 * (l / 32) ..
-// + 31 of the K step; the result element r of lane l is
-// D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
+// The A and B K-slices (128 x 128 bytes each) and the block's 128 row scales
+// move by direct global -> LDS loads (global_load_lds) into two LDS stages,
+// one block ahead; 66.5 KB of LDS and under 256 VGPRs let two workgroups
+// share a CU, so one fills the other's waits.  LDS rows are 128 bytes whose
+// eight 16-byte chunks sit at slot chunk ^ ((row / 2) % 8): sixteen
+// consecutive rows read at one chunk then cover all 64 banks.  A DMA lane
+// writes 16 bytes at (wave base + 16 * lane), so each lane fetches the
+// global chunk that the swizzle puts in its slot.  Waits and barriers are
+// explicit: before block kb is read every wave waits for its own loads, then
+// all waves meet; only after that meeting is the buffer that block kb - 1
+// used refilled.
 #include "tq_device.h"
 #include "tq_host.h"
 
 namespace tq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int GT = 128;                  // output tile and K block
 constexpr int SLICE = GT * GT;           // bytes of one operand K-slice
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * GT + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * GT + ((chunk ^ swz_key(row)) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS loads, issued from asm so that the compiler adds no
+// wait of its own for them: every lane of the wave writes `bytes` bytes at
+// M0 + bytes * lane (M0 = `lds` byte address, wave-uniform).  They count in
+// vmcnt; the kernel waits for them explicitly.  Nothing else in the kernel
+// uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, const lds_void* lds)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, const lds_void* lds)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 template <int YT>
 __global__ __launch_bounds__(256) void k_fp8_gemm(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                                   const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                                   int64_t K, int64_t N, void* __restrict__ y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][SLICE];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][SLICE];
-    __shared__ float lds_sa[2][GT];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][SLICE];
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][GT];
 
     const int t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = w >> 1, wn = w & 1;
-    const int h = lane >> 5, lr = lane & 31;
+    const int g4 = lane >> 4, l16 = lane & 15;
     const int64_t m0 = (int64_t)blockIdx.y * GT, n0 = (int64_t)blockIdx.x * GT;
     const int64_t nkb = K / GT;
-    const uint8_t* ga = qa + m0 * K;
-    const uint8_t* gb = qw + n0 * K;
     const float* gsw = sw + (n0 / GT) * nkb;
 
-    // fill: thread t moves rows t/8 + 32 i (i < 4), chunk t % 8, of both slices
-    uint4 ra[4], rb[4];
-    float rs = 0.0f;
-    auto fetch = [&](int64_t kb) {
+    const int frow = 8 * w + (lane >> 3);
+    const int fchunk = (lane & 7) ^ swz_key(frow);
+    const uint8_t* fa = qa + (m0 + frow) * K + fchunk * 16;
+    const uint8_t* fb = qw + (n0 + frow) * K + fchunk * 16;
+    const float* fs = sa + (m0 + 32 * w + (lane & 31)) * nkb;
+
+    auto issue = [&](int64_t kb) {
+        const int buf = (int)(kb & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = (t >> 3) + 32 * i;
-            ra[i] = ld16<true>(ga + row * K + kb * GT + (t & 7) * 16);
-            rb[i] = ld16<true>(gb + row * K + kb * GT + (t & 7) * 16);
+            dma16(fa + (int64_t)32 * i * K + kb * GT, (const lds_void*)&lds[buf][0][(32 * i + 8 * w) * GT]);
+            dma16(fb + (int64_t)32 * i * K + kb * GT, (const lds_void*)&lds[buf][1][(32 * i + 8 * w) * GT]);
         }
-        if (t < GT) rs = sa[(m0 + t) * nkb + kb];
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (t >> 3) + 32 * i;
-            *reinterpret_cast<uint4*>(&lds_a[buf][swz(row, t & 7)]) = ra[i];
-            *reinterpret_cast<uint4*>(&lds_b[buf][swz(row, t & 7)]) = rb[i];
-        }
-        if (t < GT) lds_sa[buf][t] = rs;
+        if (lane < 32) dma4(fs + kb, (const lds_void*)&lds_sa[buf][32 * w]);
     };
 
-    v16f acc[2][2];
+    v4f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{};
 
-    fetch(0);
-    stage(0);
-    __syncthreads();
+    issue(0);
     for (int64_t kb = 0; kb < nkb; ++kb) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kb + 1 < nkb) issue(kb + 1);
+
         const int cur = (int)(kb & 1);
-        if (kb + 1 < nkb) fetch(kb + 1);
+        const uint8_t* la = lds[cur][0];
+        const uint8_t* lb = lds[cur][1];
         const float swv = gsw[kb];
-        v16f blk[2][2];
+        v8i av[4], bv[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            v8i av[2], bv[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ar = wm * 64 + i * 32 + lr;
-                const int br = wn * 64 + i * 32 + lr;
-                const int c0 = s * 4 + h * 2;
-                const uint4 a0 = *reinterpret_cast<const uint4*>(&lds_a[cur][swz(ar, c0)]);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(&lds_a[cur][swz(ar, c0 + 1)]);
-                const uint4 b0 = *reinterpret_cast<const uint4*>(&lds_b[cur][swz(br, c0)]);
-                const uint4 b1 = *reinterpret_cast<const uint4*>(&lds_b[cur][swz(br, c0 + 1)]);
-                av[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                bv[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    blk[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        av[i], bv[j], s == 0 ? v16f{} : blk[i][j], 0, 0, 0, 127, 0, 127);
+        for (int i = 0; i < 4; ++i) {
+            const int ar = wm * 64 + i * 16 + l16;
+            const int br = wn * 64 + i * 16 + l16;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(&la[swz(ar, 2 * g4)]);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(&la[swz(ar, 2 * g4 + 1)]);
+            const uint4 b0 = *reinterpret_cast<const uint4*>(&lb[swz(br, 2 * g4)]);
+            const uint4 b1 = *reinterpret_cast<const uint4*>(&lb[swz(br, 2 * g4 + 1)]);
+            av[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            bv[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
         }
-        // total += block * (sa[row] * sw): rows of element r are 8 (r / 4) + 4 h + r % 4
+        float c[4][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 s4 = *reinterpret_cast<const float4*>(&lds_sa[cur][wm * 64 + i * 32 + 8 * g + 4 * h]);
-                const float c[4] = {s4.x * swv, s4.y * swv, s4.z * swv, s4.w * swv};
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = __builtin_fmaf(blk[i][j][4 * g + q], c[q], acc[i][j][4 * g + q]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const float4 s4 = *reinterpret_cast<const float4*>(&lds_sa[cur][wm * 64 + i * 16 + 4 * g4]);
+            c[i][0] = s4.x * swv; c[i][1] = s4.y * swv; c[i][2] = s4.z * swv; c[i][3] = s4.w * swv;
         }
-        if (kb + 1 < nkb) stage(cur ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4f blk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[i], bv[j], v4f{}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(blk[r], c[i][r], acc[i][j][r]);
+            }
     }
-    // epilogue: element r of tile (i, j) -> row m0 + 64 wm + 32 i + 8 (r/4) + 4 h + r%4, column n0 + 64 wn + 32 j + lr
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int64_t col = n0 + wn * 64 + j * 32 + lr;
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + r;
+                const int64_t col = n0 + wn * 64 + j * 16 + l16;
                 store1<YT>(y, row * N + col, acc[i][j][r]);
             }
 }
