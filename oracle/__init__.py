@@ -613,3 +613,19 @@ def fp8_block_gemm(qa, sa, qw, sw):
     if rc:
         raise ValueError("oracle rejected fp8_block_gemm arguments")
     return y, ya
+
+
+def w8a8_linear(qx, sx, qw, sw, yt):
+    """qx [M, K] s8, sx [M] f32, qw [N, K] s8, sw [N] f32 -> y [M, N] in yt
+    (f32 values, or bf16 / f16 bit patterns as uint16)."""
+    qx = np.ascontiguousarray(qx, np.int8)
+    qw = np.ascontiguousarray(qw, np.int8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = np.zeros((M, N), np.float32 if yt == "f32" else np.uint16)
+    rc = lib().orc_w8a8_linear(_p(qx), _p(np.ascontiguousarray(sx, np.float32)), _p(qw),
+                               _p(np.ascontiguousarray(sw, np.float32)), ctypes.c_int64(M), ctypes.c_int64(N),
+                               ctypes.c_int64(K), _p(y), FTYPES[yt])
+    if rc:
+        raise ValueError("oracle rejected w8a8_linear arguments")
+    return y

@@ -1035,3 +1035,29 @@ int orc_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, co
         }
     return ORC_OK;
 }
+
+/* ------------------------------------------------ W8A8 quantized linear */
+/* baracuda_kernels::quantize module list, quantized_linear: a fused W8A8
+ * quantized matmul.  The page names the operation only.  Reading: the
+ * activation codes qx [M, K] are symmetric s8 with one fp32 scale per row
+ * (the per-token quantizer's output), the weight codes qw [N, K] symmetric s8
+ * with one fp32 scale per output channel (per row of W); out = x W^T with
+ *   acc[m][n] = sum_k qx[m][k] * qw[n][k]            exact integer
+ *   y[m][n]   = ((float)acc[m][n] * sx[m]) * sw[n]   binary32, in that order
+ * rounded once more to yt.  K is limited so that every partial sum fits in
+ * 32 bits (|acc| <= 128 * 128 * K < 2^31). */
+int orc_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int64_t M, int64_t N,
+                    int64_t K, void* y, int yt)
+{
+    if (M < 0 || N < 0 || K < 0 || K > 131071 || (yt != ORC_F32 && yt != ORC_F16 && yt != ORC_BF16)) return ORC_BAD;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)qx[m * K + k] * (int64_t)qw[n * K + k];
+            float v = (float)acc;
+            v = v * sx[m];
+            v = v * sw[n];
+            store_float(y, yt, m * N + n, v);
+        }
+    return ORC_OK;
+}
