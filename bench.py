@@ -404,6 +404,23 @@ def breakdown(torch, tq, iters=20, only=None):
                                                      P(b["y"]), 2, stream), "fp8 gemm"),
                  gb, Mg * Kg + Ng * Kg, flops=2 * Mg * Ng * Kg)
         del qa0, sa0, qw0, sw0
+
+    # W8A8 quantized linear: the per-token s8 activations bf16 [8192, 4096]
+    # times the f16 weight [11008, 4096] quantized per channel to s8, bf16 out
+    if not only or only == "w8a8_linear":
+        Mq, Kq, Nq = 8192, 4096, 11008
+        xq = torch.from_numpy(workloads.make_input("c2_per_token_s8").view(np.int16)).view(bf16).cuda()
+        wq = torch.from_numpy(workloads.make_input("c3_per_group_u4_g128").view(np.int16)).view(f16).cuda()
+        qx0, sx0, _ = tq.tq_quant_per_token(xq)
+        qw0, sw0, _ = tq.tq_quant_per_token(wq)
+        del xq, wq
+        mkq = lambda i: dict(qx=qx0.clone(), sx=sx0.clone(), qw=qw0.clone(), sw=sw0.clone(), y=E((Mq, Nq), bf16))
+        qb = Mq * Kq + Nq * Kq + 2 * Mq * Nq + 4 * (Mq + Nq)
+        bench_op("w8a8_linear", "c2 s8 [8192,4096] x c3 s8 [11008,4096]^T bf16 out", qb, mkq,
+                 lambda b: check(L.tq_w8a8_linear(P(b["qx"]), P(b["sx"]), P(b["qw"]), P(b["sw"]), Mq, Nq, Kq,
+                                                  P(b["y"]), 2, stream), "w8a8"),
+                 qb, Mq * Kq + Nq * Kq, flops=2 * Mq * Nq * Kq)
+        del qx0, sx0, qw0, sw0
     return out
 
 

@@ -16,7 +16,8 @@
  *   - per-tensor fake quantization (round trip) and its backward, and
  *     dynamic-range quantization by mode and scope,
  *   - integer codes of binary64 inputs computed in binary64,
- *   - the block-scaled FP8 GEMM that consumes the FP8 activations and weights.
+ *   - the GEMMs that consume the codes: the W8A8 quantized linear and the
+ *     block-scaled FP8 GEMM.
  *
  * Sources (page titles and sections):
  *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
@@ -24,7 +25,8 @@
  *        rule dx = (dy / scale) * 1[qmin < q < qmax] with the mask recomputed
  *        from the saved input), the module list (the *_backward plans of the
  *        dequantize ops: dq = dy * scale per group; fake_quantize and its
- *        backward; dynamic_range_quantize), the re-exports (DynamicRangeMode,
+ *        backward; dynamic_range_quantize; quantized_linear, a fused W8A8
+ *        quantized matmul), the re-exports (DynamicRangeMode,
  *        DynamicRangeScope), default_q_range.
  *   [G]  teenygrad granularity.rs -- enum Granularity (PerTensor,
  *        PerChannel{axis}, Group{axis, group_size}).
@@ -364,6 +366,21 @@ tq_status tq_quant_mxfp8_backward(const void* x, int x_dtype, const uint8_t* blo
 tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t* block_scale,
                                     int64_t rows, int64_t k, void* dq, void* stream);
 
+/* W8A8 quantized linear ([Q] quantized_linear: a fused W8A8 quantized
+ * matmul; the page names the operation only).  qx [M, K] symmetric s8 codes
+ * with one fp32 scale per row sx [M] (tq_quant_per_token's output), qw [N, K]
+ * symmetric s8 codes with one fp32 scale per output channel sw [N]
+ * (tq_quant_per_token on the weight rows); out = x W^T:
+ *   acc[m][n] = sum_k qx[m][k] * qw[n][k]           exact, 32-bit
+ *   y[m][n]   = ((float)acc * sx[m]) * sw[n]        binary32, in that order
+ * rounded once more to y_dtype; y is [M, N].  Bit-exact: the integer sums
+ * are exact on the matrix cores.  N and K multiples of 128 and K <= 131071
+ * (so every sum fits 32 bits), TQ_ERR_UNSUPPORTED otherwise; any M; qx, qw
+ * 16-byte aligned.  K = 0 writes zeros (the code pointers may then be null).
+ * Launches only; no allocation. */
+tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int64_t M, int64_t N,
+                         int64_t K, void* y, int y_dtype, void* stream);
+
 /* Block-scaled FP8 GEMM ([S] Fp8BlockGemm: activations E4M3 with one fp32
  * scale per 1 x 128 group, weights E4M3 with one fp32 scale per 128 x 128
  * tile; out = x W^T).  qa [M, K] with sa [M, K/128] (tq_quant_fp8_block with
@@ -380,10 +397,9 @@ tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t*
  * the group sums and converts toward zero.  So the result is within
  * sum_kb |sa sw| (those cuts) + about 2^-18 of the magnitude sum
  * sum |sa sw val val| of the exact value, not bit-equal to it.  K and N
- * multiples of 128 (TQ_ERR_INVALID otherwise), M a multiple of 128
- * (TQ_ERR_UNSUPPORTED otherwise); qa, qw 16-byte aligned.  K = 0 writes
- * zeros (the operand pointers may then be null); M = 0 or N = 0 does
- * nothing.  Launches only; no allocation. */
+ * multiples of 128 (TQ_ERR_INVALID otherwise), any M; qa, qw 16-byte
+ * aligned.  K = 0 writes zeros (the operand pointers may then be null);
+ * M = 0 or N = 0 does nothing.  Launches only; no allocation. */
 tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* stream);
 

@@ -85,6 +85,7 @@ _SIGS = {
     "tq_quant_per_token_strided": ([_P, _I, _I64, _I64, _I64, _I, _I32, _I32, _P, _P, _P, _P], _I),
     "tq_quant_fp8_rows_strided": ([_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P], _I),
     "tq_fp8_block_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
+    "tq_w8a8_linear": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "tq_quant_f64": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "tq_dequant_f64": ([_P, _I, _I32, _SHAPE, _I, _I32, _I64, _P, _P, _P, _P], _I),
     "tq_quant_f64_backward": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
@@ -735,4 +736,16 @@ def tq_fp8_block_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16):
     y = torch.empty((M, N), dtype=out_dtype, device=qa.device)
     _call("tq_fp8_block_gemm", _ptr(qa.contiguous()), _ptr(sa.contiguous()), _ptr(qw.contiguous()),
           _ptr(sw.contiguous()), M, N, K, _ptr(y), FTYPE[out_dtype], _stream(qa.device))
+    return y
+
+
+# ------------------------------------------------------- W8A8 quantized linear
+def tq_w8a8_linear(qx, sx, qw, sw, out_dtype=torch.bfloat16):
+    """y = x W^T from s8 activation codes qx [M, K] (per-row scales sx [M])
+    and s8 weight codes qw [N, K] (per-channel scales sw [N])."""
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=qx.device)
+    _call("tq_w8a8_linear", _ptr(qx.contiguous()), _ptr(sx.contiguous()), _ptr(qw.contiguous()),
+          _ptr(sw.contiguous()), M, N, K, _ptr(y), FTYPE[out_dtype], _stream(qx.device))
     return y

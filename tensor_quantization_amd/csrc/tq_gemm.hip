@@ -1,4 +1,6 @@
-// tq_gemm.hip -- block-scaled FP8 GEMM on gfx950 matrix cores (smile.llm.quant
+// tq_gemm.hip -- the GEMMs that consume the quantized operands, on the gfx950
+// matrix cores: the W8A8 quantized linear (baracuda_kernels::quantize,
+// quantized_linear) and the block-scaled FP8 GEMM (smile.llm.quant
 // Fp8BlockGemm: E4M3 activations with one fp32 scale per 1 x 128 group, E4M3
 // weights with one fp32 scale per 128 x 128 tile, out = x W^T):
 //
@@ -43,6 +45,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int GT = 128;                  // output tile and K block
 constexpr int SLICE = GT * GT;           // bytes of one operand K-slice
 
+__device__ __forceinline__ int64_t min_i64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * GT + ((chunk ^ swz_key(row)) << 4); }
 
@@ -70,7 +73,7 @@ __device__ __forceinline__ void dma4(const void* g, const lds_void* lds)
 template <int YT>
 __global__ __launch_bounds__(256) void k_fp8_gemm(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                                   const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-                                                  int64_t K, int64_t N, void* __restrict__ y)
+                                                  int64_t M, int64_t K, int64_t N, void* __restrict__ y)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][SLICE];
     __shared__ __attribute__((aligned(16))) float lds_sa[2][GT];
@@ -84,17 +87,21 @@ __global__ __launch_bounds__(256) void k_fp8_gemm(const uint8_t* __restrict__ qa
     const int64_t nkb = K / GT;
     const float* gsw = sw + (n0 / GT) * nkb;
 
+    // fill: LDS rows 8 w + lane / 8 + 32 i (i < 4), slot lane % 8; rows past
+    // M (a ragged last tile) re-read row M - 1 and their results are dropped
     const int frow = 8 * w + (lane >> 3);
     const int fchunk = (lane & 7) ^ swz_key(frow);
-    const uint8_t* fa = qa + (m0 + frow) * K + fchunk * 16;
+    const uint8_t* fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = qa + min_i64(m0 + frow + 32 * i, M - 1) * K + fchunk * 16;
     const uint8_t* fb = qw + (n0 + frow) * K + fchunk * 16;
-    const float* fs = sa + (m0 + 32 * w + (lane & 31)) * nkb;
+    const float* fs = sa + min_i64(m0 + 32 * w + (lane & 31), M - 1) * nkb;
 
     auto issue = [&](int64_t kb) {
         const int buf = (int)(kb & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            dma16(fa + (int64_t)32 * i * K + kb * GT, (const lds_void*)&lds[buf][0][(32 * i + 8 * w) * GT]);
+            dma16(fa[i] + kb * GT, (const lds_void*)&lds[buf][0][(32 * i + 8 * w) * GT]);
             dma16(fb + (int64_t)32 * i * K + kb * GT, (const lds_void*)&lds[buf][1][(32 * i + 8 * w) * GT]);
         }
         if (lane < 32) dma4(fs + kb, (const lds_void*)&lds_sa[buf][32 * w]);
@@ -150,8 +157,97 @@ __global__ __launch_bounds__(256) void k_fp8_gemm(const uint8_t* __restrict__ qa
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + r;
                 const int64_t col = n0 + wn * 64 + j * 16 + l16;
-                store1<YT>(y, row * N + col, acc[i][j][r]);
+                if (row < M) store1<YT>(y, row * N + col, acc[i][j][r]);
             }
+}
+
+// k_w8a8_gemm: the W8A8 quantized linear on the same tile and load pipeline.
+// Each 128-wide K block is two v_mfma_i32_16x16x64_i8 steps per 16 x 16 tile
+// (lane l: row l % 16 of A / column l % 16 of B, bytes 16 (l / 16) .. + 15
+// of the 64-wide step), accumulated exactly in int32 inside the matrix core;
+// the per-row and per-channel scales are applied once, in the epilogue:
+// y = ((float)acc * sx[row]) * sw[col], each product rounded in binary32.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+template <int YT>
+__global__ __launch_bounds__(256) void k_w8a8_gemm(const int8_t* __restrict__ qx, const float* __restrict__ sx,
+                                                   const int8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                   int64_t M, int64_t K, int64_t N, void* __restrict__ y)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][SLICE];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int64_t m0 = (int64_t)blockIdx.y * GT, n0 = (int64_t)blockIdx.x * GT;
+    const int64_t nkb = K / GT;
+
+    const int frow = 8 * w + (lane >> 3);
+    const int fchunk = (lane & 7) ^ swz_key(frow);
+    const int8_t* fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = qx + min_i64(m0 + frow + 32 * i, M - 1) * K + fchunk * 16;
+    const int8_t* fb = qw + (n0 + frow) * K + fchunk * 16;
+
+    auto issue = [&](int64_t kb) {
+        const int buf = (int)(kb & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dma16(fa[i] + kb * GT, (const lds_void*)&lds[buf][0][(32 * i + 8 * w) * GT]);
+            dma16(fb + (int64_t)32 * i * K + kb * GT, (const lds_void*)&lds[buf][1][(32 * i + 8 * w) * GT]);
+        }
+    };
+
+    v4i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{};
+
+    issue(0);
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kb + 1 < nkb) issue(kb + 1);
+
+        const int cur = (int)(kb & 1);
+        const uint8_t* la = lds[cur][0];
+        const uint8_t* lb = lds[cur][1];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            v4i av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 a = *reinterpret_cast<const uint4*>(&la[swz(wm * 64 + i * 16 + l16, 4 * s + g4)]);
+                const uint4 b = *reinterpret_cast<const uint4*>(&lb[swz(wn * 64 + i * 16 + l16, 4 * s + g4)]);
+                av[i] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+                bv[i] = v4i{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    float swc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) swc[j] = sw[n0 + wn * 64 + j * 16 + l16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + r;
+            if (row >= M) continue;
+            const float sxv = sx[row];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float v = (float)acc[i][j][r];
+                v = v * sxv;
+                v = v * swc[j];
+                store1<YT>(y, row * N + n0 + wn * 64 + j * 16 + l16, v);
+            }
+        }
 }
 
 __global__ __launch_bounds__(256) void k_zero_bytes(uint8_t* __restrict__ p, int64_t n)
@@ -170,11 +266,10 @@ tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* q
 {
     if (!valid_ftype(y_dtype) || M < 0 || N < 0 || K < 0 || N % GT || K % GT) return TQ_ERR_INVALID;
     if (M == 0 || N == 0) return TQ_OK;
-    if (M % GT) return TQ_ERR_UNSUPPORTED;
     if (!y || (K > 0 && (!qa || !sa || !qw || !sw))) return TQ_ERR_INVALID;
     if (K > 0 && (!aligned16(qa) || !aligned16(qw))) return TQ_ERR_ALIGN;
-    if (M / GT > 65535 || N / GT > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
-    const dim3 grid((unsigned)(N / GT), (unsigned)(M / GT));
+    if ((M + GT - 1) / GT > 65535 || N / GT > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)(N / GT), (unsigned)((M + GT - 1) / GT));
     hipStream_t st = as_stream(stream);
     if (K == 0) {   // empty sums: zeros (a fill kernel, not a memset node, so the call can be graph-captured)
         const int64_t nbytes = M * N * (y_dtype == TQ_F32 ? 4 : 2);
@@ -183,9 +278,33 @@ tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* q
         return launch_status();
     }
     switch (y_dtype) {
-    case TQ_F32: hipLaunchKernelGGL(k_fp8_gemm<F32>, grid, dim3(256), 0, st, qa, sa, qw, sw, K, N, y); break;
-    case TQ_F16: hipLaunchKernelGGL(k_fp8_gemm<F16>, grid, dim3(256), 0, st, qa, sa, qw, sw, K, N, y); break;
-    default: hipLaunchKernelGGL(k_fp8_gemm<BF16>, grid, dim3(256), 0, st, qa, sa, qw, sw, K, N, y); break;
+    case TQ_F32: hipLaunchKernelGGL(k_fp8_gemm<F32>, grid, dim3(256), 0, st, qa, sa, qw, sw, M, K, N, y); break;
+    case TQ_F16: hipLaunchKernelGGL(k_fp8_gemm<F16>, grid, dim3(256), 0, st, qa, sa, qw, sw, M, K, N, y); break;
+    default: hipLaunchKernelGGL(k_fp8_gemm<BF16>, grid, dim3(256), 0, st, qa, sa, qw, sw, M, K, N, y); break;
+    }
+    return launch_status();
+}
+
+tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int64_t M, int64_t N,
+                         int64_t K, void* y, int y_dtype, void* stream)
+{
+    if (!valid_ftype(y_dtype) || M < 0 || N < 0 || K < 0) return TQ_ERR_INVALID;
+    if (M == 0 || N == 0) return TQ_OK;
+    if (N % GT || K % GT || K > 131071 || (M + GT - 1) / GT > 65535 || N / GT > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
+    if (!y || !sx || !sw || (K > 0 && (!qx || !qw))) return TQ_ERR_INVALID;
+    if (K > 0 && (!aligned16(qx) || !aligned16(qw))) return TQ_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    if (K == 0) {   // empty sums: zeros (a fill kernel, not a memset node, so the call can be graph-captured)
+        const int64_t nbytes = M * N * (y_dtype == TQ_F32 ? 4 : 2);
+        hipLaunchKernelGGL(k_zero_bytes, dim3((unsigned)std::min<int64_t>((nbytes + 255) / 256, 1 << 20)), dim3(256),
+                           0, st, static_cast<uint8_t*>(y), nbytes);
+        return launch_status();
+    }
+    const dim3 grid((unsigned)(N / GT), (unsigned)((M + GT - 1) / GT));
+    switch (y_dtype) {
+    case TQ_F32: hipLaunchKernelGGL(k_w8a8_gemm<F32>, grid, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
+    case TQ_F16: hipLaunchKernelGGL(k_w8a8_gemm<F16>, grid, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
+    default: hipLaunchKernelGGL(k_w8a8_gemm<BF16>, grid, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
     }
     return launch_status();
 }

@@ -139,11 +139,28 @@ def test_follow_on_validation(tq):
     assert L.tq_dynamic_range_quantize(A, 2, 2, shp, 0, 2, 5, 0, B, C, None, None, 0, None) == INV  # bad axis
 
 
+def test_gemm_validation(tq):
+    L = tq._lib
+    INV, UNS, ALIGN = tq.TQ_ERR_INVALID, tq.TQ_ERR_UNSUPPORTED, tq.TQ_ERR_ALIGN
+    assert L.tq_fp8_block_gemm(A, C, A, C, 128, 100, 128, B, 2, None) == INV      # N % 128
+    assert L.tq_fp8_block_gemm(A, C, A, C, 128, 128, 64, B, 2, None) == INV       # K % 128
+    assert L.tq_fp8_block_gemm(A, C, A, C, 128, 128, 128, B, 5, None) == INV      # bad dtype
+    assert L.tq_fp8_block_gemm(None, C, A, C, 128, 128, 128, B, 2, None) == INV
+    assert L.tq_fp8_block_gemm(MIS, C, A, C, 128, 128, 128, B, 2, None) == ALIGN
+    assert L.tq_w8a8_linear(A, C, A, C, 128, 100, 128, B, 2, None) == UNS         # N % 128
+    assert L.tq_w8a8_linear(A, C, A, C, 128, 128, 131072, B, 2, None) == UNS      # sums would pass 32 bits
+    assert L.tq_w8a8_linear(A, C, A, C, 128, 128, 128, B, 7, None) == INV
+    assert L.tq_w8a8_linear(A, None, A, C, 128, 128, 128, B, 2, None) == INV
+    assert L.tq_w8a8_linear(A, C, MIS, C, 128, 128, 128, B, 2, None) == ALIGN
+
+
 def test_empty_inputs_enqueue_nothing(tq):
     L = tq._lib
     assert L.tq_quant_per_token(A, 2, 0, 8, 0, -127, 127, B, C, None, None) == 0
     assert L.tq_quant_fp8_block(A, 2, 0, 128, 1, 128, B, C, None) == 0
     assert L.tq_quant_fp4_block(A, 2, 0, 32, 1, B, C, None, 0, None, 0, None) == 0
+    assert L.tq_fp8_block_gemm(A, C, A, C, 0, 128, 128, B, 2, None) == 0
+    assert L.tq_w8a8_linear(A, C, A, C, 5, 0, 128, B, 2, None) == 0
 
 
 def test_product_path_does_not_touch_the_oracle():

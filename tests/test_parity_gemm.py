@@ -24,7 +24,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import TORCH, from_dev, note, to_dev
+from gpu_util import TORCH, assert_same, from_dev, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,8 @@ def _operands(tq, M, N, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K,yt", [(128, 128, 128, "f32"), (256, 384, 512, "f32"), (128, 256, 1024, "bf16"),
-                                      (384, 128, 256, "f16"), (128, 128, 7168, "f32")])
+                                      (384, 128, 256, "f16"), (128, 128, 7168, "f32"), (100, 256, 512, "f32"),
+                                      (1, 128, 1024, "bf16"), (300, 128, 256, "f32")])
 def test_fp8_block_gemm(tq, orc, M, N, K, yt):
     """Operands from the FP8 quantizers (1 x 128 activations, 128 x 128 weights)."""
     note("fp8 gemm", M, N, K, yt)
@@ -150,10 +151,11 @@ def test_fp8_block_gemm_full_size_sampled(tq, orc):
 def test_fp8_block_gemm_shapes(tq):
     qa = torch.zeros((100, 128), dtype=torch.uint8, device="cuda")
     sa = torch.ones((100, 1), dtype=torch.float32, device="cuda")
-    qw = torch.zeros((128, 128), dtype=torch.uint8, device="cuda")
+    qw = torch.zeros((100, 128), dtype=torch.uint8, device="cuda")
     sw = torch.ones((1, 1), dtype=torch.float32, device="cuda")
-    with pytest.raises(tq.TQError):                       # M = 100: no tile kernel for it
+    with pytest.raises(tq.TQError):                       # N = 100: weights come in 128-row tiles
         tq.tq_fp8_block_gemm(qa, sa, qw, sw)
+    qw = torch.zeros((128, 128), dtype=torch.uint8, device="cuda")
     y = tq.tq_fp8_block_gemm(qa[:0], sa[:0], qw, sw)
     assert y.numel() == 0
     y = tq.tq_fp8_block_gemm(torch.zeros((128, 0), dtype=torch.uint8, device="cuda"),
@@ -161,3 +163,67 @@ def test_fp8_block_gemm_shapes(tq):
                              torch.zeros((128, 0), dtype=torch.uint8, device="cuda"),
                              torch.zeros((1, 0), dtype=torch.float32, device="cuda"), out_dtype=torch.float32)
     assert y.shape == (128, 128) and bool((y == 0).all())
+
+
+# ------------------------------------------------------- W8A8 quantized linear
+def _w8a8_operands(tq, x, xt, w, wt):
+    qx, sx, _ = tq.tq_quant_per_token(to_dev(x, xt))
+    qw, sw, _ = tq.tq_quant_per_token(to_dev(w, wt))
+    return qx, sx, qw, sw
+
+
+def _i8(t):
+    return from_dev(t).view(np.int8)
+
+
+@pytest.mark.parametrize("M,N,K,yt", [(128, 128, 128, "f32"), (256, 384, 512, "bf16"), (100, 256, 1024, "f16"),
+                                      (1, 128, 4096, "bf16"), (300, 128, 256, "f32"), (128, 128, 7168, "f32")])
+def test_w8a8_linear(tq, orc, M, N, K, yt):
+    """Bit-exact against the oracle: per-token s8 activations (1% outlier
+    columns x20, as in the activation workload) times per-channel s8 weights."""
+    note("w8a8", M, N, K, yt)
+    x = workloads.normal_with_outlier_columns((M, K), 1.0, M + K, "bf16", 0.01, 20.0, K)
+    w = workloads.normal((N, K), 0.02, N + K, "f16")
+    qx, sx, qw, sw = _w8a8_operands(tq, x, "bf16", w, "f16")
+    y = tq.tq_w8a8_linear(qx, sx, qw, sw, out_dtype=TORCH[yt])
+    assert_same(from_dev(y), orc.w8a8_linear(_i8(qx), from_dev(sx), _i8(qw), from_dev(sw), yt), "y")
+
+
+def test_w8a8_linear_extreme_codes(tq, orc):
+    """All codes at -128 / 127 / 0 patterns: the largest integer sums, and
+    sums past 2^24 that the conversion to binary32 must round to nearest."""
+    note("w8a8 extreme")
+    M, N, K = 128, 128, 4096
+    rng = np.random.default_rng(7)
+    QX = rng.choice(np.array([-128, 127, 0, -127], np.int8), (M, K))
+    QW = rng.choice(np.array([-128, 127, 1], np.int8), (N, K))
+    QX[0, :] = -128
+    QW[0, :] = -128                                       # acc = 2^26 exactly
+    SX = rng.uniform(1e-4, 1e-2, M).astype(np.float32)
+    SW = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    d = lambda a: torch.from_numpy(a).cuda()
+    y = tq.tq_w8a8_linear(d(QX), d(SX), d(QW), d(SW), out_dtype=torch.float32)
+    assert_same(from_dev(y), orc.w8a8_linear(QX, SX, QW, SW, "f32"), "y")
+
+
+def test_w8a8_linear_full_size_sampled(tq, orc):
+    """The activation workload bf16 [8192, 4096] (per-token s8) times the
+    weight workload f16 [11008, 4096] (per-channel s8), bf16 out as timed:
+    rows sampled for the oracle, all columns."""
+    note("w8a8 full size")
+    x = workloads.make_input("c2_per_token_s8")
+    w = workloads.make_input("c3_per_group_u4_g128")
+    qx, sx, qw, sw = _w8a8_operands(tq, x, "bf16", w, "f16")
+    y = tq.tq_w8a8_linear(qx, sx, qw, sw, out_dtype=torch.bfloat16)
+    rows = np.array([0, 1, 127, 128, 4097, 8191])
+    ref = orc.w8a8_linear(_i8(qx)[rows], from_dev(sx)[rows], _i8(qw), from_dev(sw), "bf16")
+    assert_same(from_dev(y)[rows], ref, "y")
+
+
+def test_w8a8_linear_shapes(tq):
+    z8 = lambda r, c: torch.zeros((r, c), dtype=torch.int8, device="cuda")
+    ones = lambda n: torch.ones(n, dtype=torch.float32, device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.tq_w8a8_linear(z8(4, 128), ones(4), z8(100, 128), ones(100))      # N % 128
+    y = tq.tq_w8a8_linear(z8(3, 0), ones(3), z8(128, 0), ones(128), out_dtype=torch.float32)
+    assert y.shape == (3, 128) and bool((y == 0).all())
