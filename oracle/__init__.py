@@ -629,3 +629,21 @@ def w8a8_linear(qx, sx, qw, sw, yt):
     if rc:
         raise ValueError("oracle rejected w8a8_linear arguments")
     return y
+
+
+def fp4_linear(x, packed, bscale, global_scale, kind):
+    """x bf16 bits [M, K] (uint16), packed [N, K/2], bscale [N, K/gs] (E4M3
+    bytes for NVFP4, E8M0 for MXFP4), global_scale (NVFP4).  Returns
+    (y [M, N] float64, yabs [M, N] float64)."""
+    x = np.ascontiguousarray(x, np.uint16)
+    packed = np.ascontiguousarray(packed, np.uint8)
+    M, K = x.shape
+    N = packed.shape[0]
+    y = np.zeros((M, N), np.float64)
+    ya = np.zeros((M, N), np.float64)
+    rc = lib().orc_fp4_linear(_p(x), _p(packed), _p(np.ascontiguousarray(bscale, np.uint8)),
+                              ctypes.c_float(float(np.asarray(global_scale).reshape(-1)[0])), FP4_KINDS[kind], ctypes.c_int64(M),
+                              ctypes.c_int64(N), ctypes.c_int64(K), _p(y), _p(ya))
+    if rc:
+        raise ValueError("oracle rejected fp4_linear arguments")
+    return y, ya

@@ -1061,3 +1061,38 @@ int orc_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, const f
         }
     return ORC_OK;
 }
+
+/* ------------------------------------------------ FP4 weight-only linear */
+/* metrale QuantizedWeight (the packed E2M1 weight [N, K/2] with its block
+ * scales and fp32 per-tensor scale, made for a 16-bit-activation tile GEMM,
+ * w4a16) and smile.llm.quant Nvfp4Linear (an NVFP4 weight-only linear):
+ * out = x W^T with W the dequantized weight,
+ *   W[n][k] = E2M1(code(n, k)) * val(bscale[n][k / gs]) * s_g     (NVFP4)
+ *   W[n][k] = E2M1(code(n, k)) * 2^(bscale[n][k / 32] - 127)      (MXFP4)
+ *   y[m][n] = sum_k x[m][k] * W[n][k]
+ * x is bf16 [M, K]; codes low nibble first as in the quantizer.  Evaluated in
+ * binary64: each product x * E2M1 * scale * s_g has at most 8 + 2 + 4 + 24
+ * significant bits, so it is exact, and only the sum rounds (at 2^-53).
+ * yabs receives the same sum of magnitudes. */
+int orc_fp4_linear(const uint16_t* x, const uint8_t* packed, const uint8_t* bscale, float global_scale, int kind,
+                   int64_t M, int64_t N, int64_t K, double* y, double* yabs)
+{
+    if (fp4_dims(kind, N, K) || M < 0) return ORC_BAD;
+    const int gs = fp4_gs(kind);
+    const double sg = (kind == ORC_NVFP4) ? (double)global_scale : 1.0;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t sb = bscale[n * (K / gs) + k / gs];
+                const double s = (kind == ORC_NVFP4) ? (double)orc_dec_e4m3(sb) : (double)orc_dec_e8m0(sb);
+                const double p = (double)orc_bf16_to_f32(x[m * K + k]) *
+                                 ((double)orc_dec_e2m1(fp4_code_at(packed + n * (K / 2), k)) * s * sg);
+                acc += p;
+                aacc += fabs(p);
+            }
+            y[m * N + n] = acc;
+            if (yabs) yabs[m * N + n] = aacc;
+        }
+    return ORC_OK;
+}
