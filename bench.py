@@ -42,7 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-FP8_PEAK_TFLOPS = 5000.0      # dense fp8 matrix-core peak
+FP8_PEAK_TFLOPS = 5000.0      # dense fp8 (and int8) matrix-core peak
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak
 METRIC = "quantize GB/s (bytes in+out) & % HBM peak: per-token s8, g128 4-bit, FP4"
 
 
@@ -211,7 +212,7 @@ def breakdown(torch, tq, iters=20, only=None):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = []
 
-    def bench_op(name, cfg, nbytes, make_set, launch, set_bytes, read_bytes, flops=None):
+    def bench_op(name, cfg, nbytes, make_set, launch, set_bytes, read_bytes, flops=None, peak=FP8_PEAK_TFLOPS):
         if only and only != name:
             return
         log("breakdown:", name)
@@ -234,7 +235,7 @@ def breakdown(torch, tq, iters=20, only=None):
         else:
             tf = flops / (us * 1e-6) / 1e12
             out.append({"op": name, "workload": cfg, "flops": flops, "us": round(us, 3), "TFLOPs": round(tf, 1),
-                        "frac": round(tf / FP8_PEAK_TFLOPS, 4), "bound": "mfma"})
+                        "frac": round(tf / peak, 4), "bound": "mfma"})
         del sets
         torch.cuda.empty_cache()
 
@@ -421,6 +422,23 @@ def breakdown(torch, tq, iters=20, only=None):
                                                   P(b["y"]), 2, stream), "w8a8"),
                  qb, Mq * Kq + Nq * Kq, flops=2 * Mq * Nq * Kq)
         del qx0, sx0, qw0, sw0
+
+    # FP4 weight-only linear: bf16 activations [8192, 4096] (the activation
+    # workload's shape and recipe) times the NVFP4 weight [14336, 4096], bf16
+    # out; the products run on the bf16 matrix cores
+    if not only or only == "fp4_linear_nvfp4":
+        Mf, Kf, Nf = 8192, 4096, 14336
+        xf0 = torch.from_numpy(workloads.make_input("c2_per_token_s8").view(np.int16)).view(bf16).cuda()
+        wf = torch.from_numpy(workloads.make_input("c5_fp4_weight").view(np.int16)).view(bf16).cuda()
+        pf0, bf0, gf0 = tq.tq_quant_fp4_block(wf, "nvfp4")
+        del wf
+        mkf4 = lambda i: dict(x=xf0.clone(), p=pf0.clone(), b=bf0.clone(), g=gf0.clone(), y=E((Mf, Nf), bf16))
+        fb4 = Mf * Kf * 2 + Nf * Kf // 2 + Nf * Kf // 16 + 2 * Mf * Nf
+        bench_op("fp4_linear_nvfp4", "bf16 [8192,4096] x c5 nvfp4 [14336,4096]^T bf16 out", fb4, mkf4,
+                 lambda b: check(L.tq_fp4_linear(P(b["x"]), 2, P(b["p"]), P(b["b"]), P(b["g"]), 0, Mf, Nf, Kf,
+                                                 P(b["y"]), 2, stream), "fp4 linear"),
+                 fb4, Mf * Kf * 2 + Nf * Kf // 2, flops=2 * Mf * Nf * Kf, peak=BF16_PEAK_TFLOPS)
+        del xf0, pf0, bf0, gf0
     return out
 
 

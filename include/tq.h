@@ -16,8 +16,8 @@
  *   - per-tensor fake quantization (round trip) and its backward, and
  *     dynamic-range quantization by mode and scope,
  *   - integer codes of binary64 inputs computed in binary64,
- *   - the GEMMs that consume the codes: the W8A8 quantized linear and the
- *     block-scaled FP8 GEMM.
+ *   - the GEMMs that consume the codes: the W8A8 quantized linear, the FP4
+ *     weight-only linear and the block-scaled FP8 GEMM.
  *
  * Sources (page titles and sections):
  *   [Q]  docs.rs baracuda_kernels::quantize -- module overview (dtype
@@ -37,7 +37,8 @@
  *        concat_rows and predequant_to_fp8.
  *   [S]  smile.llm.quant package summary -- Fp8BlockGemm (E4M3, one fp32 scale
  *        per 1x128 activation group and per 128x128 weight tile),
- *        Fp8BlockDequant, MxFp8 (E8M0 scale per 32 elements).
+ *        Fp8BlockDequant, MxFp8 (E8M0 scale per 32 elements), Nvfp4Linear
+ *        (an NVFP4 weight-only linear).
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless the argument name starts with
@@ -380,6 +381,27 @@ tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t*
  * Launches only; no allocation. */
 tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int64_t M, int64_t N,
                          int64_t K, void* y, int y_dtype, void* stream);
+
+/* FP4 weight-only linear ([W] the packed E2M1 weight with its block scales
+ * and fp32 per-tensor scale, made for a 16-bit-activation tile GEMM;
+ * [S] Nvfp4Linear).  x [M, K] bf16 activations times the weight in the
+ * quantizer's own layout, packed [N, K/2] (low nibble = even k) and
+ * block_scale [N, K/gs] (E4M3 bytes, gs = 16, for kind TQ_NVFP4; E8M0 bytes,
+ * gs = 32, for TQ_MXFP4); global_scale (device, one float) is the NVFP4
+ * per-tensor scale (ignored for MXFP4).  out = x W^T, y [M, N]:
+ *   y[m][n] = s_g * sum_k x[m][k] * E2M1(code(n, k)) * scale(n, k / gs)
+ * The weight is expanded to bf16 exactly (E2M1 x block scale), the products
+ * are summed on the bf16 matrix cores in 64-wide blocks and the block sums
+ * in binary32; the result is within a few 2^-24 of the magnitude sum
+ * sum |x w| per block of the exact value, then rounded to y_dtype.  The
+ * K-contiguous [N, K/2] layout is the matrix cores' operand order, so no
+ * transposed twin is read.  x_dtype must be TQ_BF16, N a multiple of 128 and
+ * K of 64 (TQ_ERR_UNSUPPORTED otherwise); any M; x, packed 16-byte aligned,
+ * block_scale 4-byte aligned; MXFP4 scale bytes 1 .. 254.  K = 0 writes
+ * zeros.  Launches only; no allocation. */
+tq_status tq_fp4_linear(const void* x, int x_dtype, const uint8_t* packed, const uint8_t* block_scale,
+                        const float* global_scale, int kind, int64_t M, int64_t N, int64_t K, void* y,
+                        int y_dtype, void* stream);
 
 /* Block-scaled FP8 GEMM ([S] Fp8BlockGemm: activations E4M3 with one fp32
  * scale per 1 x 128 group, weights E4M3 with one fp32 scale per 128 x 128

@@ -86,6 +86,7 @@ _SIGS = {
     "tq_quant_fp8_rows_strided": ([_P, _I, _I64, _I64, _I64, _I32, _P, _P, _P], _I),
     "tq_fp8_block_gemm": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
     "tq_w8a8_linear": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P], _I),
+    "tq_fp4_linear": ([_P, _I, _P, _P, _P, _I, _I64, _I64, _I64, _P, _I, _P], _I),
     "tq_quant_f64": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _I, _P, _P, _P, _P, _SZ, _P], _I),
     "tq_dequant_f64": ([_P, _I, _I32, _SHAPE, _I, _I32, _I64, _P, _P, _P, _P], _I),
     "tq_quant_f64_backward": ([_P, _I32, _SHAPE, _I, _I32, _I64, _I, _I32, _I32, _P, _P, _P, _P, _P], _I),
@@ -748,4 +749,18 @@ def tq_w8a8_linear(qx, sx, qw, sw, out_dtype=torch.bfloat16):
     y = torch.empty((M, N), dtype=out_dtype, device=qx.device)
     _call("tq_w8a8_linear", _ptr(qx.contiguous()), _ptr(sx.contiguous()), _ptr(qw.contiguous()),
           _ptr(sw.contiguous()), M, N, K, _ptr(y), FTYPE[out_dtype], _stream(qx.device))
+    return y
+
+
+# ------------------------------------------------------ FP4 weight-only linear
+def tq_fp4_linear(x, packed, block_scale, global_scale, kind="nvfp4", out_dtype=torch.bfloat16):
+    """y = x W^T from bf16 activations x [M, K] and an FP4 weight in the
+    quantizer's layout (packed [N, K/2], block scales [N, K/gs], NVFP4
+    per-tensor scale as a one-element device tensor)."""
+    M, K = x.shape
+    N = packed.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _call("tq_fp4_linear", _ptr(x.contiguous()), FTYPE[x.dtype], _ptr(packed.contiguous()), _ptr(block_scale.contiguous()),
+          _ptr(global_scale) if global_scale is not None else None, FP4_KIND[kind], M, N, K, _ptr(y), FTYPE[out_dtype],
+          _stream(x.device))
     return y

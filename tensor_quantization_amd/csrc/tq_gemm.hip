@@ -250,6 +250,168 @@ __global__ __launch_bounds__(256) void k_w8a8_gemm(const int8_t* __restrict__ qx
         }
 }
 
+// k_fp4_linear: bf16 activations x [M, K] times an FP4 weight in the
+// quantizer's own layout (packed [N, K/2] low nibble first, block scales
+// [N, K/gs]): K-contiguous rows are what the matrix-core B operand wants, so
+// the GEMM reads that layout directly and needs no transposed twin.  Same
+// 128 x 128 tile and DMA pipeline as above with 64-wide K blocks (A slice
+// 16 KB and packed slice 4 KB per stage).  Per 32-wide step
+// a lane expands its 8 weight nibbles (one dword) to bf16 in registers:
+// MXFP4 by v_cvt_scalef32_pk_bf16_fp4, whose scale operand applies the
+// power of two 2^(e8m0 - 127) exactly; NVFP4 by the same conversion to f32
+// at scale 1, a binary32 multiply by the E4M3 block scale and a bf16 pack --
+// E2M1 x E4M3 has at most 6 significant bits, so the bf16 weight is exact.
+// Two v_mfma_f32_16x16x32_bf16 steps per block chain in the matrix core from
+// zero; the block sum is added to a binary32 accumulator (the matrix core's
+// own accumulator input joins its truncating alignment, so it is kept short),
+// and the NVFP4 per-tensor scale multiplies the total once.  A lane's block
+// scale bytes (one dword of four E4M3 bytes, or two E8M0 bytes, per weight
+// row it expands) come straight from global memory into registers one block
+// ahead, covered by the same wait as the DMA.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+constexpr int FKB = 64;                  // K per block
+enum { FP4_NV = 0, FP4_MX = 1 };
+
+__device__ __forceinline__ v2bf fp4_pair_nv(uint32_t word, int sel, float sc)
+{
+    v2f f;
+    switch (sel) {
+    case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
+    case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
+    case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
+    default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+    }
+    return v2bf{(__bf16)(f.x * sc), (__bf16)(f.y * sc)};
+}
+__device__ __forceinline__ v2bf fp4_pair_mx(uint32_t word, int sel, float sc)
+{
+    switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3);
+    }
+}
+
+template <int KIND, int YT>
+__global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
+                                                    const uint8_t* __restrict__ bscale,
+                                                    const float* __restrict__ global_scale, int64_t M, int64_t K,
+                                                    int64_t N, void* __restrict__ y)
+{
+    constexpr int GS = KIND == FP4_NV ? 16 : 32;
+    constexpr int SPB = FKB / GS;        // scale bytes per weight row per block
+    __shared__ __attribute__((aligned(16))) uint8_t la[2][GT * 2 * FKB];
+    __shared__ __attribute__((aligned(16))) uint8_t lb[2][GT * FKB / 2];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int64_t m0 = (int64_t)blockIdx.y * GT, n0 = (int64_t)blockIdx.x * GT;
+    const int64_t nkb = K / FKB;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    const float sg = KIND == FP4_NV ? *global_scale : 1.0f;
+
+    // A rows are 128 bytes per block (64 bf16): the FP8 kernel's fill and swizzle
+    const int frow = 8 * w + (lane >> 3);
+    const int fchunk = (lane & 7) ^ swz_key(frow);
+    const uint8_t* fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = xb + min_i64(m0 + frow + 32 * i, M - 1) * (2 * K) + fchunk * 16;
+    // packed rows are 32 bytes per block: thread t moves half t % 2 of row t / 2
+    const uint8_t* fb = packed + (n0 + (t >> 1)) * (K / 2) + (t & 1) * 16;
+    // this lane's block scale bytes: weight rows wn 64 + 16 j + l % 16, SPB bytes per block
+    const uint8_t* fs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fs[j] = bscale + (n0 + wn * 64 + j * 16 + l16) * (K / GS);
+    auto scale_words = [&](int64_t kb, uint32_t* sc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sc[j] = KIND == FP4_NV ? *reinterpret_cast<const uint32_t*>(fs[j] + kb * SPB)
+                                   : (uint32_t)*reinterpret_cast<const uint16_t*>(fs[j] + kb * SPB);
+    };
+
+    auto issue = [&](int64_t kb) {
+        const int buf = (int)(kb & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(fa[i] + kb * 2 * FKB, (const lds_void*)&la[buf][(32 * i + 8 * w) * GT]);
+        dma16(fb + kb * (FKB / 2), (const lds_void*)&lb[buf][w * 1024]);
+    };
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{};
+
+    uint32_t scw[4], scn[4];
+    issue(0);
+    scale_words(0, scw);
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kb + 1 < nkb) {
+            issue(kb + 1);
+            scale_words(kb + 1, scn);
+        }
+
+        const int cur = (int)(kb & 1);
+        v4f blk[4][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            v8bf av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 a = *reinterpret_cast<const uint4*>(&la[cur][swz(wm * 64 + i * 16 + l16, 4 * s + g4)]);
+                av[i] = __builtin_bit_cast(v8bf, a);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rn = wn * 64 + j * 16 + l16;
+                const uint32_t word = *reinterpret_cast<const uint32_t*>(&lb[cur][rn * (FKB / 2) + 16 * s + 4 * g4]);
+                v2bf p0, p1, p2, p3;
+                if (KIND == FP4_NV) {
+                    const float sc = e4m3_val(scw[j] >> (8 * (2 * s + (g4 >> 1))), 0);
+                    p0 = fp4_pair_nv(word, 0, sc); p1 = fp4_pair_nv(word, 1, sc);
+                    p2 = fp4_pair_nv(word, 2, sc); p3 = fp4_pair_nv(word, 3, sc);
+                } else {
+                    const float sc = __uint_as_float(((scw[j] >> (8 * s)) & 0xff) << 23);
+                    p0 = fp4_pair_mx(word, 0, sc); p1 = fp4_pair_mx(word, 1, sc);
+                    p2 = fp4_pair_mx(word, 2, sc); p3 = fp4_pair_mx(word, 3, sc);
+                }
+                bv[j] = v8bf{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    blk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], s == 0 ? v4f{} : blk[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] + blk[i][j][r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) scw[j] = scn[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + r;
+                const int64_t col = n0 + wn * 64 + j * 16 + l16;
+                const float v = KIND == FP4_NV ? acc[i][j][r] * sg : acc[i][j][r];   // NVFP4 per-tensor scale
+                if (row < M) store1<YT>(y, row * N + col, v);
+            }
+}
+
 __global__ __launch_bounds__(256) void k_zero_bytes(uint8_t* __restrict__ p, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
@@ -306,6 +468,42 @@ tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, co
     case TQ_F16: hipLaunchKernelGGL(k_w8a8_gemm<F16>, grid, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
     default: hipLaunchKernelGGL(k_w8a8_gemm<BF16>, grid, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
     }
+    return launch_status();
+}
+
+tq_status tq_fp4_linear(const void* x, int x_dtype, const uint8_t* packed, const uint8_t* block_scale,
+                        const float* global_scale, int kind, int64_t M, int64_t N, int64_t K, void* y,
+                        int y_dtype, void* stream)
+{
+    if (!valid_ftype(y_dtype) || (kind != TQ_NVFP4 && kind != TQ_MXFP4) || M < 0 || N < 0 || K < 0)
+        return TQ_ERR_INVALID;
+    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
+    if (M == 0 || N == 0) return TQ_OK;
+    if (x_dtype != TQ_BF16 || N % GT || K % FKB || (M + GT - 1) / GT > 65535 || N / GT > 0x7fffffff)
+        return TQ_ERR_UNSUPPORTED;
+    if (!y || (K > 0 && (!x || !packed || !block_scale))) return TQ_ERR_INVALID;
+    if (K > 0 && (!aligned16(x) || !aligned16(packed) || ((uintptr_t)block_scale & 3))) return TQ_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    if (K == 0) {   // empty sums: zeros (a fill kernel, not a memset node, so the call can be graph-captured)
+        const int64_t nbytes = M * N * (y_dtype == TQ_F32 ? 4 : 2);
+        hipLaunchKernelGGL(k_zero_bytes, dim3((unsigned)std::min<int64_t>((nbytes + 255) / 256, 1 << 20)), dim3(256),
+                           0, st, static_cast<uint8_t*>(y), nbytes);
+        return launch_status();
+    }
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    const dim3 grid((unsigned)(N / GT), (unsigned)((M + GT - 1) / GT));
+#define TQ_FP4_LAUNCH(KD, YD) \
+    hipLaunchKernelGGL((k_fp4_linear<KD, YD>), grid, dim3(256), 0, st, xs, packed, block_scale, global_scale, M, K, N, y)
+    if (kind == TQ_NVFP4) {
+        if (y_dtype == TQ_F32) TQ_FP4_LAUNCH(FP4_NV, F32);
+        else if (y_dtype == TQ_F16) TQ_FP4_LAUNCH(FP4_NV, F16);
+        else TQ_FP4_LAUNCH(FP4_NV, BF16);
+    } else {
+        if (y_dtype == TQ_F32) TQ_FP4_LAUNCH(FP4_MX, F32);
+        else if (y_dtype == TQ_F16) TQ_FP4_LAUNCH(FP4_MX, F16);
+        else TQ_FP4_LAUNCH(FP4_MX, BF16);
+    }
+#undef TQ_FP4_LAUNCH
     return launch_status();
 }
 

@@ -152,6 +152,12 @@ def test_gemm_validation(tq):
     assert L.tq_w8a8_linear(A, C, A, C, 128, 128, 128, B, 7, None) == INV
     assert L.tq_w8a8_linear(A, None, A, C, 128, 128, 128, B, 2, None) == INV
     assert L.tq_w8a8_linear(A, C, MIS, C, 128, 128, 128, B, 2, None) == ALIGN
+    assert L.tq_fp4_linear(A, 2, A, C, C, 0, 128, 100, 64, B, 2, None) == UNS     # N % 128
+    assert L.tq_fp4_linear(A, 2, A, C, C, 0, 128, 128, 32, B, 2, None) == UNS     # K % 64
+    assert L.tq_fp4_linear(A, 1, A, C, C, 0, 128, 128, 64, B, 2, None) == UNS     # f16 activations
+    assert L.tq_fp4_linear(A, 2, A, C, None, 0, 128, 128, 64, B, 2, None) == INV  # NVFP4 needs s_g
+    assert L.tq_fp4_linear(A, 2, A, C, C, 4, 128, 128, 64, B, 2, None) == INV     # bad kind
+    assert L.tq_fp4_linear(MIS, 2, A, C, C, 1, 128, 128, 64, B, 2, None) == ALIGN
 
 
 def test_empty_inputs_enqueue_nothing(tq):

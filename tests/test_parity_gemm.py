@@ -227,3 +227,75 @@ def test_w8a8_linear_shapes(tq):
         tq.tq_w8a8_linear(z8(4, 128), ones(4), z8(100, 128), ones(100))      # N % 128
     y = tq.tq_w8a8_linear(z8(3, 0), ones(3), z8(128, 0), ones(128), out_dtype=torch.float32)
     assert y.shape == (3, 128) and bool((y == 0).all())
+
+
+# ------------------------------------------------------ FP4 weight-only linear
+def check_fp4(y, ref, yabs, K, yt):
+    """Bound from the bf16 matrix-core arithmetic (probed on single-wave
+    inputs): a step aligns its 32 exact bf16 x bf16 products and its
+    accumulator input to the largest of them, keeps bits down to 2^(E - 24)
+    and rounds the sum to nearest.  A 64-wide block is two chained steps from
+    zero: <= (32 + 1 + 33 + 1) 2^-24 of the block's magnitude sum, taken
+    four times over here; each block sum is then added in binary32
+    (2^-24 of the running magnitude) and the NVFP4 per-tensor scale applied
+    once (2^-24)."""
+    nkb = K // 64
+    bound = (4 * 67 + nkb + 1) * 2.0 ** -24 * yabs + 1e-30
+    if yt == "bf16":
+        bound = bound + 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -7)
+    elif yt == "f16":
+        bound = bound + 2.0 ** -11 * np.abs(ref) * (1 + 2.0 ** -10) + 2.0 ** -25
+    err = np.abs(y.astype(np.float64) - ref)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, ("%d outputs outside the bound; first %s: got %r want %r bound %r"
+                           % (len(bad), tuple(bad[0]), y[tuple(bad[0])], ref[tuple(bad[0])], bound[tuple(bad[0])]))
+    return float((err / bound).max())
+
+
+def _fp4_weight(tq, w, kind):
+    packed, bs, sg = tq.tq_quant_fp4_block(to_dev(w, "bf16"), kind)
+    return packed, bs, sg
+
+
+@pytest.mark.parametrize("kind", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("M,N,K,yt", [(128, 128, 64, "f32"), (256, 256, 512, "f32"), (100, 384, 1024, "bf16"),
+                                      (1, 128, 4096, "f16"), (300, 128, 4096, "f32")])
+def test_fp4_linear(tq, orc, kind, M, N, K, yt):
+    """bf16 activations (1% outlier columns x20) times an FP4 weight quantized
+    on the GPU from bf16 ~N(0, 0.02)."""
+    note("fp4 linear", kind, M, N, K, yt)
+    x = workloads.normal_with_outlier_columns((M, K), 1.0, M + K + 1, "bf16", 0.01, 20.0, K)
+    w = workloads.normal((N, K), 0.02, N + K + 2, "bf16")
+    packed, bs, sg = _fp4_weight(tq, w, kind)
+    y = tq.tq_fp4_linear(to_dev(x, "bf16"), packed, bs, sg, kind, out_dtype=TORCH[yt])
+    ref, yabs = orc.fp4_linear(x, from_dev(packed), from_dev(bs), from_dev(sg) if sg is not None else 1.0, kind)
+    check_fp4(_as_f32(y, yt), ref, yabs, K, yt)
+
+
+def test_fp4_linear_full_size_sampled(tq, orc):
+    """The bf16 [8192, 4096] activations times the NVFP4 weight workload
+    [14336, 4096], bf16 out as timed: rows sampled for the oracle."""
+    note("fp4 linear full size")
+    x = workloads.make_input("c2_per_token_s8")
+    w = workloads.make_input("c5_fp4_weight")
+    packed, bs, sg = _fp4_weight(tq, w, "nvfp4")
+    y = tq.tq_fp4_linear(to_dev(x, "bf16"), packed, bs, sg, "nvfp4", out_dtype=torch.bfloat16)
+    rows = np.array([0, 1, 127, 128, 4097, 8191])
+    ref, yabs = orc.fp4_linear(x[rows], from_dev(packed), from_dev(bs), from_dev(sg), "nvfp4")
+    check_fp4(_as_f32(y, "bf16")[rows], ref, yabs, 4096, "bf16")
+
+
+def test_fp4_linear_shapes(tq):
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    p = torch.zeros((100, 32), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((100, 4), dtype=torch.uint8, device="cuda")
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(tq.TQError):                       # N % 128
+        tq.tq_fp4_linear(x, p, b, g, "nvfp4")
+    p128 = torch.zeros((128, 32), dtype=torch.uint8, device="cuda")
+    b128 = torch.zeros((128, 4), dtype=torch.uint8, device="cuda")
+    with pytest.raises(tq.TQError):                       # f16 activations
+        tq.tq_fp4_linear(x.half(), p128, b128, g, "nvfp4")
+    y = tq.tq_fp4_linear(x[:, :0], torch.zeros((128, 0), dtype=torch.uint8, device="cuda"),
+                         torch.zeros((128, 0), dtype=torch.uint8, device="cuda"), g, "nvfp4", out_dtype=torch.float32)
+    assert y.shape == (4, 128) and bool((y == 0).all())
