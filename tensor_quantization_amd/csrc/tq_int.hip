@@ -101,6 +101,100 @@ __device__ __forceinline__ void store_fake8(void* y, int64_t e, const float c[8]
 }
 
 // ------------------------------------------------------------ team kernel
+// f16 inputs skip the widening pass: the group max / min runs on packed f16
+// pairs (v_pk_max_f16 / v_pk_min_f16, exact), and the division widens each
+// element inside its two FMAs (v_fma_mix_f32): q0 = fma(x, y, -0) is x * y
+// with the same rounding and the same signed zeros, r = fma(q0, s, -x).
+// Packed f16 max / min from asm: the builtins would first quiet each loaded
+// pair (one more v_pk_max_f16 per dword); NaN inputs are out of contract.
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ uint32_t pk_min_f16(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+template <int W, bool SYM>
+__device__ __forceinline__ void f16_stats(const Raw8<F16>* raw, float& amax, float& mn, float& mx)
+{
+    typedef uint16_t u2v __attribute__((ext_vector_type(2)));
+    u2v amx = {0, 0};                    // |x| patterns: unsigned order is magnitude order
+    uint32_t hmx = 0, hmn = 0;           // two packed f16 zeros
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const uint32_t d[4] = {raw[w].w[0].x, raw[w].w[0].y, raw[w].w[0].z, raw[w].w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (SYM) {
+                amx = __builtin_elementwise_max(amx, __builtin_bit_cast(u2v, d[i] & 0x7fff7fffu));
+            } else {
+                hmn = pk_min_f16(hmn, d[i]);
+                hmx = pk_max_f16(hmx, d[i]);
+            }
+        }
+    }
+    if constexpr (SYM) {
+        amax = mx = f16_lo(amx.x > amx.y ? amx.x : amx.y);
+        mn = 0.0f;
+    } else {
+        amax = mx = __builtin_fmaxf(f16_lo(hmx), f16_hi(hmx));
+        mn = __builtin_fminf(f16_lo(hmn), f16_hi(hmn));
+    }
+}
+
+// The binary32 quotient of an f16 dividend (widened inside the FMAs; nz is
+// an opaque -0 so the first FMA is not folded back into a multiply).
+__device__ __forceinline__ float div_q_mix(float x, float s, float y, float nz)
+{
+    const float q0 = __builtin_fmaf(x, y, nz);
+    const float r = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-r, y, q0);
+}
+
+// Per-nibble sum modulo 16 of eight packed nibbles (no carries between them).
+__device__ __forceinline__ uint32_t nibble_add(uint32_t a, uint32_t b)
+{
+    return ((a & 0x77777777u) + (b & 0x77777777u)) ^ ((a ^ b) & 0x88888888u);
+}
+
+// Codes of 8 elements of one group, stored.  Asymmetric 4-bit codes clamp
+// before the zero-point, med3(t + M, M + qmin - zp, M + qmax - zp), and add
+// the zero-point to the eight packed nibbles at once: the result of each is
+// in [qmin, qmax] within [0, 15], so the sum modulo 16 is the code itself.
+template <int FT, bool FAST, bool SYM, int BITS, bool NT>
+__device__ __forceinline__ void encode_store8(const float* v, const Raw8<FT>& raw, const GP& p, float lo, float hi,
+                                              float lo_z, float hi_z, uint32_t zn, float nz, uint8_t* q, int64_t e)
+{
+    float c[8];
+    if constexpr (FT == F16) {
+        const uint32_t d[4] = {raw.w[0].x, raw.w[0].y, raw.w[0].z, raw.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = (i & 1) ? f16_hi(d[i >> 1]) : f16_lo(d[i >> 1]);
+            const float t = FAST ? div_q_mix(x, p.s, p.y, nz) : x / p.s;
+            if constexpr (SYM) c[i] = t + MAGIC;
+            else if constexpr (BITS == 4) c[i] = __builtin_amdgcn_fmed3f(t + MAGIC, lo_z, hi_z);
+            else c[i] = int_code_f(t, p.zpf, lo, hi);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float t = FAST ? div_q<FT>(v[i], p.s, p.y) : v[i] / p.s;
+            if constexpr (SYM) c[i] = t + MAGIC;
+            else if constexpr (BITS == 4) c[i] = __builtin_amdgcn_fmed3f(t + MAGIC, lo_z, hi_z);
+            else c[i] = int_code_f(t, p.zpf, lo, hi);
+        }
+    }
+    if constexpr (BITS == 4 && !SYM) st4<NT>(q + (e >> 1), nibble_add(pack_nibbles8(c, true), zn));
+    else store_codes8<BITS, NT>(q, e, c);
+}
+
 // Groups of L = 8*T*W contiguous elements.  Lane j of a team of T lanes
 // holds vectors w*T + j (w < W) of its group, so each load instruction of a
 // team reads 16*T contiguous bytes; a wave runs U rounds of 64/T groups.
@@ -128,15 +222,22 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
         }
     }
     float v[U][W][8];
+    if constexpr (FT != F16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int w = 0; w < W; ++w) widen8<FT>(raw[u][w], v[u][w]);
+            for (int w = 0; w < W; ++w) widen8<FT>(raw[u][w], v[u][w]);
+    }
 
     GP p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if constexpr (SYM) {
+        if constexpr (FT == F16) {
+            float a, mn, mx;
+            f16_stats<W, SYM>(raw[u], a, mn, mx);
+            if constexpr (SYM) p[u] = make_gp<FT, true>(team_max<T>(a), 0.0f, 0.0f, qmin, qmax, yc);
+            else p[u] = make_gp<FT, false>(0.0f, team_min<T>(mn), team_max<T>(mx), qmin, qmax, yc);
+        } else if constexpr (SYM) {
             float a = 0.0f;
 #pragma unroll
             for (int w = 0; w < W; ++w)
@@ -157,24 +258,23 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
     }
 
     const float lo = MAGIC + qmin, hi = MAGIC + qmax;
+    const float nz = opaque(-0.0f);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t g = g0 + (int64_t)u * P;
         if (g >= G) continue;
+        const float lo_z = lo - p[u].zpf, hi_z = hi - p[u].zpf;          // exact: small integers
+        const uint32_t zn = ((uint32_t)(int)p[u].zpf & 0xfu) * 0x11111111u;   // the zero-point in every nibble
         if (p[u].fast) {
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                float c[8];
-                enc8<FT, true, !SYM>(v[u][w], p[u], lo, hi, c);
-                store_codes8<BITS, (T == 64)>(q, g * L + (int64_t)(w * T + j) * 8, c);
-            }
+            for (int w = 0; w < W; ++w)
+                encode_store8<FT, true, SYM, BITS, (T == 64)>(v[u][w], raw[u][w], p[u], lo, hi, lo_z, hi_z, zn, nz, q,
+                                                             g * L + (int64_t)(w * T + j) * 8);
         } else {
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                float c[8];
-                enc8<FT, false, !SYM>(v[u][w], p[u], lo, hi, c);
-                store_codes8<BITS, (T == 64)>(q, g * L + (int64_t)(w * T + j) * 8, c);
-            }
+            for (int w = 0; w < W; ++w)
+                encode_store8<FT, false, SYM, BITS, (T == 64)>(v[u][w], raw[u][w], p[u], lo, hi, lo_z, hi_z, zn, nz, q,
+                                                              g * L + (int64_t)(w * T + j) * 8);
         }
         if (j == 0) {
             scale[g] = p[u].s;
