@@ -177,7 +177,8 @@ def _i8(t):
 
 
 @pytest.mark.parametrize("M,N,K,yt", [(128, 128, 128, "f32"), (256, 384, 512, "bf16"), (100, 256, 1024, "f16"),
-                                      (1, 128, 4096, "bf16"), (300, 128, 256, "f32"), (128, 128, 7168, "f32")])
+                                      (1, 128, 4096, "bf16"), (300, 128, 256, "f32"), (128, 128, 7168, "f32"),
+                                      (300, 512, 768, "bf16"), (1, 256, 128, "f32")])
 def test_w8a8_linear(tq, orc, M, N, K, yt):
     """Bit-exact against the oracle: per-token s8 activations (1% outlier
     columns x20, as in the activation workload) times per-channel s8 weights."""
@@ -189,11 +190,13 @@ def test_w8a8_linear(tq, orc, M, N, K, yt):
     assert_same(from_dev(y), orc.w8a8_linear(_i8(qx), from_dev(sx), _i8(qw), from_dev(sw), yt), "y")
 
 
-def test_w8a8_linear_extreme_codes(tq, orc):
+@pytest.mark.parametrize("N", [128, 256])
+def test_w8a8_linear_extreme_codes(tq, orc, N):
     """All codes at -128 / 127 / 0 patterns: the largest integer sums, and
-    sums past 2^24 that the conversion to binary32 must round to nearest."""
-    note("w8a8 extreme")
-    M, N, K = 128, 128, 4096
+    sums past 2^24 that the conversion to binary32 must round to nearest
+    (both tile kernels)."""
+    note("w8a8 extreme", N)
+    M, K = 128, 4096
     rng = np.random.default_rng(7)
     QX = rng.choice(np.array([-128, 127, 0, -127], np.int8), (M, K))
     QW = rng.choice(np.array([-128, 127, 1], np.int8), (N, K))
