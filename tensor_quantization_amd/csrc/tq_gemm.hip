@@ -344,20 +344,21 @@ __global__ __launch_bounds__(512) void k_w8a8_gemm_256(const int8_t* __restrict_
 // quantizer's own layout (packed [N, K/2] low nibble first, block scales
 // [N, K/gs]): K-contiguous rows are what the matrix-core B operand wants, so
 // the GEMM reads that layout directly and needs no transposed twin.  Same
-// 128 x 128 tile and DMA pipeline as above with 64-wide K blocks (A slice
-// 16 KB and packed slice 4 KB per stage).  Per 32-wide step
-// a lane expands its 8 weight nibbles (one dword) to bf16 in registers:
-// MXFP4 by v_cvt_scalef32_pk_bf16_fp4, whose scale operand applies the
-// power of two 2^(e8m0 - 127) exactly; NVFP4 by the same conversion to f32
-// at scale 1, a binary32 multiply by the E4M3 block scale and a bf16 pack --
-// E2M1 x E4M3 has at most 6 significant bits, so the bf16 weight is exact.
-// Two v_mfma_f32_16x16x32_bf16 steps per block chain in the matrix core from
+// 128 x 128 tile as above with 64-wide K blocks.  The activation slice
+// (128 rows x 128 bytes) moves by DMA into two LDS stages.  The weight is
+// expanded once per workgroup: thread t loads half a row (16 packed bytes,
+// 32 values) of the next block and its scale bytes into registers while the
+// matrix cores work on the current block, then writes them as exact bf16
+// into the other of two LDS weight buffers, laid out (128-byte rows, same
+// swizzle) like the activation slice.  MXFP4 expands by
+// v_cvt_scalef32_pk_bf16_fp4, whose scale operand applies the power of two
+// 2^(e8m0 - 127) exactly; NVFP4 by the same conversion to f32 at scale 1, a
+// binary32 multiply by the E4M3 block scale and a bf16 pack (E2M1 x E4M3 has
+// at most 6 significant bits, so the bf16 weight is exact).  Two
+// v_mfma_f32_16x16x32_bf16 steps per block chain in the matrix core from
 // zero; the block sum is added to a binary32 accumulator (the matrix core's
-// own accumulator input joins its truncating alignment, so it is kept short),
-// and the NVFP4 per-tensor scale multiplies the total once.  A lane's block
-// scale bytes (one dword of four E4M3 bytes, or two E8M0 bytes, per weight
-// row it expands) come straight from global memory into registers one block
-// ahead, covered by the same wait as the DMA.
+// own accumulator input joins its truncating alignment, so the chain is kept
+// short), and the NVFP4 per-tensor scale multiplies the total once.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -385,6 +386,22 @@ __device__ __forceinline__ v2bf fp4_pair_mx(uint32_t word, int sel, float sc)
     }
 }
 
+// 8 weight values (one packed dword) as a 16-byte bf16 chunk
+template <int KIND>
+__device__ __forceinline__ uint4 fp4_expand8(uint32_t word, float sc)
+{
+    v2bf p0, p1, p2, p3;
+    if (KIND == FP4_NV) {
+        p0 = fp4_pair_nv(word, 0, sc); p1 = fp4_pair_nv(word, 1, sc);
+        p2 = fp4_pair_nv(word, 2, sc); p3 = fp4_pair_nv(word, 3, sc);
+    } else {
+        p0 = fp4_pair_mx(word, 0, sc); p1 = fp4_pair_mx(word, 1, sc);
+        p2 = fp4_pair_mx(word, 2, sc); p3 = fp4_pair_mx(word, 3, sc);
+    }
+    return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                      __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 template <int KIND, int YT>
 __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed,
                                                     const uint8_t* __restrict__ bscale,
@@ -394,7 +411,7 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
     constexpr int GS = KIND == FP4_NV ? 16 : 32;
     constexpr int SPB = FKB / GS;        // scale bytes per weight row per block
     __shared__ __attribute__((aligned(16))) uint8_t la[2][GT * 2 * FKB];
-    __shared__ __attribute__((aligned(16))) uint8_t lb[2][GT * FKB / 2];
+    __shared__ __attribute__((aligned(16))) uint8_t lw[2][GT * 2 * FKB];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -406,30 +423,38 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
     const float sg = KIND == FP4_NV ? *global_scale : 1.0f;
 
-    // A rows are 128 bytes per block (64 bf16): the FP8 kernel's fill and swizzle
+    // activation rows are 128 bytes per block (64 bf16): the FP8 kernel's fill and swizzle
     const int frow = 8 * w + (lane >> 3);
     const int fchunk = (lane & 7) ^ swz_key(frow);
     const uint8_t* fa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = xb + min_i64(m0 + frow + 32 * i, M - 1) * (2 * K) + fchunk * 16;
-    // packed rows are 32 bytes per block: thread t moves half t % 2 of row t / 2
-    const uint8_t* fb = packed + (n0 + (t >> 1)) * (K / 2) + (t & 1) * 16;
-    // this lane's block scale bytes: weight rows wn 64 + 16 j + l % 16, SPB bytes per block
-    const uint8_t* fs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fs[j] = bscale + (n0 + wn * 64 + j * 16 + l16) * (K / GS);
-    auto scale_words = [&](int64_t kb, uint32_t* sc) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sc[j] = KIND == FP4_NV ? *reinterpret_cast<const uint32_t*>(fs[j] + kb * SPB)
-                                   : (uint32_t)*reinterpret_cast<const uint16_t*>(fs[j] + kb * SPB);
-    };
-
     auto issue = [&](int64_t kb) {
         const int buf = (int)(kb & 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(fa[i] + kb * 2 * FKB, (const lds_void*)&la[buf][(32 * i + 8 * w) * GT]);
-        dma16(fb + kb * (FKB / 2), (const lds_void*)&lb[buf][w * 1024]);
+    };
+
+    // weight expansion: thread t owns half h = t % 2 of weight row r = t / 2 (32 values = chunks 4h .. 4h+3)
+    const int wr = t >> 1, wh = t & 1;
+    const uint8_t* fw = packed + (n0 + wr) * (K / 2) + wh * 16;
+    const uint8_t* fsc = bscale + (n0 + wr) * (K / GS);
+    uint4 pk;
+    uint32_t sbytes;
+    auto fetch_w = [&](int64_t kb) {
+        pk = *reinterpret_cast<const uint4*>(fw + kb * (FKB / 2));
+        sbytes = KIND == FP4_NV ? *reinterpret_cast<const uint32_t*>(fsc + kb * SPB)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(fsc + kb * SPB);
+    };
+    auto expand_w = [&](int buf) {
+        const uint32_t d[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // values 32 wh + 8 c .. + 7 of the block: NVFP4 group 2 wh + c / 2, MXFP4 group wh
+            const float sc = KIND == FP4_NV ? e4m3_val(sbytes >> (8 * (2 * wh + (c >> 1))), 0)
+                                            : __uint_as_float(((sbytes >> (8 * wh)) & 0xff) << 23);
+            *reinterpret_cast<uint4*>(&lw[buf][swz(wr, 4 * wh + c)]) = fp4_expand8<KIND>(d[c], sc);
+        }
     };
 
     v4f acc[4][4];
@@ -438,14 +463,17 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{};
 
-    uint32_t scw[4], scn[4];
     issue(0);
-    scale_words(0, scw);
+    fetch_w(0);
+    expand_w(0);
     for (int64_t kb = 0; kb < nkb; ++kb) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kb + 1 < nkb) {
+        // block kb's activations have landed and its expanded weights are written
+        // by every thread; every wave is done with the buffers of block kb - 1
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const bool more = kb + 1 < nkb;
+        if (more) {
             issue(kb + 1);
-            scale_words(kb + 1, scn);
+            fetch_w(kb + 1);
         }
 
         const int cur = (int)(kb & 1);
@@ -455,24 +483,10 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
             v8bf av[4], bv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 a = *reinterpret_cast<const uint4*>(&la[cur][swz(wm * 64 + i * 16 + l16, 4 * s + g4)]);
-                av[i] = __builtin_bit_cast(v8bf, a);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rn = wn * 64 + j * 16 + l16;
-                const uint32_t word = *reinterpret_cast<const uint32_t*>(&lb[cur][rn * (FKB / 2) + 16 * s + 4 * g4]);
-                v2bf p0, p1, p2, p3;
-                if (KIND == FP4_NV) {
-                    const float sc = e4m3_val(scw[j] >> (8 * (2 * s + (g4 >> 1))), 0);
-                    p0 = fp4_pair_nv(word, 0, sc); p1 = fp4_pair_nv(word, 1, sc);
-                    p2 = fp4_pair_nv(word, 2, sc); p3 = fp4_pair_nv(word, 3, sc);
-                } else {
-                    const float sc = __uint_as_float(((scw[j] >> (8 * s)) & 0xff) << 23);
-                    p0 = fp4_pair_mx(word, 0, sc); p1 = fp4_pair_mx(word, 1, sc);
-                    p2 = fp4_pair_mx(word, 2, sc); p3 = fp4_pair_mx(word, 3, sc);
-                }
-                bv[j] = v8bf{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+                av[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
+                                                     &la[cur][swz(wm * 64 + i * 16 + l16, 4 * s + g4)]));
+                bv[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(
+                                                     &lw[cur][swz(wn * 64 + i * 16 + l16, 4 * s + g4)]));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -480,14 +494,13 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
                 for (int j = 0; j < 4; ++j)
                     blk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], s == 0 ? v4f{} : blk[i][j], 0, 0, 0);
         }
+        if (more) expand_w(cur ^ 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] + blk[i][j][r];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) scw[j] = scn[j];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
