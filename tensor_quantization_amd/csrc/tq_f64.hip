@@ -27,6 +27,68 @@
 
 namespace tq {
 
+// Group index of an element.  Groups along the last axis (inner = 1: per
+// token, per group along the last axis, per channel of the last axis) need a
+// single division, e / g or e % A; below 2^32 elements it is a multiply-high
+// by a host-computed magic number (Granlund and Montgomery's round-up method,
+// exact for every 32-bit dividend) instead of the general map's 64-bit
+// divisions, which cost more than the whole binary64 encode.
+struct FMap {
+    DMap m;
+    int mode;                 // 0: general map, 1: one group, 2: e / d, 3: e % d
+    uint32_t d, mul, sh;      // divisor, magic multiplier, shift (d == 1: identity)
+
+    __device__ __forceinline__ uint32_t div(uint32_t n) const
+    {
+        if (d == 1) return n;
+        const uint32_t t = __umulhi(mul, n);
+        return (t + ((n - t) >> 1)) >> sh;
+    }
+    __device__ __forceinline__ int64_t group_of(int64_t e) const
+    {
+        switch (mode) {
+        case 1: return 0;
+        case 2: return div((uint32_t)e);
+        case 3: return (uint32_t)e - div((uint32_t)e) * d;
+        default: return m.group_of(e);
+        }
+    }
+    // element j of group gid
+    __device__ __forceinline__ int64_t elem(int64_t gid, int64_t j) const
+    {
+        switch (mode) {
+        case 2: return gid * (int64_t)d + j;
+        case 3: return j * (int64_t)d + gid;
+        default: return m.elem(gid, j);
+        }
+    }
+};
+
+static FMap to_fmap(const GroupMap& gm)
+{
+    FMap f;
+    f.m = to_dmap(gm);
+    f.mode = 0;
+    f.d = 1;
+    f.mul = 0;
+    f.sh = 0;
+    if (gm.kind == KIND_TENSOR) {
+        f.mode = 1;
+        return f;
+    }
+    const int64_t dv = gm.kind == KIND_CHANNEL ? gm.A : gm.g;
+    if (gm.inner != 1 || gm.numel > 0xffffffffLL || dv < 1 || dv > 0xffffffffLL) return f;
+    f.mode = gm.kind == KIND_CHANNEL ? 3 : 2;
+    f.d = (uint32_t)dv;
+    if (f.d > 1) {
+        int l = 0;
+        while (((uint64_t)1 << l) < f.d) ++l;                      // ceil(log2 d)
+        f.mul = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - f.d)) / f.d + 1);
+        f.sh = (uint32_t)(l - 1);
+    }
+    return f;
+}
+
 __device__ __forceinline__ double dmax_team64(double v)
 {
 #pragma unroll
@@ -72,21 +134,31 @@ __device__ __forceinline__ void f64_params(bool sym, double mn, double mx, doubl
     }
 }
 
-__global__ __launch_bounds__(256) void k_f64_group_params(const double* __restrict__ x, DMap m, int sym,
+__global__ __launch_bounds__(256) void k_f64_group_params(const double* __restrict__ x, FMap m, int sym,
                                                           double qmin, double qmax, double* __restrict__ scale,
                                                           uint8_t* __restrict__ zp)
 {
     const int64_t gid = blockIdx.x;
-    const int64_t n = m.count();
+    const int64_t n = m.m.count();
     double mn = 0.0, mx = 0.0;
-    for (int64_t j = threadIdx.x; j < n; j += 256) {
-        const double v = x[m.elem(gid, j)];
+    auto take = [&](double v) {
         if (sym) {
             mx = fmax(mx, fabs(v));
         } else {
             mn = fmin(mn, v);
             mx = fmax(mx, v);
         }
+    };
+    const double* base = x + gid * (int64_t)m.d;
+    if (m.mode == 2 && (m.d & 1) == 0 && ((uintptr_t)base & 15) == 0) {
+        // a contiguous group of even length: 16-byte loads
+        for (int64_t j = threadIdx.x; 2 * j < n; j += 256) {
+            const double2 v = reinterpret_cast<const double2*>(base)[j];
+            take(v.x);
+            take(v.y);
+        }
+    } else {
+        for (int64_t j = threadIdx.x; j < n; j += 256) take(x[m.elem(gid, j)]);
     }
     dblock_minmax(mn, mx);
     if (threadIdx.x == 0) {
@@ -154,17 +226,17 @@ __device__ __forceinline__ int f64_code(double x, double s, double z, double qmi
 
 // Thread t handles elements 2t and 2t+1 (a code byte for 4-bit codes).
 template <int BITS>
-__global__ __launch_bounds__(256) void k_f64_encode(const double* __restrict__ x, DMap m, double qmin, double qmax,
+__global__ __launch_bounds__(256) void k_f64_encode(const double* __restrict__ x, FMap m, double qmin, double qmax,
                                                     const double* __restrict__ scale, const uint8_t* __restrict__ zp,
                                                     bool zs, uint8_t* __restrict__ q)
 {
-    const int64_t npair = (m.numel + 1) / 2;
+    const int64_t npair = (m.m.numel + 1) / 2;
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < npair; t += (int64_t)gridDim.x * 256) {
         int c[2] = {0, 0};
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int64_t e = 2 * t + k;
-            if (e < m.numel) {
+            if (e < m.m.numel) {
                 const int64_t g = m.group_of(e);
                 c[k] = f64_code(x[e], scale[g], f64_zp(zp, g, zs), qmin, qmax);
             }
@@ -173,26 +245,116 @@ __global__ __launch_bounds__(256) void k_f64_encode(const double* __restrict__ x
             q[t] = (uint8_t)((c[0] & 0xf) | ((c[1] & 0xf) << 4));
         } else {
             q[2 * t] = (uint8_t)c[0];
-            if (2 * t + 1 < m.numel) q[2 * t + 1] = (uint8_t)c[1];
+            if (2 * t + 1 < m.m.numel) q[2 * t + 1] = (uint8_t)c[1];
         }
+    }
+}
+
+// Pair-interleaved: a wave-iteration covers 256 element pairs (512
+// elements); lane l takes pairs 64 k + l (k < 4), so each 16-byte access
+// instruction of the wave covers 1 KB of consecutive pairs.  Needs an even
+// element count and 16-byte aligned binary64 buffers.  SAMEG: the 512 share
+// a group (one tensor, or groups along the last axis whose length is a
+// multiple of 512), so the group index, scale and zero-point are read once.
+template <int BITS, bool SAMEG>
+__global__ __launch_bounds__(256) void k_f64_encode8(const double* __restrict__ x, FMap m, double qmin, double qmax,
+                                                     const double* __restrict__ scale, const uint8_t* __restrict__ zp,
+                                                     bool zs, uint8_t* __restrict__ q)
+{
+    const int64_t npair = m.m.numel / 2;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwave = (int64_t)gridDim.x * 4;
+    for (int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wv * 256 < npair; wv += nwave) {
+        const int64_t p0 = wv * 256 + lane;
+        double2 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (p0 + 64 * k < npair) v[k] = reinterpret_cast<const double2*>(x)[p0 + 64 * k];
+        double sc = 0.0, z = 0.0;
+        if constexpr (SAMEG) {
+            const int64_t g = m.group_of(wv * 512);
+            sc = scale[g];
+            z = f64_zp(zp, g, zs);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t p = p0 + 64 * k;
+            if (p >= npair) break;
+            int c0, c1;
+            if constexpr (SAMEG) {
+                c0 = f64_code(v[k].x, sc, z, qmin, qmax);
+                c1 = f64_code(v[k].y, sc, z, qmin, qmax);
+            } else {
+                const int64_t g0 = m.group_of(2 * p), g1 = m.group_of(2 * p + 1);
+                c0 = f64_code(v[k].x, scale[g0], f64_zp(zp, g0, zs), qmin, qmax);
+                c1 = f64_code(v[k].y, scale[g1], f64_zp(zp, g1, zs), qmin, qmax);
+            }
+            if constexpr (BITS == 4) q[p] = (uint8_t)((c0 & 0xf) | ((c1 & 0xf) << 4));
+            else reinterpret_cast<uint16_t*>(q)[p] = (uint16_t)((c0 & 0xff) | ((c1 & 0xff) << 8));
+        }
+    }
+}
+
+// One pass for contiguous groups of even length L <= 4096: a workgroup per
+// group holds it in registers (up to 8 pairs per thread, 16-byte loads),
+// reduces its max / min, derives scale and zero-point (every thread computes
+// the same values; thread 0 stores them) and encodes from the registers.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_f64_rows(const double* __restrict__ x, int64_t L, int sym, double qmin,
+                                                  double qmax, double* __restrict__ scale, uint8_t* __restrict__ zp,
+                                                  uint8_t* __restrict__ q)
+{
+    const int64_t g = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t n2 = L / 2;
+    const double2* base = reinterpret_cast<const double2*>(x + g * L);
+    double2 v[8];
+    double mn = 0.0, mx = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t j = t + 256 * i;
+        v[i] = j < n2 ? base[j] : make_double2(0.0, 0.0);
+        if (sym) {
+            mx = fmax(mx, fmax(fabs(v[i].x), fabs(v[i].y)));
+        } else {
+            mn = fmin(mn, fmin(v[i].x, v[i].y));
+            mx = fmax(mx, fmax(v[i].x, v[i].y));
+        }
+    }
+    dblock_minmax(mn, mx);
+    double s;
+    int zi;
+    f64_params(sym, mn, mx, qmin, qmax, &s, &zi);
+    if (t == 0) {
+        scale[g] = s;
+        if (!sym) zp[g] = (uint8_t)zi;
+    }
+    const double z = sym ? 0.0 : (double)zi;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t j = t + 256 * i;
+        if (j >= n2) break;
+        const int c0 = f64_code(v[i].x, s, z, qmin, qmax), c1 = f64_code(v[i].y, s, z, qmin, qmax);
+        if constexpr (BITS == 4) q[g * n2 + j] = (uint8_t)((c0 & 0xf) | ((c1 & 0xf) << 4));
+        else reinterpret_cast<uint16_t*>(q + g * L)[j] = (uint16_t)((c0 & 0xff) | ((c1 & 0xff) << 8));
     }
 }
 
 enum { F64_DEQ = 0, F64_STE = 1, F64_DQB = 2 };
 
 template <int OP, int BITS, bool SIGNED>
-__global__ __launch_bounds__(256) void k_f64_ew(const void* __restrict__ a, const double* __restrict__ b, DMap m,
+__global__ __launch_bounds__(256) void k_f64_ew(const void* __restrict__ a, const double* __restrict__ b, FMap m,
                                                 double qmin, double qmax, const double* __restrict__ scale,
                                                 const uint8_t* __restrict__ zp, double* __restrict__ out)
 {
-    const int64_t npair = (m.numel + 1) / 2;
+    const int64_t npair = (m.m.numel + 1) / 2;
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < npair; t += (int64_t)gridDim.x * 256) {
         uint32_t qb = 0;
         if (OP == F64_DEQ && BITS == 4) qb = static_cast<const uint8_t*>(a)[t];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int64_t e = 2 * t + k;
-            if (e >= m.numel) break;
+            if (e >= m.m.numel) break;
             const int64_t g = m.group_of(e);
             const double s = scale[g];
             if constexpr (OP == F64_DEQ) {
@@ -210,6 +372,80 @@ __global__ __launch_bounds__(256) void k_f64_ew(const void* __restrict__ a, cons
     }
 }
 
+// Pair-interleaved as k_f64_encode8; binary64 outputs leave by non-temporal
+// 16-byte stores (whole lines per wave instruction).
+template <int OP, int BITS, bool SIGNED, bool SAMEG>
+__global__ __launch_bounds__(256) void k_f64_ew8(const void* __restrict__ a, const double* __restrict__ b, FMap m,
+                                                 double qmin, double qmax, const double* __restrict__ scale,
+                                                 const uint8_t* __restrict__ zp, double* __restrict__ out)
+{
+    const int64_t npair = m.m.numel / 2;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwave = (int64_t)gridDim.x * 4;
+    for (int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wv * 256 < npair; wv += nwave) {
+        const int64_t p0 = wv * 256 + lane;
+        double2 va[4], vb[4];
+        uint32_t cw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t p = p0 + 64 * k;
+            if (p >= npair) break;
+            if constexpr (OP == F64_DEQ) {
+                cw[k] = BITS == 4 ? (uint32_t) static_cast<const uint8_t*>(a)[p]
+                                  : (uint32_t) reinterpret_cast<const uint16_t*>(a)[p];
+            } else {
+                va[k] = reinterpret_cast<const double2*>(a)[p];
+                if constexpr (OP == F64_STE) vb[k] = reinterpret_cast<const double2*>(b)[p];
+            }
+        }
+        double s1 = 0.0, z1 = 0.0;
+        if constexpr (SAMEG) {
+            const int64_t g = m.group_of(wv * 512);
+            s1 = scale[g];
+            z1 = f64_zp(zp, g, SIGNED);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t p = p0 + 64 * k;
+            if (p >= npair) break;
+            double s[2], z[2];
+            if constexpr (SAMEG) {
+                s[0] = s[1] = s1;
+                z[0] = z[1] = z1;
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t g = m.group_of(2 * p + h);
+                    s[h] = scale[g];
+                    z[h] = f64_zp(zp, g, SIGNED);
+                }
+            }
+            double o[2];
+            if constexpr (OP == F64_DEQ) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t c = BITS == 4 ? (cw[k] >> (4 * h)) & 0xfu : (cw[k] >> (8 * h)) & 0xffu;
+                    int v = (int)c;
+                    if (SIGNED) v = BITS == 4 ? (int)((c ^ 8u) - 8u) : (int)(int8_t)c;
+                    o[h] = ((double)v - z[h]) * s[h];
+                }
+            } else if constexpr (OP == F64_DQB) {
+                o[0] = va[k].x * s[0];
+                o[1] = va[k].y * s[1];
+            } else {
+                const double xa[2] = {va[k].x, va[k].y}, ya[2] = {vb[k].x, vb[k].y};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c = f64_code(xa[h], s[h], z[h], qmin, qmax);
+                    o[h] = (ya[h] / s[h]) * ((qmin < c && c < qmax) ? 1.0 : 0.0);
+                }
+            }
+            const uint64_t b0 = __builtin_bit_cast(uint64_t, o[0]), b1 = __builtin_bit_cast(uint64_t, o[1]);
+            st16<true>(out + 2 * p, make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32)));
+        }
+    }
+}
+
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static unsigned grid_for(int64_t work, int64_t per_block)
@@ -218,6 +454,50 @@ static unsigned grid_for(int64_t work, int64_t per_block)
     if (g < 1) g = 1;
     if (g > (1 << 20)) g = 1 << 20;
     return (unsigned)g;
+}
+
+static bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// The pair-interleaved kernels need an even element count and aligned
+// buffers; their SAMEG form needs each wave-iteration's 512 elements inside
+// one group.
+static bool same_group8(const FMap& d) { return d.mode == 1 || (d.mode == 2 && d.d % 512 == 0); }
+
+template <int BITS>
+static void launch_encode(const double* x, const FMap& d, double qmin, double qmax, const double* scale,
+                          const uint8_t* zb, bool zs, uint8_t* q, hipStream_t st)
+{
+    const bool vec = d.m.numel % 2 == 0 && al(x, 16) && (BITS == 4 || al(q, 2));
+    if (vec) {
+        const dim3 grid(grid_for(d.m.numel / 2, 1024));
+        if (same_group8(d))
+            hipLaunchKernelGGL((k_f64_encode8<BITS, true>), grid, dim3(256), 0, st, x, d, qmin, qmax, scale, zb, zs, q);
+        else
+            hipLaunchKernelGGL((k_f64_encode8<BITS, false>), grid, dim3(256), 0, st, x, d, qmin, qmax, scale, zb, zs, q);
+        return;
+    }
+    const dim3 grid(grid_for((d.m.numel + 1) / 2, 256));
+    hipLaunchKernelGGL(k_f64_encode<BITS>, grid, dim3(256), 0, st, x, d, qmin, qmax, scale, zb, zs, q);
+}
+
+template <int OP, int BITS, bool SIGNED>
+static void launch_ew(const void* a, const double* b, const FMap& d, double qmin, double qmax, const double* scale,
+                      const uint8_t* zb, double* out, hipStream_t st)
+{
+    const uintptr_t aa = OP == F64_DEQ ? (BITS == 4 ? 1 : 2) : 16;
+    const bool vec = d.m.numel % 2 == 0 && al(a, aa) && (!b || al(b, 16)) && al(out, 16);
+    if (vec) {
+        const dim3 grid(grid_for(d.m.numel / 2, 1024));
+        if (same_group8(d))
+            hipLaunchKernelGGL((k_f64_ew8<OP, BITS, SIGNED, true>), grid, dim3(256), 0, st, a, b, d, qmin, qmax, scale, zb,
+                               out);
+        else
+            hipLaunchKernelGGL((k_f64_ew8<OP, BITS, SIGNED, false>), grid, dim3(256), 0, st, a, b, d, qmin, qmax, scale,
+                               zb, out);
+        return;
+    }
+    const dim3 grid(grid_for((d.m.numel + 1) / 2, 256));
+    hipLaunchKernelGGL((k_f64_ew<OP, BITS, SIGNED>), grid, dim3(256), 0, st, a, b, d, qmin, qmax, scale, zb, out);
 }
 
 // Group layout of a call; false for a bad granularity / shape.
@@ -263,7 +543,19 @@ tq_status tq_quant_f64(const double* x, int32_t ndim, const int64_t* host_shape,
     hipStream_t st = as_stream(stream);
     const double dmin = qmin, dmax = qmax;
     uint8_t* zb = static_cast<uint8_t*>(zero_point);
-    const DMap d = to_dmap(m);
+    const FMap d = to_fmap(m);
+    if (!static_scale && d.mode == 2 && d.d % 2 == 0 && d.d <= 4096 && al(x, 16) && al(q, 2) &&
+        m.ngroups <= 0x7fffffff) {
+        // contiguous groups that fit a workgroup's registers: one pass
+        uint8_t* qb = static_cast<uint8_t*>(q);
+        if (code_bits(code) == 4)
+            hipLaunchKernelGGL(k_f64_rows<4>, dim3((unsigned)m.ngroups), dim3(256), 0, st, x, (int64_t)d.d, (int)sym,
+                               dmin, dmax, scale, zb, qb);
+        else
+            hipLaunchKernelGGL(k_f64_rows<8>, dim3((unsigned)m.ngroups), dim3(256), 0, st, x, (int64_t)d.d, (int)sym,
+                               dmin, dmax, scale, zb, qb);
+        return launch_status();
+    }
     if (!static_scale) {
         if (m.kind == KIND_TENSOR) {
             if (!workspace || workspace_bytes < tq_workspace_bytes(3, m.numel)) return TQ_ERR_INVALID;
@@ -279,12 +571,9 @@ tq_status tq_quant_f64(const double* x, int32_t ndim, const int64_t* host_shape,
         }
         if (launch_status()) return TQ_ERR_HIP;
     }
-    const dim3 grid(grid_for((m.numel + 1) / 2, 256));
     uint8_t* qb = static_cast<uint8_t*>(q);
-    if (code_bits(code) == 4)
-        hipLaunchKernelGGL(k_f64_encode<4>, grid, dim3(256), 0, st, x, d, dmin, dmax, scale, zb, code_signed(code), qb);
-    else
-        hipLaunchKernelGGL(k_f64_encode<8>, grid, dim3(256), 0, st, x, d, dmin, dmax, scale, zb, code_signed(code), qb);
+    if (code_bits(code) == 4) launch_encode<4>(x, d, dmin, dmax, scale, zb, code_signed(code), qb, st);
+    else launch_encode<8>(x, d, dmin, dmax, scale, zb, code_signed(code), qb, st);
     return launch_status();
 }
 
@@ -296,17 +585,16 @@ tq_status tq_dequant_f64(const void* q, int code, int32_t ndim, const int64_t* h
     if (code_bits(code) == 4 && (host_shape[ndim - 1] & 1)) return TQ_ERR_INVALID;
     if (m.numel == 0) return TQ_OK;
     if (!q || !scale || !y) return TQ_ERR_INVALID;
-    const DMap d = to_dmap(m);
-    const dim3 grid(grid_for((m.numel + 1) / 2, 256));
+    const FMap d = to_fmap(m);
     const uint8_t* zb = static_cast<const uint8_t*>(zero_point);
     hipStream_t st = as_stream(stream);
     const bool sg = code_signed(code);
     if (code_bits(code) == 4) {
-        if (sg) hipLaunchKernelGGL((k_f64_ew<F64_DEQ, 4, true>), grid, dim3(256), 0, st, q, nullptr, d, 0.0, 0.0, scale, zb, y);
-        else hipLaunchKernelGGL((k_f64_ew<F64_DEQ, 4, false>), grid, dim3(256), 0, st, q, nullptr, d, 0.0, 0.0, scale, zb, y);
+        if (sg) launch_ew<F64_DEQ, 4, true>(q, nullptr, d, 0.0, 0.0, scale, zb, y, st);
+        else launch_ew<F64_DEQ, 4, false>(q, nullptr, d, 0.0, 0.0, scale, zb, y, st);
     } else {
-        if (sg) hipLaunchKernelGGL((k_f64_ew<F64_DEQ, 8, true>), grid, dim3(256), 0, st, q, nullptr, d, 0.0, 0.0, scale, zb, y);
-        else hipLaunchKernelGGL((k_f64_ew<F64_DEQ, 8, false>), grid, dim3(256), 0, st, q, nullptr, d, 0.0, 0.0, scale, zb, y);
+        if (sg) launch_ew<F64_DEQ, 8, true>(q, nullptr, d, 0.0, 0.0, scale, zb, y, st);
+        else launch_ew<F64_DEQ, 8, false>(q, nullptr, d, 0.0, 0.0, scale, zb, y, st);
     }
     return launch_status();
 }
@@ -320,16 +608,11 @@ tq_status tq_quant_f64_backward(const double* x, int32_t ndim, const int64_t* ho
     if (!valid_range(code, qmin, qmax, zero_point == nullptr)) return TQ_ERR_INVALID;
     if (m.numel == 0) return TQ_OK;
     if (!x || !scale || !dy || !dx) return TQ_ERR_INVALID;
-    const DMap d = to_dmap(m);
-    const dim3 grid(grid_for((m.numel + 1) / 2, 256));
+    const FMap d = to_fmap(m);
     const uint8_t* zb = static_cast<const uint8_t*>(zero_point);
     hipStream_t st = as_stream(stream);
-    if (code_signed(code))
-        hipLaunchKernelGGL((k_f64_ew<F64_STE, 8, true>), grid, dim3(256), 0, st, x, dy, d, (double)qmin, (double)qmax,
-                           scale, zb, dx);
-    else
-        hipLaunchKernelGGL((k_f64_ew<F64_STE, 8, false>), grid, dim3(256), 0, st, x, dy, d, (double)qmin, (double)qmax,
-                           scale, zb, dx);
+    if (code_signed(code)) launch_ew<F64_STE, 8, true>(x, dy, d, (double)qmin, (double)qmax, scale, zb, dx, st);
+    else launch_ew<F64_STE, 8, false>(x, dy, d, (double)qmin, (double)qmax, scale, zb, dx, st);
     return launch_status();
 }
 
@@ -340,10 +623,8 @@ tq_status tq_dequant_f64_backward(const double* dy, int32_t ndim, const int64_t*
     if (!f64_map(ndim, host_shape, gran, axis, group_size, &m)) return TQ_ERR_INVALID;
     if (m.numel == 0) return TQ_OK;
     if (!dy || !scale || !dq) return TQ_ERR_INVALID;
-    const DMap d = to_dmap(m);
-    const dim3 grid(grid_for((m.numel + 1) / 2, 256));
-    hipLaunchKernelGGL((k_f64_ew<F64_DQB, 8, false>), grid, dim3(256), 0, as_stream(stream), dy, nullptr, d, 0.0, 0.0,
-                       scale, nullptr, dq);
+    const FMap d = to_fmap(m);
+    launch_ew<F64_DQB, 8, false>(dy, nullptr, d, 0.0, 0.0, scale, nullptr, dq, as_stream(stream));
     return launch_status();
 }
 

@@ -52,6 +52,8 @@ def run_f64(tq, orc, x, gran, axis, g, code, sym, dy=None, scale=None, zp=None):
     ((12, 34), "channel", 1, 0, "u8", False),
     ((1000,), "tensor", 0, 0, "s8", True),
     ((2048, 4096), "tensor", 0, 0, "u8", False),    # two-pass reduction (chunk partials + finalize)
+    ((16, 12), "token", 0, 0, "s8", False),         # 8-element vectors that straddle rows
+    ((8, 60), "group", 1, 12, "s4", True),          # ... and groups along the last axis
 ])
 def test_f64(tq, orc, shape, gran, axis, g, code, sym):
     x = np.random.default_rng(len(shape) * 100 + shape[-1]).standard_normal(shape) * 2.5
