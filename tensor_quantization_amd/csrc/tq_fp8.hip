@@ -190,17 +190,57 @@ __device__ __forceinline__ int64_t fp8_block_of(int64_t e, int64_t cols, int64_t
     return ((e / cols) / br) * nbc + (e % cols) / bc;
 }
 
+// Block index of element e for power-of-two block shapes in a tensor of
+// fewer than 2^32 elements: row = e / cols by a multiply-high with a
+// host-computed magic number (Granlund and Montgomery's round-up method,
+// exact for every 32-bit dividend), the rest by shifts.
+struct BlkIdx {
+    uint32_t cols, mul, sh;   // cols == 0: not available
+    int lbr, lbc;
+    uint32_t nbc;
+    __device__ __forceinline__ int64_t of(int64_t e) const
+    {
+        const uint32_t n = (uint32_t)e;
+        uint32_t row = n;
+        if (cols != 1) {
+            const uint32_t t = __umulhi(mul, n);
+            row = (t + ((n - t) >> 1)) >> sh;
+        }
+        const uint32_t col = n - row * cols;
+        return (int64_t)(row >> lbr) * nbc + (col >> lbc);
+    }
+};
+
+static BlkIdx make_blkidx(int64_t n, int64_t cols, int64_t br, int64_t bc, int64_t nbc)
+{
+    BlkIdx b{};
+    const bool pow2 = br > 0 && bc > 0 && (br & (br - 1)) == 0 && (bc & (bc - 1)) == 0;
+    if (!pow2 || n > 0xffffffffLL || cols < 1 || cols > 0xffffffffLL) return b;
+    b.cols = (uint32_t)cols;
+    if (b.cols > 1) {
+        int l = 0;
+        while (((uint64_t)1 << l) < b.cols) ++l;
+        b.mul = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - b.cols)) / b.cols + 1);
+        b.sh = (uint32_t)(l - 1);
+    }
+    while (((int64_t)1 << b.lbr) < br) ++b.lbr;
+    while (((int64_t)1 << b.lbc) < bc) ++b.lbc;
+    b.nbc = (uint32_t)nbc;
+    return b;
+}
+
 // Vector path (cols % 8 == 0 and bc % 8 == 0: the 8 elements share a block).
 // SHIFT >= 0: 1 x bc blocks with cols % bc == 0 and bc = 2^SHIFT, so the
 // block of element e is e >> SHIFT (no 64-bit divisions per vector).
 template <int OP, int FT>
 __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, const void* __restrict__ b,
                                                 int64_t nvec, int64_t cols, int64_t br, int64_t bc, int64_t nbc,
-                                                int shift, const float* __restrict__ scale, void* __restrict__ out)
+                                                int shift, BlkIdx bi, const float* __restrict__ scale,
+                                                void* __restrict__ out)
 {
     for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
         const int64_t e = vi * 8;
-        const float s = scale[shift >= 0 ? (e >> shift) : fp8_block_of(e, cols, br, bc, nbc)];
+        const float s = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
         float o[8];
         if constexpr (OP == OP_DEQ) {
             const uint2 w = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + e)
@@ -549,8 +589,9 @@ static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t r
         int shift = -1;
         if (br == 1 && cols % bc == 0 && (bc & (bc - 1)) == 0)
             for (shift = 0; ((int64_t)1 << shift) < bc; ++shift) {}
+        const BlkIdx bi = shift >= 0 ? BlkIdx{} : make_blkidx(n, cols, br, bc, nbc);
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256)), dim3(256), 0, st,
-                                            a, b, n / 8, cols, br, bc, nbc, shift, scale, out));
+                                            a, b, n / 8, cols, br, bc, nbc, shift, bi, scale, out));
     } else {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew_generic<OP, FTV>), dim3(grid_for(n, 256)), dim3(256), 0, st,
                                             a, b, n, cols, br, bc, nbc, scale, out));
