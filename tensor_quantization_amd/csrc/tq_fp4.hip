@@ -255,12 +255,14 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
 // dst[c * ldd + off + r] = src[r][c] for a [R, C] byte matrix: the transpose
 // written into columns off..off+R-1 of a [C, ldd] matrix (ldd = R, off = 0 for
 // a plain transpose).  Fast path: R, C, ldd and off multiples of 16 and
-// 16-byte aligned bases; tiles of 128 x 128 bytes, so that
-// every wave-wide load and store instruction covers whole 128-byte lines.  Thread (d, m) of the read-out phase owns input columns 4d..4d+3 and
-// input rows 16m..16m+15: it reads 16 dwords from LDS, transposes four 4x4
-// byte blocks in registers and writes 16 bytes to each of 4 output rows; the
-// 8 threads with the same d write one full 128-byte output line per row.
-constexpr int TR = 128, TR_PITCH = TR / 4 + 1;   // dwords per LDS row, padded
+// 16-byte aligned bases; tiles of 256 x 256 bytes staged through LDS, so that
+// every input row is read and every output row written in 256-byte segments
+// (measured on the FP4 weight transposes: 128 x 128 tiles reach about 55% of
+// HBM peak, 256 x 256 tiles about 62%).
+constexpr int TRR = 256, TRC = 256, TR_PITCH = TRC / 4 + 1;   // dwords per LDS row, padded
+// 65 KB of LDS per workgroup: two resident per CU, 512 on the chip; the
+// launch never asks for more, and each workgroup walks its share of tiles.
+constexpr int64_t TR_GRID = 512;
 
 __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t o[4])
 {
@@ -275,52 +277,78 @@ __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t 
     o[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-// One 128 x 128-byte tile (rows R0.., columns C0.. of src) through LDS.
-__device__ __forceinline__ void transpose_tile(const uint8_t* __restrict__ src, int64_t R, int64_t C,
-                                               uint8_t* __restrict__ dst, int64_t ldd, int64_t R0, int64_t C0,
-                                               uint32_t* tile)
+// One 128 x 128-byte tile (rows R0.., columns C0.. of src) of job J.
+struct TileAt {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t R, C, ldd, R0, C0;
+};
+
+// Tiles of TRR rows x TRC bytes.  Load: TRC/16 threads share an input row, so
+// each wave instruction reads whole lines; read-out: thread (m, d) owns input
+// columns 4d..4d+3 and input rows 16m..16m+15, reads 16 dwords from LDS,
+// transposes four 4x4 byte blocks in registers and writes 16 bytes to each of
+// 4 output rows; the TRR/16 threads with the same d write one TRR-byte output
+// segment per row.
+constexpr int TR_LOADS = TRR * TRC / 16 / 256, TR_OUTS = TRR * TRC / 64 / 256;
+
+__device__ __forceinline__ void tile_load(const TileAt& T, uint4 w[TR_LOADS])
 {
     const int t = threadIdx.x;
-    uint4 w[4];
+    constexpr int TPR = TRC / 16, RPP = 256 / TPR;    // threads per row, rows per pass
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int r = t / 8 + 32 * k;
-        const int cq = (t % 8) * 16;
+    for (int k = 0; k < TR_LOADS; ++k) {
+        const int r = t / TPR + RPP * k;
+        const int cq = (t % TPR) * 16;
         w[k] = make_uint4(0, 0, 0, 0);
-        if (R0 + r < R && C0 + cq < C) w[k] = ld16<true>(src + (R0 + r) * C + C0 + cq);
+        if (T.R0 + r < T.R && T.C0 + cq < T.C) w[k] = ld16<true>(T.src + (T.R0 + r) * T.C + T.C0 + cq);
     }
+}
+
+__device__ __forceinline__ void tile_stage(const uint4 w[TR_LOADS], uint32_t* tile)
+{
+    const int t = threadIdx.x;
+    constexpr int TPR = TRC / 16, RPP = 256 / TPR;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t* row = tile + (t / 8 + 32 * k) * TR_PITCH + (t % 8) * 4;
+    for (int k = 0; k < TR_LOADS; ++k) {
+        uint32_t* row = tile + (t / TPR + RPP * k) * TR_PITCH + (t % TPR) * 4;
         row[0] = w[k].x;
         row[1] = w[k].y;
         row[2] = w[k].z;
         row[3] = w[k].w;
     }
-    __syncthreads();
-    const int m = t % 8, d = t / 8;        // read-out: rows 16m..16m+15, columns 4d..4d+3
-    uint32_t o[4][4];                       // o[c][qd]: output row 4d+c, bytes 4*qd.. of this 16-byte piece
+}
+
+__device__ __forceinline__ void tile_store(const TileAt& T, const uint32_t* tile)
+{
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-        const int rb = 16 * m + 4 * qd;
-        uint32_t tr[4];
-        transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d], tile[(rb + 2) * TR_PITCH + d],
-                     tile[(rb + 3) * TR_PITCH + d], tr);
+    for (int p = 0; p < TR_OUTS; ++p) {
+        const int t = threadIdx.x + 256 * p;
+        const int m = t % (TRR / 16), d = t / (TRR / 16);
+        uint32_t o[4][4];                       // o[c][qd]: output row 4d+c, bytes 4*qd.. of this 16-byte piece
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
-    }
+        for (int qd = 0; qd < 4; ++qd) {
+            const int rb = 16 * m + 4 * qd;
+            uint32_t tr[4];
+            transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d],
+                         tile[(rb + 2) * TR_PITCH + d], tile[(rb + 3) * TR_PITCH + d], tr);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int64_t oc = C0 + 4 * d + c;        // output row = input column
-        const int64_t orr = R0 + 16 * m;          // output column = input row
-        if (oc < C && orr < R) st16<true>(dst + oc * ldd + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
+            for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t oc = T.C0 + 4 * d + c;      // output row = input column
+            const int64_t orr = T.R0 + 16 * m;        // output column = input row
+            if (oc < T.C && orr < T.R)
+                st16<true>(T.dst + oc * T.ldd + orr, make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]));
+        }
     }
 }
 
 // Several transposes in one launch (codes and block scales of a weight, every
-// part of a concatenation): block b does tile b - tile0 of the job whose
-// range holds b, so small matrices (the block scales) fill the chip together
-// with the large ones instead of running as a separate under-occupied launch.
+// part of a concatenation): tile b belongs to the job whose range holds b, so
+// small matrices (the block scales) fill the chip together with the large ones
+// instead of running as a separate under-occupied launch.
 struct TJob {
     const uint8_t* src;
     uint8_t* dst;
@@ -331,18 +359,46 @@ constexpr int MAX_TJOBS = 8;
 struct TJobs {
     TJob j[MAX_TJOBS];
     int n;
+    int64_t tiles;
 };
 
-__global__ __launch_bounds__(256) void k_transpose_jobs(const TJobs jobs)
+__device__ __forceinline__ TileAt tile_at(const TJobs& jobs, int64_t b)
 {
-    __shared__ uint32_t tile[TR * TR_PITCH];
-    const int64_t b = blockIdx.x;
     int k = 0;
     for (int i = 1; i < jobs.n; ++i)
         if (b >= jobs.j[i].tile0) k = i;
-    const TJob J = jobs.j[k];
+    const TJob& J = jobs.j[k];
     const int64_t tl = b - J.tile0;
-    transpose_tile(J.src, J.R, J.C, J.dst, J.ldd, (tl / J.tiles_c) * TR, (tl % J.tiles_c) * TR, tile);
+    return TileAt{J.src, J.dst, J.R, J.C, J.ldd, (tl / J.tiles_c) * TRR, (tl % J.tiles_c) * TRC};
+}
+
+// A workgroup walks tiles b, b + gridDim.x, ...; the next tile's loads are
+// issued as soon as the current one sits in LDS, so they are in flight while
+// the current tile is read out and stored (with one tile per workgroup every
+// workgroup on the chip would read, then write, in lock step).
+__global__ __launch_bounds__(256) void k_transpose_jobs(const TJobs jobs)
+{
+    __shared__ uint32_t tile[TRR * TR_PITCH];
+    int64_t b = blockIdx.x;
+    TileAt T = tile_at(jobs, b);
+    uint4 w[TR_LOADS];
+    tile_load(T, w);
+    for (;;) {
+        tile_stage(w, tile);
+        __syncthreads();
+        const int64_t nb = b + gridDim.x;
+        const bool more = nb < jobs.tiles;
+        TileAt Tn = T;
+        if (more) {
+            Tn = tile_at(jobs, nb);
+            tile_load(Tn, w);
+        }
+        tile_store(T, tile);
+        if (!more) break;
+        __syncthreads();
+        b = nb;
+        T = Tn;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_transpose_u8_generic(const uint8_t* __restrict__ src, int64_t R, int64_t C,
@@ -479,7 +535,9 @@ struct TransposeBatch {
             err = TQ_ERR_UNSUPPORTED;
             return;
         }
-        hipLaunchKernelGGL(k_transpose_jobs, dim3((unsigned)tiles), dim3(256), 0, st, jobs);
+        jobs.tiles = tiles;
+        const int64_t grid = tiles < TR_GRID ? tiles : TR_GRID;
+        hipLaunchKernelGGL(k_transpose_jobs, dim3((unsigned)grid), dim3(256), 0, st, jobs);
         err = launch_status();
         jobs.n = 0;
         tiles = 0;
@@ -496,8 +554,8 @@ struct TransposeBatch {
             j.C = C;
             j.ldd = ldd;
             j.tile0 = tiles;
-            j.tiles_c = cdiv(C, TR);
-            tiles += j.tiles_c * cdiv(R, TR);
+            j.tiles_c = cdiv(C, TRC);
+            tiles += j.tiles_c * cdiv(R, TRR);
         } else {
             if (cdiv(R, 64) > 65535) {
                 err = TQ_ERR_UNSUPPORTED;

@@ -85,7 +85,10 @@ def test_e2m1_conversion_dense(tq, orc):
 
 
 def test_transpose_for_gemm(tq, orc):
-    for (n, k, kind) in [(14336 // 7, 4096, "nvfp4"), (256, 1024, "mxfp4"), (40, 96, "nvfp4"), (24, 64, "mxfp4")]:
+    # tiled path with whole tiles, tiled path with ragged 256 x 256 tiles in
+    # both directions, generic path (rows not a multiple of 16)
+    for (n, k, kind) in [(14336 // 7, 4096, "nvfp4"), (256, 1024, "mxfp4"), (784, 1056, "nvfp4"),
+                         (528, 2080, "mxfp4"), (40, 96, "nvfp4"), (24, 64, "mxfp4")]:
         gs = 16 if kind == "nvfp4" else 32
         x = workloads.normal((n, k), 0.02, n + k, "bf16")
         p, b, _ = tq.tq_quant_fp4_block(to_dev(x, "bf16"), kind)
@@ -133,6 +136,7 @@ def _quant_parts(tq, ns, k, kind, seed0):
 @pytest.mark.parametrize("ns,k,kind,align", [
     ([2048, 512, 512], 4096, "nvfp4", 1),       # fused QKV-like: tiled path, no pad
     ([256, 128], 1024, "mxfp4", 512),           # tiled path, 128 pad columns
+    ([272, 48], 544, "nvfp4", 1),               # tiled path, ragged tiles, part offset inside a tile
     ([1001], 256, "nvfp4", 16),                 # odd N: generic path, 7 pad columns
     ([40, 24, 33], 96, "nvfp4", 64),            # ragged parts
     ([0, 48, 0, 16], 64, "mxfp4", 1),           # empty parts
