@@ -23,3 +23,14 @@ def test_one_correction_division_is_exact(prog, fbits):
     out = subprocess.run([prog, str(fbits)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stdout + out.stderr
     assert " 0 mismatches" in out.stdout
+
+
+def test_two_correction_binary64_division(tmp_path):
+    """The binary64 quantize kernels divide by x * RN(1/s) with two FMA
+    corrections: equal to IEEE a / b on 4M random pairs and 1.5M pairs whose
+    quotient lies within 2^-105 of a midpoint between binary64 numbers."""
+    exe = str(tmp_path / "division_f64")
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-o", exe, os.path.join(HERE, "division_f64.c"), "-lm"])
+    out = subprocess.run([exe, "2000000"], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "two corrections: 0 mismatches" in out.stdout

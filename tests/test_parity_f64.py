@@ -54,6 +54,11 @@ def run_f64(tq, orc, x, gran, axis, g, code, sym, dy=None, scale=None, zp=None):
     ((2048, 4096), "tensor", 0, 0, "u8", False),    # two-pass reduction (chunk partials + finalize)
     ((16, 12), "token", 0, 0, "s8", False),         # 8-element vectors that straddle rows
     ((8, 60), "group", 1, 12, "s4", True),          # ... and groups along the last axis
+    ((30, 400), "token", 0, 0, "u8", False),        # one-pass rows at 64, 128, 256, 512 and 1024
+    ((40, 1000), "token", 0, 0, "u8", False),       # threads, rows not a multiple of the
+    ((6, 4096), "group", 1, 2048, "u4", False),     # workgroup's reach
+    ((20, 2050), "token", 0, 0, "s4", True),
+    ((4, 6000), "token", 0, 0, "u8", False),
 ])
 def test_f64(tq, orc, shape, gran, axis, g, code, sym):
     x = np.random.default_rng(len(shape) * 100 + shape[-1]).standard_normal(shape) * 2.5
@@ -78,3 +83,34 @@ def test_f64_empty(tq):
     x = torch.empty((0, 8), dtype=torch.float64, device="cuda")
     q, s, _ = tq.tq_quant_f64(x, "token")
     assert q.numel() == 0
+
+
+def _near_ties(rng, s, n):
+    """n elements next to (k + 1/2) * s, |k| <= 126: the tie itself and up to
+    two binary64 steps either side."""
+    x = (rng.integers(-126, 126, size=n).astype(np.float64) + 0.5) * s
+    for _ in range(2):
+        step = rng.integers(-1, 2, size=n)
+        x = np.where(step > 0, np.nextafter(x, np.inf), np.where(step < 0, np.nextafter(x, -np.inf), x))
+    return x
+
+
+def test_f64_quotient_edges(tq, orc):
+    """The quantize kernels divide by two FMA corrections of x * RN(1/s) when
+    2^-400 <= |s| <= 2^400 (and, for static scales, |x| <= 2^600), otherwise
+    by IEEE division: quotients at and next to the ties k + 1/2, scales on
+    both sides of the guard, huge, infinite and subnormal elements."""
+    rng = np.random.default_rng(21)
+    # dynamic per-token (one pass): amax fixes s = amax / 127, the rest sit at ties of s
+    amax = rng.uniform(1.0, 2.0, size=6) * 2.0 ** np.array([-40, -3, 0, 5, 300, -398])
+    x = np.stack([_near_ties(rng, a / 127.0, 1024) for a in amax])
+    x[:, 7] = amax
+    run_f64(tq, orc, x, "token", 0, 0, "s8", True)
+    # static per-tensor scales: fast (2^-300, exactly 2^-400, 1.5) and slow (2^-401, 2^401)
+    for s, sub in ((2.0 ** -300, False), (2.0 ** -400, True), (1.5, True), (2.0 ** -401, True), (2.0 ** 401, False)):
+        x = _near_ties(rng, s, 8 * 1024).reshape(8, 1024)
+        if sub:
+            x[0, :4] = [5e-324, -5e-324, 1e-310, -2.0 ** -1000]
+        x[1, :6] = [np.inf, -np.inf, 2.0 ** 601, -2.0 ** 600, 1e308, -1e308]
+        run_f64(tq, orc, x, "tensor", 0, 0, "s8", True, scale=np.array([s]))
+        run_f64(tq, orc, x, "tensor", 0, 0, "u8", False, scale=np.array([s]), zp=np.array([128], np.uint8))
