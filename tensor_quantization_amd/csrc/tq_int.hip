@@ -41,21 +41,26 @@ struct GP {
 // RN(1/(qmax - qmin)) (asymmetric), computed once on the host.  amax and mn
 // are element values of type FT (or 0); the asymmetric range mx - mn is a
 // general binary32 value.
+// f16 groups never leave the fast ranges: amax, -mn and mx - mn are 0 or in
+// [2^-24, 131008], so with 1 <= qmax, qmax - qmin <= 255 the scale lies in
+// [2^-32, 131008] (or is 1) and every guard below is statically true.
 template <int FT, bool SYM>
 __device__ __forceinline__ GP make_gp(float amax, float mn, float mx, float qmin, float qmax, float yc)
 {
+    constexpr bool ALWAYS_FAST = FT == F16;
     GP p;
     float s;
-    if constexpr (SYM) s = div_by<FT>(amax, qmax, yc);
-    else s = div_by<F32>(mx - mn, qmax - qmin, yc);
+    if constexpr (SYM) s = ALWAYS_FAST ? div_q<FT>(amax, qmax, yc) : div_by<FT>(amax, qmax, yc);
+    else s = ALWAYS_FAST ? div_q<F32>(mx - mn, qmax - qmin, yc) : div_by<F32>(mx - mn, qmax - qmin, yc);
     s = (s == 0.0f) ? 1.0f : s;
     p.s = s;
-    p.fast = scale_in_fast_range(s);
+    p.fast = ALWAYS_FAST || scale_in_fast_range(s);
     p.y = p.fast ? rcp_rn(s) : 0.0f;
     if constexpr (SYM) {
         p.zpf = 0.0f;
     } else {
-        const float t = (p.fast && (value_in_fast_range(mn) || mn == 0.0f)) ? div_q<FT>(mn, s, p.y) : mn / s;
+        const float t = (ALWAYS_FAST || (p.fast && (value_in_fast_range(mn) || mn == 0.0f))) ? div_q<FT>(mn, s, p.y)
+                                                                                              : mn / s;
         p.zpf = __builtin_amdgcn_fmed3f(qmin - __builtin_rintf(t), qmin, qmax);
     }
     return p;
@@ -126,18 +131,32 @@ __device__ __forceinline__ void f16_stats(const Raw8<F16>* raw, float& amax, flo
     typedef uint16_t u2v __attribute__((ext_vector_type(2)));
     u2v amx = {0, 0};                    // |x| patterns: unsigned order is magnitude order
     uint32_t hmx = 0, hmn = 0;           // two packed f16 zeros
+    if constexpr (SYM) {
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-        const uint32_t d[4] = {raw[w].w[0].x, raw[w].w[0].y, raw[w].w[0].z, raw[w].w[0].w};
+        for (int w = 0; w < W; ++w) {
+            const uint32_t d[4] = {raw[w].w[0].x, raw[w].w[0].y, raw[w].w[0].z, raw[w].w[0].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (SYM) {
-                amx = __builtin_elementwise_max(amx, __builtin_bit_cast(u2v, d[i] & 0x7fff7fffu));
-            } else {
-                hmn = pk_min_f16(hmn, d[i]);
-                hmx = pk_max_f16(hmx, d[i]);
-            }
+            for (int i = 0; i < 4; ++i) amx = __builtin_elementwise_max(amx, __builtin_bit_cast(u2v, d[i] & 0x7fff7fffu));
         }
+    } else {
+        // pairwise tree over the 4W words (independent neighbours, no stalls
+        // between dependent packed ops), then the zeros
+        uint32_t lo[4 * W], hi[4 * W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const uint32_t d[4] = {raw[w].w[0].x, raw[w].w[0].y, raw[w].w[0].z, raw[w].w[0].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lo[4 * w + i] = hi[4 * w + i] = d[i];
+        }
+#pragma unroll
+        for (int n = 4 * W; n > 1; n /= 2)
+#pragma unroll
+            for (int i = 0; i < n / 2; ++i) {
+                lo[i] = pk_min_f16(lo[2 * i], lo[2 * i + 1]);
+                hi[i] = pk_max_f16(hi[2 * i], hi[2 * i + 1]);
+            }
+        hmn = pk_min_f16(hmn, lo[0]);
+        hmx = pk_max_f16(hmx, hi[0]);
     }
     if constexpr (SYM) {
         amax = mx = f16_lo(amx.x > amx.y ? amx.x : amx.y);
