@@ -180,10 +180,8 @@ __global__ __launch_bounds__(256) void k_fp8_generic(const void* __restrict__ x,
 
 // ------------------------------------------------------------ elementwise
 enum { OP_DEQ = 0, OP_STE = 1, OP_DQB = 2 };
-#ifndef TQ_EW_NT
-#define TQ_EW_NT 0
-#endif
-constexpr bool EW_NT = TQ_EW_NT != 0;   // non-temporal code loads in the dequantizers
+// Plain code loads in the dequantizers (non-temporal ones measured no faster).
+constexpr bool EW_NT = false;
 
 __device__ __forceinline__ int64_t fp8_block_of(int64_t e, int64_t cols, int64_t br, int64_t bc, int64_t nbc)
 {
@@ -545,10 +543,7 @@ static bool quant_fast(const void* x, int64_t rows, int64_t cols, int64_t br, in
         case 16: launch_rows<FT, 2, 1, 8>(x, nb, q, scale, st); return true;
         case 32: launch_rows<FT, 4, 1, 8>(x, nb, q, scale, st); return true;
         case 64: launch_rows<FT, 8, 1, 8>(x, nb, q, scale, st); return true;
-#ifndef TQ_FP8_U
-#define TQ_FP8_U 1
-#endif
-        case 128: launch_rows<FT, 8, 2, TQ_FP8_U>(x, nb, q, scale, st); return true;
+        case 128: launch_rows<FT, 8, 2, 1>(x, nb, q, scale, st); return true;
         case 256: launch_rows<FT, 16, 2, 4>(x, nb, q, scale, st); return true;
         case 512: launch_rows<FT, 64, 1, 8>(x, nb, q, scale, st); return true;
         default: return false;
@@ -686,10 +681,7 @@ tq_status tq_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t k, ui
     if (s || rows * k == 0) return s;
     if (!x || !q || !block_scale) return TQ_ERR_INVALID;
     if (!aligned16(x) || !aligned16(q)) return TQ_ERR_ALIGN;
-#ifndef TQ_MX8_U
-#define TQ_MX8_U 2
-#endif
-    constexpr int U = TQ_MX8_U;
+    constexpr int U = 2;   // 32-element blocks per lane in flight (1 and 4 measured slower)
     const int64_t nb = rows * k / 32;
     const int64_t grid = cdiv(cdiv(nb, U * 16), 4);
     if (grid > 0x7fffffff) return TQ_ERR_UNSUPPORTED;

@@ -812,31 +812,19 @@ __device__ __forceinline__ float zp_f(const uint8_t* zp, int64_t g)
     return SIGNED ? (float)(int8_t)zp[g] : (float)zp[g];
 }
 
-#ifndef TQ_VPT
-#define TQ_VPT 1
-#endif
-#ifndef TQ_VPT4
-#define TQ_VPT4 TQ_VPT
-#endif
-#ifndef TQ_STE_VPT
-#define TQ_STE_VPT 1
-#endif
-constexpr int SVPT = TQ_STE_VPT;
-#ifndef TQ_DEQ_NT
-#define TQ_DEQ_NT 1
-#endif
-constexpr bool DEQ_NT = TQ_DEQ_NT != 0;
-#ifndef TQ_DQB_VPT
-#define TQ_DQB_VPT 1
-#endif
-constexpr int DVPT = TQ_DQB_VPT;
+// Vectors of 8 per thread and grid step in the streaming kernels: one each
+// (two or four, and grids capped at 1024 or 2048 workgroups, measured slower).
+// 8-bit codes come through non-temporal loads, 4-bit codes through plain ones
+// (the 4-byte lane loads of a 1:4 read:write stream are faster that way).
+constexpr int DQV1 = 1, SVPT = 1, DVPT = 1;
+constexpr bool DEQ_NT = true;
 
 template <int MAPK, int YT, int BITS, bool SIGNED>
 __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__ q, int64_t nvec, int64_t P1,
                                                      int64_t P2, int sh, const float* __restrict__ scale,
                                                      const uint8_t* __restrict__ zp, void* __restrict__ y)
 {
-    constexpr int DQV = BITS == 4 ? TQ_VPT4 : TQ_VPT;   // vectors per thread per iteration
+    constexpr int DQV = DQV1;   // vectors per thread per iteration
     for (int64_t base = (int64_t)blockIdx.x * 256 * DQV; base < nvec; base += (int64_t)gridDim.x * 256 * DQV) {
 #pragma unroll
         for (int k = 0; k < DQV; ++k) {
@@ -1101,28 +1089,16 @@ static void quant_contig(const void* x, int64_t G, int64_t L, int64_t ldx, float
     case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
-#ifndef TQ_G128_U
-#define TQ_G128_U 1
-#endif
-#ifndef TQ_G128_T
-#define TQ_G128_T 8
-#endif
-    case 128: launch_team<FT, BITS, SYM, TQ_G128_T, 16 / TQ_G128_T, TQ_G128_U>(x, G, ldx, qmin, qmax, yc, q, scale, zp,
-                                                                             st);
-        return;
+    case 128: launch_team<FT, BITS, SYM, 8, 2, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 256: launch_team<FT, BITS, SYM, 16, 2, 4>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 2048: launch_team<FT, BITS, SYM, 64, 4, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
-#ifndef TQ_ROW4096
-#define TQ_ROW4096 4
-#endif
     case 4096:
-        if (TQ_ROW4096 == 4 && G <= 0x7fffffff) {
+        // a 4-wave workgroup per group, 2 loads per thread (8 waves with 1 load and a wave per group with 8
+        // measured slower)
+        if (G <= 0x7fffffff) {
             hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 4, 2>), dim3((unsigned)G), dim3(256), 0, st, x, ldx, qmin,
-                               qmax, yc, q, scale, zp);
-        } else if (TQ_ROW4096 == 8 && G <= 0x7fffffff) {
-            hipLaunchKernelGGL((k_quant_rows<FT, BITS, SYM, 8, 1>), dim3((unsigned)G), dim3(512), 0, st, x, ldx, qmin,
                                qmax, yc, q, scale, zp);
         } else {
             launch_team<FT, BITS, SYM, 64, 8, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st);
@@ -1215,19 +1191,11 @@ static int log2_exact(int64_t v)
     return k;
 }
 
-#ifndef TQ_EW_GRID
-#define TQ_EW_GRID 0
-#endif
-static unsigned ew_grid(int64_t nvec, int64_t per_block)
-{
-    const unsigned g = grid_for(nvec, per_block);
-    return (TQ_EW_GRID > 0 && g > (unsigned)TQ_EW_GRID) ? (unsigned)TQ_EW_GRID : g;
-}
 
 template <int MAPK>
 static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int64_t P2, hipStream_t st)
 {
-    const dim3 grid(ew_grid(nvec, 256 * (code_bits(a.code) == 4 ? TQ_VPT4 : TQ_VPT))), block(256);
+    const dim3 grid(grid_for(nvec, 256 * DQV1)), block(256);
     const bool sg = code_signed(a.code);
     const int bits = code_bits(a.code);
     const int sh = MAPK == MAP_CONTIG ? log2_exact(P1) : -1;
@@ -1241,12 +1209,12 @@ static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int
         });
     } else if (op == OP_STE) {
         TQ_FT_SWITCH(a.in_type, {
-            const dim3 sgrid(ew_grid(nvec, 256 * SVPT));
+            const dim3 sgrid(grid_for(nvec, 256 * SVPT));
             if (sg) hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, true>), sgrid, block, 0, st, a.a, a.b, nvec, P1, P2, sh, a.qmin, a.qmax, a.scale, a.zp, a.out);
             else hipLaunchKernelGGL((k_ste_vec<MAPK, FTV, false>), sgrid, block, 0, st, a.a, a.b, nvec, P1, P2, sh, a.qmin, a.qmax, a.scale, a.zp, a.out);
         });
     } else {
-        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), dim3(ew_grid(nvec, 256 * DVPT)), block, 0, st, a.a, nvec, P1, P2, sh, a.scale, a.out));
+        TQ_FT_SWITCH(a.in_type, hipLaunchKernelGGL((k_dqb_vec<MAPK, FTV>), dim3(grid_for(nvec, 256 * DVPT)), block, 0, st, a.a, nvec, P1, P2, sh, a.scale, a.out));
     }
 }
 
