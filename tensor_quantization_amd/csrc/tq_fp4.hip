@@ -18,7 +18,7 @@
 //   k_fp4_quant      a team of 2 (NVFP4) / 4 (MXFP4) lanes per block, block max
 //                    through DPP, U rounds per wave; reads s_g from global_scale.
 //   k_fp4_ew         dequant / STE / dequant-backward, 8 elements per step.
-//   k_transpose_jobs byte transposes through 128 x 128-byte LDS tiles with
+//   k_transpose_jobs byte transposes through 256 x 256-byte LDS tiles with
 //                    4 x 4 register transposes and 16-byte stores, into a
 //                    destination of any row stride (concatenation, padding).
 //   k_fp4_to_fp8     FP4 -> E4M3 with the per-tensor scale folded in.
@@ -275,7 +275,7 @@ __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t 
     o[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-// One 128 x 128-byte tile (rows R0.., columns C0.. of src) of job J.
+// One TRR x TRC-byte tile (rows R0.., columns C0.. of src) of a transpose job.
 struct TileAt {
     const uint8_t* src;
     uint8_t* dst;
