@@ -543,7 +543,8 @@ __global__ __launch_bounds__(256) void k_f64_ew8(const void* __restrict__ a, con
                 }
             }
             const uint64_t b0 = __builtin_bit_cast(uint64_t, o[0]), b1 = __builtin_bit_cast(uint64_t, o[1]);
-            st16<true>(out + 2 * p, make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32)));
+            st16<OP == F64_DEQ ? WT : 1>(out + 2 * p,
+                                         make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32)));
         }
     }
 }

@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void k_copy_segments(const CSegs segs)
     const CSeg S = segs.s[k];
     const int64_t i = (b - S.block0) * 256 + threadIdx.x;
     if (i >= S.units) return;
-    if (S.unit == 16) st16<true>(S.dst + i * 16, ld16<true>(S.src + i * 16));
+    if (S.unit == 16) st16<WT>(S.dst + i * 16, ld16<true>(S.src + i * 16));
     else if (S.unit == 8) st8<true>(S.dst + i * 8, ld8<true>(S.src + i * 8));
     else S.dst[i] = S.src[i];
 }
@@ -492,9 +492,9 @@ __global__ __launch_bounds__(256) void k_fp4_to_fp8(const uint8_t* __restrict__ 
             d[8 + 2 * b] = hi.x * eff;
             d[8 + 2 * b + 1] = hi.y * eff;
         }
-        st16<true>(out + i * 16, make_uint4(e4m3_pack4(d[0], d[1], d[2], d[3]), e4m3_pack4(d[4], d[5], d[6], d[7]),
-                                            e4m3_pack4(d[8], d[9], d[10], d[11]),
-                                            e4m3_pack4(d[12], d[13], d[14], d[15])));
+        st16<WT>(out + i * 16, make_uint4(e4m3_pack4(d[0], d[1], d[2], d[3]), e4m3_pack4(d[4], d[5], d[6], d[7]),
+                                          e4m3_pack4(d[8], d[9], d[10], d[11]),
+                                          e4m3_pack4(d[12], d[13], d[14], d[15])));
     }
 }
 

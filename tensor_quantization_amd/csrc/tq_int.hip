@@ -863,7 +863,7 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
                 const uint32_t c = BITS == 8 ? (cw[i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[0] >> (i * 4)) & 0xfu;
                 out[i] = (code_f<SIGNED>(c, BITS) - zv[i]) * sv[i];
             }
-            store8<YT, true>(y, e, out);
+            store8<YT, BITS == 8 ? WT : 1>(y, e, out);
         }
     }
 }
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(256) void k_dqb_vec(const void* __restrict__ dy, in
             widen8<FT>(raw[k], v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = v[i] * scale[MAPK == MAP_CONTIG ? g : g + i];
-            store8<FT, true>(dq, e, v);
+            store8<FT, WT>(dq, e, v);
         }
     }
 }
