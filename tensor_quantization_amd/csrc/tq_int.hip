@@ -278,6 +278,10 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
 
     const float lo = MAGIC + qmin, hi = MAGIC + qmax;
     const float nz = opaque(-0.0f);
+    // Non-temporal code stores where a wave's store instructions cover whole
+    // lines: T = 64 (each instruction), T = 8 (the W = 2 instructions of a
+    // team together; measured 1% faster on g = 128 4-bit codes).
+    constexpr bool CNT = T == 64 || T == 8;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t g = g0 + (int64_t)u * P;
@@ -287,12 +291,12 @@ __global__ __launch_bounds__(256) void k_quant_team(const void* __restrict__ x, 
         if (p[u].fast) {
 #pragma unroll
             for (int w = 0; w < W; ++w)
-                encode_store8<FT, true, SYM, BITS, (T == 64)>(v[u][w], raw[u][w], p[u], lo, hi, lo_z, hi_z, zn, nz, q,
+                encode_store8<FT, true, SYM, BITS, CNT>(v[u][w], raw[u][w], p[u], lo, hi, lo_z, hi_z, zn, nz, q,
                                                              g * L + (int64_t)(w * T + j) * 8);
         } else {
 #pragma unroll
             for (int w = 0; w < W; ++w)
-                encode_store8<FT, false, SYM, BITS, (T == 64)>(v[u][w], raw[u][w], p[u], lo, hi, lo_z, hi_z, zn, nz, q,
+                encode_store8<FT, false, SYM, BITS, CNT>(v[u][w], raw[u][w], p[u], lo, hi, lo_z, hi_z, zn, nz, q,
                                                               g * L + (int64_t)(w * T + j) * 8);
         }
         if (j == 0) {
