@@ -357,6 +357,17 @@ def breakdown(torch, tq, iters=20, only=None):
             bench_op("quant_mxfp4", cfg, nb, mk,
                      lambda b: check(L.tq_quant_fp4_block(P(b["x"]), 2, N5, K5, 1, P(b["p"]), P(b["b"]), None, 1,
                                                           None, 0, stream), "mxfp4"), nb + n5, n5 * 2)
+        # dequantize -> bf16 (A7 on the c5 weight): valid E2M1 codes, block scales of 1 (E4M3 0x38 / E8M0 127)
+        mkd = lambda i, gs=gs, kind=kind: dict(
+            p=torch.randint(0, 256, (N5, K5 // 2), dtype=u8, device="cuda"),
+            b=torch.full((N5, K5 // gs), 0x38 if kind == "nvfp4" else 127, dtype=u8, device="cuda"),
+            g=torch.full((1,), 1.2e-5, dtype=f32, device="cuda"), y=E((N5, K5), bf16))
+        db = n5 // 2 + n5 // gs + (4 if kind == "nvfp4" else 0) + n5 * 2
+        bench_op("dequant_" + kind, cfg, db, mkd,
+                 lambda b, kd=(0 if kind == "nvfp4" else 1): check(
+                     L.tq_dequant_fp4_block(P(b["p"]), P(b["b"]), P(b["g"]) if kd == 0 else None, N5, K5, kd,
+                                            P(b["y"]), 2, stream), "fp4 dequant"),
+                 db, n5 // 2 + n5 // gs)
         tb = 2 * (n5 // 2 + n5 // gs)
         bench_op("transpose_for_gemm_" + kind, cfg, tb, mk,
                  lambda b, gs=gs: check(L.tq_fp4_transpose_for_gemm(P(b["p"]), P(b["b"]), N5, K5, gs, P(b["pt"]),
