@@ -1,4 +1,4 @@
-"""Randomized GPU parity sweep of the integer-code family: 64 seeded cases
+"""Randomized GPU parity sweeps.  The integer-code family: 64 seeded cases
 draw the granularity, the rank (1-3), the shape (ragged and odd sizes
 included), the axis, the group size among the divisors of that axis, the
 input type, the code, symmetric or zero-point, and plain or "nasty" values;
@@ -87,3 +87,24 @@ def test_random_fp8_and_fp4_cases(tq, orc):
         note("random fp4 case", case)
         x = workloads.normal((rows, k), float(rng.choice([0.02, 1.0, 50.0])), 8000 + case, xt)
         run_fp4(tq, orc, x, xt, kind, dy=workloads.normal((rows, k), 1.0, 8500 + case, xt))
+
+
+def test_random_f64_and_mxfp8_cases(tq, orc):
+    """24 seeded binary64 cases (every granularity, rank 1-3, integer codes)
+    and 16 MXFP8 cases (K a multiple of 32, all three input types)."""
+    from test_parity_f64 import run_f64
+    from test_parity_mxfp8 import run_mx8
+    rng = np.random.default_rng(31)
+    for case in range(24):
+        gran, shape, axis, g, code, sym, _, _ = _draw(rng)
+        note("random f64 case", case)
+        x = np.random.default_rng(6000 + case).standard_normal(shape) * float(rng.choice([1e-3, 2.5, 1e5]))
+        dy = np.random.default_rng(6500 + case).standard_normal(shape)
+        run_f64(tq, orc, x, gran, axis, g, code, sym, dy=dy)
+    for case in range(16):
+        rows = int(rng.integers(1, 200))
+        k = 32 * int(rng.integers(1, 40))
+        xt = FTS[rng.integers(len(FTS))]
+        note("random mxfp8 case", case)
+        x = workloads.normal((rows, k), float(rng.choice([0.02, 1.0, 100.0])), 5000 + case, xt)
+        run_mx8(tq, orc, x, xt, dy=workloads.normal((rows, k), 1.0, 5500 + case, xt))
