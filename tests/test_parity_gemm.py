@@ -302,3 +302,36 @@ def test_fp4_linear_shapes(tq):
     y = tq.tq_fp4_linear(x[:, :0], torch.zeros((128, 0), dtype=torch.uint8, device="cuda"),
                          torch.zeros((128, 0), dtype=torch.uint8, device="cuda"), g, "nvfp4", out_dtype=torch.float32)
     assert y.shape == (4, 128) and bool((y == 0).all())
+
+
+def test_random_gemm_shapes(tq, orc):
+    """Seeded random (M, N, K, output type) for the three GEMMs: M any size
+    (ragged last tile), N a multiple of 128 (so both W8A8 tiles run), K a
+    multiple of 128 (64 for the FP4 linear); the same checks as above."""
+    rng = np.random.default_rng(4096)
+    for case in range(10):
+        M = int(rng.integers(1, 400))
+        N = 128 * int(rng.integers(1, 5))
+        K = 128 * int(rng.integers(1, 9))
+        yt = ("f32", "bf16", "f16")[int(rng.integers(3))]
+        note("random gemm case", case, M, N, K, yt)
+        qa, sa, qw, sw = _operands(tq, M, N, K, 300 + case)
+        y = tq.tq_fp8_block_gemm(qa, sa, qw, sw, out_dtype=TORCH[yt])
+        QA, SA, QW, SW = from_dev(qa), from_dev(sa), from_dev(qw), from_dev(sw)
+        ref, yabs = orc.fp8_block_gemm(QA, SA, QW, SW)
+        check(_as_f32(y, yt), ref, yabs, intra_bound(orc, QA, SA, QW, SW), K, yt)
+
+        x = workloads.normal_with_outlier_columns((M, K), 1.0, 400 + case, "bf16", 0.01, 20.0, K)
+        w = workloads.normal((N, K), 0.02, 500 + case, "f16")
+        qx, sx, qw8, sw8 = _w8a8_operands(tq, x, "bf16", w, "f16")
+        y = tq.tq_w8a8_linear(qx, sx, qw8, sw8, out_dtype=TORCH[yt])
+        assert_same(from_dev(y), orc.w8a8_linear(_i8(qx), from_dev(sx), _i8(qw8), from_dev(sw8), yt), "w8a8 y")
+
+        kind = ("nvfp4", "mxfp4")[case % 2]
+        K4 = 64 * int(rng.integers(1, 17))
+        x4 = workloads.normal_with_outlier_columns((M, K4), 1.0, 600 + case, "bf16", 0.01, 20.0, K4)
+        w4 = workloads.normal((N, K4), 0.02, 700 + case, "bf16")
+        packed, bs, sg = _fp4_weight(tq, w4, kind)
+        y = tq.tq_fp4_linear(to_dev(x4, "bf16"), packed, bs, sg, kind, out_dtype=TORCH[yt])
+        ref, yabs = orc.fp4_linear(x4, from_dev(packed), from_dev(bs), from_dev(sg) if sg is not None else 1.0, kind)
+        check_fp4(_as_f32(y, yt), ref, yabs, K4, yt)
