@@ -108,3 +108,43 @@ def test_random_f64_and_mxfp8_cases(tq, orc):
         note("random mxfp8 case", case)
         x = workloads.normal((rows, k), float(rng.choice([0.02, 1.0, 100.0])), 5000 + case, xt)
         run_mx8(tq, orc, x, xt, dy=workloads.normal((rows, k), 1.0, 5500 + case, xt))
+
+
+def test_random_fp4_layouts(tq, orc):
+    """Seeded random shapes for the GEMM-layout transposes (tiled 256 x 256
+    path with ragged tiles, and the generic path) and the transpose-concat
+    with padding, against the oracle's numpy layouts."""
+    from gpu_util import assert_same, from_dev, to_dev
+    rng = np.random.default_rng(77)
+    for case in range(16):
+        kind = ("nvfp4", "mxfp4")[case % 2]
+        gs = 16 if kind == "nvfp4" else 32
+        n = int(rng.choice([16, 32, 48, 272, 512, 784, 1000, 1040])) + int(rng.choice([0, 0, 0, 3]))
+        k = gs * int(rng.integers(1, 80))
+        note("random transpose case", case, n, k, kind)
+        x = workloads.normal((n, k), 0.02, 300 + case, "bf16")
+        p, b, _ = tq.tq_quant_fp4_block(to_dev(x, "bf16"), kind)
+        pt, bt = tq.tq_fp4_transpose_for_gemm(p, b, n, k, gs)
+        op, ob = orc.fp4_transpose_for_gemm(from_dev(p), from_dev(b), n, k, gs)
+        assert_same(from_dev(pt), op, "packed^T")
+        assert_same(from_dev(bt), ob, "scales^T")
+    for case in range(8):
+        kind = ("nvfp4", "mxfp4")[case % 2]
+        gs = 16 if kind == "nvfp4" else 32
+        k = gs * int(rng.integers(2, 40))
+        ns = [int(rng.choice([0, 16, 48, 256, 272, 300, 512])) for _ in range(int(rng.integers(1, 4)))]
+        if sum(ns) == 0:
+            ns[0] = 32
+        align = int(rng.choice([1, 16, 64, 128, 512]))
+        note("random concat case", case, ns, k, kind, align)
+        parts = []
+        for i, nn in enumerate(ns):
+            xx = workloads.normal((nn, k), 0.02, 400 + 10 * case + i, "bf16")
+            sgl = torch.tensor([2e-5], dtype=torch.float32, device="cuda") if kind == "nvfp4" else None
+            pp, bb, _ = tq.tq_quant_fp4_block(to_dev(xx, "bf16"), kind, global_scale=sgl)
+            parts.append((pp, bb))
+        pt, bt, stride = tq.tq_fp4_transpose_concat_for_gemm(parts, k, gs, align)
+        op, ob, ostride = orc.fp4_transpose_concat([(from_dev(a), from_dev(c)) for a, c in parts], k, gs, align)
+        assert stride == ostride
+        assert_same(from_dev(pt), op, "packed^T concat")
+        assert_same(from_dev(bt), ob, "scales^T concat")
