@@ -321,6 +321,13 @@ def breakdown(torch, tq, iters=20, only=None):
                  lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_dequant_fp8_block(P(b["q"]), R, C, br, bc, P(b["s"]),
                                                                                 P(b["y"]), 2, stream), "fp8 deq"),
                  nb + R * C * 2, R * C + ns * 4)
+        if name == "fp8_1x128":     # dequantize backward (A9) on the activation shape: dq = dy * scale
+            mkb = lambda i, R=R, C=C, ns=ns: dict(dy=dev_bits(xa, "bf16", torch), s=torch.ones(ns, dtype=f32, device="cuda"),
+                                                  dq=E((R, C), bf16))
+            bench_op("dequant_backward_" + name, cfg, R * C * 4 + ns * 4, mkb,
+                     lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_dequant_fp8_block_backward(
+                         P(b["dy"]), 2, R, C, br, bc, P(b["s"]), P(b["dq"]), stream), "fp8 dqb"),
+                     R * C * 4 + ns * 4, R * C * 2 + ns * 4)
 
     # MXFP8 on the c4 activations bf16 [4096, 7168]: E4M3 + E8M0 per 32
     xm = workloads.make_input("c4_fp8_act_1x128")
@@ -368,6 +375,15 @@ def breakdown(torch, tq, iters=20, only=None):
                      L.tq_dequant_fp4_block(P(b["p"]), P(b["b"]), P(b["g"]) if kd == 0 else None, N5, K5, kd,
                                             P(b["y"]), 2, stream), "fp4 dequant"),
                  db, n5 // 2 + n5 // gs)
+        if kind == "nvfp4":         # dequantize backward (A9) on the weight shape: dq = dy * eff
+            mkq = lambda i, gs=gs: dict(dy=dev_bits(w5, "bf16", torch), b=torch.full((N5, K5 // gs), 0x38, dtype=u8,
+                                                                                     device="cuda"),
+                                        g=torch.full((1,), 1.2e-5, dtype=f32, device="cuda"), dq=E((N5, K5), bf16))
+            qb = n5 * 4 + n5 // gs + 4
+            bench_op("dequant_backward_nvfp4", cfg, qb, mkq,
+                     lambda b: check(L.tq_dequant_fp4_block_backward(P(b["dy"]), 2, P(b["b"]), P(b["g"]), N5, K5, 0,
+                                                                      P(b["dq"]), stream), "nvfp4 dqb"),
+                     qb, n5 * 2 + n5 // gs)
         tb = 2 * (n5 // 2 + n5 // gs)
         bench_op("transpose_for_gemm_" + kind, cfg, tb, mk,
                  lambda b, gs=gs: check(L.tq_fp4_transpose_for_gemm(P(b["p"]), P(b["b"]), N5, K5, gs, P(b["pt"]),

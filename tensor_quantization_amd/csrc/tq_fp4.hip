@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = g[i] * (((w >> (4 * i)) & 7u) != 7u ? 1.0f : 0.0f);
         }
-        store8<FT, true>(out, e, o);
+        store8<FT, OP == OP_DQB ? WT : 1>(out, e, o);
     }
 }
 

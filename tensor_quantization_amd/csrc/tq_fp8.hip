@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
                 o[i] = g[i] * (c < 0x7eu ? 1.0f : 0.0f);
             }
         }
-        store8<FT, OP == OP_DEQ ? WT : 1>(out, e, o);
+        store8<FT, (OP == OP_DEQ || OP == OP_DQB) ? WT : 1>(out, e, o);
     }
 }
 
