@@ -52,7 +52,7 @@ __device__ __forceinline__ uint2 ld8(const void* p)
 // with device scope (nt sc1), which passes the L2 on to memory instead of
 // leaving dirty lines behind.  Measured per kernel (same code otherwise,
 // interleaved runs): WT is 2-7% faster for the 8-bit dequantize, the
-// dequantize backward (integer, FP8, FP4), the FP8 dequantize, row
+// dequantize backward (integer, FP8, MXFP8, FP4), the FP8 dequantize, row
 // concatenation, the FP4 -> FP8 expansion and the binary64 dequantize, and
 // 1-3% slower for the 4-bit and FP4 dequantize, the byte transposes and the
 // fake-quantization kernels, which keep NT = 1.  A store has no output register, so the asm form is safe to

@@ -480,7 +480,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, co
                 o[i] = (d[i] * inv) * (c < 0x7eu ? 1.0f : 0.0f);
             }
         }
-        store8<FT, true>(out, e, o);
+        store8<FT, OP == OP_DQB ? WT : 1>(out, e, o);
     }
 }
 
