@@ -54,9 +54,11 @@ __device__ __forceinline__ uint2 ld8(const void* p)
 // interleaved runs): WT is 2-7% faster for the 8-bit dequantize, the
 // dequantize backward (integer, FP8, MXFP8, FP4), the FP8 dequantize, row
 // concatenation, the FP4 -> FP8 expansion and the binary64 dequantize, and
-// 1-3% slower for the 4-bit and FP4 dequantize, the byte transposes and the
-// fake-quantization kernels, which keep NT = 1.  A store has no output register, so the asm form is safe to
-// leave in flight; it only makes the compiler's own vmcnt waits conservative.
+// 1-3% slower for the 4-bit and FP4 dequantize, the binary64 dequantize
+// backward, the byte transposes and the fake-quantization kernels, which
+// keep NT = 1.  A store has no output register, so the asm form is safe to
+// leave in flight; it only makes the compiler's own vmcnt waits
+// conservative.
 constexpr int WT = 2;
 
 template <int NT = 0>
