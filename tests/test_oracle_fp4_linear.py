@@ -43,7 +43,7 @@ def _weights(kind, n, k, seed):
 
 
 def test_matches_dequantized_matmul():
-    # the same product through the (separately pinned) dequantize and a float64 matmul
+    # the same product through the dequantize (pinned exactly in test_oracle_fp_backward.py) and a float64 matmul
     for kind in ("nvfp4", "mxfp4"):
         packed, bs, sg = _weights(kind, 24, 128, 11)
         x = workloads.normal((5, 128), 1.0, 12, "bf16")

@@ -493,3 +493,28 @@ def test_fp8_per_tensor(orc, xt, static):
     assert (q == want).all()
     if static is not None:
         assert ((q & 0x7F) == 0x7E).sum() > 10
+
+
+# ------------------------------------------------------------ subnormal scales
+def test_subnormal_symmetric_scale_clamps(orc):
+    """A group whose amax lies below qmax * 2^-126 gets a subnormal scale
+    with a large relative error, so |x / scale| can pass qmax: worked by
+    hand, amax = 190 * 2^-149 gives scale = RN(190/127 * 2^-149) = 2^-149
+    (1.496 rounds to 1 on the subnormal grid), x / scale = 190 and the code
+    clamps to 127 (s8) or 7 (s4); -amax gives -127 / -7."""
+    tiny = np.float32(2.0 ** -149)
+    x = np.zeros((2, 16), np.float32)
+    x[0, 3] = np.float32(190) * tiny
+    x[1, 5] = -np.float32(190) * tiny
+    x[1, 6] = np.float32(64) * tiny                 # 64 / 1 -> 64 (inside s8, clamps in s4)
+    q, s, _ = orc.quant_int(x, "f32", "token", code="s8")
+    assert (s.view(np.uint32) == 1).all()
+    c = q.view(np.int8).reshape(2, 16)
+    assert c[0, 3] == 127 and c[1, 5] == -127 and c[1, 6] == 64
+    assert (np.delete(c[0], 3) == 0).all()
+    q4, s4, _ = orc.quant_int(x, "f32", "token", code="s4")
+    c4 = _unpack(q4, "s4", (2, 16))
+    assert (s4.view(np.uint32) == np.float32(190 / 7 * 2.0 ** -149).view(np.uint32)).all()
+    # 190 / 7 = 27.14 -> scale 27 * 2^-149: codes rne(190/27) = 7, rne(64/27) = 2
+    assert s4[0].view(np.uint32) == 27
+    assert c4[0, 3] == 7 and c4[1, 5] == -7 and c4[1, 6] == 2
