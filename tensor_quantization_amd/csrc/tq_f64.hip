@@ -549,7 +549,6 @@ __global__ __launch_bounds__(256) void k_f64_ew8(const void* __restrict__ a, con
     }
 }
 
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static unsigned grid_for(int64_t work, int64_t per_block)
 {

@@ -485,7 +485,6 @@ __global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, co
 }
 
 // ============================================================ host side
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static unsigned grid_for(int64_t work, int64_t per_block)
 {

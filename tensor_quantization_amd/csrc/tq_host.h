@@ -18,6 +18,7 @@ inline int code_bits(int c) { return (c == TQ_S4 || c == TQ_U4) ? 4 : 8; }
 inline bool code_signed(int c) { return c == TQ_S8 || c == TQ_S4; }
 inline int ftype_size(int t) { return t == TQ_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline tq_status launch_status()
 {

@@ -67,15 +67,21 @@ __device__ __forceinline__ GP make_gp(float amax, float mn, float mx, float qmin
 }
 
 // Encode 8 values of one group into code floats (MAGIC + code).  A
-// symmetric dynamic scale s = RN(amax / qmax) keeps |x / s| below qmax + 0.5
-// for every element, so only asymmetric groups (and static scales) clamp.
+// symmetric dynamic scale s = RN(amax / qmax) that is a normal number keeps
+// |x / s| below qmax + 0.5 for every element (its relative error is at most
+// 2^-24), so fast symmetric groups skip the clamp.  A subnormal scale (amax
+// below qmax * 2^-126) carries up to half an ulp of 2^-149 of absolute
+// error, so |x / s| can exceed qmax by far (amax = 190 * 2^-149 gives
+// s = 2^-149 and x / s = 190 with qmax = 127): such scales lie outside the
+// fast range and the slow branch always clamps.
 template <int FT, bool FAST, bool CLAMP>
 __device__ __forceinline__ void enc8(const float v[8], const GP& p, float lo, float hi, float c[8])
 {
+    constexpr bool CL = CLAMP || !FAST;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float t = FAST ? div_q<FT>(v[i], p.s, p.y) : v[i] / p.s;
-        c[i] = CLAMP ? int_code_f(t, p.zpf, lo, hi) : (t + MAGIC) + p.zpf;
+        c[i] = CL ? int_code_f(t, p.zpf, lo, hi) : (t + MAGIC) + p.zpf;
     }
 }
 
@@ -197,7 +203,7 @@ __device__ __forceinline__ void encode_store8(const float* v, const Raw8<FT>& ra
         for (int i = 0; i < 8; ++i) {
             const float x = (i & 1) ? f16_hi(d[i >> 1]) : f16_lo(d[i >> 1]);
             const float t = FAST ? div_q_mix(x, p.s, p.y, nz) : x / p.s;
-            if constexpr (SYM) c[i] = t + MAGIC;
+            if constexpr (SYM) c[i] = FAST ? t + MAGIC : __builtin_amdgcn_fmed3f(t + MAGIC, lo, hi);
             else if constexpr (BITS == 4) c[i] = __builtin_amdgcn_fmed3f(t + MAGIC, lo_z, hi_z);
             else c[i] = int_code_f(t, p.zpf, lo, hi);
         }
@@ -205,7 +211,7 @@ __device__ __forceinline__ void encode_store8(const float* v, const Raw8<FT>& ra
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float t = FAST ? div_q<FT>(v[i], p.s, p.y) : v[i] / p.s;
-            if constexpr (SYM) c[i] = t + MAGIC;
+            if constexpr (SYM) c[i] = FAST ? t + MAGIC : __builtin_amdgcn_fmed3f(t + MAGIC, lo, hi);
             else if constexpr (BITS == 4) c[i] = __builtin_amdgcn_fmed3f(t + MAGIC, lo_z, hi_z);
             else c[i] = int_code_f(t, p.zpf, lo, hi);
         }
@@ -1047,7 +1053,6 @@ __global__ __launch_bounds__(256) void k_ste_generic(const void* __restrict__ x,
 }
 
 // ============================================================ host side
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static unsigned grid_for(int64_t work, int64_t per_block)
 {
@@ -1304,8 +1309,10 @@ static tq_status tensor_scale_passes(const void* x, int xt, int64_t numel, bool 
                                      hipStream_t st)
 {
     if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
-    const int64_t chunk = std::max<int64_t>(256 * 8 * 4, ((numel / 1024) + 2047) / 2048 * 2048);
+    // chunk >= numel / 1024 rounded up, so at most 1024 partial pairs
+    const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
     const int nblk = (int)cdiv(numel, chunk);
+    if (nblk > 1024) return TQ_ERR_INVALID;
     float* ws = static_cast<float*>(workspace);
     TQ_FT_SWITCH(xt, {
         if (sym) {

@@ -84,35 +84,6 @@ def test_e4m3_conversion_dense(tq, orc):
     assert_same(from_dev(q), orc.enc_e4m3(x), "E4M3 codes")
 
 
-def test_full_c4_activation_sampled(tq, orc):
-    x = workloads.make_input("c4_fp8_act_1x128")
-    xd = to_dev(x, "bf16")
-    q, s = tq.tq_quant_fp8_block(xd, 1, 128)
-    y = tq.tq_dequant_fp8_block(q, s, 1, 128, out_dtype=torch.bfloat16)
-    q, s, y = map(from_dev, (q, s, y))
-    rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(3).choice(4096, 64, replace=False)]))
-    xs = np.ascontiguousarray(x[rows])
-    oq, os_ = orc.quant_fp8_block(xs, "bf16", 1, 128)
-    assert_same(q[rows], oq, "q")
-    assert_same(s[rows], os_, "scale")
-    assert_same(y[rows], orc.dequant_fp8_block(oq, 1, 128, os_, "bf16"), "dequant")
-
-
-def test_full_c4_weight_sampled(tq, orc):
-    w = workloads.make_input("c4_fp8_weight_128x128")
-    wd = to_dev(w, "bf16")
-    q, s = tq.tq_quant_fp8_block(wd, 128, 128)
-    y = tq.tq_dequant_fp8_block(q, s, 128, 128, out_dtype=torch.bfloat16)
-    q, s, y = map(from_dev, (q, s, y))
-    for tr in (0, 17, 55):                       # tile rows: 128-row slabs are independent
-        r0 = tr * 128
-        ws = np.ascontiguousarray(w[r0:r0 + 128])
-        oq, os_ = orc.quant_fp8_block(ws, "bf16", 128, 128)
-        assert_same(q[r0:r0 + 128], oq, "q slab %d" % tr)
-        assert_same(s[tr:tr + 1], os_, "scale slab %d" % tr)
-        assert_same(y[r0:r0 + 128], orc.dequant_fp8_block(oq, 128, 128, os_, "bf16"), "dequant slab %d" % tr)
-
-
 @pytest.mark.parametrize("shape,xt,block", [
     ((5, 7000), "bf16", (1, 128)),        # ragged K: last 1x128 group has 88 elements
     ((200, 330), "f32", (128, 128)),      # partial tiles on both edges

@@ -2,9 +2,8 @@
 group; quantize, dequantize, STE backward, dequantize backward) against the
 oracle, bit for bit.  Shapes cover every kernel path: team kernels
 (L = 16..4096), the long-group kernel, column groups, the generic index path,
-ragged tails, empty inputs and degenerate values; the full-size workloads are
-checked on sampled rows (rows are independent, so the oracle runs on them
-alone)."""
+ragged tails, empty inputs and degenerate values.  The full-size workloads
+are in test_parity_full.py."""
 import numpy as np
 import pytest
 import torch
@@ -196,45 +195,3 @@ def test_empty_inputs(tq):
     assert q.numel() == 0 and s.numel() == 0
     q, s, z = tq.tq_quant_per_group(x, axis=1, group_size=128, code="u4")
     assert q.shape == (0, 64)
-
-
-def _sample_rows(n, k, seed):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, k, replace=False)]))
-
-
-def test_full_c2_per_token_sampled(tq, orc):
-    """Full [8192, 4096] bf16 workload (with outlier columns) in the launch
-    configuration the benchmark times; rows sampled for the oracle."""
-    x = workloads.make_input("c2_per_token_s8")
-    dy = workloads.make_dy("c2_per_token_s8")
-    xd, dyd = to_dev(x, "bf16"), to_dev(dy, "bf16")
-    q, s, _ = tq.tq_quant_per_token(xd, code="s8")
-    y = tq.tq_dequant_per_token(q, x.shape, s, None, code="s8", out_dtype=torch.bfloat16)
-    dx = tq.tq_quant_per_token_backward(xd, dyd, s, None, code="s8")
-    dq = tq.tq_dequant_per_token_backward(dyd, s)
-    q, s, y, dx, dq = map(from_dev, (q, s, y, dx, dq))
-    rows = _sample_rows(8192, 96, 1)
-    xs, dys = np.ascontiguousarray(x[rows]), np.ascontiguousarray(dy[rows])
-    oq, os_, _ = orc.quant_int(xs, "bf16", "token", code="s8")
-    assert_same(q[rows], oq, "q")
-    assert_same(s[rows], os_, "scale")
-    assert_same(y[rows], orc.dequant_int(oq, "s8", xs.shape, "token", scale=os_, yt="bf16"), "dequant")
-    assert_same(dx[rows], orc.quant_int_backward(xs, "bf16", "token", code="s8", scale=os_, dy=dys), "ste")
-    assert_same(dq[rows], orc.dequant_int_backward(dys, "bf16", "token", scale=os_), "dq")
-
-
-def test_full_c3_per_group_sampled(tq, orc):
-    """Full [11008, 4096] f16 GPTQ-style weight, u4 g=128 asymmetric."""
-    w = workloads.make_input("c3_per_group_u4_g128")
-    wd = to_dev(w, "f16")
-    q, s, z = tq.tq_quant_per_group(wd, axis=1, group_size=128, code="u4", symmetric=False)
-    y = tq.tq_dequant_per_group(q, w.shape, s, z, axis=1, group_size=128, code="u4", out_dtype=torch.float16)
-    q, s, z, y = map(from_dev, (q, s, z, y))
-    rows = _sample_rows(11008, 96, 2)
-    ws = np.ascontiguousarray(w[rows])
-    oq, os_, oz = orc.quant_int(ws, "f16", "group", axis=1, group_size=128, code="u4", symmetric=False)
-    assert_same(q[rows], oq, "q")
-    assert_same(s[rows], os_, "scale")
-    assert_same(z[rows], oz, "zp")
-    assert_same(y[rows], orc.dequant_int(oq, "u4", ws.shape, "group", 1, 128, os_, oz, "f16"), "dequant")
