@@ -115,6 +115,24 @@ tq_status tq_default_q_range(int code, int symmetric, int32_t* host_qmin, int32_
  * dynamic scale (16 KiB).  numel = elements. */
 size_t tq_workspace_bytes(int op, int64_t numel);
 
+/* Measurement utility (not a step of the method): the streaming ceiling a
+ * kernel is compared with.  `nthreads` units each read `in_bytes` from `src`
+ * and write `out_bytes` to `dst`, folding the loaded words into the stored
+ * ones and doing nothing else, with the per-lane widths of the quantization
+ * kernels: in_bytes 4, 8, 16 (one load at src + t*in_bytes) or 32 (two
+ * 16-byte loads, at src + 16 t and src + 16 (nthreads + t): two input
+ * streams); out_bytes 4, 8, 16 (one store at dst + t*out_bytes) or 32 (two
+ * 16-byte stores).  Each lane takes `vectors` units (1, 2 or 4; a workgroup
+ * of 256 lanes covers 256*vectors consecutive units, lane j the units
+ * k*256 + j), issuing all its loads before its stores.  16-byte loads are
+ * non-temporal; stores follow `policy`: 0 plain, 1 non-temporal, 2
+ * non-temporal with device scope (16-byte stores only).  src holds
+ * nthreads*in_bytes bytes, dst nthreads*out_bytes; both 16-byte aligned
+ * (TQ_ERR_ALIGN).  Supported mixes (in:out) 16:8, 16:4, 8:16, 4:16, 32:16,
+ * 16:16, 16:32; others return TQ_ERR_UNSUPPORTED. */
+tq_status tq_stream_mix(const void* src, void* dst, int64_t nthreads, int in_bytes, int out_bytes, int policy,
+                        int vectors, void* stream);
+
 /* ===================================================================== */
 /* Integer codes                                                          */
 /* ===================================================================== */

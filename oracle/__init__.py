@@ -24,7 +24,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tq_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# TQ_ORACLE_SANITIZE=1 builds and loads a separate copy instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (host code only; the
+# process must preload the ASan runtime, e.g.
+#   TQ_ORACLE_SANITIZE=1 ASAN_OPTIONS=detect_leaks=0 \
+#   LD_PRELOAD=$(gcc -print-file-name=libasan.so) python -m pytest tests -m "not gpu"
+# ); any report aborts the run.
+_SANITIZE = os.environ.get("TQ_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 
 FTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 CODES = {"s8": 0, "u8": 1, "s4": 2, "u4": 3}
@@ -33,13 +40,14 @@ FP4_KINDS = {"nvfp4": 0, "mxfp4": 1}
 FP4_GROUP = {"nvfp4": 16, "mxfp4": 32}
 
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc into ``oracle/liboracle.so``."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *_CFLAGS, *(_SAN_FLAGS if _SANITIZE else []), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 

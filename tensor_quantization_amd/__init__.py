@@ -94,6 +94,7 @@ _SIGS = {
     "tq_dequant_mxfp8": ([_P, _P, _I64, _I64, _P, _I, _P], _I),
     "tq_quant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P, _P], _I),
     "tq_dequant_mxfp8_backward": ([_P, _I, _P, _I64, _I64, _P, _P], _I),
+    "tq_stream_mix": ([_P, _P, _I64, _I, _I, _I, _I, _P], _I),
 }
 
 for _name, (_args, _ret) in _SIGS.items():
@@ -173,6 +174,14 @@ def tq_default_q_range(code, symmetric):
 
 def tq_workspace_bytes(op, numel):
     return int(_lib.tq_workspace_bytes(op, numel))
+
+
+def tq_stream_mix(src, dst, nthreads, in_bytes, out_bytes, policy=1, vectors=1):
+    """Measurement utility: the streaming ceiling of an access mix (each of
+    `nthreads` units reads `in_bytes` of src and writes `out_bytes` of dst;
+    a lane takes `vectors` units)."""
+    _call("tq_stream_mix", _ptr(src), _ptr(dst), int(nthreads), int(in_bytes), int(out_bytes), int(policy),
+          int(vectors), _stream(src.device))
 
 
 def _range(code, qmin, qmax, symmetric):

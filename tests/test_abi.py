@@ -160,6 +160,19 @@ def test_gemm_validation(tq):
     assert L.tq_fp4_linear(MIS, 2, A, C, C, 1, 128, 128, 64, B, 2, None) == ALIGN
 
 
+def test_stream_mix_validation(tq):
+    L = tq._lib
+    INV, UNS, ALIGN = tq.TQ_ERR_INVALID, tq.TQ_ERR_UNSUPPORTED, tq.TQ_ERR_ALIGN
+    assert L.tq_stream_mix(A, B, 0, 16, 8, 1, 1, None) == 0           # nothing to do
+    assert L.tq_stream_mix(None, B, 64, 16, 8, 1, 1, None) == INV
+    assert L.tq_stream_mix(A, B, -1, 16, 8, 1, 1, None) == INV
+    assert L.tq_stream_mix(A, B, 64, 16, 8, 3, 1, None) == INV        # unknown store policy
+    assert L.tq_stream_mix(A, B, 64, 16, 8, 1, 3, None) == INV        # 1, 2 or 4 units per lane
+    assert L.tq_stream_mix(MIS, B, 64, 16, 8, 1, 1, None) == ALIGN
+    assert L.tq_stream_mix(A, B, 64, 16, 8, 2, 1, None) == UNS        # device scope needs 16-byte stores
+    assert L.tq_stream_mix(A, B, 64, 2, 8, 0, 1, None) == UNS         # mix not offered
+
+
 def test_empty_inputs_enqueue_nothing(tq):
     L = tq._lib
     assert L.tq_quant_per_token(A, 2, 0, 8, 0, -127, 127, B, C, None, None) == 0

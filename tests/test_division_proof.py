@@ -34,3 +34,19 @@ def test_two_correction_binary64_division(tmp_path):
     out = subprocess.run([exe, "2000000"], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "two corrections: 0 mismatches" in out.stdout
+
+
+def test_two_correction_binary32_division(tmp_path):
+    """Binary32 dividends (f32 inputs, the asymmetric range mx - mn) take two
+    FMA corrections of x * RN(1/s): equal to IEEE x / s on 8M random pairs
+    over the guarded range 2^-40 <= |s| <= 2^40, 2^-78 <= |x| <= 2^86 (half of
+    them with |x / s| <= 255, the code range) and on about 3M pairs whose
+    quotient lies within 15 * 2^-48 of a midpoint between binary32 numbers."""
+    exe = str(tmp_path / "division_f32")
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-o", exe, os.path.join(HERE, "division_f32.c"),
+                           "-lm"])
+    out = subprocess.run([exe, "4000000"], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "two corrections: 0 mismatches" in out.stdout
+    hard = int(out.stdout.split(" near-midpoint pairs")[0].split("\n")[-1])
+    assert hard > 2_000_000
