@@ -112,7 +112,11 @@ tq_status tq_default_q_range(int code, int symmetric, int32_t* host_qmin, int32_
  * TQ_SCOPE_TENSOR dynamic-range call likewise), 1 = tq_quant_fp4_block with
  * a dynamic global scale, 2 = tq_quant_fp8_per_tensor with a dynamic scale
  * (0 bytes up to 65536 elements), 3 = tq_quant_f64 at TQ_GRAN_TENSOR with a
- * dynamic scale (16 KiB).  numel = elements. */
+ * dynamic scale (16 KiB).  numel = elements.  A workspace is device memory,
+ * 16-byte aligned (TQ_ERR_ALIGN otherwise), whose contents on entry are
+ * ignored; a call in flight owns it (two calls that overlap must not share
+ * one).  The first launch of such a call writes up to 1024 partial maxima
+ * into it and every workgroup of the second merges them. */
 size_t tq_workspace_bytes(int op, int64_t numel);
 
 /* Measurement utility (not a step of the method): the streaming ceiling a

@@ -550,14 +550,6 @@ __global__ __launch_bounds__(256) void k_f64_ew8(const void* __restrict__ a, con
 }
 
 
-static unsigned grid_for(int64_t work, int64_t per_block)
-{
-    int64_t g = cdiv(work, per_block);
-    if (g < 1) g = 1;
-    if (g > (1 << 20)) g = 1 << 20;
-    return (unsigned)g;
-}
-
 static bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // The pair-interleaved kernels need an even element count and aligned

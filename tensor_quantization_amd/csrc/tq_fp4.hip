@@ -13,10 +13,11 @@
 // Codes are packed two per byte along K, even index in the low nibble.
 //
 // Kernels:
-//   k_amax_partial + k_nv_global_scale   dynamic NVFP4 s_g: chunk maxima, then
-//                    one workgroup publishes s_g into global_scale.
+//   k_amax_partial   dynamic NVFP4 s_g, pass 1: chunk maxima.
 //   k_fp4_quant      a team of 2 (NVFP4) / 4 (MXFP4) lanes per block, block max
-//                    through DPP, U rounds per wave; reads s_g from global_scale.
+//                    through DPP, U rounds per wave; reads s_g from global_scale,
+//                    or (dynamic s_g) merges the chunk maxima in every
+//                    workgroup and publishes s_g from workgroup 0.
 //   k_fp4_ew         dequant / STE / dequant-backward, 8 elements per step.
 //   k_transpose_jobs byte transposes through 256 x 256-byte LDS tiles with
 //                    4 x 4 register transposes and 16-byte stores, into a
@@ -31,7 +32,9 @@ namespace tq {
 
 enum { NV = 0, MX = 1 };
 
-// Per-tensor max |x|, pass 1 (block partials into ws).
+// Per-tensor max |x|, pass 1 (block partials into ws).  Plain loads, four
+// in flight per thread (non-temporal loads measured 3% slower; two or eight
+// in flight and 512- or 1024-thread blocks within 1%).
 template <int FT>
 __global__ __launch_bounds__(256) void k_amax_partial(const void* __restrict__ x, int64_t numel, int64_t chunk,
                                                       float* __restrict__ ws)
@@ -61,25 +64,6 @@ __global__ __launch_bounds__(256) void k_amax_partial(const void* __restrict__ x
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
     __syncthreads();
     if (threadIdx.x == 0) ws[blk] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
-}
-
-// Pass 1b: one workgroup merges the partials and publishes
-// s_g = amax / 2688 (1 if 0); the encode pass then reads s_g like a static
-// scale instead of every workgroup merging the partials again.
-__global__ __launch_bounds__(256) void k_nv_global_scale(const float* __restrict__ ws, int nws,
-                                                         float* __restrict__ global_scale)
-{
-    __shared__ float sm[4];
-    float a = 0.0f;
-    for (int k = threadIdx.x; k < nws; k += 256) a = __builtin_fmaxf(a, ws[k]);
-    a = team_max<64>(a);
-    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        a = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
-        const float g = a / 2688.0f;
-        global_scale[0] = (g == 0.0f) ? 1.0f : g;
-    }
 }
 
 struct BP {
@@ -132,17 +116,20 @@ __device__ __forceinline__ void fp4_div8(const float v[8], const BP& p, float t[
 // elements 8j..8j+7 of its block, so each load instruction of a wave reads
 // 1 KB contiguously and each code store writes 256 bytes contiguously; the
 // block max takes one or two DPP steps.  U rounds of 64/T blocks per wave.
-template <int FT, int KIND, int U>
+// DYN (NVFP4 with s_g from the data): `parts` holds the nparts chunk maxima
+// of pass 1; every workgroup merges them, s_g = max / 2688 (1 if 0), and
+// workgroup 0 publishes it into global_scale.
+template <int FT, int KIND, int U, bool DYN = false>
 __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, int64_t nblocks,
-                                                   const float* __restrict__ global_scale,
-                                                   uint8_t* __restrict__ packed, uint8_t* __restrict__ bscale)
+                                                   float* __restrict__ global_scale, const float* __restrict__ parts,
+                                                   int nparts, uint8_t* __restrict__ packed,
+                                                   uint8_t* __restrict__ bscale)
 {
     constexpr int GS = KIND == NV ? 16 : 32;
     constexpr int T = GS / 8;
     constexpr int P = 64 / T;
-    const float sg = KIND == NV ? global_scale[0] : 1.0f;
-    const float six_sg = 6.0f * sg;
-    const float y6 = scale_in_fast_range(six_sg) ? rcp_rn(six_sg) : 0.0f;
+    Part4 pp;
+    if constexpr (DYN) pp = load_partials<false>(parts, nparts);
     const int lane = threadIdx.x & 63;
     const int j = lane % T;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -154,6 +141,18 @@ __global__ __launch_bounds__(256) void k_fp4_quant(const void* __restrict__ x, i
         if (b < nblocks) raw[u] = load8<FT, true>(x, b * GS + j * 8);
         else raw[u] = Raw8<FT>{};
     }
+    float sg;
+    if constexpr (DYN) {
+        float amax, unused;
+        merge_partials<false>(pp, amax, unused);
+        const float g = amax / 2688.0f;
+        sg = (g == 0.0f) ? 1.0f : g;
+        if (blockIdx.x == 0 && threadIdx.x == 0) global_scale[0] = sg;
+    } else {
+        sg = KIND == NV ? global_scale[0] : 1.0f;
+    }
+    const float six_sg = 6.0f * sg;
+    const float y6 = scale_in_fast_range(six_sg) ? rcp_rn(six_sg) : 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float v[8];
@@ -191,22 +190,45 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
 {
     constexpr int GS = KIND == NV ? 16 : 32;
     const float sg = KIND == NV ? global_scale[0] : 1.0f;
+    if constexpr (OP == OP_DEQ) {
+        for (int64_t base = (int64_t)blockIdx.x * 256 * DEQ_V; base < nvec;
+             base += (int64_t)gridDim.x * 256 * DEQ_V) {
+            uint32_t w[DEQ_V], sb[DEQ_V];
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi < nvec)
+                    w[k] = EW_NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+                                       static_cast<const uint8_t*>(a) + vi * 4))
+                                 : *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a) + vi * 4);
+            }
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi < nvec) sb[k] = bscale[vi * 8 / GS];
+            }
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi >= nvec) break;
+                const float eff = fp4_eff(KIND, sb[k], sg);
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f2v d = e2m1_val2(w[k], i);
+                    o[2 * i] = d.x * eff;
+                    o[2 * i + 1] = d.y * eff;
+                }
+                store8<FT, 1>(out, vi * 8, o);
+            }
+        }
+        return;
+    }
     for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
         const int64_t e = vi * 8;
         const uint32_t sb = bscale[e / GS];
         float o[8];
-        if constexpr (OP == OP_DEQ) {
-            const float eff = fp4_eff(KIND, sb, sg);
-            const uint32_t w = EW_NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
-                                           static_cast<const uint8_t*>(a) + e / 2))
-                                     : *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a) + e / 2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f2v d = e2m1_val2(w, i);
-                o[2 * i] = d.x * eff;
-                o[2 * i + 1] = d.y * eff;
-            }
-        } else if constexpr (OP == OP_DQB) {
+        if constexpr (OP == OP_DQB) {
             const float eff = fp4_eff(KIND, sb, sg);
             float d[8];
             widen8<FT>(load8<FT, true>(a, e), d);
@@ -500,14 +522,6 @@ __global__ __launch_bounds__(256) void k_fp4_to_fp8(const uint8_t* __restrict__ 
 
 // ============================================================ host side
 
-static unsigned grid_for(int64_t work, int64_t per_block)
-{
-    int64_t g = cdiv(work, per_block);
-    if (g < 1) g = 1;
-    if (g > (1 << 20)) g = 1 << 20;
-    return (unsigned)g;
-}
-
 #define TQ_FT_SWITCH(ft, ...)                                     \
     switch (ft) {                                                 \
     case TQ_F32: { constexpr int FTV = F32; __VA_ARGS__; } break; \
@@ -578,13 +592,58 @@ static tq_status check_fp4(int64_t rows, int64_t k, int kind)
     return TQ_OK;
 }
 
+tq_status check_fp4_quant(const void* x, int x_dtype, int64_t rows, int64_t k, int kind, const uint8_t* packed,
+                          const uint8_t* block_scale, const float* global_scale)
+{
+    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
+    tq_status s = check_fp4(rows, k, kind);
+    if (s || rows * k == 0) return s;
+    if (!x || !packed || !block_scale) return TQ_ERR_INVALID;
+    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(packed)) return TQ_ERR_ALIGN;
+    return TQ_OK;
+}
+
+// The quantize launches.  A dynamic NVFP4 s_g takes two: the chunk maxima
+// into ws (TENSOR_PARTS floats at most, 16-byte aligned), then the encode,
+// whose every workgroup merges them.
+tq_status fp4_quant_launch(const void* x, int x_dtype, int64_t numel, int kind, uint8_t* packed,
+                           uint8_t* block_scale, float* global_scale, int static_global, float* ws, hipStream_t st)
+{
+    constexpr int U = 2;   // 16- or 32-element blocks per lane in flight (1, 4 and 8 measured slower)
+    if (kind == TQ_NVFP4) {
+        const int64_t nb = numel / 16;
+        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 32), 4));
+        if (static_global) {
+            TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U>), grid, dim3(256), 0, st, x, nb,
+                                                     global_scale, nullptr, 0, packed, block_scale));
+        } else {
+            // (one workgroup publishing s_g between the passes measured the same; at most 256
+            // larger chunks instead of 1024 made the call 16% slower)
+            int nparts;
+            const int64_t chunk = tensor_chunk(numel, &nparts);
+            TQ_FT_SWITCH(x_dtype, {
+                hipLaunchKernelGGL((k_amax_partial<FTV>), dim3(nparts), dim3(256), 0, st, x, numel, chunk, ws);
+                hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U, true>), grid, dim3(256), 0, st, x, nb, global_scale, ws,
+                                   nparts, packed, block_scale);
+            });
+        }
+    } else {
+        const int64_t nb = numel / 32;
+        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 16), 4));
+        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U>), grid, dim3(256), 0, st, x, nb, nullptr,
+                                                 nullptr, 0, packed, block_scale));
+    }
+    return launch_status();
+}
+
 template <int OP>
 static tq_status fp4_elementwise(const void* a, const void* b, int ft, const uint8_t* bscale, const float* sg,
                                  int64_t rows, int64_t k, int kind, void* out, hipStream_t st)
 {
     const int64_t nvec = rows * k / 8;
     if (nvec == 0) return TQ_OK;
-    const dim3 grid(grid_for(nvec, 256)), block(256);
+    const dim3 grid(grid_for(nvec, 256 * (OP == OP_DEQ ? DEQ_V : 1))), block(256);
     if (kind == TQ_NVFP4) {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp4_ew<OP, NV, FTV>), grid, block, 0, st, a, b, bscale, sg, nvec, out));
     } else {
@@ -603,42 +662,14 @@ tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k
                              uint8_t* block_scale, float* global_scale, int static_global, void* workspace,
                              size_t workspace_bytes, void* stream)
 {
-    if (!valid_ftype(x_dtype)) return TQ_ERR_INVALID;
-    tq_status s = check_fp4(rows, k, kind);
-    if (s) return s;
-    const int64_t numel = rows * k;
-    if (numel == 0) return TQ_OK;
-    if (!x || !packed || !block_scale) return TQ_ERR_INVALID;
-    if (kind == TQ_NVFP4 && !global_scale) return TQ_ERR_INVALID;
-    if (!aligned16(x) || !aligned16(packed)) return TQ_ERR_ALIGN;
-    hipStream_t st = as_stream(stream);
-    int nws = 0;
-    float* ws = static_cast<float*>(workspace);
+    tq_status s = check_fp4_quant(x, x_dtype, rows, k, kind, packed, block_scale, global_scale);
+    if (s || rows * k == 0) return s;
     if (kind == TQ_NVFP4 && !static_global) {
-        if (!workspace || workspace_bytes < tq_workspace_bytes(1, numel)) return TQ_ERR_INVALID;
-        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
-        nws = (int)cdiv(numel, chunk);
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_amax_partial<FTV>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws));
-        if (launch_status()) return TQ_ERR_HIP;
+        if (!workspace || workspace_bytes < tq_workspace_bytes(1, rows * k)) return TQ_ERR_INVALID;
+        if (!aligned16(workspace)) return TQ_ERR_ALIGN;
     }
-    constexpr int U = 2;   // 16- or 32-element blocks per lane in flight (1, 4 and 8 measured slower)
-    if (kind == TQ_NVFP4) {
-        if (!static_global) {
-            hipLaunchKernelGGL(k_nv_global_scale, dim3(1), dim3(256), 0, st, ws, nws, global_scale);
-            if (launch_status()) return TQ_ERR_HIP;
-        }
-        const int64_t nb = numel / 16;
-        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 32), 4));
-        // s_g is in global_scale now (the caller's, or just published)
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, NV, U>), grid, dim3(256), 0, st, x, nb, global_scale,
-                                                 packed, block_scale));
-    } else {
-        const int64_t nb = numel / 32;
-        const dim3 grid((unsigned)cdiv(cdiv(nb, U * 16), 4));
-        TQ_FT_SWITCH(x_dtype, hipLaunchKernelGGL((k_fp4_quant<FTV, MX, U>), grid, dim3(256), 0, st, x, nb, global_scale,
-                                                 packed, block_scale));
-    }
-    return launch_status();
+    return fp4_quant_launch(x, x_dtype, rows * k, kind, packed, block_scale, global_scale, static_global,
+                            static_cast<float*>(workspace), as_stream(stream));
 }
 
 tq_status tq_dequant_fp4_block(const uint8_t* packed, const uint8_t* block_scale, const float* global_scale,

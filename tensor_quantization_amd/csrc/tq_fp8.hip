@@ -236,19 +236,44 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
                                                 int shift, BlkIdx bi, const float* __restrict__ scale,
                                                 void* __restrict__ out)
 {
+    if constexpr (OP == OP_DEQ) {
+        for (int64_t base = (int64_t)blockIdx.x * 256 * DEQ_V; base < nvec;
+             base += (int64_t)gridDim.x * 256 * DEQ_V) {
+            uint2 w[DEQ_V];
+            float s[DEQ_V];
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi < nvec)
+                    w[k] = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + vi * 8)
+                                 : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + vi * 8);
+            }
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t e = (base + k * 256 + threadIdx.x) * 8;
+                if (e < nvec * 8)
+                    s[k] = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
+            }
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi >= nvec) break;
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = e4m3_val(w[k].x, i) * s[k];
+                    o[4 + i] = e4m3_val(w[k].y, i) * s[k];
+                }
+                store8<FT, WT>(out, vi * 8, o);
+            }
+        }
+        return;
+    }
     for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
         const int64_t e = vi * 8;
         const float s = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
         float o[8];
-        if constexpr (OP == OP_DEQ) {
-            const uint2 w = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + e)
-                                  : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[i] = e4m3_val(w.x, i) * s;
-                o[4 + i] = e4m3_val(w.y, i) * s;
-            }
-        } else if constexpr (OP == OP_DQB) {
+        if constexpr (OP == OP_DQB) {
             float d[8];
             widen8<FT>(load8<FT, true>(a, e), d);
 #pragma unroll
@@ -342,52 +367,47 @@ __global__ __launch_bounds__(256) void k_fp8_tensor_amax(const void* __restrict_
         ws[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
 }
 
-// Pass 1b: one workgroup merges the partials and publishes the scale.
-template <int FT>
-__global__ __launch_bounds__(256) void k_fp8_tensor_finalize(const float* __restrict__ ws, int nws,
-                                                             float* __restrict__ scale)
-{
-    __shared__ float sm[4];
-    float a = 0.0f;
-    for (int k = threadIdx.x; k < nws; k += 256) a = __builtin_fmaxf(a, ws[k]);
-    a = team_max<64>(a);
-    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        scale[0] = fp8_params<FT>(__builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]))).s;
-}
-
-// Pass 2: with a static (or already published) scale every block reads it
-// and encodes; with a dynamic scale the single block of a small tensor
-// (<= 65536 elements) reduces it itself first.
+// Pass 2, by `mode`: 0 one block reduces the (small, <= 65536 elements)
+// tensor itself, then encodes; 1 the scale is an input; 2 every block
+// merges pass 1's nparts chunk maxima and block 0 publishes the scale.
 template <int FT, bool VEC>
-__global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restrict__ x, int64_t numel,
-                                                           int static_scale, float* __restrict__ scale,
-                                                           uint8_t* __restrict__ q)
+__global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restrict__ x, int64_t numel, int mode,
+                                                           const float* __restrict__ parts, int nparts,
+                                                           float* __restrict__ scale, uint8_t* __restrict__ q)
 {
-    __shared__ float sm[4];
-    __shared__ FP sp;
-    if (!static_scale) {
-        float a = 0.0f;
-        for (int64_t e = threadIdx.x; e < numel; e += 256) a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, e)));
-        a = team_max<64>(a);
-        if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        FP p;
-        if (static_scale) {
-            p.s = scale[0];
-            p.fast = scale_in_fast_range(p.s);
-            p.y = p.fast ? rcp_rn(p.s) : 0.0f;
-        } else {
-            p = fp8_params<FT>(__builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3])));
-            scale[0] = p.s;
+    FP p;
+    if (mode == 2) {
+        const Part4 pp = load_partials<false>(parts, nparts);
+        float amax, unused;
+        merge_partials<false>(pp, amax, unused);
+        p = fp8_params<FT>(amax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = p.s;
+    } else {
+        __shared__ float sm[4];
+        __shared__ FP sp;
+        if (mode == 0) {
+            float a = 0.0f;
+            for (int64_t e = threadIdx.x; e < numel; e += 256)
+                a = __builtin_fmaxf(a, __builtin_fabsf(load1<FT>(x, e)));
+            a = team_max<64>(a);
+            if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = a;
         }
-        sp = p;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            FP g;
+            if (mode == 1) {
+                g.s = scale[0];
+                g.fast = scale_in_fast_range(g.s);
+                g.y = g.fast ? rcp_rn(g.s) : 0.0f;
+            } else {
+                g = fp8_params<FT>(__builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3])));
+                scale[0] = g.s;
+            }
+            sp = g;
+        }
+        __syncthreads();
+        p = sp;
     }
-    __syncthreads();
-    const FP p = sp;
     const int64_t stride = (int64_t)gridDim.x * 256;
     if constexpr (VEC) {
         for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < numel / 8; vi += stride) {
@@ -446,20 +466,44 @@ __global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, co
                                                   const uint8_t* __restrict__ bscale, int64_t nvec,
                                                   void* __restrict__ out)
 {
+    if constexpr (OP == OP_DEQ) {
+        for (int64_t base = (int64_t)blockIdx.x * 256 * DEQ_V; base < nvec;
+             base += (int64_t)gridDim.x * 256 * DEQ_V) {
+            uint2 w[DEQ_V];
+            uint32_t sb[DEQ_V];
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi < nvec)
+                    w[k] = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + vi * 8)
+                                 : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + vi * 8);
+            }
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi < nvec) sb[k] = bscale[vi / 4];
+            }
+#pragma unroll
+            for (int k = 0; k < DEQ_V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi >= nvec) break;
+                const float X = e8m0_val(sb[k]);
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    o[i] = e4m3_val(w[k].x, i) * X;
+                    o[4 + i] = e4m3_val(w[k].y, i) * X;
+                }
+                store8<FT, 1>(out, vi * 8, o);
+            }
+        }
+        return;
+    }
     for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
         const int64_t e = vi * 8;
         const uint32_t sb = bscale[e / 32];
         float o[8];
-        if constexpr (OP == OP_DEQ) {
-            const float X = e8m0_val(sb);
-            const uint2 w = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + e)
-                                  : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + e);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[i] = e4m3_val(w.x, i) * X;
-                o[4 + i] = e4m3_val(w.y, i) * X;
-            }
-        } else if constexpr (OP == OP_DQB) {
+        if constexpr (OP == OP_DQB) {
             const float X = e8m0_val(sb);
             float d[8];
             widen8<FT>(load8<FT, true>(a, e), d);
@@ -485,14 +529,6 @@ __global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, co
 }
 
 // ============================================================ host side
-
-static unsigned grid_for(int64_t work, int64_t per_block)
-{
-    int64_t g = cdiv(work, per_block);
-    if (g < 1) g = 1;
-    if (g > (1 << 20)) g = 1 << 20;
-    return (unsigned)g;
-}
 
 #define TQ_FT_SWITCH(ft, ...)                                     \
     switch (ft) {                                                 \
@@ -584,7 +620,8 @@ static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t r
         if (br == 1 && cols % bc == 0 && (bc & (bc - 1)) == 0)
             for (shift = 0; ((int64_t)1 << shift) < bc; ++shift) {}
         const BlkIdx bi = shift >= 0 ? BlkIdx{} : make_blkidx(n, cols, br, bc, nbc);
-        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256)), dim3(256), 0, st,
+        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256 * (OP == OP_DEQ ? DEQ_V : 1))),
+                                            dim3(256), 0, st,
                                             a, b, n / 8, cols, br, bc, nbc, shift, bi, scale, out));
     } else {
         TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew_generic<OP, FTV>), dim3(grid_for(n, 256)), dim3(256), 0, st,
@@ -604,7 +641,7 @@ static tq_status mx8_elementwise(const void* a, const void* b, int ft, const uin
                                  void* out, hipStream_t st)
 {
     const int64_t nvec = rows * k / 8;
-    const dim3 grid(grid_for(nvec, 256)), block(256);
+    const dim3 grid(grid_for(nvec, 256 * (OP == OP_DEQ ? DEQ_V : 1))), block(256);
     TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_mxfp8_ew<OP, FTV>), grid, block, 0, st, a, b, bscale, nvec, out));
     return launch_status();
 }
@@ -732,24 +769,26 @@ tq_status tq_quant_fp8_per_tensor(const void* x, int x_dtype, int64_t numel, int
     hipStream_t st = as_stream(stream);
     const bool vec = numel % 8 == 0;
     const bool small = numel <= 65536;
-    if (!static_scale && !small) {
+    const int mode = static_scale ? 1 : small ? 0 : 2;
+    int nparts = 0;
+    float* ws = static_cast<float*>(workspace);
+    if (mode == 2) {
         if (!workspace || workspace_bytes < tq_workspace_bytes(2, numel)) return TQ_ERR_INVALID;
-        const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
-        const int nws = (int)cdiv(numel, chunk);
-        float* ws = static_cast<float*>(workspace);
+        if (!aligned16(workspace)) return TQ_ERR_ALIGN;
+        const int64_t chunk = tensor_chunk(numel, &nparts);
         TQ_FT_SWITCH(x_dtype, {
-            if (vec) hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, true>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws);
-            else hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, false>), dim3(nws), dim3(256), 0, st, x, numel, chunk, ws);
-            hipLaunchKernelGGL((k_fp8_tensor_finalize<FTV>), dim3(1), dim3(256), 0, st, ws, nws, scale);
+            if (vec) hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, true>), dim3(nparts), dim3(256), 0, st, x, numel, chunk,
+                                        ws);
+            else hipLaunchKernelGGL((k_fp8_tensor_amax<FTV, false>), dim3(nparts), dim3(256), 0, st, x, numel, chunk,
+                                    ws);
         });
         if (launch_status()) return TQ_ERR_HIP;
     }
-    const int eff_static = static_scale || !small;   // the scale is known before the encode
-    const dim3 grid(eff_static ? grid_for(vec ? numel / 8 : numel, 256 * 4) : 1u);
+    const dim3 grid(mode != 0 ? grid_for(vec ? numel / 8 : numel, 256 * 4) : 1u);
     TQ_FT_SWITCH(x_dtype, {
-        if (vec) hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, true>), grid, dim3(256), 0, st, x, numel, eff_static,
-                                    scale, q);
-        else hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, false>), grid, dim3(256), 0, st, x, numel, eff_static,
+        if (vec) hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, true>), grid, dim3(256), 0, st, x, numel, mode, ws,
+                                    nparts, scale, q);
+        else hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, false>), grid, dim3(256), 0, st, x, numel, mode, ws, nparts,
                                 scale, q);
     });
     return launch_status();

@@ -20,6 +20,39 @@ inline int ftype_size(int t) { return t == TQ_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Workgroups for a grid-stride kernel: one per `per_block` units of work,
+// at least 1 and at most 2^20.
+inline unsigned grid_for(int64_t work, int64_t per_block)
+{
+    int64_t g = cdiv(work, per_block);
+    if (g < 1) g = 1;
+    if (g > (1 << 20)) g = 1 << 20;
+    return (unsigned)g;
+}
+
+// Per-tensor statistics of a large tensor are reduced in two launches: a
+// first pass writes one partial per chunk, at most TENSOR_PARTS of them
+// (padded to a multiple of 4 with chunks past the end, whose partials are 0),
+// and every workgroup of the encoding pass merges them itself.  tensor_chunk
+// gives the chunk length (a multiple of 2048 elements, at least 8192) and the
+// padded partial count.
+constexpr int TENSOR_PARTS = 1024;
+
+// FP4 block quantize (tq_fp4.hip): argument checks, and the launches on
+// checked arguments (ws: TENSOR_PARTS floats, 16-byte aligned, used only
+// for a dynamic NVFP4 per-tensor scale).
+tq_status check_fp4_quant(const void* x, int x_dtype, int64_t rows, int64_t k, int kind, const uint8_t* packed,
+                          const uint8_t* block_scale, const float* global_scale);
+tq_status fp4_quant_launch(const void* x, int x_dtype, int64_t numel, int kind, uint8_t* packed,
+                           uint8_t* block_scale, float* global_scale, int static_global, float* ws, hipStream_t st);
+
+inline int64_t tensor_chunk(int64_t numel, int* nparts)
+{
+    const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, TENSOR_PARTS), 2048) * 2048);
+    *nparts = (int)(cdiv(cdiv(numel, chunk), 4) * 4);
+    return chunk;
+}
+
 inline tq_status launch_status()
 {
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;

@@ -640,69 +640,59 @@ __global__ __launch_bounds__(256) void k_tensor_partial(const void* __restrict__
     }
 }
 
-// Pass 1b: one workgroup merges the partials and publishes scale (and
-// zero-point); the encode pass then reads them like a static scale instead of
-// every workgroup merging the partials again.
-template <int FT, bool SYM>
-__global__ __launch_bounds__(256) void k_tensor_finalize(const float* __restrict__ ws, int nblk, float qmin,
-                                                         float qmax, float yc, float* __restrict__ scale,
-                                                         uint8_t* __restrict__ zp)
-{
-    __shared__ float smx[4], smn[4];
-    float mx = 0.0f, nmn = 0.0f;
-    for (int k = threadIdx.x; k < nblk; k += 256) {
-        mx = __builtin_fmaxf(mx, ws[k]);
-        nmn = __builtin_fmaxf(nmn, ws[nblk + k]);
-    }
-    mx = team_max<64>(mx);
-    nmn = team_max<64>(nmn);
-    if ((threadIdx.x & 63) == 0) {
-        smx[threadIdx.x >> 6] = mx;
-        smn[threadIdx.x >> 6] = nmn;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        mx = __builtin_fmaxf(__builtin_fmaxf(smx[0], smx[1]), __builtin_fmaxf(smx[2], smx[3]));
-        nmn = __builtin_fmaxf(__builtin_fmaxf(smn[0], smn[1]), __builtin_fmaxf(smn[2], smn[3]));
-        const GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
-                         : make_gp<FT, false>(0.0f, -nmn, mx, qmin, qmax, yc);
-        scale[0] = p.s;
-        if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
-    }
-}
+// Pass 2, by `mode`:
+//   TENSOR_ONE    one block reduces the (small, <= 65536 elements) tensor
+//                 itself, publishes scale / zero-point and encodes: one launch;
+//   TENSOR_STATIC scale / zero-point are inputs;
+//   TENSOR_MERGE  every block merges pass 1's partials (parts[0..nparts) the
+//                 maxima, parts[nparts..2 nparts) the |minima|), block 0
+//                 publishes scale / zero-point.
+enum { TENSOR_ONE = 0, TENSOR_STATIC = 1, TENSOR_MERGE = 2 };
 
-// Pass 2: with a static (or already published) scale every block reads
-// scale / zero-point and encodes; with a dynamic scale the single block of a
-// small tensor (<= 65536 elements) reduces it itself first: one launch.
 template <int FT, int BITS, bool SYM, bool FAKE = false>
-__global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ x, int64_t numel,
-                                                       int static_scale, float qmin, float qmax, float yc,
-                                                       void* __restrict__ out, float* __restrict__ scale,
-                                                       uint8_t* __restrict__ zp, bool zp_signed)
+__global__ __launch_bounds__(256) void k_tensor_encode(const void* __restrict__ x, int64_t numel, int mode,
+                                                       const float* __restrict__ parts, int nparts, float qmin,
+                                                       float qmax, float yc, void* __restrict__ out,
+                                                       float* __restrict__ scale, uint8_t* __restrict__ zp,
+                                                       bool zp_signed)
 {
     uint8_t* const q = static_cast<uint8_t*>(out);
-    __shared__ GP sp;
-    if (!static_scale) {
-        float mn = 0.0f, mx = 0.0f;
-        range_minmax<FT, SYM>(x, 0, numel, (numel & 7) == 0, mn, mx);
-        block_minmax(mn, mx);
-        if (threadIdx.x == 0) {
-            GP p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
-                       : make_gp<FT, false>(0.0f, mn, mx, qmin, qmax, yc);
-            sp = p;
+    GP p;
+    if (mode == TENSOR_MERGE) {
+        const Part4 pp = load_partials<!SYM>(parts, nparts);
+        float mx, nmn;
+        merge_partials<!SYM>(pp, mx, nmn);
+        p = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
+                : make_gp<FT, false>(0.0f, -nmn, mx, qmin, qmax, yc);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
             scale[0] = p.s;
             if (!SYM) zp[0] = (uint8_t)(int)p.zpf;
         }
-    } else if (threadIdx.x == 0) {
-        GP p;
-        p.s = scale[0];
-        p.fast = scale_in_fast_range(p.s);
-        p.y = p.fast ? rcp_rn(p.s) : 0.0f;
-        p.zpf = zp_at(zp, 0, zp_signed);
-        sp = p;
+    } else {
+        __shared__ GP sp;
+        if (mode == TENSOR_ONE) {
+            float mn = 0.0f, mx = 0.0f;
+            range_minmax<FT, SYM>(x, 0, numel, (numel & 7) == 0, mn, mx);
+            block_minmax(mn, mx);
+            if (threadIdx.x == 0) {
+                GP g = SYM ? make_gp<FT, true>(mx, 0.0f, 0.0f, qmin, qmax, yc)
+                           : make_gp<FT, false>(0.0f, mn, mx, qmin, qmax, yc);
+                sp = g;
+                scale[0] = g.s;
+                if (!SYM) zp[0] = (uint8_t)(int)g.zpf;
+            }
+        } else if (threadIdx.x == 0) {
+            GP g;
+            g.s = scale[0];
+            g.fast = scale_in_fast_range(g.s);
+            g.y = g.fast ? rcp_rn(g.s) : 0.0f;
+            g.zpf = zp_at(zp, 0, zp_signed);
+            sp = g;
+        }
+        __syncthreads();
+        p = sp;
     }
-    __syncthreads();
-    const GP p = sp;
+    const bool static_scale = mode == TENSOR_STATIC;
     const float lo = MAGIC + qmin, hi = MAGIC + qmax;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     if ((numel & 7) == 0) {
@@ -822,11 +812,12 @@ __device__ __forceinline__ float zp_f(const uint8_t* zp, int64_t g)
     return SIGNED ? (float)(int8_t)zp[g] : (float)zp[g];
 }
 
-// Vectors of 8 per thread and grid step in the streaming kernels: one each
-// (two or four, and grids capped at 1024 or 2048 workgroups, measured slower).
-// 8-bit codes come through non-temporal loads, 4-bit codes through plain ones
-// (the 4-byte lane loads of a 1:4 read:write stream are faster that way).
-constexpr int DQV1 = 1, SVPT = 1, DVPT = 1;
+// Vectors of 8 per thread and grid step in the STE and dequantize-backward
+// kernels: one each (two or four, and grids capped at 1024 or 2048
+// workgroups, measured slower); the dequantizers take DEQ_V.  8-bit codes come
+// through non-temporal loads, 4-bit codes through plain ones (the 4-byte lane
+// loads of a 1:4 read:write stream are faster that way).
+constexpr int SVPT = 1, DVPT = 1;
 constexpr bool DEQ_NT = true;
 
 template <int MAPK, int YT, int BITS, bool SIGNED>
@@ -834,46 +825,49 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
                                                      int64_t P2, int sh, const float* __restrict__ scale,
                                                      const uint8_t* __restrict__ zp, void* __restrict__ y)
 {
-    constexpr int DQV = DQV1;   // vectors per thread per iteration
-    for (int64_t base = (int64_t)blockIdx.x * 256 * DQV; base < nvec; base += (int64_t)gridDim.x * 256 * DQV) {
+    constexpr int V = DEQ_V;    // vectors per thread: all their loads before any store
+    constexpr int NS = MAPK == MAP_CONTIG ? 1 : 8;   // scales per vector
+    for (int64_t base = (int64_t)blockIdx.x * 256 * V; base < nvec; base += (int64_t)gridDim.x * 256 * V) {
+        uint32_t cw[V][2];
+        float sv[V][NS], zv[V][NS];
 #pragma unroll
-        for (int k = 0; k < DQV; ++k) {
+        for (int k = 0; k < V; ++k) {
             const int64_t vi = base + k * 256 + threadIdx.x;
-            if (vi >= nvec) break;
+            cw[k][0] = cw[k][1] = 0;
+            if (vi >= nvec) continue;
             const int64_t e = vi * 8;
-            uint32_t cw[2];
             if constexpr (BITS == 8) {
                 const uint2 w = DEQ_NT ? ld8<true>(q + e) : *reinterpret_cast<const uint2*>(q + e);
-                cw[0] = w.x;
-                cw[1] = w.y;
+                cw[k][0] = w.x;
+                cw[k][1] = w.y;
             } else {
                 // 4-bit codes: plain loads (measured faster than non-temporal ones for this
                 // 1:4 read:write shape, where the 4-byte lane loads are a fifth of the bytes)
-                cw[0] = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
-                cw[1] = 0;
+                cw[k][0] = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
             }
-            const int64_t g = vec_group<MAPK>(e, P1, P2, sh);
-            float out[8], sv[8], zv[8];
-            if constexpr (MAPK == MAP_CONTIG) {
-                const float s1 = scale[g], z1 = zp_f<SIGNED>(zp, g);
+        }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    sv[i] = s1;
-                    zv[i] = z1;
-                }
-            } else {
+        for (int k = 0; k < V; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi >= nvec) continue;
+            const int64_t g = vec_group<MAPK>(vi * 8, P1, P2, sh);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    sv[i] = scale[g + i];
-                    zv[i] = zp_f<SIGNED>(zp, g + i);
-                }
+            for (int i = 0; i < NS; ++i) {
+                sv[k][i] = scale[g + i];
+                zv[k][i] = zp_f<SIGNED>(zp, g + i);
             }
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi >= nvec) break;
+            float out[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t c = BITS == 8 ? (cw[i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[0] >> (i * 4)) & 0xfu;
-                out[i] = (code_f<SIGNED>(c, BITS) - zv[i]) * sv[i];
+                const uint32_t c = BITS == 8 ? (cw[k][i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[k][0] >> (i * 4)) & 0xfu;
+                out[i] = (code_f<SIGNED>(c, BITS) - zv[k][NS == 1 ? 0 : i]) * sv[k][NS == 1 ? 0 : i];
             }
-            store8<YT, BITS == 8 ? WT : 1>(y, e, out);
+            store8<YT, BITS == 8 ? WT : 1>(y, vi * 8, out);
         }
     }
 }
@@ -1054,14 +1048,6 @@ __global__ __launch_bounds__(256) void k_ste_generic(const void* __restrict__ x,
 
 // ============================================================ host side
 
-static unsigned grid_for(int64_t work, int64_t per_block)
-{
-    int64_t g = cdiv(work, per_block);
-    if (g < 1) g = 1;
-    if (g > (1 << 20)) g = 1 << 20;
-    return (unsigned)g;
-}
-
 // Dispatch helpers over the runtime (ftype, bits, symmetric) triple.
 #define TQ_FT_SWITCH(ft, ...)                                     \
     switch (ft) {                                                 \
@@ -1098,7 +1084,10 @@ static void quant_contig(const void* x, int64_t G, int64_t L, int64_t ldx, float
     case 16: launch_team<FT, BITS, SYM, 2, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 32: launch_team<FT, BITS, SYM, 4, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 64: launch_team<FT, BITS, SYM, 8, 1, 8>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
-    case 128: launch_team<FT, BITS, SYM, 8, 2, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
+    case 128:
+        // 8 lanes x 2 vectors per group (16 lanes x 1 vector with 1 or 2 groups per lane measured 9-19% slower)
+        launch_team<FT, BITS, SYM, 8, 2, 1>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st);
+        return;
     case 256: launch_team<FT, BITS, SYM, 16, 2, 4>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 512: launch_team<FT, BITS, SYM, 64, 1, 4>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
     case 1024: launch_team<FT, BITS, SYM, 64, 2, 2>(x, G, ldx, qmin, qmax, yc, q, scale, zp, st); return;
@@ -1204,7 +1193,7 @@ static int log2_exact(int64_t v)
 template <int MAPK>
 static void launch_ew_vec(int op, const EwArgs& a, int64_t nvec, int64_t P1, int64_t P2, hipStream_t st)
 {
-    const dim3 grid(grid_for(nvec, 256 * DQV1)), block(256);
+    const dim3 grid(grid_for(nvec, 256 * DEQ_V)), block(256);
     const bool sg = code_signed(a.code);
     const int bits = code_bits(a.code);
     const int sh = MAPK == MAP_CONTIG ? log2_exact(P1) : -1;
@@ -1302,28 +1291,18 @@ static tq_status check_map_args(int32_t ndim, const int64_t* shape, int32_t axis
     return TQ_OK;
 }
 
-// Per-tensor dynamic scale of a large tensor: block partials (pass 1), then
-// one workgroup publishes scale / zero-point (pass 1b).
-static tq_status tensor_scale_passes(const void* x, int xt, int64_t numel, bool sym, float qmin, float qmax,
-                                     float yc, void* workspace, size_t workspace_bytes, float* scale, uint8_t* zp,
-                                     hipStream_t st)
+// Per-tensor dynamic scale of a large tensor, pass 1: the chunk partials
+// (maxima, then |minima|) into the workspace; the encode merges them.
+static tq_status tensor_partials(const void* x, int xt, int64_t numel, bool sym, void* workspace,
+                                 size_t workspace_bytes, int* nparts, hipStream_t st)
 {
     if (!workspace || workspace_bytes < tq_workspace_bytes(0, numel)) return TQ_ERR_INVALID;
-    // chunk >= numel / 1024 rounded up, so at most 1024 partial pairs
-    const int64_t chunk = std::max<int64_t>(256 * 8 * 4, cdiv(cdiv(numel, 1024), 2048) * 2048);
-    const int nblk = (int)cdiv(numel, chunk);
-    if (nblk > 1024) return TQ_ERR_INVALID;
+    if (!aligned16(workspace)) return TQ_ERR_ALIGN;
+    const int64_t chunk = tensor_chunk(numel, nparts);
     float* ws = static_cast<float*>(workspace);
     TQ_FT_SWITCH(xt, {
-        if (sym) {
-            hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
-            hipLaunchKernelGGL((k_tensor_finalize<FTV, true>), dim3(1), dim3(256), 0, st, ws, nblk, qmin, qmax, yc,
-                               scale, zp);
-        } else {
-            hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(nblk), dim3(256), 0, st, x, numel, chunk, ws);
-            hipLaunchKernelGGL((k_tensor_finalize<FTV, false>), dim3(1), dim3(256), 0, st, ws, nblk, qmin, qmax, yc,
-                               scale, zp);
-        }
+        if (sym) hipLaunchKernelGGL((k_tensor_partial<FTV, true>), dim3(*nparts), dim3(256), 0, st, x, numel, chunk, ws);
+        else hipLaunchKernelGGL((k_tensor_partial<FTV, false>), dim3(*nparts), dim3(256), 0, st, x, numel, chunk, ws);
     });
     return launch_status();
 }
@@ -1425,17 +1404,19 @@ tq_status tq_quant_per_tensor(const void* x, int x_dtype, int64_t numel, int cod
     const bool small = numel <= 65536;
     uint8_t* qb = static_cast<uint8_t*>(q);
     uint8_t* zb = static_cast<uint8_t*>(zero_point);
-    if (!static_scale && !small) {
-        s = tensor_scale_passes(x, x_dtype, numel, sym, fmin, fmax, yc, workspace, workspace_bytes, scale, zb, st);
+    const int mode = static_scale ? TENSOR_STATIC : small ? TENSOR_ONE : TENSOR_MERGE;
+    int nparts = 0;
+    if (mode == TENSOR_MERGE) {
+        s = tensor_partials(x, x_dtype, numel, sym, workspace, workspace_bytes, &nparts, st);
         if (s) return s;
     }
-    const int eff_static = static_scale || !small;   // the scale is known before the encode
+    const float* parts = static_cast<const float*>(workspace);
     const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
-    const dim3 grid(eff_static ? grid_for(work, 256 * 4) : 1u);
+    const dim3 grid(mode != TENSOR_ONE ? grid_for(work, 256 * 4) : 1u);
     const bool zs = code_signed(code);
     TQ_FT_SWITCH(x_dtype, TQ_BITS_SYM_SWITCH(bits, sym,
-        hipLaunchKernelGGL((k_tensor_encode<FTV, BV, SV>), grid, dim3(256), 0, st, x, numel, eff_static, fmin, fmax,
-                           yc, qb, scale, zb, zs)));
+        hipLaunchKernelGGL((k_tensor_encode<FTV, BV, SV>), grid, dim3(256), 0, st, x, numel, mode, parts, nparts, fmin,
+                           fmax, yc, qb, scale, zb, zs)));
     return launch_status();
 }
 
@@ -1460,19 +1441,21 @@ tq_status tq_fake_quant_per_tensor(const void* x, int x_dtype, int64_t numel, in
         return launch_status();
     }
     const bool small = numel <= 65536;
-    if (!static_scale && !small) {
-        s = tensor_scale_passes(x, x_dtype, numel, sym, fmin, fmax, yc, workspace, workspace_bytes, scale, zb, st);
+    const int mode = static_scale ? TENSOR_STATIC : small ? TENSOR_ONE : TENSOR_MERGE;
+    int nparts = 0;
+    if (mode == TENSOR_MERGE) {
+        s = tensor_partials(x, x_dtype, numel, sym, workspace, workspace_bytes, &nparts, st);
         if (s) return s;
     }
-    const int eff_static = static_scale || !small;
+    const float* parts = static_cast<const float*>(workspace);
     const int64_t work = (numel % 8 == 0) ? numel / 8 : numel;
-    const dim3 grid(eff_static ? grid_for(work, 256 * 4) : 1u);
+    const dim3 grid(mode != TENSOR_ONE ? grid_for(work, 256 * 4) : 1u);
     const bool zs = code_signed(code);
     TQ_FT_SWITCH(x_dtype, {
-        if (sym) hipLaunchKernelGGL((k_tensor_encode<FTV, 8, true, true>), grid, dim3(256), 0, st, x, numel,
-                                    eff_static, fmin, fmax, yc, y, scale, zb, zs);
-        else hipLaunchKernelGGL((k_tensor_encode<FTV, 8, false, true>), grid, dim3(256), 0, st, x, numel, eff_static,
-                                fmin, fmax, yc, y, scale, zb, zs);
+        if (sym) hipLaunchKernelGGL((k_tensor_encode<FTV, 8, true, true>), grid, dim3(256), 0, st, x, numel, mode,
+                                    parts, nparts, fmin, fmax, yc, y, scale, zb, zs);
+        else hipLaunchKernelGGL((k_tensor_encode<FTV, 8, false, true>), grid, dim3(256), 0, st, x, numel, mode,
+                                parts, nparts, fmin, fmax, yc, y, scale, zb, zs);
     });
     return launch_status();
 }
