@@ -469,6 +469,19 @@ tq_status tq_quant_fp4_block(const void* x, int x_dtype, int64_t rows, int64_t k
                              uint8_t* packed, uint8_t* block_scale, float* global_scale,
                              int static_global, void* workspace, size_t workspace_bytes,
                              void* stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, hosts that forbid hipMalloc):
+ * tq_quant_fp4_block without the workspace, same arguments otherwise and the
+ * same results bit for bit.  A dynamic NVFP4 per-tensor scale keeps its up
+ * to 1024 chunk maxima in a 4 KiB device array of the library's own (one per
+ * GPU, held until the process ends, found by hipGetSymbolAddress on the first
+ * call on that GPU); nothing is allocated, freed or synchronized.  Any tensor
+ * size is taken (the chunks grow so that 1024 partials always suffice;
+ * TQ_ERR_UNSUPPORTED if that ever failed).  Calls that overlap on one GPU
+ * share that array and race: serialize them (one stream, or events). */
+tq_status tq_quant_fp4_block_noalloc(const void* x, int x_dtype, int64_t rows, int64_t k, int kind,
+                                     uint8_t* packed, uint8_t* block_scale, float* global_scale,
+                                     int static_global, void* stream);
 /* y = val(q) * eff, rounded once to y_dtype. */
 tq_status tq_dequant_fp4_block(const uint8_t* packed, const uint8_t* block_scale,
                                const float* global_scale, int64_t rows, int64_t k, int kind,

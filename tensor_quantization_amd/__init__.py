@@ -68,6 +68,7 @@ _SIGS = {
     "tq_quant_fp8_block_backward": ([_P, _I, _I64, _I64, _I32, _I32, _P, _P, _P, _P], _I),
     "tq_dequant_fp8_block_backward": ([_P, _I, _I64, _I64, _I32, _I32, _P, _P, _P], _I),
     "tq_quant_fp4_block": ([_P, _I, _I64, _I64, _I, _P, _P, _P, _I, _P, _SZ, _P], _I),
+    "tq_quant_fp4_block_noalloc": ([_P, _I, _I64, _I64, _I, _P, _P, _P, _I, _P], _I),
     "tq_dequant_fp4_block": ([_P, _P, _P, _I64, _I64, _I, _P, _I, _P], _I),
     "tq_quant_fp4_block_backward": ([_P, _I, _P, _P, _I64, _I64, _I, _P, _P, _P], _I),
     "tq_dequant_fp4_block_backward": ([_P, _I, _P, _P, _I64, _I64, _I, _P, _P], _I),
@@ -439,6 +440,18 @@ def tq_quant_fp4_block(x, kind="nvfp4", global_scale=None):
     _call("tq_quant_fp4_block", _ptr(x), _ft(x), rows, k, FP4_KIND[kind], _ptr(packed), _ptr(bs), _ptr(sg),
           int(static), _ptr(ws), ws.numel(), _stream(x.device))
     return packed, bs, sg
+
+
+def tq_quant_fp4_block_noalloc(x, packed, block_scale, global_scale=None, kind="nvfp4", static_global=False):
+    """tq_quant_fp4_block into caller-provided outputs, with no workspace and
+    no allocation in the library (packed [rows, k/2] u8, block_scale
+    [rows, k/gs] u8, global_scale float32[1] for NVFP4: an input when
+    static_global, else written)."""
+    x = _dev_float(x, "x")
+    rows, k = x.shape
+    _call("tq_quant_fp4_block_noalloc", _ptr(x), _ft(x), rows, k, FP4_KIND[kind], _ptr(packed), _ptr(block_scale),
+          _ptr(global_scale), int(bool(static_global)), _stream(x.device))
+    return packed, block_scale, global_scale
 
 
 def tq_dequant_fp4_block(packed, block_scale, global_scale=None, kind="nvfp4", out_dtype=torch.bfloat16):
