@@ -151,10 +151,6 @@ def rate(nbytes, us):
 KERNEL_SOURCES = {
     "quant_per_token_s8": ("tq_int.hip", "tq_device.h", "tq_host.h"),
     "quant_per_group_u4_g128": ("tq_int.hip", "tq_device.h", "tq_host.h"),
-    "quant_per_token_s8_backward": ("tq_int.hip", "tq_device.h", "tq_host.h"),
-    "dequant_per_token_s8": ("tq_int.hip", "tq_device.h", "tq_host.h"),
-    "dequant_per_token_backward": ("tq_int.hip", "tq_device.h", "tq_host.h"),
-    "dequant_per_group_u4_g128": ("tq_int.hip", "tq_device.h", "tq_host.h"),
 }
 
 
@@ -216,63 +212,63 @@ class Inputs:
 def quantizers(torch, tq, inp):
     """(name, workload, algorithmic bytes, make base set, launch, reads,
     ceiling mix (in, out, store policy, threads)) for every workload's
-    quantize call."""
+    quantize call.  Inputs are generated when a set is first made."""
+    import workloads
     L = tq._lib
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     E = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")   # noqa: E731
     u8, f32 = torch.uint8, torch.float32
+    shape = lambda key: tuple(workloads.CONFIGS[key]["shape"])           # noqa: E731
     ops = []
 
-    x1 = inp.get("x:c1_per_tensor_s8")
-    n1 = x1.size
+    R1, C1 = shape("c1_per_tensor_s8")
+    n1 = R1 * C1
     ops.append(("per_tensor_s8", "f32 [64,256] per-tensor s8 (launch-bound)", n1 * 4 + n1 + 4,
-                lambda: dict(x=dev_bits(x1, "f32", torch), q=E(n1, u8), s=E(1, f32), ws=E(8192, u8)),
+                lambda: dict(x=dev_bits(inp.get("x:c1_per_tensor_s8"), "f32", torch), q=E(n1, u8), s=E(1, f32),
+                             ws=E(8192, u8)),
                 lambda b: check(L.tq_quant_per_tensor(P(b["x"]), F32, n1, S8, -127, 127, 0, P(b["q"]), P(b["s"]),
                                                       None, P(b["ws"]), 8192, stream), "c1 quant"),
                 n1 * 4, None))
 
-    x2 = inp.get("x:c2_per_token_s8")
-    R2, C2 = x2.shape
-    n2 = x2.size
+    R2, C2 = shape("c2_per_token_s8")
+    n2 = R2 * C2
     ops.append(("per_token_s8", "bf16 [8192,4096] per-token s8", n2 * 3 + R2 * 4,
-                lambda: dict(x=dev_bits(x2, "bf16", torch), q=E((R2, C2), u8), s=E(R2, f32)),
+                lambda: dict(x=dev_bits(inp.get("x:c2_per_token_s8"), "bf16", torch), q=E((R2, C2), u8),
+                             s=E(R2, f32)),
                 lambda b: check(L.tq_quant_per_token(P(b["x"]), BF16, R2, C2, S8, -127, 127, P(b["q"]), P(b["s"]),
                                                      None, stream), "c2 quant"),
                 n2 * 2, (16, 8, 1, n2 // 8)))
 
-    w3 = inp.get("x:c3_per_group_u4_g128")
-    N3, K3 = w3.shape
-    n3 = w3.size
+    N3, K3 = shape("c3_per_group_u4_g128")
+    n3 = N3 * K3
     shp3 = (ctypes.c_int64 * 2)(N3, K3)
     ops.append(("per_group_u4_g128", "f16 [11008,4096] per-group u4 g=128 asymmetric", n3 * 2 + n3 // 2 +
                 (n3 // 128) * 5,
-                lambda: dict(x=dev_bits(w3, "f16", torch), q=E((N3, K3 // 2), u8), s=E((N3, K3 // 128), f32),
-                             z=E((N3, K3 // 128), u8)),
+                lambda: dict(x=dev_bits(inp.get("x:c3_per_group_u4_g128"), "f16", torch), q=E((N3, K3 // 2), u8),
+                             s=E((N3, K3 // 128), f32), z=E((N3, K3 // 128), u8)),
                 lambda b: check(L.tq_quant_per_group(P(b["x"]), F16, 2, shp3, 1, 128, U4, 0, 15, P(b["q"]), P(b["s"]),
                                                      P(b["z"]), stream), "c3 quant"),
                 n3 * 2, (16, 4, 1, n3 // 8)))
 
     for key, name in (("c4_fp8_act_1x128", "fp8_1x128"), ("c4_fp8_weight_128x128", "fp8_128x128")):
-        import workloads
-        xa = inp.get("x:" + key)
-        R, C = xa.shape
+        R, C = shape(key)
         br, bc = workloads.CONFIGS[key]["block"]
         ns = (R // br) * (C // bc)
         ops.append((name, "bf16 [%d,%d] FP8 E4M3 %dx%d" % (R, C, br, bc), R * C * 3 + ns * 4,
-                    lambda xa=xa, R=R, C=C, ns=ns: dict(x=dev_bits(xa, "bf16", torch), q=E((R, C), u8), s=E(ns, f32)),
+                    lambda key=key, R=R, C=C, ns=ns: dict(x=dev_bits(inp.get("x:" + key), "bf16", torch),
+                                                          q=E((R, C), u8), s=E(ns, f32)),
                     lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_quant_fp8_block(P(b["x"]), BF16, R, C, br, bc,
                                                                                  P(b["q"]), P(b["s"]), stream),
                                                             "fp8 quant"),
                     R * C * 2, (16, 8, 1, R * C // 8)))
 
-    w5 = inp.get("x:c5_fp4_weight")
-    N5, K5 = w5.shape
-    n5 = w5.size
+    N5, K5 = shape("c5_fp4_weight")
+    n5 = N5 * K5
     for kind, gs in (("nvfp4", 16), ("mxfp4", 32)):
         nb = n5 * 2 + n5 // 2 + n5 // gs + (4 if kind == "nvfp4" else 0)
-        mk = lambda gs=gs: dict(x=dev_bits(w5, "bf16", torch), p=E((N5, K5 // 2), u8),          # noqa: E731
-                                b=E((N5, K5 // gs), u8), g=torch.full((1,), 1.2e-5, dtype=f32, device="cuda"),
-                                ws=E(8192, u8))
+        mk = lambda gs=gs: dict(x=dev_bits(inp.get("x:c5_fp4_weight"), "bf16", torch),       # noqa: E731
+                                p=E((N5, K5 // 2), u8), b=E((N5, K5 // gs), u8),
+                                g=torch.full((1,), 1.2e-5, dtype=f32, device="cuda"), ws=E(8192, u8))
         cfg = "bf16 [14336,4096] %s" % kind.upper()
         if kind == "nvfp4":
             ops.append(("nvfp4_static_global", cfg + " (static per-tensor scale)", nb, mk,
@@ -331,6 +327,9 @@ def run_quantizers(torch, tq, inp, steps, warmup, iters, only=None):
             d["ceiling"] = {"mix": "%d:%d per unit" % mix[:2], "GBps": c["GBps"], "frac": c["frac"],
                             "units_per_lane": c["units_per_lane"]}
             d["of_ceiling"] = round(d["GBps"] / c["GBps"], 4)
+        t = read_traffic("quant_" + name)
+        if t is not None:
+            d["traffic"] = t
         out[name] = d
     return out, head, ceil_cache
 
@@ -471,11 +470,13 @@ def breakdown(torch, tq, inp, iters=30, only=None):
 
     # per-tensor s8, f32 [64, 256]: STE, dequantize, dequantize backward on
     # the quantizer's scale and codes
-    x1, dy1 = inp.get("x:c1_per_tensor_s8"), inp.get("dy:c1_per_tensor_s8")
-    n1 = x1.size
+    import workloads
+    shape = lambda key: tuple(workloads.CONFIGS[key]["shape"])           # noqa: E731
+    n1 = int(np.prod(shape("c1_per_tensor_s8")))
 
     def mk1():
-        b = dict(x=dev_bits(x1, "f32", torch), dy=dev_bits(dy1, "f32", torch), q=E(n1, u8), s=E(1, f32),
+        b = dict(x=dev_bits(inp.get("x:c1_per_tensor_s8"), "f32", torch),
+                 dy=dev_bits(inp.get("dy:c1_per_tensor_s8"), "f32", torch), q=E(n1, u8), s=E(1, f32),
                  ws=E(8192, u8), y=E(n1, f32), dx=E(n1, f32))
         check(L.tq_quant_per_tensor(P(b["x"]), F32, n1, S8, -127, 127, 0, P(b["q"]), P(b["s"]), None, P(b["ws"]),
                                     8192, stream), "c1 producer")
@@ -490,11 +491,11 @@ def breakdown(torch, tq, inp, iters=30, only=None):
 
     # per-token s8 on bf16 [8192, 4096]: fake quantization (round trip) and
     # its backward at per-tensor scope
-    x2, dy2 = inp.get("x:c2_per_token_s8"), inp.get("dy:c2_per_token_s8")
-    n2 = x2.size
+    n2 = int(np.prod(shape("c2_per_token_s8")))
 
     def mkf2():
-        b = dict(x=dev_bits(x2, "bf16", torch), dy=dev_bits(dy2, "bf16", torch), y=E(n2, bf16), s=E(1, f32),
+        b = dict(x=dev_bits(inp.get("x:c2_per_token_s8"), "bf16", torch),
+                 dy=dev_bits(inp.get("dy:c2_per_token_s8"), "bf16", torch), y=E(n2, bf16), s=E(1, f32),
                  ws=E(8192, u8), dx=E(n2, bf16))
         check(L.tq_fake_quant_per_tensor(P(b["x"]), BF16, n2, S8, -127, 127, 0, P(b["y"]), P(b["s"]), None,
                                          P(b["ws"]), 8192, stream), "fake producer")
@@ -512,11 +513,10 @@ def breakdown(torch, tq, inp, iters=30, only=None):
              n2 * 4)
 
     # binary64 inputs: the per-token workload's shape in f64 (N(0,1) values)
-    xf = inp.get("f64:per_token")
     shpf = (ctypes.c_int64 * 2)(8192, 4096)
 
     def mkd():
-        b = dict(x=torch.from_numpy(xf).cuda(), q=E(n2, u8), s=E(8192, torch.float64), y=E((8192, 4096), torch.float64))
+        b = dict(x=torch.from_numpy(inp.get("f64:per_token")).cuda(), q=E(n2, u8), s=E(8192, torch.float64), y=E((8192, 4096), torch.float64))
         check(L.tq_quant_f64(P(b["x"]), 2, shpf, 2, 0, 0, S8, -127, 127, 0, P(b["q"]), P(b["s"]), None, None, 0,
                              stream), "f64 producer")
         return b
@@ -529,14 +529,14 @@ def breakdown(torch, tq, inp, iters=30, only=None):
                              "f64 dequant"), n2)
 
     # per-group u4 g128 asymmetric, f16 [11008, 4096]: dequantize to f16
-    w3 = inp.get("x:c3_per_group_u4_g128")
-    N3, K3 = w3.shape
-    n3 = w3.size
+    N3, K3 = shape("c3_per_group_u4_g128")
+    n3 = N3 * K3
     shp3 = (ctypes.c_int64 * 2)(N3, K3)
     b3 = n3 * 2 + n3 // 2 + (n3 // 128) * 5
 
     def mk3():
-        b = dict(x=dev_bits(w3, "f16", torch), q=E((N3, K3 // 2), u8), s=E((N3, K3 // 128), f32),
+        b = dict(x=dev_bits(inp.get("x:c3_per_group_u4_g128"), "f16", torch), q=E((N3, K3 // 2), u8),
+                 s=E((N3, K3 // 128), f32),
                  z=E((N3, K3 // 128), u8), y=E((N3, K3), f16))
         check(L.tq_quant_per_group(P(b["x"]), F16, 2, shp3, 1, 128, U4, 0, 15, P(b["q"]), P(b["s"]), P(b["z"]),
                                    stream), "c3 producer")
@@ -547,16 +547,15 @@ def breakdown(torch, tq, inp, iters=30, only=None):
                                                     F16, stream), "c3 dequant"), n3 // 2 + (n3 // 128) * 5)
 
     # FP8 1x128 activations bf16 [4096, 7168]; 128x128 weights bf16 [7168, 7168]
-    import workloads
     for key, name in (("c4_fp8_act_1x128", "fp8_1x128"), ("c4_fp8_weight_128x128", "fp8_128x128")):
-        xa, dya = inp.get("x:" + key), inp.get("dy:" + key)
-        R, C = xa.shape
+        R, C = shape(key)
         br, bc = workloads.CONFIGS[key]["block"]
         ns = (R // br) * (C // bc)
         nb = R * C * 3 + ns * 4
 
-        def mk(xa=xa, dya=dya, R=R, C=C, ns=ns, br=br, bc=bc):
-            b = dict(x=dev_bits(xa, "bf16", torch), dy=dev_bits(dya, "bf16", torch), q=E((R, C), u8), s=E(ns, f32),
+        def mk(key=key, R=R, C=C, ns=ns, br=br, bc=bc):
+            b = dict(x=dev_bits(inp.get("x:" + key), "bf16", torch), dy=dev_bits(inp.get("dy:" + key), "bf16", torch),
+                     q=E((R, C), u8), s=E(ns, f32),
                      y=E((R, C), bf16))
             check(L.tq_quant_fp8_block(P(b["x"]), BF16, R, C, br, bc, P(b["q"]), P(b["s"]), stream), "fp8 producer")
             return b
@@ -576,13 +575,13 @@ def breakdown(torch, tq, inp, iters=30, only=None):
                      R * C * 2 + ns * 4)
 
     # MXFP8 on the FP8 activation workload bf16 [4096, 7168]: E4M3 + E8M0 per 32
-    xm = inp.get("x:c4_fp8_act_1x128")
-    Rm, Cm = xm.shape
-    nm = xm.size
+    Rm, Cm = shape("c4_fp8_act_1x128")
+    nm = Rm * Cm
     bm = nm * 2 + nm + nm // 32
 
     def mkm():
-        b = dict(x=dev_bits(xm, "bf16", torch), q=E((Rm, Cm), u8), b=E((Rm, Cm // 32), u8), y=E((Rm, Cm), bf16))
+        b = dict(x=dev_bits(inp.get("x:c4_fp8_act_1x128"), "bf16", torch), q=E((Rm, Cm), u8), b=E((Rm, Cm // 32), u8),
+                 y=E((Rm, Cm), bf16))
         check(L.tq_quant_mxfp8(P(b["x"]), BF16, Rm, Cm, P(b["q"]), P(b["b"]), stream), "mxfp8 producer")
         return b
     bench_op("quant_mxfp8", "bf16 [4096,7168] MXFP8", bm, mkm,
@@ -594,20 +593,19 @@ def breakdown(torch, tq, inp, iters=30, only=None):
 
     # FP4 weight bf16 [14336, 4096]: dequantize, STE, dequantize backward and
     # the GEMM-layout transposes on the quantizer's outputs
-    w5, dy5 = inp.get("x:c5_fp4_weight"), inp.get("dy:c5_fp4_weight")
-    N5, K5 = w5.shape
-    n5 = w5.size
+    N5, K5 = shape("c5_fp4_weight")
+    n5 = N5 * K5
     for kind, gs in (("nvfp4", 16), ("mxfp4", 32)):
         kd = 0 if kind == "nvfp4" else 1
 
         def mk(gs=gs, kd=kd, with_x=False):
-            b = dict(x=dev_bits(w5, "bf16", torch), p=E((N5, K5 // 2), u8), b=E((N5, K5 // gs), u8),
-                     g=E(1, f32), ws=E(8192, u8), pt=E((K5 // 2, N5), u8), bt=E((K5 // gs, N5), u8),
+            b = dict(x=dev_bits(inp.get("x:c5_fp4_weight"), "bf16", torch), p=E((N5, K5 // 2), u8),
+                     b=E((N5, K5 // gs), u8), g=E(1, f32), ws=E(8192, u8), pt=E((K5 // 2, N5), u8), bt=E((K5 // gs, N5), u8),
                      y=E((N5, K5), bf16))
             check(L.tq_quant_fp4_block(P(b["x"]), BF16, N5, K5, kd, P(b["p"]), P(b["b"]), P(b["g"]), 0, P(b["ws"]),
                                        8192, stream), "fp4 producer")
             if with_x:
-                b["dy"] = dev_bits(dy5, "bf16", torch)
+                b["dy"] = dev_bits(inp.get("dy:c5_fp4_weight"), "bf16", torch)
             else:
                 del b["x"]
             return b
@@ -641,7 +639,8 @@ def breakdown(torch, tq, inp, iters=30, only=None):
     sg5 = {}
 
     def mkf():
-        b = dict(x=dev_bits(w5, "bf16", torch), p1=E((N5, K5 // 2), u8), b1=E((N5, K5 // 16), u8), g=E(1, f32),
+        b = dict(x=dev_bits(inp.get("x:c5_fp4_weight"), "bf16", torch), p1=E((N5, K5 // 2), u8),
+                 b1=E((N5, K5 // 16), u8), g=E(1, f32),
                  ws=E(8192, u8))
         check(L.tq_quant_fp4_block(P(b["x"]), BF16, N5, K5, 0, P(b["p1"]), P(b["b1"]), P(b["g"]), 0, P(b["ws"]),
                                    8192, stream), "nvfp4 producer")
@@ -711,7 +710,7 @@ def breakdown(torch, tq, inp, iters=30, only=None):
 
         def mkf4():
             xf0 = dev_bits(inp.get("x:c2_per_token_s8"), "bf16", torch)
-            p, b_, g = tq.tq_quant_fp4_block(dev_bits(w5, "bf16", torch), "nvfp4")
+            p, b_, g = tq.tq_quant_fp4_block(dev_bits(inp.get("x:c5_fp4_weight"), "bf16", torch), "nvfp4")
             return dict(x=xf0, p=p, b=b_, g=g, y=E((Mf, Nf), bf16))
         fb4 = Mf * Kf * 2 + Nf * Kf // 2 + Nf * Kf // 16 + 2 * Mf * Nf
         bench_op("fp4_linear_nvfp4", "bf16 [8192,4096] x nvfp4 [14336,4096]^T bf16 out", fb4, mkf4,
