@@ -51,12 +51,12 @@ __device__ __forceinline__ uint2 ld8(const void* p)
 // 16-byte stores.  NT = 0: plain; 1: non-temporal; 2 (WT): non-temporal
 // with device scope (nt sc1), which passes the L2 on to memory instead of
 // leaving dirty lines behind.  Measured per kernel (same code otherwise,
-// interleaved runs): WT is 2-7% faster for the 8-bit dequantize, the
-// dequantize backward (integer, FP8, MXFP8, FP4), the FP8 dequantize, row
-// concatenation, the FP4 -> FP8 expansion and the binary64 dequantize, and
-// 1-3% slower for the 4-bit and FP4 dequantize, the binary64 dequantize
-// backward, the byte transposes and the fake-quantization kernels, which
-// keep NT = 1.  A store has no output register, so the asm form is safe to
+// interleaved runs): WT is 2-7% faster for the 8-bit and 4-bit integer
+// dequantize, the FP4 dequantize (with two vectors per thread; with one it
+// was slower), the dequantize backward (integer, FP8, MXFP8, FP4), the FP8
+// dequantize, row concatenation, the FP4 -> FP8 expansion and the binary64
+// dequantize, and 1-3% slower for the binary64 dequantize backward, the byte
+// transposes and the fake-quantization kernels, which keep NT = 1.  A store has no output register, so the asm form is safe to
 // leave in flight; it only makes the compiler's own vmcnt waits
 // conservative.
 constexpr int WT = 2;

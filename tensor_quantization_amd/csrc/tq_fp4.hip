@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void k_fp4_ew(const void* __restrict__ a, cons
                     o[2 * i] = d.x * eff;
                     o[2 * i + 1] = d.y * eff;
                 }
-                store8<FT, 1>(out, vi * 8, o);
+                store8<FT, WT>(out, vi * 8, o);
             }
         }
         return;

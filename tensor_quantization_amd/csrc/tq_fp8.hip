@@ -98,10 +98,33 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, in
         const FP p = fp8_params<FT>(team_max<T>(a));
         const int64_t g = g0 + (int64_t)u * P;
         if (g >= nblocks) continue;
+        if constexpr (T == 8 && W == 2) {
+            // 1 x 128 groups: lane j encodes vectors j and 8 + j; exchanges within the team give
+            // it the codes of vectors 2j and 2j + 1, stored as 16 contiguous bytes, so each store
+            // instruction of the wave writes 1 KB of whole lines (3% faster than two 8-byte stores
+            // per lane; non-temporal 8-byte stores measured 3% slower)
+            uint2 c[2];
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const uint2 c = p.fast ? fp8_enc8<FT, true>(v[w], p) : fp8_enc8<FT, false>(v[w], p);
-            *reinterpret_cast<uint2*>(q + g * L + (w * T + j) * 8) = c;
+            for (int w = 0; w < 2; ++w) c[w] = p.fast ? fp8_enc8<FT, true>(v[w], p) : fp8_enc8<FT, false>(v[w], p);
+            const int base = lane & ~7;
+            const int slo = (base + ((2 * j) & 7)) << 2, shi = (base + ((2 * j + 1) & 7)) << 2;
+            const bool upper = j >= 4;   // vectors 2j, 2j + 1 >= 8: the lanes' second vectors
+            const uint32_t ax0 = (uint32_t)__builtin_amdgcn_ds_bpermute(slo, (int)c[0].x);
+            const uint32_t ay0 = (uint32_t)__builtin_amdgcn_ds_bpermute(slo, (int)c[0].y);
+            const uint32_t ax1 = (uint32_t)__builtin_amdgcn_ds_bpermute(slo, (int)c[1].x);
+            const uint32_t ay1 = (uint32_t)__builtin_amdgcn_ds_bpermute(slo, (int)c[1].y);
+            const uint32_t bx0 = (uint32_t)__builtin_amdgcn_ds_bpermute(shi, (int)c[0].x);
+            const uint32_t by0 = (uint32_t)__builtin_amdgcn_ds_bpermute(shi, (int)c[0].y);
+            const uint32_t bx1 = (uint32_t)__builtin_amdgcn_ds_bpermute(shi, (int)c[1].x);
+            const uint32_t by1 = (uint32_t)__builtin_amdgcn_ds_bpermute(shi, (int)c[1].y);
+            st16<1>(q + g * L + 16 * j, make_uint4(upper ? ax1 : ax0, upper ? ay1 : ay0, upper ? bx1 : bx0,
+                                                   upper ? by1 : by0));
+        } else {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const uint2 c = p.fast ? fp8_enc8<FT, true>(v[w], p) : fp8_enc8<FT, false>(v[w], p);
+                *reinterpret_cast<uint2*>(q + g * L + (w * T + j) * 8) = c;
+            }
         }
         if (j == 0) scale[g] = p.s;
     }
@@ -109,7 +132,8 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, in
 
 // ------------------------------------------------------------ br x bc tiles
 // Thread t covers columns (t % T) * 8 .. +8 and rows t / T + k * (256 / T),
-// k = 0..NP-1, of its tile.
+// k = 0..NP-1, of its tile.  (128 x 128 tiles over 512 or 1024 threads, with
+// 8 waves per SIMD resident instead of 5, measured the same or slower.)
 template <int FT, int T, int NP>
 __global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, int64_t cols, int64_t nbc,
                                                   uint8_t* __restrict__ q, float* __restrict__ scale)
@@ -236,26 +260,27 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
                                                 int shift, BlkIdx bi, const float* __restrict__ scale,
                                                 void* __restrict__ out)
 {
+    constexpr int FV = DEQ_V;
     if constexpr (OP == OP_DEQ) {
-        for (int64_t base = (int64_t)blockIdx.x * 256 * DEQ_V; base < nvec;
-             base += (int64_t)gridDim.x * 256 * DEQ_V) {
-            uint2 w[DEQ_V];
-            float s[DEQ_V];
+        for (int64_t base = (int64_t)blockIdx.x * 256 * FV; base < nvec;
+             base += (int64_t)gridDim.x * 256 * FV) {
+            uint2 w[FV];
+            float s[FV];
 #pragma unroll
-            for (int k = 0; k < DEQ_V; ++k) {
+            for (int k = 0; k < FV; ++k) {
                 const int64_t vi = base + k * 256 + threadIdx.x;
                 if (vi < nvec)
                     w[k] = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + vi * 8)
                                  : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + vi * 8);
             }
 #pragma unroll
-            for (int k = 0; k < DEQ_V; ++k) {
+            for (int k = 0; k < FV; ++k) {
                 const int64_t e = (base + k * 256 + threadIdx.x) * 8;
                 if (e < nvec * 8)
                     s[k] = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
             }
 #pragma unroll
-            for (int k = 0; k < DEQ_V; ++k) {
+            for (int k = 0; k < FV; ++k) {
                 const int64_t vi = base + k * 256 + threadIdx.x;
                 if (vi >= nvec) break;
                 float o[8];

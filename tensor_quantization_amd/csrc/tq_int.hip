@@ -867,7 +867,7 @@ __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__
                 const uint32_t c = BITS == 8 ? (cw[k][i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[k][0] >> (i * 4)) & 0xfu;
                 out[i] = (code_f<SIGNED>(c, BITS) - zv[k][NS == 1 ? 0 : i]) * sv[k][NS == 1 ? 0 : i];
             }
-            store8<YT, BITS == 8 ? WT : 1>(y, vi * 8, out);
+            store8<YT, WT>(y, vi * 8, out);
         }
     }
 }
