@@ -325,7 +325,7 @@ def run_quantizers(torch, tq, inp, steps, warmup, iters, only=None):
                 ceil_cache[mix] = stream_ceiling(torch, tq, *mix, iters=iters)
             c = ceil_cache[mix]
             d["ceiling"] = {"mix": "%d:%d per unit" % mix[:2], "GBps": c["GBps"], "frac": c["frac"],
-                            "units_per_lane": c["units_per_lane"]}
+                            "units_per_lane": c["units_per_lane"], "store_policy": c["store_policy"]}
             d["of_ceiling"] = round(d["GBps"] / c["GBps"], 4)
         t = read_traffic("quant_" + name)
         if t is not None:
@@ -337,7 +337,8 @@ def run_quantizers(torch, tq, inp, steps, warmup, iters, only=None):
 # ------------------------------------------------------------------ ceilings
 def stream_ceiling(torch, tq, in_b, out_b, policy, nthr, iters=30):
     """The streaming ceiling of one access mix at one size: the best of the
-    stream kernel with 1, 2 and 4 units per lane (each shape's figure kept)."""
+    stream kernel with 1, 2 and 4 units per lane and, for 16-byte stores, both
+    non-temporal store policies (each shape's figure kept)."""
     L = tq._lib
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     src_bytes = nthr * in_b
@@ -345,18 +346,20 @@ def stream_ceiling(torch, tq, in_b, out_b, policy, nthr, iters=30):
                 dst=torch.empty(nthr * out_b, dtype=torch.uint8, device="cuda"))
     base["src"].fill_(0x3c)
     sets = replicate(base, nsets_for(src_bytes, set_bytes(base)))
+    policies = [policy] + ([3 - policy] if out_b >= 16 and policy in (1, 2) else [])
     shapes = {}
-    for v in (1, 2, 4):
-        us = time_launches(torch, lambda b, v=v: check(L.tq_stream_mix(P(b["src"]), P(b["dst"]), nthr, in_b, out_b,
-                                                                       policy, v, stream), "stream mix"), sets, iters)
-        shapes[v] = rate(nthr * (in_b + out_b), us)
+    for pol in policies:
+        for v in (1, 2, 4):
+            us = time_launches(torch, lambda b, v=v, pol=pol: check(L.tq_stream_mix(
+                P(b["src"]), P(b["dst"]), nthr, in_b, out_b, pol, v, stream), "stream mix"), sets, iters)
+            shapes[(pol, v)] = rate(nthr * (in_b + out_b), us)
     del sets, base
     torch.cuda.empty_cache()
-    v = min(shapes, key=lambda k: shapes[k]["us"])
-    d = dict(shapes[v])
-    d["mix"] = "%d:%d bytes per unit, store policy %d, %d units" % (in_b, out_b, policy, nthr)
-    d["units_per_lane"] = v
-    d["GBps_by_units_per_lane"] = {str(k): shapes[k]["GBps"] for k in shapes}
+    best = min(shapes, key=lambda k: shapes[k]["us"])
+    d = dict(shapes[best])
+    d["mix"] = "%d:%d bytes per unit, %d units" % (in_b, out_b, nthr)
+    d["store_policy"], d["units_per_lane"] = best
+    d["GBps_by_shape"] = {"policy%d_x%d" % k: shapes[k]["GBps"] for k in shapes}
     return d
 
 
