@@ -266,18 +266,33 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
              base += (int64_t)gridDim.x * 256 * FV) {
             uint2 w[FV];
             float s[FV];
+            if (shift < 0) {
+                // general block index: codes and scales at a clamped index with no
+                // branch, so all 2 FV loads are in flight (under `if (vi < nvec)`
+                // each load was waited for before the next: 128 x 128 blocks 10%
+                // slower; the 1 x 2^k blocks below measured 1-3% faster as they are)
 #pragma unroll
-            for (int k = 0; k < FV; ++k) {
-                const int64_t vi = base + k * 256 + threadIdx.x;
-                if (vi < nvec)
+                for (int k = 0; k < FV; ++k) {
+                    const int64_t vk = base + k * 256 + threadIdx.x;
+                    const int64_t vi = vk < nvec ? vk : nvec - 1;
                     w[k] = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + vi * 8)
                                  : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + vi * 8);
-            }
+                    const int64_t e = vi * 8;
+                    s[k] = scale[bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
+                }
+            } else {
 #pragma unroll
-            for (int k = 0; k < FV; ++k) {
-                const int64_t e = (base + k * 256 + threadIdx.x) * 8;
-                if (e < nvec * 8)
-                    s[k] = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
+                for (int k = 0; k < FV; ++k) {
+                    const int64_t vi = base + k * 256 + threadIdx.x;
+                    if (vi < nvec)
+                        w[k] = EW_NT ? ld8<true>(static_cast<const uint8_t*>(a) + vi * 8)
+                                     : *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a) + vi * 8);
+                }
+#pragma unroll
+                for (int k = 0; k < FV; ++k) {
+                    const int64_t e = (base + k * 256 + threadIdx.x) * 8;
+                    if (e < nvec * 8) s[k] = scale[e >> shift];
+                }
             }
 #pragma unroll
             for (int k = 0; k < FV; ++k) {

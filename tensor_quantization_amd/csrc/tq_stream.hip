@@ -23,6 +23,25 @@ namespace tq {
 
 __device__ __forceinline__ uint32_t fold4(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+// Two 16-byte stores of a and of a with its words reversed.  A store reads
+// its data registers after it issues; the compiler has built the reversed
+// words into the first store's data registers right behind it with no wait
+// state, so the second value is formed in registers of its own before the
+// first store and two wait states follow that store before anything else.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int POL>
+__device__ __forceinline__ void st16_pair(uint8_t* p, uint4 a)
+{
+    const uint4 b = make_uint4(a.w, a.z, a.y, a.x);
+    st16<POL>(p, a);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    st16<POL>(p + 16, b);
+}
+#pragma clang diagnostic pop
+
 template <int IN, int OUT, int POL>
 __device__ __forceinline__ void mix_unit(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n,
                                          int64_t t)
@@ -50,8 +69,7 @@ __device__ __forceinline__ void mix_unit(const uint8_t* __restrict__ src, uint8_
     } else if constexpr (OUT == 16) {
         st16<POL>(dst + t * 16, a);
     } else {
-        st16<POL>(dst + t * 32, a);
-        st16<POL>(dst + t * 32 + 16, make_uint4(a.w, a.z, a.y, a.x));
+        st16_pair<POL>(dst + t * 32, a);
     }
 }
 
@@ -66,12 +84,16 @@ __global__ __launch_bounds__(256) void k_stream_mix(const uint8_t* __restrict__ 
     if constexpr (V == 1) {
         if (t0 < n) mix_unit<IN, OUT, POL>(src, dst, n, t0);
     } else {
-        // all loads first, then all stores (what the quantizers do)
+        // all loads first, then all stores (what the quantizers do); the loads
+        // take a clamped index and no branch, so the compiler keeps all V in
+        // flight (a load under `if (t < n)` with its transform inside the branch
+        // was waited for before the next one was issued)
         uint4 a[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            const int64_t t = t0 + (int64_t)k * 256;
-            if (t < n) {
+            const int64_t tk = t0 + (int64_t)k * 256;
+            const int64_t t = tk < n ? tk : n - 1;
+            {
                 if constexpr (IN == 16) a[k] = ld16<true>(src + t * 16);
                 else if constexpr (IN == 32) {
                     const uint4 u = ld16<true>(src + t * 16), v = ld16<true>(src + (n + t) * 16);
@@ -98,8 +120,7 @@ __global__ __launch_bounds__(256) void k_stream_mix(const uint8_t* __restrict__ 
             } else if constexpr (OUT == 16) {
                 st16<POL>(dst + t * 16, a[k]);
             } else {
-                st16<POL>(dst + t * 32, a[k]);
-                st16<POL>(dst + t * 32 + 16, make_uint4(a[k].w, a[k].z, a[k].y, a[k].x));
+                st16_pair<POL>(dst + t * 32, a[k]);
             }
         }
     }

@@ -4,8 +4,17 @@ build time), no mixed-precision FMA with an f16 result (v_fma_mixlo_f16 /
 v_fma_mixhi_f16 / v_mad_mix* round a product once into f16), and no scratch
 spills.  v_fma_mix_f32 is allowed: it widens f16 operands exactly and rounds
 once to binary32, the same result as the f32 FMA of the widened values.
+
+Nor does any 12- or 16-byte global store have its data VGPRs overwritten by
+a vector instruction right behind it.  A VMEM store reads its data registers
+after it issues; hipcc for gfx950 has placed a 64-bit VALU write
+(v_lshl_add_u64, v_pk_mov_b32) into those registers on the next instruction
+with no wait state, and the store then wrote the new values (an FP4
+dequantize variant stored its next address as data).  Kernels that build a
+second value right behind such a store separate the two with s_nop.
+
 Compiles each kernel source to AMD assembly on the CPU (hipcc
-cross-compiles)."""
+cross-compiles) with the library's own flags."""
 import os
 import re
 import subprocess
@@ -29,7 +38,8 @@ def _build_module():
 def _asm(src, tmp):
     b = _build_module()
     out = os.path.join(tmp, os.path.basename(src) + ".s")
-    subprocess.check_call([b.HIPCC, *b.FLAGS, "-S", "--cuda-device-only", src, "-o", out],
+    subprocess.check_call([b.HIPCC, *b.FLAGS, *b.FILE_FLAGS.get(os.path.basename(src), []),
+                           "-S", "--cuda-device-only", src, "-o", out],
                           stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
     return open(out).read()
 
@@ -52,3 +62,70 @@ def test_no_scratch(listings):
     for src, text in listings.items():
         sizes = [int(v) for v in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
         assert max(sizes, default=0) == 0, os.path.basename(src)
+
+
+_STORE = re.compile(r"^(?:global|buffer)_store_dword(?:x3|x4)\s+\S+\s+(v\[\d+:\d+\])")
+
+
+def _vregs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _vector_dst(ins):
+    parts = ins.replace(",", " ").split()
+    if len(parts) < 2 or not parts[0].startswith("v_") or parts[0].startswith(("v_cmp", "v_readlane",
+                                                                                 "v_readfirstlane")):
+        return set()            # not a VALU op, or one whose result goes to SGPRs / VCC
+    return _vregs(parts[1])
+
+
+def _bodies(text):
+    name, body = None, []
+    for line in text.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            name, body = m.group(1), []
+        elif name is not None and line.startswith(".Lfunc_end"):
+            yield name, body
+            name = None
+        elif name is not None:
+            code = line.split(";")[0].strip()
+            if code and not code.startswith(".") and not code.endswith(":"):
+                body.append(code)
+
+
+def store_data_hazards(text, window=2):
+    """(kernel, store, instruction) for every VALU write of a wide store's data
+    VGPRs within `window` instructions of it with no s_nop in between."""
+    hits = []
+    for name, body in _bodies(text):
+        for i, ins in enumerate(body):
+            m = _STORE.match(ins.replace(",", " "))
+            if not m:
+                continue
+            data = _vregs(m.group(1))
+            for nxt in body[i + 1:i + 1 + window]:
+                if nxt.startswith("s_nop"):
+                    break
+                if _vector_dst(nxt) & data:
+                    hits.append((name, ins, nxt))
+                    break
+    return hits
+
+
+def test_store_hazard_detector():
+    bad = ("_Z1kv:\n\tglobal_store_dwordx4 v[10:11], v[6:9], off nt sc1\n"
+           "\tv_lshl_add_u64 v[6:7], v[0:1], 0, s[10:11]\n.Lfunc_end0:\n")
+    assert len(store_data_hazards(bad)) == 1
+    assert store_data_hazards(bad.replace("\tv_lshl", "\ts_nop 1\n\tv_lshl")) == []
+    assert store_data_hazards(bad.replace("v_lshl_add_u64 v[6:7]", "v_lshl_add_u64 v[12:13]")) == []
+    assert store_data_hazards(bad.replace("dwordx4 v[10:11], v[6:9]", "dwordx2 v[10:11], v[6:7]")) == []
+
+
+def test_no_store_data_hazard(listings):
+    hits = [(os.path.basename(src),) + h for src, text in listings.items() for h in store_data_hazards(text)]
+    assert not hits, "\n".join("%s %s\n    %s\n    %s" % h for h in hits[:10])
