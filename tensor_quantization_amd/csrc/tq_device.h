@@ -58,14 +58,18 @@ __device__ __forceinline__ uint2 ld8(const void* p)
 // dequantize, and 1-3% slower for the binary64 dequantize backward, the byte
 // transposes and the fake-quantization kernels, which keep NT = 1.  A store has no output register, so the asm form is safe to
 // leave in flight; it only makes the compiler's own vmcnt waits
-// conservative.
+// conservative.  It does read its data VGPRs after it issues: a store of
+// more than 8 bytes needs two wait states before a vector instruction may
+// write them (the ISA's store-data hazard), which the compiler inserts after
+// its own stores but cannot see inside asm, so the asm carries the s_nop.
 constexpr int WT = 2;
 
 template <int NT = 0>
 __device__ __forceinline__ void st16(void* p, uint4 w)
 {
     const u32x4 v = {w.x, w.y, w.z, w.w};
-    if constexpr (NT == WT) asm volatile("global_store_dwordx4 %0, %1, off nt sc1" ::"v"(p), "v"(v) : "memory");
+    if constexpr (NT == WT)
+        asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
     else if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
     else *static_cast<u32x4*>(p) = v;
 }

@@ -840,54 +840,114 @@ __device__ __forceinline__ float zp_f(const uint8_t* zp, int64_t g)
 constexpr int SVPT = 1, DVPT = 1;
 constexpr bool DEQ_NT = true;
 
+// One grid-stride pass of the 4-bit dequantizer.  Every code, scale and zero-point
+// load of a thread's DEQ_V vectors is issued at a clamped index with no
+// branch, and a scheduling barrier keeps all of them ahead of the arithmetic,
+// so they are in flight together.  The arithmetic runs on the clamped data
+// too and only the stores are guarded: with the arithmetic under
+// `if (vi < nvec)` the compiler moved each vector's loads into that branch,
+// and each vector's loads were then waited for before the next ones issued
+// (u4 g = 128 -> f16 [11008, 4096] 22.4 -> 20.8 us).
+template <int MAPK, int YT, bool SIGNED, bool POW2, bool HASZP>
+__device__ __forceinline__ void dequant4_pass(const uint8_t* __restrict__ q, int64_t nvec, int64_t P1,
+                                                 int64_t P2, int sh, const float* __restrict__ scale,
+                                                 const uint8_t* __restrict__ zp, void* __restrict__ y)
+{
+    constexpr int V = DEQ_V;
+    constexpr int NS = MAPK == MAP_CONTIG ? 1 : 8;   // scales per vector
+    for (int64_t base = (int64_t)blockIdx.x * 256 * V; base < nvec; base += (int64_t)gridDim.x * 256 * V) {
+        uint32_t cw[V];
+        float sv[V][NS];
+        uint32_t zb[V][NS];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int64_t vk = base + k * 256 + threadIdx.x;
+            const int64_t e = (vk < nvec ? vk : nvec - 1) * 8;
+            // plain code loads (measured faster than non-temporal ones for this 1:4
+            // read:write shape, where the 4-byte lane loads are a fifth of the bytes)
+            cw[k] = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
+            int64_t g;
+            if constexpr (MAPK == MAP_CONTIG) g = POW2 ? (e >> sh) : e / P1;
+            else g = (e / (P1 * P2)) * P2 + e % P2;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                sv[k][i] = scale[g + i];
+                zb[k][i] = HASZP ? zp[g + i] : 0u;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float out[V][8];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t zi = zb[k][NS == 1 ? 0 : i];
+                const float z = HASZP ? (SIGNED ? (float)(int8_t)zi : (float)zi) : 0.0f;
+                out[k][i] = (code_f<SIGNED>((cw[k] >> (i * 4)) & 0xfu, 4) - z) * sv[k][NS == 1 ? 0 : i];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int64_t vi = base + k * 256 + threadIdx.x;
+            if (vi < nvec) store8<YT, WT>(y, vi * 8, out[k]);
+        }
+    }
+}
+
 template <int MAPK, int YT, int BITS, bool SIGNED>
 __global__ __launch_bounds__(256) void k_dequant_vec(const uint8_t* __restrict__ q, int64_t nvec, int64_t P1,
                                                      int64_t P2, int sh, const float* __restrict__ scale,
                                                      const uint8_t* __restrict__ zp, void* __restrict__ y)
 {
-    constexpr int V = DEQ_V;    // vectors per thread: all their loads before any store
-    constexpr int NS = MAPK == MAP_CONTIG ? 1 : 8;   // scales per vector
-    for (int64_t base = (int64_t)blockIdx.x * 256 * V; base < nvec; base += (int64_t)gridDim.x * 256 * V) {
-        uint32_t cw[V][2];
-        float sv[V][NS], zv[V][NS];
+    if constexpr (BITS == 4) {
+        // the shift-or-divide group map and the zero point are uniform: chosen once
+        if (MAPK == MAP_CONTIG && sh >= 0) {
+            if (zp) dequant4_pass<MAPK, YT, SIGNED, true, true>(q, nvec, P1, P2, sh, scale, zp, y);
+            else dequant4_pass<MAPK, YT, SIGNED, true, false>(q, nvec, P1, P2, sh, scale, zp, y);
+        } else {
+            if (zp) dequant4_pass<MAPK, YT, SIGNED, false, true>(q, nvec, P1, P2, sh, scale, zp, y);
+            else dequant4_pass<MAPK, YT, SIGNED, false, false>(q, nvec, P1, P2, sh, scale, zp, y);
+        }
+    } else {
+        // 8-bit codes: this loop already keeps every load of a thread in flight,
+        // and the fenced pass measured 3% slower for per-token s8
+        constexpr int V = DEQ_V;    // vectors per thread: all their loads before any store
+        constexpr int NS = MAPK == MAP_CONTIG ? 1 : 8;   // scales per vector
+        for (int64_t base = (int64_t)blockIdx.x * 256 * V; base < nvec; base += (int64_t)gridDim.x * 256 * V) {
+            uint32_t cw[V][2];
+            float sv[V][NS], zv[V][NS];
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const int64_t vi = base + k * 256 + threadIdx.x;
-            cw[k][0] = cw[k][1] = 0;
-            if (vi >= nvec) continue;
-            const int64_t e = vi * 8;
-            if constexpr (BITS == 8) {
-                const uint2 w = DEQ_NT ? ld8<true>(q + e) : *reinterpret_cast<const uint2*>(q + e);
+            for (int k = 0; k < V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                cw[k][0] = cw[k][1] = 0;
+                if (vi >= nvec) continue;
+                const uint2 w = DEQ_NT ? ld8<true>(q + vi * 8) : *reinterpret_cast<const uint2*>(q + vi * 8);
                 cw[k][0] = w.x;
                 cw[k][1] = w.y;
-            } else {
-                // 4-bit codes: plain loads (measured faster than non-temporal ones for this
-                // 1:4 read:write shape, where the 4-byte lane loads are a fifth of the bytes)
-                cw[k][0] = *reinterpret_cast<const uint32_t*>(q + (e >> 1));
             }
-        }
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const int64_t vi = base + k * 256 + threadIdx.x;
-            if (vi >= nvec) continue;
-            const int64_t g = vec_group<MAPK>(vi * 8, P1, P2, sh);
+            for (int k = 0; k < V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi >= nvec) continue;
+                const int64_t g = vec_group<MAPK>(vi * 8, P1, P2, sh);
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                sv[k][i] = scale[g + i];
-                zv[k][i] = zp_f<SIGNED>(zp, g + i);
+                for (int i = 0; i < NS; ++i) {
+                    sv[k][i] = scale[g + i];
+                    zv[k][i] = zp_f<SIGNED>(zp, g + i);
+                }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const int64_t vi = base + k * 256 + threadIdx.x;
-            if (vi >= nvec) break;
-            float out[8];
+            for (int k = 0; k < V; ++k) {
+                const int64_t vi = base + k * 256 + threadIdx.x;
+                if (vi >= nvec) break;
+                float out[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t c = BITS == 8 ? (cw[k][i >> 2] >> ((i & 3) * 8)) & 0xffu : (cw[k][0] >> (i * 4)) & 0xfu;
-                out[i] = (code_f<SIGNED>(c, BITS) - zv[k][NS == 1 ? 0 : i]) * sv[k][NS == 1 ? 0 : i];
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t c = (cw[k][i >> 2] >> ((i & 3) * 8)) & 0xffu;
+                    out[i] = (code_f<SIGNED>(c, 8) - zv[k][NS == 1 ? 0 : i]) * sv[k][NS == 1 ? 0 : i];
+                }
+                store8<YT, WT>(y, vi * 8, out);
             }
-            store8<YT, WT>(y, vi * 8, out);
         }
     }
 }

@@ -23,25 +23,6 @@ namespace tq {
 
 __device__ __forceinline__ uint32_t fold4(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
-// Two 16-byte stores of a and of a with its words reversed.  A store reads
-// its data registers after it issues; the compiler has built the reversed
-// words into the first store's data registers right behind it with no wait
-// state, so the second value is formed in registers of its own before the
-// first store and two wait states follow that store before anything else.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-template <int POL>
-__device__ __forceinline__ void st16_pair(uint8_t* p, uint4 a)
-{
-    const uint4 b = make_uint4(a.w, a.z, a.y, a.x);
-    st16<POL>(p, a);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 1" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    st16<POL>(p + 16, b);
-}
-#pragma clang diagnostic pop
-
 template <int IN, int OUT, int POL>
 __device__ __forceinline__ void mix_unit(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n,
                                          int64_t t)
@@ -69,7 +50,8 @@ __device__ __forceinline__ void mix_unit(const uint8_t* __restrict__ src, uint8_
     } else if constexpr (OUT == 16) {
         st16<POL>(dst + t * 16, a);
     } else {
-        st16_pair<POL>(dst + t * 32, a);
+        st16<POL>(dst + t * 32, a);
+        st16<POL>(dst + t * 32 + 16, make_uint4(a.w, a.z, a.y, a.x));
     }
 }
 
@@ -120,7 +102,8 @@ __global__ __launch_bounds__(256) void k_stream_mix(const uint8_t* __restrict__ 
             } else if constexpr (OUT == 16) {
                 st16<POL>(dst + t * 16, a[k]);
             } else {
-                st16_pair<POL>(dst + t * 32, a[k]);
+                st16<POL>(dst + t * 32, a[k]);
+                st16<POL>(dst + t * 32 + 16, make_uint4(a[k].w, a[k].z, a[k].y, a[k].x));
             }
         }
     }

@@ -7,11 +7,13 @@ once to binary32, the same result as the f32 FMA of the widened values.
 
 Nor does any 12- or 16-byte global store have its data VGPRs overwritten by
 a vector instruction right behind it.  A VMEM store reads its data registers
-after it issues; hipcc for gfx950 has placed a 64-bit VALU write
-(v_lshl_add_u64, v_pk_mov_b32) into those registers on the next instruction
-with no wait state, and the store then wrote the new values (an FP4
-dequantize variant stored its next address as data).  Kernels that build a
-second value right behind such a store separate the two with s_nop.
+after it issues, and the ISA requires two wait states between a store of
+more than 8 bytes and a vector write of those registers.  The compiler
+inserts them after the stores it emits, but not after a store written in
+inline asm (the device-scope non-temporal store), so that asm carries its
+own s_nop; without it a schedule put a 64-bit VALU write (v_lshl_add_u64,
+v_pk_mov_b32) on the next instruction and the store wrote the new values (an
+FP4 dequantize variant stored its next address as data).
 
 Compiles each kernel source to AMD assembly on the CPU (hipcc
 cross-compiles) with the library's own flags."""
@@ -98,9 +100,10 @@ def _bodies(text):
                 body.append(code)
 
 
-def store_data_hazards(text, window=2):
+def store_data_hazards(text, need=2):
     """(kernel, store, instruction) for every VALU write of a wide store's data
-    VGPRs within `window` instructions of it with no s_nop in between."""
+    VGPRs with fewer than `need` wait states between the two (`s_nop n` gives
+    n + 1, any other instruction one)."""
     hits = []
     for name, body in _bodies(text):
         for i, ins in enumerate(body):
@@ -108,12 +111,17 @@ def store_data_hazards(text, window=2):
             if not m:
                 continue
             data = _vregs(m.group(1))
-            for nxt in body[i + 1:i + 1 + window]:
-                if nxt.startswith("s_nop"):
+            waited = 0
+            for nxt in body[i + 1:]:
+                if waited >= need:
                     break
+                if nxt.startswith("s_nop"):
+                    waited += int(nxt.split()[1], 0) + 1
+                    continue
                 if _vector_dst(nxt) & data:
                     hits.append((name, ins, nxt))
                     break
+                waited += 1
     return hits
 
 
@@ -122,6 +130,9 @@ def test_store_hazard_detector():
            "\tv_lshl_add_u64 v[6:7], v[0:1], 0, s[10:11]\n.Lfunc_end0:\n")
     assert len(store_data_hazards(bad)) == 1
     assert store_data_hazards(bad.replace("\tv_lshl", "\ts_nop 1\n\tv_lshl")) == []
+    assert len(store_data_hazards(bad.replace("\tv_lshl", "\ts_nop 0\n\tv_lshl"))) == 1
+    assert len(store_data_hazards(bad.replace("\tv_lshl", "\tv_mov_b32 v20, 0\n\tv_lshl"))) == 1
+    assert store_data_hazards(bad.replace("\tv_lshl", "\tv_mov_b32 v20, 0\n\tv_mov_b32 v21, 0\n\tv_lshl")) == []
     assert store_data_hazards(bad.replace("v_lshl_add_u64 v[6:7]", "v_lshl_add_u64 v[12:13]")) == []
     assert store_data_hazards(bad.replace("dwordx4 v[10:11], v[6:9]", "dwordx2 v[10:11], v[6:7]")) == []
 
