@@ -347,9 +347,9 @@ __global__ __launch_bounds__(512) void k_w8a8_gemm_256(const int8_t* __restrict_
 // 128 x 128 tile as above with 64-wide K blocks.  The activation slice
 // (128 rows x 128 bytes) moves by DMA into two LDS stages.  The weight is
 // expanded once per workgroup: thread t loads half a row (16 packed bytes,
-// 32 values) of the next block and its scale bytes into registers while the
-// matrix cores work on the current block, then writes them as exact bf16
-// into the other of two LDS weight buffers, laid out (128-byte rows, same
+// 32 values) and its scale bytes into registers two blocks ahead, and while
+// the matrix cores work on block kb writes block kb + 1 as exact bf16 into
+// the other of two LDS weight buffers, laid out (128-byte rows, same
 // swizzle) like the activation slice.  MXFP4 expands by
 // v_cvt_scalef32_pk_bf16_fp4, whose scale operand applies the power of two
 // 2^(e8m0 - 127) exactly; NVFP4 by the same conversion to f32 at scale 1, a
@@ -439,14 +439,12 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
     const int wr = t >> 1, wh = t & 1;
     const uint8_t* fw = packed + (n0 + wr) * (K / 2) + wh * 16;
     const uint8_t* fsc = bscale + (n0 + wr) * (K / GS);
-    uint4 pk;
-    uint32_t sbytes;
-    auto fetch_w = [&](int64_t kb) {
+    auto fetch_w = [&](int64_t kb, uint4& pk, uint32_t& sbytes) {
         pk = *reinterpret_cast<const uint4*>(fw + kb * (FKB / 2));
         sbytes = KIND == FP4_NV ? *reinterpret_cast<const uint32_t*>(fsc + kb * SPB)
                                 : (uint32_t)*reinterpret_cast<const uint16_t*>(fsc + kb * SPB);
     };
-    auto expand_w = [&](int buf) {
+    auto expand_w = [&](int buf, const uint4& pk, uint32_t sbytes) {
         const uint32_t d[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -463,19 +461,22 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{};
 
-    issue(0);
-    fetch_w(0);
-    expand_w(0);
-    for (int64_t kb = 0; kb < nkb; ++kb) {
-        // block kb's activations have landed and its expanded weights are written
-        // by every thread; every wave is done with the buffers of block kb - 1
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        const bool more = kb + 1 < nkb;
-        if (more) {
-            issue(kb + 1);
-            fetch_w(kb + 1);
-        }
-
+    // One block: its activations have landed and its expanded weights are in
+    // LDS (every thread wrote them during the block before); the weights of
+    // the next block are expanded from registers into the other buffer, and
+    // those of the block after next are fetched into the other register set.
+    // The register sets alternate between the two steps of the loop, so no
+    // weight load is waited for before the barrier of the block that expands
+    // it: with one set, the expansion waited for the fetch issued at the top
+    // of the same block (and, the waits counting in order, for the activation
+    // loads issued before it).  The barrier's own wait is a builtin so that the
+    // compiler knows those loads have completed and adds no wait of its own.
+    auto step = [&](int64_t kb, const uint4& pkx, uint32_t sbx, uint4& pkf, uint32_t& sbf) {
+        __builtin_amdgcn_s_waitcnt(0x70);    // vmcnt(0) lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + 1 < nkb) issue(kb + 1);
+        fetch_w(kb + 2 < nkb ? kb + 2 : nkb - 1, pkf, sbf);
+        __builtin_amdgcn_sched_barrier(0);   // keep the fetch ahead of the products
         const int cur = (int)(kb & 1);
         v4f blk[4][4];
 #pragma unroll
@@ -494,14 +495,30 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
                 for (int j = 0; j < 4; ++j)
                     blk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], s == 0 ? v4f{} : blk[i][j], 0, 0, 0);
         }
-        if (more) expand_w(cur ^ 1);
+        // the last block expands a repeat of itself into a buffer no one reads again
+        expand_w(cur ^ 1, pkx, sbx);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] + blk[i][j][r];
+    };
+
+    uint4 pka, pkb;
+    uint32_t sba, sbb;
+    issue(0);
+    fetch_w(0, pka, sba);
+    expand_w(0, pka, sba);
+    fetch_w(nkb > 1 ? 1 : 0, pka, sba);
+    // both steps unconditional inside the loop: a conditional second step let
+    // the compiler sink the first step's fetch into it, behind its barrier
+    int64_t kb = 0;
+    for (; kb + 1 < nkb; kb += 2) {
+        step(kb, pka, sba, pkb, sbb);
+        step(kb + 1, pkb, sbb, pka, sba);
     }
+    if (kb < nkb) step(kb, pka, sba, pkb, sbb);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
