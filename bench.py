@@ -515,6 +515,22 @@ def breakdown(torch, tq, inp, iters=30, only=None):
                                                                  P(b["dy"]), P(b["dx"]), stream), "fake bwd"),
              n2 * 4)
 
+    # per-tensor FP8 E4M3 on the same bf16 [8192, 4096] input: the dynamic
+    # scale (chunk maxima, then the encode merging them) and a static one
+    def mkq8t():
+        b = dict(x=dev_bits(inp.get("x:c2_per_token_s8"), "bf16", torch), q=E(n2, u8), s=E(1, f32),
+                 ws=E(8192, u8))
+        check(L.tq_quant_fp8_per_tensor(P(b["x"]), BF16, n2, 0, P(b["q"]), P(b["s"]), P(b["ws"]), 8192, stream),
+              "fp8 per-tensor producer")
+        return b
+    cfg8 = "bf16 [8192,4096] per-tensor FP8 E4M3"
+    bench_op("quant_fp8_per_tensor_dynamic", cfg8, n2 * 3 + 4, mkq8t,
+             lambda b: check(L.tq_quant_fp8_per_tensor(P(b["x"]), BF16, n2, 0, P(b["q"]), P(b["s"]), P(b["ws"]), 8192,
+                                                       stream), "fp8 per-tensor dyn"), n2 * 2)
+    bench_op("quant_fp8_per_tensor_static", cfg8, n2 * 3 + 4, mkq8t,
+             lambda b: check(L.tq_quant_fp8_per_tensor(P(b["x"]), BF16, n2, 1, P(b["q"]), P(b["s"]), None, 0,
+                                                       stream), "fp8 per-tensor static"), n2 * 2)
+
     # binary64 inputs: the per-token workload's shape in f64 (N(0,1) values)
     shpf = (ctypes.c_int64 * 2)(8192, 4096)
 

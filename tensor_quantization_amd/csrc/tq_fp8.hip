@@ -407,6 +407,13 @@ __global__ __launch_bounds__(256) void k_fp8_tensor_amax(const void* __restrict_
         ws[blockIdx.x] = __builtin_fmaxf(__builtin_fmaxf(sm[0], sm[1]), __builtin_fmaxf(sm[2], sm[3]));
 }
 
+// Per-tensor FP8 encode: FP8_TENSOR_EV vectors per thread with both loads in
+// flight; a static-scale grid gives each thread one such pair, a dynamic one
+// two (every workgroup merges the chunk maxima first, so twice the workgroups
+// measured 5% slower there; static 18.8 -> 18.0 us on bf16 [8192, 4096])
+constexpr int FP8_TENSOR_EV = 2;
+constexpr int FP8_TENSOR_VPT_STATIC = 2, FP8_TENSOR_VPT_MERGE = 4;
+
 // Pass 2, by `mode`: 0 one block reduces the (small, <= 65536 elements)
 // tensor itself, then encodes; 1 the scale is an input; 2 every block
 // merges pass 1's nparts chunk maxima and block 0 publishes the scale.
@@ -450,12 +457,27 @@ __global__ __launch_bounds__(256) void k_fp8_tensor_encode(const void* __restric
     }
     const int64_t stride = (int64_t)gridDim.x * 256;
     if constexpr (VEC) {
-        for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < numel / 8; vi += stride) {
-            float v[8];
-            widen8<FT>(load8<FT, true>(x, vi * 8), v);
-            // a static scale does not bound |x|: keep x / s from overflowing on the fast path
-            const bool fast = p.fast & codes_fast8(v);
-            st8<true>(q + vi * 8, fast ? fp8_enc8<FT, true>(v, p) : fp8_enc8<FT, false>(v, p));
+        // FP8_TENSOR_EV vectors per grid step, both loads before any store (one
+        // vector per step kept one load in flight at a time)
+        const int64_t nvec = numel / 8;
+        for (int64_t base = (int64_t)blockIdx.x * 256 * FP8_TENSOR_EV + threadIdx.x; base < nvec;
+             base += stride * FP8_TENSOR_EV) {
+            Raw8<FT> r[FP8_TENSOR_EV];
+#pragma unroll
+            for (int k = 0; k < FP8_TENSOR_EV; ++k) {
+                const int64_t vi = base + (int64_t)k * 256;
+                r[k] = vi < nvec ? load8<FT, true>(x, vi * 8) : Raw8<FT>{};
+            }
+#pragma unroll
+            for (int k = 0; k < FP8_TENSOR_EV; ++k) {
+                const int64_t vi = base + (int64_t)k * 256;
+                if (vi >= nvec) continue;
+                float v[8];
+                widen8<FT>(r[k], v);
+                // a static scale does not bound |x|: keep x / s from overflowing on the fast path
+                const bool fast = p.fast & codes_fast8(v);
+                st8<true>(q + vi * 8, fast ? fp8_enc8<FT, true>(v, p) : fp8_enc8<FT, false>(v, p));
+            }
         }
     } else {
         for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < numel; e += stride)
@@ -824,7 +846,8 @@ tq_status tq_quant_fp8_per_tensor(const void* x, int x_dtype, int64_t numel, int
         });
         if (launch_status()) return TQ_ERR_HIP;
     }
-    const dim3 grid(mode != 0 ? grid_for(vec ? numel / 8 : numel, 256 * 4) : 1u);
+    const int vpt = mode == 2 ? FP8_TENSOR_VPT_MERGE : FP8_TENSOR_VPT_STATIC;
+    const dim3 grid(mode == 0 ? 1u : vec ? grid_for(numel / 8, 256 * vpt) : grid_for(numel, 256 * 4));
     TQ_FT_SWITCH(x_dtype, {
         if (vec) hipLaunchKernelGGL((k_fp8_tensor_encode<FTV, true>), grid, dim3(256), 0, st, x, numel, mode, ws,
                                     nparts, scale, q);
