@@ -442,15 +442,20 @@ def run_path(torch, tq, inp, steps):
 
 
 # ------------------------------------------------------------------ breakdown
-def breakdown(torch, tq, inp, iters=30, only=None):
+def breakdown(torch, tq, inp, iters=30, only=None, ceil_cache=None):
     """Every other op timed alone; each buffer set holds what the op's
-    producer (the matching quantize call) wrote."""
+    producer (the matching quantize call) wrote.  A streaming op with a
+    `mix` (bytes read and written per unit, store policy, units at its size)
+    also gets the same-run streaming ceiling of that mix (`ceiling`,
+    `of_ceiling`); `ceil_cache` shares ceilings already measured."""
     import numpy as np
     L = tq._lib
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = []
 
-    def bench_op(name, cfg, nbytes, make_base, launch, read_bytes, flops=None, peak=FP8_PEAK_TFLOPS):
+    ceil_cache = {} if ceil_cache is None else ceil_cache
+
+    def bench_op(name, cfg, nbytes, make_base, launch, read_bytes, flops=None, peak=FP8_PEAK_TFLOPS, mix=None):
         if only and only != name:
             return
         log("breakdown:", name)
@@ -459,12 +464,22 @@ def breakdown(torch, tq, inp, iters=30, only=None):
         sets = replicate(base, nsets_for(read_bytes, set_bytes(base)))
         us = time_launches(torch, launch, sets, iters)
         if flops is None:
-            d = rate(nbytes, us)
-            out.append(dict(op=name, workload=cfg, **d))
-        else:
-            tf = flops / (us * 1e-6) / 1e12
-            out.append({"op": name, "workload": cfg, "flops": flops, "us": round(us, 3), "TFLOPs": round(tf, 1),
-                        "frac": round(tf / peak, 4), "bound": "mfma"})
+            d = dict(op=name, workload=cfg, **rate(nbytes, us))
+            del sets, base
+            torch.cuda.empty_cache()
+            if mix is not None and not only:
+                if mix not in ceil_cache:
+                    ceil_cache[mix] = stream_ceiling(torch, tq, *mix, iters=iters)
+                c = ceil_cache[mix]
+                d["ceiling"] = {"mix": "%d:%d per unit, %d units" % (mix[0], mix[1], mix[3]), "GBps": c["GBps"],
+                                "frac": c["frac"], "units_per_lane": c["units_per_lane"],
+                                "store_policy": c["store_policy"]}
+                d["of_ceiling"] = round(d["GBps"] / c["GBps"], 4)
+            out.append(d)
+            return
+        tf = flops / (us * 1e-6) / 1e12
+        out.append({"op": name, "workload": cfg, "flops": flops, "us": round(us, 3), "TFLOPs": round(tf, 1),
+                    "frac": round(tf / peak, 4), "bound": "mfma"})
         del sets, base
         torch.cuda.empty_cache()
 
@@ -509,11 +524,12 @@ def breakdown(torch, tq, inp, iters=30, only=None):
                                                         None, P(b["ws"]), 8192, stream), "fake dyn"), n2 * 2)
     bench_op("fake_quant_per_tensor_s8_static", cfg2, n2 * 4 + 4, mkf2,
              lambda b: check(L.tq_fake_quant_per_tensor(P(b["x"]), BF16, n2, S8, -127, 127, 1, P(b["y"]), P(b["s"]),
-                                                        None, None, 0, stream), "fake static"), n2 * 2)
+                                                        None, None, 0, stream), "fake static"), n2 * 2,
+             mix=(16, 16, 1, n2 // 8))
     bench_op("fake_quant_per_tensor_s8_backward", cfg2, n2 * 6 + 4, mkf2,
              lambda b: check(L.tq_fake_quant_per_tensor_backward(P(b["x"]), BF16, n2, S8, -127, 127, P(b["s"]), None,
                                                                  P(b["dy"]), P(b["dx"]), stream), "fake bwd"),
-             n2 * 4)
+             n2 * 4, mix=(32, 16, 1, n2 // 8))
 
     # per-tensor FP8 E4M3 on the same bf16 [8192, 4096] input: the dynamic
     # scale (chunk maxima, then the encode merging them) and a static one
@@ -529,7 +545,8 @@ def breakdown(torch, tq, inp, iters=30, only=None):
                                                        stream), "fp8 per-tensor dyn"), n2 * 2)
     bench_op("quant_fp8_per_tensor_static", cfg8, n2 * 3 + 4, mkq8t,
              lambda b: check(L.tq_quant_fp8_per_tensor(P(b["x"]), BF16, n2, 1, P(b["q"]), P(b["s"]), None, 0,
-                                                       stream), "fp8 per-tensor static"), n2 * 2)
+                                                       stream), "fp8 per-tensor static"), n2 * 2,
+             mix=(16, 8, 1, n2 // 8))
 
     # binary64 inputs: the per-token workload's shape in f64 (N(0,1) values)
     shpf = (ctypes.c_int64 * 2)(8192, 4096)
@@ -563,7 +580,8 @@ def breakdown(torch, tq, inp, iters=30, only=None):
         return b
     bench_op("dequant_per_group_u4_g128", "f16 [11008,4096] per-group u4 g=128", b3, mk3,
              lambda b: check(L.tq_dequant_per_group(P(b["q"]), U4, 2, shp3, 1, 128, P(b["s"]), P(b["z"]), P(b["y"]),
-                                                    F16, stream), "c3 dequant"), n3 // 2 + (n3 // 128) * 5)
+                                                    F16, stream), "c3 dequant"), n3 // 2 + (n3 // 128) * 5,
+             mix=(4, 16, 1, n3 // 8))
 
     # FP8 1x128 activations bf16 [4096, 7168]; 128x128 weights bf16 [7168, 7168]
     for key, name in (("c4_fp8_act_1x128", "fp8_1x128"), ("c4_fp8_weight_128x128", "fp8_128x128")):
@@ -582,16 +600,16 @@ def breakdown(torch, tq, inp, iters=30, only=None):
         bench_op("dequant_" + name, cfg, nb, mk,
                  lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_dequant_fp8_block(P(b["q"]), R, C, br, bc, P(b["s"]),
                                                                                 P(b["y"]), BF16, stream), "fp8 deq"),
-                 R * C + ns * 4)
+                 R * C + ns * 4, mix=(8, 16, 2, R * C // 8))
         if name == "fp8_1x128":
             bench_op("quant_backward_" + name, cfg, R * C * 6 + ns * 4, mk,
                      lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_quant_fp8_block_backward(
                          P(b["x"]), BF16, R, C, br, bc, P(b["s"]), P(b["dy"]), P(b["y"]), stream), "fp8 ste"),
-                     R * C * 4 + ns * 4)
+                     R * C * 4 + ns * 4, mix=(32, 16, 1, R * C // 8))
             bench_op("dequant_backward_" + name, cfg, R * C * 4 + ns * 4, mk,
                      lambda b, R=R, C=C, br=br, bc=bc: check(L.tq_dequant_fp8_block_backward(
                          P(b["dy"]), BF16, R, C, br, bc, P(b["s"]), P(b["y"]), stream), "fp8 dqb"),
-                     R * C * 2 + ns * 4)
+                     R * C * 2 + ns * 4, mix=(16, 16, 2, R * C // 8))
 
     # MXFP8 on the FP8 activation workload bf16 [4096, 7168]: E4M3 + E8M0 per 32
     Rm, Cm = shape("c4_fp8_act_1x128")
@@ -605,10 +623,10 @@ def breakdown(torch, tq, inp, iters=30, only=None):
         return b
     bench_op("quant_mxfp8", "bf16 [4096,7168] MXFP8", bm, mkm,
              lambda b: check(L.tq_quant_mxfp8(P(b["x"]), BF16, Rm, Cm, P(b["q"]), P(b["b"]), stream), "mxfp8"),
-             nm * 2)
+             nm * 2, mix=(16, 8, 1, nm // 8))
     bench_op("dequant_mxfp8", "bf16 [4096,7168] MXFP8", bm, mkm,
              lambda b: check(L.tq_dequant_mxfp8(P(b["q"]), P(b["b"]), Rm, Cm, P(b["y"]), BF16, stream), "mxfp8 deq"),
-             nm + nm // 32)
+             nm + nm // 32, mix=(8, 16, 1, nm // 8))
 
     # FP4 weight bf16 [14336, 4096]: dequantize, STE, dequantize backward and
     # the GEMM-layout transposes on the quantizer's outputs
@@ -634,22 +652,22 @@ def breakdown(torch, tq, inp, iters=30, only=None):
         bench_op("dequant_" + kind, cfg, db, mk,
                  lambda b, kd=kd, gp=gp: check(L.tq_dequant_fp4_block(P(b["p"]), P(b["b"]), gp(b), N5, K5, kd,
                                                                       P(b["y"]), BF16, stream), "fp4 dequant"),
-                 n5 // 2 + n5 // gs)
+                 n5 // 2 + n5 // gs, mix=(4, 16, 1, n5 // 8))
         if kind == "nvfp4":
             mkx = lambda: mk(with_x=True)   # noqa: E731
             bench_op("quant_backward_" + kind, cfg, n5 * 6 + n5 // gs + 4, mkx,
                      lambda b: check(L.tq_quant_fp4_block_backward(P(b["x"]), BF16, P(b["b"]), P(b["g"]), N5, K5, 0,
                                                                    P(b["dy"]), P(b["y"]), stream), "nvfp4 ste"),
-                     n5 * 4 + n5 // gs)
+                     n5 * 4 + n5 // gs, mix=(32, 16, 1, n5 // 8))
             bench_op("dequant_backward_" + kind, cfg, n5 * 4 + n5 // gs + 4, mkx,
                      lambda b: check(L.tq_dequant_fp4_block_backward(P(b["dy"]), BF16, P(b["b"]), P(b["g"]), N5, K5, 0,
                                                                      P(b["y"]), stream), "nvfp4 dqb"),
-                     n5 * 2 + n5 // gs)
+                     n5 * 2 + n5 // gs, mix=(16, 16, 2, n5 // 8))
         tb = 2 * (n5 // 2 + n5 // gs)
         bench_op("transpose_for_gemm_" + kind, cfg, tb, mk,
                  lambda b, gs=gs: check(L.tq_fp4_transpose_for_gemm(P(b["p"]), P(b["b"]), N5, K5, gs, P(b["pt"]),
                                                                     P(b["bt"]), stream), "transpose"),
-                 tb // 2)
+                 tb // 2, mix=(16, 16, 1, tb // 32))
 
     # FP4 layout follow-ons on the NVFP4 weight: two weights (the quantized
     # weight and its row reversal) fused into one [2048, 28672] GEMM operand,
@@ -678,11 +696,12 @@ def breakdown(torch, tq, inp, iters=30, only=None):
         nn = (ctypes.c_int64 * 2)(N5, N5)
         check(L.tq_fp4_transpose_concat_for_gemm(2, pp, bb, nn, K5, 16, 128, P(b["pt"]), P(b["bt"]), None,
                                                  stream), "transpose concat")
-    bench_op("transpose_concat_for_gemm_nvfp4", cfgf, 4 * (pb + sbb), mkf, concat_t, 2 * (pb + sbb))
+    bench_op("transpose_concat_for_gemm_nvfp4", cfgf, 4 * (pb + sbb), mkf, concat_t, 2 * (pb + sbb),
+             mix=(16, 16, 1, 4 * (pb + sbb) // 32))
     bench_op("concat_rows_nvfp4", cfgf, 4 * (pb + sbb), mkf,
              lambda b: check(L.tq_fp4_concat_rows(P(b["p1"]), P(b["b1"]), sg5["g"], P(b["p2"]), P(b["b2"]), sg5["g"],
                                                   N5, N5, K5, P(b["po"]), P(b["bo"]), stream), "concat rows"),
-             2 * (pb + sbb))
+             2 * (pb + sbb), mix=(16, 16, 1, 4 * (pb + sbb) // 32))
     bench_op("predequant_to_fp8_nvfp4", "NVFP4 [14336,4096]", pb + sbb + n5, mkf,
              lambda b: check(L.tq_fp4_predequant_to_fp8(P(b["p1"]), P(b["b1"]), sg5["g"], N5, K5, 0, P(b["f8"]),
                                                         stream), "predequant"),
@@ -915,7 +934,7 @@ def main():
         print(json.dumps(res))
         return
     log("quantize: per-token s8 bf16 [8192,4096], steps=%d warmup=%d" % (args.steps, args.warmup))
-    quant, head, _ = run_quantizers(torch, tq, inp, args.steps, args.warmup, args.iters)
+    quant, head, qceil = run_quantizers(torch, tq, inp, args.steps, args.warmup, args.iters)
     nbytes, wall, ev_us = head
     value = nbytes * args.steps / wall / 1e9
     q = quant["per_token_s8"]
@@ -940,7 +959,7 @@ def main():
         "path": path,
     }
     if not args.no_breakdown:
-        line["breakdown"] = breakdown(torch, tq, inp, iters=args.iters)
+        line["breakdown"] = breakdown(torch, tq, inp, iters=args.iters, ceil_cache=qceil)
     if not args.no_cpu:
         log("cpu baseline (oracle)...")
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -319,9 +319,13 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = d[i] * s;
         } else {
+            // x, dy and the scale all in flight before any of them is used (the
+            // compiler otherwise issued the x load only after testing the scale)
+            const Raw8<FT> rx = load8<FT, true>(a, e), rd = load8<FT, true>(b, e);
+            __builtin_amdgcn_sched_barrier(0);
             float xv[8], d[8];
-            widen8<FT>(load8<FT, true>(a, e), xv);
-            widen8<FT>(load8<FT, true>(b, e), d);
+            widen8<FT>(rx, xv);
+            widen8<FT>(rd, d);
             const bool ok = scale_in_fast_range(s) & values_fast8(d) & codes_fast8(xv);
             float t[8], g[8];
             if (ok) {
