@@ -101,6 +101,8 @@ def test_fp8_partial_tiles(tq, orc, shape, xt, block):
     ((333, 777), "f16", None),             # scalar path, two passes
     ((16, 1024), "f32", 0.004),            # static: many saturated codes
     ((5, 7), "bf16", 1e-3),                # static, scalar path
+    ((300, 1000), "bf16", 0.02),           # static, vectors in a partial last step
+    ((257, 1024), "f16", None),            # two passes, partial last step of the encode
 ])
 def test_fp8_per_tensor(tq, orc, shape, xt, static):
     note("fp8 per tensor", shape, xt, static)

@@ -138,6 +138,12 @@ GROUP_CASES = [
     ((6, 10, 6), "f32", 1, 5, "u4", False),        # generic (C % 8 != 0)
     ((3, 36), "f16", 1, 12, "u8", False),          # generic (L % 8 != 0)
     ((33,), "f32", 0, 1, "s8", True),              # group size 1
+    # 4-bit dequantize variants: group map by division, with and without a
+    # zero point, column groups without one, and a ragged last step
+    ((9, 96), "f16", 1, 24, "u4", False),          # L = 24: not a power of two
+    ((37, 480), "bf16", 1, 96, "s4", True),        # L = 96, symmetric
+    ((130, 40), "f32", 0, 10, "s4", True),         # column groups, symmetric 4-bit
+    ((35, 1024), "f16", 1, 128, "u4", False),      # g = 128 with a partial last step
 ]
 
 
