@@ -12,9 +12,10 @@
 // Kernels:
 //   k_fp8_rows   blocks of 1 x bc (bc = 16..512, power of two): a team of
 //                bc/8 lanes per block, 8 blocks per team per launch row.
-//   k_fp8_tile   blocks of br x bc with bc = 8*T and br = NP * 256/T: one
-//                256-thread workgroup per tile, the tile in registers, the
-//                tile max through DPP, bpermute and LDS.
+//   k_fp8_tile   blocks of br x bc with bc = 8*T and br = NP * NT/T: one
+//                NT-thread workgroup per tile (512 for 128 x 128, else 256),
+//                the tile in registers, the tile max through DPP, bpermute
+//                and LDS.
 //   k_fp8_generic  any block shape, partial edge blocks included: one
 //                  workgroup per block, two passes.
 //   k_fp8_ew     dequant / STE / dequant-backward, elementwise, 16-byte I/O.
@@ -134,12 +135,12 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const void* __restrict__ x, in
 // Thread t covers columns (t % T) * 8 .. +8 and rows t / T + k * (256 / T),
 // k = 0..NP-1, of its tile.  (128 x 128 tiles over 512 or 1024 threads, with
 // 8 waves per SIMD resident instead of 5, measured the same or slower.)
-template <int FT, int T, int NP>
-__global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, int64_t cols, int64_t nbc,
-                                                  uint8_t* __restrict__ q, float* __restrict__ scale)
+template <int FT, int T, int NP, int NT = 256>
+__global__ __launch_bounds__(NT) void k_fp8_tile(const void* __restrict__ x, int64_t cols, int64_t nbc,
+                                                 uint8_t* __restrict__ q, float* __restrict__ scale)
 {
-    constexpr int RP = 256 / T;
-    __shared__ float wmax[4];
+    constexpr int RP = NT / T, NW = NT / 64;
+    __shared__ float wmax[NW];
     const int64_t tr = blockIdx.y, tc = blockIdx.x;
     const int t = threadIdx.x;
     const int64_t r0 = tr * (RP * NP) + t / T;
@@ -147,27 +148,29 @@ __global__ __launch_bounds__(256) void k_fp8_tile(const void* __restrict__ x, in
     Raw8<FT> raw[NP];
 #pragma unroll
     for (int k = 0; k < NP; ++k) raw[k] = load8<FT, (T >= 8)>(x, (r0 + (int64_t)k * RP) * cols + c0);
-    float v[NP][8];
     float a = 0.0f;
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
-        widen8<FT>(raw[k], v[k]);
+        float v[8];
+        widen8<FT>(raw[k], v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[k][i]));
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
     }
     a = team_max<64>(a);
     if ((t & 63) == 0) wmax[t >> 6] = a;
     __syncthreads();
-    a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    a = wmax[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) a = __builtin_fmaxf(a, wmax[i]);
     const FP p = fp8_params<FT>(a);
-    if (p.fast) {
+    // only the raw inputs live across the barrier; widening them again is
+    // cheaper than holding the binary32 copies
 #pragma unroll
-        for (int k = 0; k < NP; ++k)
-            st8<(T >= 16)>(q + (r0 + (int64_t)k * RP) * cols + c0, fp8_enc8<FT, true>(v[k], p));
-    } else {
-#pragma unroll
-        for (int k = 0; k < NP; ++k)
-            st8<(T >= 16)>(q + (r0 + (int64_t)k * RP) * cols + c0, fp8_enc8<FT, false>(v[k], p));
+    for (int k = 0; k < NP; ++k) {
+        float v[8];
+        widen8<FT>(raw[k], v);
+        st8<(T >= 16)>(q + (r0 + (int64_t)k * RP) * cols + c0,
+                       p.fast ? fp8_enc8<FT, true>(v, p) : fp8_enc8<FT, false>(v, p));
     }
     if (t == 0) scale[tr * nbc + tc] = p.s;
 }
@@ -653,7 +656,9 @@ static bool quant_fast(const void* x, int64_t rows, int64_t cols, int64_t br, in
     const dim3 grid((unsigned)(cols / bc), (unsigned)(rows / br));
     if (rows / br > 65535) return false;
     if (bc == 128 && br == 128) {
-        hipLaunchKernelGGL((k_fp8_tile<FT, 16, 8>), grid, dim3(256), 0, st, x, cols, cols / bc, q, scale);
+        // 512 threads of 4 rows x 8 columns each (52 VGPRs; 256 threads of 8 rows
+        // needed 84-89 and ran 1.4% slower)
+        hipLaunchKernelGGL((k_fp8_tile<FT, 16, 4, 512>), grid, dim3(512), 0, st, x, cols, cols / bc, q, scale);
         return true;
     }
     if (bc == 128 && br == 64) {
