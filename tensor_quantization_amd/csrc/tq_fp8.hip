@@ -255,6 +255,43 @@ static BlkIdx make_blkidx(int64_t n, int64_t cols, int64_t br, int64_t bc, int64
 }
 
 // Vector path (cols % 8 == 0 and bc % 8 == 0: the 8 elements share a block).
+// STE backward of one vector of 8: dx = (dy / s) where the recomputed E4M3
+// code of x / s is finite and below the saturating magnitude, else 0.
+template <int FT>
+__device__ __forceinline__ void fp8_ste8(const Raw8<FT>& rx, const Raw8<FT>& rd, float s, float o[8])
+{
+    float xv[8], d[8];
+    widen8<FT>(rx, xv);
+    widen8<FT>(rd, d);
+    const bool ok = scale_in_fast_range(s) & values_fast8(d) & codes_fast8(xv);
+    float t[8], g[8];
+    if (ok) {
+        const float y = rcp_rn(s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            t[i] = with_sign_of(div_q<FT>(xv[i], s, y), xv[i]);
+            g[i] = div_q<FT>(d[i], s, y);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            t[i] = xv[i] / s;
+            g[i] = d[i] / s;
+        }
+    }
+    const uint32_t c0 = e4m3_pack4(t[0], t[1], t[2], t[3]);
+    const uint32_t c1 = e4m3_pack4(t[4], t[5], t[6], t[7]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t c = ((i < 4 ? c0 : c1) >> ((i & 3) * 8)) & 0x7fu;
+        o[i] = g[i] * (c < 0x7eu ? 1.0f : 0.0f);
+    }
+}
+
+// Vectors of 8 per thread and grid step in the FP8 STE backward (one, with
+// the loads in flight as below, measured 2.5% slower).
+constexpr int FP8_STE_V = 2;
+
 // SHIFT >= 0: 1 x bc blocks with cols % bc == 0 and bc = 2^SHIFT, so the
 // block of element e is e >> SHIFT (no 64-bit divisions per vector).
 template <int OP, int FT>
@@ -312,48 +349,44 @@ __global__ __launch_bounds__(256) void k_fp8_ew(const void* __restrict__ a, cons
         }
         return;
     }
+    if constexpr (OP == OP_STE) {
+        // FP8_STE_V vectors per grid step; for each, x, dy and the scale are
+        // loaded (at a clamped index) ahead of a scheduling barrier, so all of
+        // them are in flight before any is used (the compiler otherwise issued
+        // the x load only after testing the scale); only the stores are guarded
+        for (int64_t base = (int64_t)blockIdx.x * 256 * FP8_STE_V + threadIdx.x; base < nvec;
+             base += (int64_t)gridDim.x * 256 * FP8_STE_V) {
+            Raw8<FT> rx[FP8_STE_V], rd[FP8_STE_V];
+            float sv[FP8_STE_V];
+#pragma unroll
+            for (int k = 0; k < FP8_STE_V; ++k) {
+                const int64_t vk = base + k * 256;
+                const int64_t e = (vk < nvec ? vk : nvec - 1) * 8;
+                sv[k] = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
+                rx[k] = load8<FT, true>(a, e);
+                rd[k] = load8<FT, true>(b, e);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            float o[FP8_STE_V][8];
+#pragma unroll
+            for (int k = 0; k < FP8_STE_V; ++k) fp8_ste8<FT>(rx[k], rd[k], sv[k], o[k]);
+#pragma unroll
+            for (int k = 0; k < FP8_STE_V; ++k) {
+                const int64_t vk = base + k * 256;
+                if (vk < nvec) store8<FT, 1>(out, vk * 8, o[k]);
+            }
+        }
+        return;
+    }
     for (int64_t vi = (int64_t)blockIdx.x * 256 + threadIdx.x; vi < nvec; vi += (int64_t)gridDim.x * 256) {
         const int64_t e = vi * 8;
         const float s = scale[shift >= 0 ? (e >> shift) : bi.cols ? bi.of(e) : fp8_block_of(e, cols, br, bc, nbc)];
-        float o[8];
-        if constexpr (OP == OP_DQB) {
-            float d[8];
-            widen8<FT>(load8<FT, true>(a, e), d);
+        // dequantize backward: dq = dy * scale
+        float o[8], d[8];
+        widen8<FT>(load8<FT, true>(a, e), d);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = d[i] * s;
-        } else {
-            // x, dy and the scale all in flight before any of them is used (the
-            // compiler otherwise issued the x load only after testing the scale)
-            const Raw8<FT> rx = load8<FT, true>(a, e), rd = load8<FT, true>(b, e);
-            __builtin_amdgcn_sched_barrier(0);
-            float xv[8], d[8];
-            widen8<FT>(rx, xv);
-            widen8<FT>(rd, d);
-            const bool ok = scale_in_fast_range(s) & values_fast8(d) & codes_fast8(xv);
-            float t[8], g[8];
-            if (ok) {
-                const float y = rcp_rn(s);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    t[i] = with_sign_of(div_q<FT>(xv[i], s, y), xv[i]);
-                    g[i] = div_q<FT>(d[i], s, y);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    t[i] = xv[i] / s;
-                    g[i] = d[i] / s;
-                }
-            }
-            const uint32_t c0 = e4m3_pack4(t[0], t[1], t[2], t[3]);
-            const uint32_t c1 = e4m3_pack4(t[4], t[5], t[6], t[7]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t c = ((i < 4 ? c0 : c1) >> ((i & 3) * 8)) & 0x7fu;
-                o[i] = g[i] * (c < 0x7eu ? 1.0f : 0.0f);
-            }
-        }
-        store8<FT, (OP == OP_DEQ || OP == OP_DQB) ? WT : 1>(out, e, o);
+        for (int i = 0; i < 8; ++i) o[i] = d[i] * s;
+        store8<FT, WT>(out, e, o);
     }
 }
 
@@ -691,7 +724,7 @@ static tq_status fp8_elementwise(const void* a, const void* b, int ft, int64_t r
         if (br == 1 && cols % bc == 0 && (bc & (bc - 1)) == 0)
             for (shift = 0; ((int64_t)1 << shift) < bc; ++shift) {}
         const BlkIdx bi = shift >= 0 ? BlkIdx{} : make_blkidx(n, cols, br, bc, nbc);
-        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256 * (OP == OP_DEQ ? DEQ_V : 1))),
+        TQ_FT_SWITCH(ft, hipLaunchKernelGGL((k_fp8_ew<OP, FTV>), dim3(grid_for(n / 8, 256 * (OP == OP_DEQ ? DEQ_V : OP == OP_STE ? FP8_STE_V : 1))),
                                             dim3(256), 0, st,
                                             a, b, n / 8, cols, br, bc, nbc, shift, bi, scale, out));
     } else {
