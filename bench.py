@@ -583,6 +583,26 @@ def breakdown(torch, tq, inp, iters=30, only=None, ceil_cache=None):
                                                     F16, stream), "c3 dequant"), n3 // 2 + (n3 // 128) * 5,
              mix=(4, 16, 1, n3 // 8))
 
+    # and its two backward rules on the same codes: STE (f16 x, dy -> dx) and
+    # dequantize backward (f16 dy -> dq)
+    def mk3x():
+        b = dict(x=dev_bits(inp.get("x:c3_per_group_u4_g128"), "f16", torch),
+                 dy=dev_bits(inp.get("dy:c3_per_group_u4_g128"), "f16", torch), q=E((N3, K3 // 2), u8),
+                 s=E((N3, K3 // 128), f32), z=E((N3, K3 // 128), u8), dx=E((N3, K3), f16))
+        check(L.tq_quant_per_group(P(b["x"]), F16, 2, shp3, 1, 128, U4, 0, 15, P(b["q"]), P(b["s"]), P(b["z"]),
+                                   stream), "c3 producer")
+        del b["q"]
+        return b
+    cfg3 = "f16 [11008,4096] per-group u4 g=128"
+    bench_op("quant_backward_per_group_u4_g128", cfg3, n3 * 6 + (n3 // 128) * 5, mk3x,
+             lambda b: check(L.tq_quant_per_group_backward(P(b["x"]), F16, 2, shp3, 1, 128, U4, 0, 15, P(b["s"]),
+                                                           P(b["z"]), P(b["dy"]), P(b["dx"]), stream), "c3 ste"),
+             n3 * 4 + (n3 // 128) * 5, mix=(32, 16, 1, n3 // 8))
+    bench_op("dequant_backward_per_group_g128", cfg3, n3 * 4 + (n3 // 128) * 4, mk3x,
+             lambda b: check(L.tq_dequant_per_group_backward(P(b["dy"]), F16, 2, shp3, 1, 128, P(b["s"]), P(b["dx"]),
+                                                             stream), "c3 dqb"),
+             n3 * 2 + (n3 // 128) * 4, mix=(16, 16, 2, n3 // 8))
+
     # FP8 1x128 activations bf16 [4096, 7168]; 128x128 weights bf16 [7168, 7168]
     for key, name in (("c4_fp8_act_1x128", "fp8_1x128"), ("c4_fp8_weight_128x128", "fp8_128x128")):
         R, C = shape(key)
@@ -628,6 +648,19 @@ def breakdown(torch, tq, inp, iters=30, only=None, ceil_cache=None):
              lambda b: check(L.tq_dequant_mxfp8(P(b["q"]), P(b["b"]), Rm, Cm, P(b["y"]), BF16, stream), "mxfp8 deq"),
              nm + nm // 32, mix=(8, 16, 1, nm // 8))
 
+    def mkm2():
+        b = mkm()
+        b["dy"] = dev_bits(inp.get("dy:c4_fp8_act_1x128"), "bf16", torch)
+        return b
+    bench_op("quant_backward_mxfp8", "bf16 [4096,7168] MXFP8", nm * 6 + nm // 32, mkm2,
+             lambda b: check(L.tq_quant_mxfp8_backward(P(b["x"]), BF16, P(b["b"]), Rm, Cm, P(b["dy"]), P(b["y"]),
+                                                       stream), "mxfp8 ste"),
+             nm * 4 + nm // 32, mix=(32, 16, 1, nm // 8))
+    bench_op("dequant_backward_mxfp8", "bf16 [4096,7168] MXFP8", nm * 4 + nm // 32, mkm2,
+             lambda b: check(L.tq_dequant_mxfp8_backward(P(b["dy"]), BF16, P(b["b"]), Rm, Cm, P(b["y"]), stream),
+                             "mxfp8 dqb"),
+             nm * 2 + nm // 32, mix=(16, 16, 2, nm // 8))
+
     # FP4 weight bf16 [14336, 4096]: dequantize, STE, dequantize backward and
     # the GEMM-layout transposes on the quantizer's outputs
     N5, K5 = shape("c5_fp4_weight")
@@ -653,16 +686,17 @@ def breakdown(torch, tq, inp, iters=30, only=None, ceil_cache=None):
                  lambda b, kd=kd, gp=gp: check(L.tq_dequant_fp4_block(P(b["p"]), P(b["b"]), gp(b), N5, K5, kd,
                                                                       P(b["y"]), BF16, stream), "fp4 dequant"),
                  n5 // 2 + n5 // gs, mix=(4, 16, 1, n5 // 8))
-        if kind == "nvfp4":
-            mkx = lambda: mk(with_x=True)   # noqa: E731
-            bench_op("quant_backward_" + kind, cfg, n5 * 6 + n5 // gs + 4, mkx,
-                     lambda b: check(L.tq_quant_fp4_block_backward(P(b["x"]), BF16, P(b["b"]), P(b["g"]), N5, K5, 0,
-                                                                   P(b["dy"]), P(b["y"]), stream), "nvfp4 ste"),
-                     n5 * 4 + n5 // gs, mix=(32, 16, 1, n5 // 8))
-            bench_op("dequant_backward_" + kind, cfg, n5 * 4 + n5 // gs + 4, mkx,
-                     lambda b: check(L.tq_dequant_fp4_block_backward(P(b["dy"]), BF16, P(b["b"]), P(b["g"]), N5, K5, 0,
-                                                                     P(b["y"]), stream), "nvfp4 dqb"),
-                     n5 * 2 + n5 // gs, mix=(16, 16, 2, n5 // 8))
+        mkx = lambda mk=mk: mk(with_x=True)   # noqa: E731
+        gb4 = 4 if kind == "nvfp4" else 0
+        bench_op("quant_backward_" + kind, cfg, n5 * 6 + n5 // gs + gb4, mkx,
+                 lambda b, kd=kd, gp=gp: check(L.tq_quant_fp4_block_backward(P(b["x"]), BF16, P(b["b"]), gp(b), N5, K5,
+                                                                             kd, P(b["dy"]), P(b["y"]), stream),
+                                               "fp4 ste"),
+                 n5 * 4 + n5 // gs, mix=(32, 16, 1, n5 // 8))
+        bench_op("dequant_backward_" + kind, cfg, n5 * 4 + n5 // gs + gb4, mkx,
+                 lambda b, kd=kd, gp=gp: check(L.tq_dequant_fp4_block_backward(P(b["dy"]), BF16, P(b["b"]), gp(b), N5,
+                                                                               K5, kd, P(b["y"]), stream), "fp4 dqb"),
+                 n5 * 2 + n5 // gs, mix=(16, 16, 2, n5 // 8))
         tb = 2 * (n5 // 2 + n5 // gs)
         bench_op("transpose_for_gemm_" + kind, cfg, tb, mk,
                  lambda b, gs=gs: check(L.tq_fp4_transpose_for_gemm(P(b["p"]), P(b["b"]), N5, K5, gs, P(b["pt"]),
@@ -754,6 +788,18 @@ def breakdown(torch, tq, inp, iters=30, only=None, ceil_cache=None):
         bench_op("fp4_linear_nvfp4", "bf16 [8192,4096] x nvfp4 [14336,4096]^T bf16 out", fb4, mkf4,
                  lambda b: check(L.tq_fp4_linear(P(b["x"]), BF16, P(b["p"]), P(b["b"]), P(b["g"]), 0, Mf, Nf, Kf,
                                                  P(b["y"]), BF16, stream), "fp4 linear"),
+                 Mf * Kf * 2 + Nf * Kf // 2, flops=2 * Mf * Nf * Kf, peak=BF16_PEAK_TFLOPS)
+    if not only or only == "fp4_linear_mxfp4":
+        Mf, Kf, Nf = 8192, 4096, 14336
+
+        def mkm4():
+            xf0 = dev_bits(inp.get("x:c2_per_token_s8"), "bf16", torch)
+            p, b_, _ = tq.tq_quant_fp4_block(dev_bits(inp.get("x:c5_fp4_weight"), "bf16", torch), "mxfp4")
+            return dict(x=xf0, p=p, b=b_, y=E((Mf, Nf), bf16))
+        fm4 = Mf * Kf * 2 + Nf * Kf // 2 + Nf * Kf // 32 + 2 * Mf * Nf
+        bench_op("fp4_linear_mxfp4", "bf16 [8192,4096] x mxfp4 [14336,4096]^T bf16 out", fm4, mkm4,
+                 lambda b: check(L.tq_fp4_linear(P(b["x"]), BF16, P(b["p"]), P(b["b"]), None, 1, Mf, Nf, Kf,
+                                                 P(b["y"]), BF16, stream), "fp4 linear mx"),
                  Mf * Kf * 2 + Nf * Kf // 2, flops=2 * Mf * Nf * Kf, peak=BF16_PEAK_TFLOPS)
     return out
 
