@@ -106,7 +106,7 @@ def nsets_for(read_bytes, set_bytes, cap_bytes=16 << 30):
     not allocate there, so reads alone must overflow it), and at least 1.2 GB
     in total; at most 64 sets (the tiny per-tensor workload is latency-bound
     and stays cache-resident) and cap_bytes of device memory."""
-    n = max(4, -(-2 * LLC_BYTES // max(1, read_bytes)), -(-int(1.2e9) // max(1, set_bytes)))
+    n = max(4, 1 - (-2 * LLC_BYTES // max(1, read_bytes)), -(-int(1.2e9) // max(1, set_bytes)))
     return max(2, min(n, 64, cap_bytes // max(1, set_bytes)))
 
 
