@@ -15,6 +15,8 @@
 // 24 bits across groups, so its error is bounded per block and never grows
 // with K.
 //
+// Two tiles: k_fp8_gemm_w (below) for M >= 256, k_fp8_gemm for smaller M.
+//
 // k_fp8_gemm: a 256-thread workgroup owns a 128 x 128 output tile; wave w
 // computes the 64 x 64 quarter (w / 2, w % 2) as 4 x 4 tiles of 16 x 16,
 // sixteen independent products per block, so the scale-and-accumulate of
@@ -67,6 +69,27 @@ __device__ __forceinline__ void dma4(const void* g, const lds_void* lds)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+// The same from a wave-uniform 64-bit base (SGPRs) plus a 32-bit lane
+// offset.  readfirstlane returns a signed int: each half is widened through
+// uint32_t, or a low word with bit 31 set would sign-extend into the high one.
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((size_t)p >> 32));
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, const lds_void* lds)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+                 "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, const lds_void* lds)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+                 "s"(m0) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -159,6 +182,139 @@ __global__ __launch_bounds__(256) void k_fp8_gemm(const uint8_t* __restrict__ qa
                 const int64_t col = n0 + wn * 64 + j * 16 + l16;
                 if (row < M) store1<YT>(y, row * N + col, acc[i][j][r]);
             }
+}
+
+// k_fp8_gemm_w: 256 x 128 output tile (M x N) per 256-thread workgroup.
+// Wave w owns rows 64 w .. + 63 and all 128 columns (4 x 8 tiles of 16 x 16).
+// The weight K-slice (128 rows x 128 bytes) is shared by the four waves
+// through two LDS stages; each wave's own 64 activation rows and their scales
+// come by DMA into a private LDS region one block ahead and move to
+// registers at the start of the block, which frees the region for the next
+// one.  The product is taken as D^T = W_j A_i^T, so element r of lane l is
+// y[16 i + l % 16][16 j + 4 (l / 16) + r]: one row scale per lane per tile
+// and 4 consecutive output columns per store.
+template <int YT>
+__global__ __launch_bounds__(256, 2) void k_fp8_gemm_w(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                                       const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                       int64_t M, int64_t K, int64_t N, void* __restrict__ y)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t ldsb[2][SLICE];       // weight slices
+    __shared__ __attribute__((aligned(16))) uint8_t ldsa[4][64 * GT];     // activation rows, one region per wave
+    __shared__ __attribute__((aligned(16))) float ldss[4][64];            // their scales
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * GT;
+    const int64_t nkb = K / GT;
+    const float* gsw = sw + (n0 / GT) * nkb;
+
+    // weight slice fill: lane writes LDS row 8 w + lane / 8 + 32 i (i < 4), slot
+    // lane % 8, from a wave-uniform row base and one 32-bit lane offset
+    const int frow = 8 * w + (lane >> 3);
+    const uint32_t fo = (uint32_t)((lane >> 3) * K + (((lane & 7) ^ swz_key(frow)) << 4));
+    const uint8_t* fb = qw + (n0 + 8 * w) * K;
+    // activation fill: instruction q writes region rows 8 q + lane / 8, slot lane % 8;
+    // rows past M re-read row M - 1 (their results are never stored)
+    const int64_t mloc = M - m0;                     // rows of this tile that exist (>= 1)
+    uint32_t oa[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const int64_t row = min_i64(64 * w + r, mloc - 1);
+        oa[q] = (uint32_t)(row * K + (((lane & 7) ^ swz_key(r)) << 4));
+    }
+    const uint32_t os = (uint32_t)(min_i64(64 * w + lane, mloc - 1) * nkb * 4);
+    const uint8_t* ga = qa + m0 * K;
+    const uint8_t* gs = reinterpret_cast<const uint8_t*>(sa + m0 * nkb);
+
+    auto issue_b = [&](int64_t kb) {
+        const int buf = (int)(kb & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16s(fb + (int64_t)32 * i * K + kb * GT, fo, (const lds_void*)&ldsb[buf][(32 * i + 8 * w) * GT]);
+    };
+    auto issue_a = [&](int64_t kb) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dma16s(ga + kb * GT, oa[q], (const lds_void*)&ldsa[w][8 * q * GT]);
+        dma4s(gs + kb * 4, os, (const lds_void*)&ldss[w][0]);
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{};
+
+    issue_b(0);
+    issue_a(0);
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        __builtin_amdgcn_s_waitcnt(0x70);          // vmcnt(0) lgkmcnt(0): this wave's loads of block kb are in
+        asm volatile("s_barrier" ::: "memory");    // every wave's share of the weight slice is in LDS
+        if (kb + 1 < nkb) issue_b(kb + 1);
+        v8i ac[4];
+        float c[4];
+        const float swv = gsw[kb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ar = i * 16 + l16;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(&ldsa[w][swz(ar, 2 * g4)]);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(&ldsa[w][swz(ar, 2 * g4 + 1)]);
+            ac[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            c[i] = ldss[w][ar] * swv;
+        }
+        // the region is refilled only after these reads have returned
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
+        if (kb + 1 < nkb) issue_a(kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* lb = ldsb[kb & 1];
+        uint4 bq[3][2];
+        auto read_b = [&](int j, uint4 (&q)[2]) {
+            const int br = j * 16 + l16;
+            q[0] = *reinterpret_cast<const uint4*>(&lb[swz(br, 2 * g4)]);
+            q[1] = *reinterpret_cast<const uint4*>(&lb[swz(br, 2 * g4 + 1)]);
+        };
+        // column j's products are issued before column j - 1's scale-and-add,
+        // so the matrix core never waits for the vector unit
+        read_b(0, bq[0]);
+        read_b(1, bq[1]);
+        v4f blk[2][4];
+#pragma unroll
+        for (int j = 0; j <= 8; ++j) {
+            if (j + 2 < 8) read_b(j + 2, bq[(j + 2) % 3]);
+            if (j < 8) {
+                const uint4 b0 = bq[j % 3][0], b1 = bq[j % 3][1];
+                const v8i bv = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    blk[j & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, ac[i], v4f{}, 0, 0, 0, 127, 0, 127);
+            }
+            if (j > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j - 1][r] = __builtin_fmaf(blk[(j - 1) & 1][i][r], c[i], acc[i][j - 1][r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + 64 * w + 16 * i + l16;
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t e = row * N + n0 + 16 * j + 4 * g4;
+            if constexpr (YT == F32)
+                *reinterpret_cast<uint4*>(static_cast<float*>(y) + e) =
+                    make_uint4(as_u(acc[i][j][0]), as_u(acc[i][j][1]), as_u(acc[i][j][2]), as_u(acc[i][j][3]));
+            else
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + e) =
+                    make_uint2(narrow2<YT>(acc[i][j][0], acc[i][j][1]), narrow2<YT>(acc[i][j][2], acc[i][j][3]));
+        }
+    }
 }
 
 // k_w8a8_gemm: the W8A8 quantized linear on the same tile and load pipeline.
@@ -557,6 +713,16 @@ tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* q
         const int64_t nbytes = M * N * (y_dtype == TQ_F32 ? 4 : 2);
         hipLaunchKernelGGL(k_zero_bytes, dim3((unsigned)std::min<int64_t>((nbytes + 255) / 256, 1 << 20)), dim3(256),
                            0, st, static_cast<uint8_t*>(y), nbytes);
+        return launch_status();
+    }
+    if (M >= 256 && K <= ((int64_t)1 << 24) && (M + 255) / 256 <= 65535) {
+        // the 256 x 128 tile (its 32-bit lane offsets need K <= 2^24)
+        const dim3 g2((unsigned)(N / GT), (unsigned)((M + 255) / 256));
+        switch (y_dtype) {
+        case TQ_F32: hipLaunchKernelGGL(k_fp8_gemm_w<F32>, g2, dim3(256), 0, st, qa, sa, qw, sw, M, K, N, y); break;
+        case TQ_F16: hipLaunchKernelGGL(k_fp8_gemm_w<F16>, g2, dim3(256), 0, st, qa, sa, qw, sw, M, K, N, y); break;
+        default: hipLaunchKernelGGL(k_fp8_gemm_w<BF16>, g2, dim3(256), 0, st, qa, sa, qw, sw, M, K, N, y); break;
+        }
         return launch_status();
     }
     switch (y_dtype) {

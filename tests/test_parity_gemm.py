@@ -101,7 +101,8 @@ def _operands(tq, M, N, K, seed):
 
 @pytest.mark.parametrize("M,N,K,yt", [(128, 128, 128, "f32"), (256, 384, 512, "f32"), (128, 256, 1024, "bf16"),
                                       (384, 128, 256, "f16"), (128, 128, 7168, "f32"), (100, 256, 512, "f32"),
-                                      (1, 128, 1024, "bf16"), (300, 128, 256, "f32")])
+                                      (1, 128, 1024, "bf16"), (300, 128, 256, "f32"), (257, 256, 384, "bf16"),
+                                      (520, 128, 640, "f32"), (511, 256, 256, "f16"), (1024, 384, 1152, "bf16")])
 def test_fp8_block_gemm(tq, orc, M, N, K, yt):
     """Operands from the FP8 quantizers (1 x 128 activations, 128 x 128 weights)."""
     note("fp8 gemm", M, N, K, yt)
@@ -132,6 +133,19 @@ def test_fp8_block_gemm_narrow_exponents(tq, orc, M, N, K):
     check(from_dev(y), ref, yabs, intra, K, "f32")
 
 
+@pytest.mark.parametrize("yt", ["f32", "bf16"])
+def test_fp8_block_gemm_tiles_agree(tq, yt):
+    """M >= 256 runs the 256 x 128 tile, smaller M the 128 x 128 one; both
+    take the same block sums and binary32 scale-and-add steps in the same
+    order, so the first rows of a 300-row product equal, bit for bit, the
+    product of those rows alone."""
+    note("fp8 gemm tiles agree", yt)
+    qa, sa, qw, sw = _operands(tq, 300, 256, 896, 77)
+    big = from_dev(tq.tq_fp8_block_gemm(qa, sa, qw, sw, out_dtype=TORCH[yt]))
+    small = from_dev(tq.tq_fp8_block_gemm(qa[:200].contiguous(), sa[:200].contiguous(), qw, sw, out_dtype=TORCH[yt]))
+    assert_same(big[:200], small, "rows 0..199")
+
+
 def test_fp8_block_gemm_full_size_sampled(tq, orc):
     """The c4 operands: activations bf16 [4096, 7168] (1 x 128) times weights
     bf16 [7168, 7168] (128 x 128), bf16 out as timed: rows sampled for the
@@ -142,7 +156,7 @@ def test_fp8_block_gemm_full_size_sampled(tq, orc):
     qa, sa = tq.tq_quant_fp8_block(to_dev(x, "bf16"), 1, 128)
     qw, sw = tq.tq_quant_fp8_block(to_dev(w, "bf16"), 128, 128)
     y = tq.tq_fp8_block_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16)
-    rows = np.array([0, 1, 127, 128, 2049, 4095])
+    rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 2049, 4095])
     QA, SA, QW, SW = from_dev(qa)[rows], from_dev(sa)[rows], from_dev(qw), from_dev(sw)
     ref, yabs = orc.fp8_block_gemm(QA, SA, QW, SW)
     check(_as_f32(y, "bf16")[rows], ref, yabs, intra_bound(orc, QA, SA, QW, SW), 7168, "bf16")
