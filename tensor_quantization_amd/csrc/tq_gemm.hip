@@ -496,7 +496,8 @@ __global__ __launch_bounds__(512) void k_w8a8_gemm_256(const int8_t* __restrict_
         }
 }
 
-// k_fp4_linear: bf16 activations x [M, K] times an FP4 weight in the
+// k_fp4_linear (M < 256; k_fp4_linear_w below for larger M): bf16
+// activations x [M, K] times an FP4 weight in the
 // quantizer's own layout (packed [N, K/2] low nibble first, block scales
 // [N, K/gs]): K-contiguous rows are what the matrix-core B operand wants, so
 // the GEMM reads that layout directly and needs no transposed twin.  Same
@@ -688,6 +689,152 @@ __global__ __launch_bounds__(256) void k_fp4_linear(const uint16_t* __restrict__
             }
 }
 
+// k_fp4_linear_w: the FP4 linear on a 256 x 128 tile (M x N), the FP8
+// GEMM's wide-tile scheme: wave w owns rows 64 w .. + 63 and all 128
+// columns; its activation rows (128 bytes per 64-K block) come by DMA into a
+// private LDS region one block ahead and move to registers at the start of
+// the block.  The weight slice is expanded once per workgroup exactly as in
+// k_fp4_linear (two LDS buffers, fetched two blocks ahead in alternating
+// register sets), now for twice the rows of activations.  Same arithmetic:
+// two chained bf16 steps from zero per block, the block sum added in
+// binary32; the product is taken as D^T, 4 consecutive outputs per lane.
+template <int KIND, int YT>
+__global__ __launch_bounds__(256, 2) void k_fp4_linear_w(const uint16_t* __restrict__ x,
+                                                         const uint8_t* __restrict__ packed,
+                                                         const uint8_t* __restrict__ bscale,
+                                                         const float* __restrict__ global_scale, int64_t M, int64_t K,
+                                                         int64_t N, void* __restrict__ y)
+{
+    constexpr int GS = KIND == FP4_NV ? 16 : 32;
+    constexpr int SPB = FKB / GS;        // scale bytes per weight row per block
+    __shared__ __attribute__((aligned(16))) uint8_t lw[2][GT * 2 * FKB];     // expanded weights
+    __shared__ __attribute__((aligned(16))) uint8_t lx[4][64 * 2 * FKB];     // activation rows, one region per wave
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * GT;
+    const int64_t nkb = K / FKB;
+    const float sg = KIND == FP4_NV ? *global_scale : 1.0f;
+
+    // activation fill: instruction q writes region rows 8 q + lane / 8, slot
+    // lane % 8; rows past M re-read row M - 1 (their results are never stored)
+    const int64_t mloc = M - m0;
+    uint32_t oa[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        oa[q] = (uint32_t)(min_i64(64 * w + r, mloc - 1) * (2 * K) + (((lane & 7) ^ swz_key(r)) << 4));
+    }
+    const uint8_t* ga = reinterpret_cast<const uint8_t*>(x) + m0 * (2 * K);
+    auto issue_a = [&](int64_t kb) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dma16s(ga + kb * (2 * FKB), oa[q], (const lds_void*)&lx[w][8 * q * GT]);
+    };
+
+    // weight expansion: thread t owns half h = t % 2 of weight row r = t / 2 (32 values = chunks 4h .. 4h+3)
+    const int wr = t >> 1, wh = t & 1;
+    const uint8_t* fw = packed + (n0 + wr) * (K / 2) + wh * 16;
+    const uint8_t* fsc = bscale + (n0 + wr) * (K / GS);
+    auto fetch_w = [&](int64_t kb, uint4& pk, uint32_t& sbytes) {
+        pk = *reinterpret_cast<const uint4*>(fw + kb * (FKB / 2));
+        sbytes = KIND == FP4_NV ? *reinterpret_cast<const uint32_t*>(fsc + kb * SPB)
+                                : (uint32_t)*reinterpret_cast<const uint16_t*>(fsc + kb * SPB);
+    };
+    auto expand_w = [&](int buf, const uint4& pk, uint32_t sbytes) {
+        const uint32_t d[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float sc = KIND == FP4_NV ? e4m3_val(sbytes >> (8 * (2 * wh + (c >> 1))), 0)
+                                            : __uint_as_float(((sbytes >> (8 * wh)) & 0xff) << 23);
+            *reinterpret_cast<uint4*>(&lw[buf][swz(wr, 4 * wh + c)]) = fp4_expand8<KIND>(d[c], sc);
+        }
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{};
+
+    auto step = [&](int64_t kb, const uint4& pkx, uint32_t sbx, uint4& pkf, uint32_t& sbf) {
+        __builtin_amdgcn_s_waitcnt(0x70);    // vmcnt(0) lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        v8bf ac[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                ac[i][s] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&lx[w][swz(16 * i + l16, 4 * s + g4)]));
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the region is refilled only after these reads
+        if (kb + 1 < nkb) issue_a(kb + 1);
+        fetch_w(kb + 2 < nkb ? kb + 2 : nkb - 1, pkf, sbf);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* lb = lw[kb & 1];
+        uint4 bq[2][2];
+        auto read_b = [&](int j, uint4 (&q)[2]) {
+            q[0] = *reinterpret_cast<const uint4*>(&lb[swz(16 * j + l16, g4)]);
+            q[1] = *reinterpret_cast<const uint4*>(&lb[swz(16 * j + l16, 4 + g4)]);
+        };
+        read_b(0, bq[0]);
+        v4f blk[2][4];
+#pragma unroll
+        for (int j = 0; j <= 8; ++j) {
+            if (j + 1 < 8) read_b(j + 1, bq[(j + 1) & 1]);
+            if (j < 8) {
+                const v8bf b0 = __builtin_bit_cast(v8bf, bq[j & 1][0]), b1 = __builtin_bit_cast(v8bf, bq[j & 1][1]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) blk[j & 1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, ac[i][0], v4f{}, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    blk[j & 1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, ac[i][1], blk[j & 1][i], 0, 0, 0);
+            }
+            if (j > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j - 1][r] = acc[i][j - 1][r] + blk[(j - 1) & 1][i][r];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the last block expands a repeat of itself into a buffer no one reads again
+        expand_w((int)(kb & 1) ^ 1, pkx, sbx);
+    };
+
+    uint4 pka, pkb;
+    uint32_t sba, sbb;
+    issue_a(0);
+    fetch_w(0, pka, sba);
+    expand_w(0, pka, sba);
+    fetch_w(nkb > 1 ? 1 : 0, pka, sba);
+    // one step per iteration (the two-step loop of k_fp4_linear spills here):
+    // the set fetched during a block becomes the next block's expansion
+    // source by a register copy at its end, a block after its fetch
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        step(kb, pka, sba, pkb, sbb);
+        pka = pkb;
+        sba = sbb;
+    }
+    __builtin_amdgcn_s_waitcnt(0x70);        // nothing in flight past the last block
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + 64 * w + 16 * i + l16;
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t e = row * N + n0 + 16 * j + 4 * g4;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = KIND == FP4_NV ? acc[i][j][r] * sg : acc[i][j][r];   // NVFP4 per-tensor scale
+            if constexpr (YT == F32)
+                *reinterpret_cast<uint4*>(static_cast<float*>(y) + e) = make_uint4(as_u(v[0]), as_u(v[1]), as_u(v[2]), as_u(v[3]));
+            else
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + e) = make_uint2(narrow2<YT>(v[0], v[1]), narrow2<YT>(v[2], v[3]));
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_zero_bytes(uint8_t* __restrict__ p, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
@@ -786,6 +933,23 @@ tq_status tq_fp4_linear(const void* x, int x_dtype, const uint8_t* packed, const
         return launch_status();
     }
     const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (M >= 256 && K <= ((int64_t)1 << 22) && (M + 255) / 256 <= 65535) {
+        // the 256 x 128 tile (its 32-bit lane offsets need K <= 2^22)
+        const dim3 g2((unsigned)(N / GT), (unsigned)((M + 255) / 256));
+#define TQ_FP4W_LAUNCH(KD, YD) \
+    hipLaunchKernelGGL((k_fp4_linear_w<KD, YD>), g2, dim3(256), 0, st, xs, packed, block_scale, global_scale, M, K, N, y)
+        if (kind == TQ_NVFP4) {
+            if (y_dtype == TQ_F32) TQ_FP4W_LAUNCH(FP4_NV, F32);
+            else if (y_dtype == TQ_F16) TQ_FP4W_LAUNCH(FP4_NV, F16);
+            else TQ_FP4W_LAUNCH(FP4_NV, BF16);
+        } else {
+            if (y_dtype == TQ_F32) TQ_FP4W_LAUNCH(FP4_MX, F32);
+            else if (y_dtype == TQ_F16) TQ_FP4W_LAUNCH(FP4_MX, F16);
+            else TQ_FP4W_LAUNCH(FP4_MX, BF16);
+        }
+#undef TQ_FP4W_LAUNCH
+        return launch_status();
+    }
     const dim3 grid((unsigned)(N / GT), (unsigned)((M + GT - 1) / GT));
 #define TQ_FP4_LAUNCH(KD, YD) \
     hipLaunchKernelGGL((k_fp4_linear<KD, YD>), grid, dim3(256), 0, st, xs, packed, block_scale, global_scale, M, K, N, y)

@@ -232,7 +232,7 @@ def test_w8a8_linear_full_size_sampled(tq, orc):
     w = workloads.make_input("c3_per_group_u4_g128")
     qx, sx, qw, sw = _w8a8_operands(tq, x, "bf16", w, "f16")
     y = tq.tq_w8a8_linear(qx, sx, qw, sw, out_dtype=torch.bfloat16)
-    rows = np.array([0, 1, 127, 128, 4097, 8191])
+    rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 4097, 8191])
     ref = orc.w8a8_linear(_i8(qx)[rows], from_dev(sx)[rows], _i8(qw), from_dev(sw), "bf16")
     assert_same(from_dev(y)[rows], ref, "y")
 
@@ -277,7 +277,8 @@ def _fp4_weight(tq, w, kind):
 @pytest.mark.parametrize("kind", ["nvfp4", "mxfp4"])
 @pytest.mark.parametrize("M,N,K,yt", [(128, 128, 64, "f32"), (256, 256, 512, "f32"), (100, 384, 1024, "bf16"),
                                       (1, 128, 4096, "f16"), (300, 128, 4096, "f32"), (128, 128, 192, "f32"),
-                                      (200, 256, 320, "bf16")])
+                                      (200, 256, 320, "bf16"), (257, 256, 320, "bf16"), (520, 128, 640, "f16"),
+                                      (1024, 256, 1024, "bf16")])
 def test_fp4_linear(tq, orc, kind, M, N, K, yt):
     """bf16 activations (1% outlier columns x20) times an FP4 weight quantized
     on the GPU from bf16 ~N(0, 0.02).  The kernel walks K in pairs of 64-wide
@@ -291,6 +292,19 @@ def test_fp4_linear(tq, orc, kind, M, N, K, yt):
     check_fp4(_as_f32(y, yt), ref, yabs, K, yt)
 
 
+@pytest.mark.parametrize("kind", ["nvfp4", "mxfp4"])
+def test_fp4_linear_tiles_agree(tq, kind):
+    """M >= 256 runs the 256 x 128 tile, smaller M the 128 x 128 one: the
+    same block sums and binary32 adds in the same order, so the first rows
+    of a 300-row product equal, bit for bit, the product of those rows alone."""
+    note("fp4 linear tiles agree", kind)
+    x = to_dev(workloads.normal((300, 960), 1.0, 91, "bf16"), "bf16")
+    packed, bs, sg = _fp4_weight(tq, workloads.normal((256, 960), 0.02, 92, "bf16"), kind)
+    big = from_dev(tq.tq_fp4_linear(x, packed, bs, sg, kind, out_dtype=torch.float32))
+    small = from_dev(tq.tq_fp4_linear(x[:200].contiguous(), packed, bs, sg, kind, out_dtype=torch.float32))
+    assert_same(big[:200], small, "rows 0..199")
+
+
 def test_fp4_linear_full_size_sampled(tq, orc):
     """The bf16 [8192, 4096] activations times the NVFP4 weight workload
     [14336, 4096], bf16 out as timed: rows sampled for the oracle."""
@@ -299,7 +313,7 @@ def test_fp4_linear_full_size_sampled(tq, orc):
     w = workloads.make_input("c5_fp4_weight")
     packed, bs, sg = _fp4_weight(tq, w, "nvfp4")
     y = tq.tq_fp4_linear(to_dev(x, "bf16"), packed, bs, sg, "nvfp4", out_dtype=torch.bfloat16)
-    rows = np.array([0, 1, 127, 128, 4097, 8191])
+    rows = np.array([0, 1, 63, 64, 127, 128, 255, 256, 4097, 8191])
     ref, yabs = orc.fp4_linear(x[rows], from_dev(packed), from_dev(bs), from_dev(sg), "nvfp4")
     check_fp4(_as_f32(y, "bf16")[rows], ref, yabs, 4096, "bf16")
 
