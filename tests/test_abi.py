@@ -158,6 +158,10 @@ def test_gemm_validation(tq):
     assert L.tq_fp4_linear(A, 2, A, C, None, 0, 128, 128, 64, B, 2, None) == INV  # NVFP4 needs s_g
     assert L.tq_fp4_linear(A, 2, A, C, C, 4, 128, 128, 64, B, 2, None) == INV     # bad kind
     assert L.tq_fp4_linear(MIS, 2, A, C, C, 1, 128, 128, 64, B, 2, None) == ALIGN
+    # outputs are stored four elements at a time: y aligned to 4 elements
+    assert L.tq_fp8_block_gemm(A, C, A, C, 128, 128, 128, P(0x20008), 0, None) == ALIGN   # f32 y on 8 bytes
+    assert L.tq_w8a8_linear(A, C, A, C, 128, 128, 128, P(0x20004), 2, None) == ALIGN       # bf16 y on 4 bytes
+    assert L.tq_fp4_linear(A, 2, A, C, C, 1, 128, 128, 64, P(0x20002), 1, None) == ALIGN   # f16 y on 2 bytes
 
 
 def test_stream_mix_validation(tq):

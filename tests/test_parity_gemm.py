@@ -204,13 +204,13 @@ def test_w8a8_linear(tq, orc, M, N, K, yt):
     assert_same(from_dev(y), orc.w8a8_linear(_i8(qx), from_dev(sx), _i8(qw), from_dev(sw), yt), "y")
 
 
-@pytest.mark.parametrize("N", [128, 256])
-def test_w8a8_linear_extreme_codes(tq, orc, N):
+@pytest.mark.parametrize("M,N", [(128, 128), (128, 256), (300, 128), (300, 256)])
+def test_w8a8_linear_extreme_codes(tq, orc, M, N):
     """All codes at -128 / 127 / 0 patterns: the largest integer sums, and
     sums past 2^24 that the conversion to binary32 must round to nearest
-    (both tile kernels)."""
-    note("w8a8 extreme", N)
-    M, K = 128, 4096
+    (every tile kernel: M >= 256 takes the 256-row tile)."""
+    note("w8a8 extreme", M, N)
+    K = 4096
     rng = np.random.default_rng(7)
     QX = rng.choice(np.array([-128, 127, 0, -127], np.int8), (M, K))
     QW = rng.choice(np.array([-128, 127, 1], np.int8), (N, K))
