@@ -11,8 +11,9 @@ Every function states the definition it follows in ``tq_oracle.c``; the
 readings taken where the pages are silent are documented there.  Functions
 pinned to outside facts are listed in the tests (``tests/test_oracle_*.py``);
 the choices the pages leave open (NVFP4 scale bits, MX clipping, the
-asymmetric formula, degenerate groups) are pinned only by internal
-invariants -- "parity unpinned" against any outside source.
+asymmetric formula, degenerate groups) have no printed value to compare
+with and are pinned by brute-force re-derivation on tiny tensors, closed
+forms and special cases there.
 """
 from __future__ import annotations
 

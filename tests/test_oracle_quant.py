@@ -8,9 +8,9 @@ within half a step, the STE mask), granularity identities, row independence
 and re-quantization idempotence.
 
 Readings that no outside source fixes -- the asymmetric zero-point formula,
-the NVFP4 two-level scale bits, MX clipping, degenerate groups -- are checked
-only through internal invariants here ("parity unpinned" against any
-outside implementation).
+the NVFP4 two-level scale bits, MX clipping, degenerate groups -- are pinned
+here by the brute-force re-derivation and by closed forms and special cases;
+no printed value exists to compare them with.
 """
 import itertools
 import zlib
