@@ -372,13 +372,22 @@ __device__ __forceinline__ void tile_load(const TileAt& T, uint4 w[TR_LOADS])
     }
 }
 
+// LDS dword column c of tile row r sits at r * TR_PITCH + (c ^ tr_swz(r)).
+// The read-out has sixteen row groups 16 m apart in one wave instruction; with
+// the 65-dword pitch alone rows 64 apart share banks (4 lanes per bank), and
+// flipping column bits 2-3 by (r / 64) % 4 spreads them over distinct banks.
+// The stage writes stay conflict-free: the flip moves whole 4-dword chunks
+// (NVFP4 / MXFP4 weight transpose 12.7 / 12.3 -> 12.3 / 11.8 us).
+__device__ __forceinline__ int tr_swz(int r) { return 4 * ((r >> 6) & 3); }
+
 __device__ __forceinline__ void tile_stage(const uint4 w[TR_LOADS], uint32_t* tile)
 {
     const int t = threadIdx.x;
     constexpr int TPR = TRC / 16, RPP = 256 / TPR;
 #pragma unroll
     for (int k = 0; k < TR_LOADS; ++k) {
-        uint32_t* row = tile + (t / TPR + RPP * k) * TR_PITCH + (t % TPR) * 4;
+        const int r = t / TPR + RPP * k;
+        uint32_t* row = tile + r * TR_PITCH + (((t % TPR) * 4) ^ tr_swz(r));
         row[0] = w[k].x;
         row[1] = w[k].y;
         row[2] = w[k].z;
@@ -392,13 +401,14 @@ __device__ __forceinline__ void tile_store(const TileAt& T, const uint32_t* tile
     for (int p = 0; p < TR_OUTS; ++p) {
         const int t = threadIdx.x + 256 * p;
         const int m = t % (TRR / 16), d = t / (TRR / 16);
+        const int ds = d ^ tr_swz(16 * m);      // rows 16m .. 16m + 15 share the flip
         uint32_t o[4][4];                       // o[c][qd]: output row 4d+c, bytes 4*qd.. of this 16-byte piece
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
             const int rb = 16 * m + 4 * qd;
             uint32_t tr[4];
-            transpose4x4(tile[(rb + 0) * TR_PITCH + d], tile[(rb + 1) * TR_PITCH + d],
-                         tile[(rb + 2) * TR_PITCH + d], tile[(rb + 3) * TR_PITCH + d], tr);
+            transpose4x4(tile[(rb + 0) * TR_PITCH + ds], tile[(rb + 1) * TR_PITCH + ds],
+                         tile[(rb + 2) * TR_PITCH + ds], tile[(rb + 3) * TR_PITCH + ds], tr);
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[c][qd] = tr[c];
         }
