@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one op alone (profiling)")
-    ap.add_argument("--iters", type=int, default=30, help="launches per op outside the headline")
+    ap.add_argument("--iters", type=int, default=100, help="timed launches per op outside the headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy 10 times (scales the HBM byte counters)")
     ap.add_argument("--trace-summary", default=None, help="summarize rocprofv3 kernel-trace CSVs under DIR")
@@ -125,7 +125,7 @@ def check(rc, what):
         raise RuntimeError("%s failed with status %d" % (what, rc))
 
 
-def time_launches(torch, launch, sets, iters, warmup=3):
+def time_launches(torch, launch, sets, iters, warmup=20):
     """Mean launch time (us) of `iters` back-to-back launches rotating over
     `sets`, from one HIP event pair on the launch stream.  The untimed warmup
     launches touch every set once, so no timed launch is the first GPU access
@@ -346,7 +346,7 @@ def run_quantizers(torch, tq, inp, steps, warmup, iters, only=None):
 
 
 # ------------------------------------------------------------------ ceilings
-def stream_ceiling(torch, tq, in_b, out_b, policy, nthr, iters=30):
+def stream_ceiling(torch, tq, in_b, out_b, policy, nthr, iters=100):
     """The streaming ceiling of one access mix at one size: the best of the
     stream kernel with 1, 2 and 4 units per lane and, for 16-byte stores, both
     non-temporal store policies (each shape's figure kept)."""
@@ -453,7 +453,7 @@ def run_path(torch, tq, inp, steps):
 
 
 # ------------------------------------------------------------------ breakdown
-def breakdown(torch, tq, inp, iters=30, only=None, ceil_cache=None):
+def breakdown(torch, tq, inp, iters=100, only=None, ceil_cache=None):
     """Every other op timed alone; each buffer set holds what the op's
     producer (the matching quantize call) wrote.  A streaming op with a
     `mix` (bytes read and written per unit, store policy, units at its size)
