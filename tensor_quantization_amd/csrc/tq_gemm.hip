@@ -66,6 +66,31 @@ __device__ __forceinline__ int swz8_key(int row)
 }
 __device__ __forceinline__ int swz8(int row, int chunk) { return row * GT + ((chunk ^ swz8_key(row)) << 4); }
 
+// Tile order of the 256 x 128 kernels.  Workgroup i of a launch goes to XCD
+// i % 8 (each XCD has its own L2) as that XCD's (i / 8)-th workgroup.  The
+// launch index is renumbered so that each XCD takes one contiguous run of
+// tiles, walked in slabs of GN = min(ceil(column tiles / 8), 16) column tiles
+// (column tile fastest, then the row tile): the ~64 workgroups resident on an
+// XCD at a time then share GN weight slices and a few activation row tiles in
+// that XCD's L2.  When the column tiles are a multiple of 8 this is the slab
+// each XCD already had in launch order; otherwise launch order scattered every
+// column tile over every XCD (W8A8 on [8192,4096] x [11008,4096]: HBM-side
+// reads 1.77 GB -> 0.9 GB per launch).  A bijection of the tile grid: the
+// results do not change, only which workgroup computes which tile.
+__device__ __forceinline__ void wide_tile(int64_t& m0, int64_t& n0)
+{
+    const int64_t nt = gridDim.x, mt = gridDim.y, T = nt * mt;
+    const int64_t i = (int64_t)blockIdx.y * nt + blockIdx.x;
+    const int64_t xcd = i % 8, loc = i / 8, q = T / 8, r = T % 8;
+    const int64_t L = xcd < r ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
+    const int64_t gn8 = (nt + 7) / 8, GN = gn8 < 16 ? gn8 : 16;
+    const int64_t per = GN * mt, first = (L / per) * GN;
+    const int64_t gsz = nt - first < GN ? nt - first : GN;
+    const int64_t w = L % per;
+    n0 = (first + w % gsz) * GT;
+    m0 = (w / gsz) * 256;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global -> LDS loads, issued from asm so that the compiler adds no
@@ -221,7 +246,8 @@ __global__ __launch_bounds__(256, 2) void k_fp8_gemm_w(const uint8_t* __restrict
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
-    const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * GT;
+    int64_t m0, n0;
+    wide_tile(m0, n0);
     const int64_t nkb = K / GT;
     const float* gsw = sw + (n0 / GT) * nkb;
 
@@ -441,7 +467,8 @@ __global__ __launch_bounds__(256, 2) void k_w8a8_gemm_w(const int8_t* __restrict
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
-    const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * GT;
+    int64_t m0, n0;
+    wide_tile(m0, n0);
     const int64_t nkb = K / GT;
 
     // fills as in k_fp8_gemm_w: weight rows 8 w + lane / 8 + 32 i, activation
@@ -764,7 +791,8 @@ __global__ __launch_bounds__(256, 2) void k_fp4_linear_w(const uint16_t* __restr
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int g4 = lane >> 4, l16 = lane & 15;
-    const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * GT;
+    int64_t m0, n0;
+    wide_tile(m0, n0);
     const int64_t nkb = K / FKB;
     const float sg = KIND == FP4_NV ? *global_scale : 1.0f;
 
